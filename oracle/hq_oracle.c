@@ -1,0 +1,453 @@
+/*
+ * hq_oracle.c -- plain, slow CPU oracle for the randomized Hadamard rotation
+ * fused with symmetric per-row low-bit quantization.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code, header, table or constant with
+ * the HIP kernels.
+ *
+ * Everything is computed in fp64 with explicit loops and no blocking, fusion
+ * or reordering beyond the definitions below.  Pages cited:
+ *   [HQA] "哈特曼旋转，轻量级QAT，流式注意力" (Q&A post on Hadamard rotation of
+ *         Q/K), section 1.
+ *   [QT]  "手把手教你用QuaRot实现LLM的4位量化：从原理到代码实践" (QuaRot
+ *         tutorial), sections 2.1, 2.2 and 4.2.
+ *   [RQ]  "旋转量化：大模型低比特量化中的离群值克星" (rotation-quantization
+ *         blog), sections 1.1, 2.1 and 2.2.
+ *   [MS]  "QuaRot：基于旋转的离群值抑制算法说明" (msModelSlim QuaRot page),
+ *         section "原理" (principle) and the YAML field table.
+ *
+ * Definitions followed (all readings of the pages are listed in the
+ * repository's design notes):
+ *   H_1 = [1];  H_2m = [[H_m, H_m], [H_m, -H_m]]     Sylvester doubling,
+ *        entries +-1, normalised once by 1/sqrt(b)     ([RQ] 2.1, [HQA] 1)
+ *   u = x * s (elementwise sign flip, s shared by every row)   ([QT] 2.1)
+ *   for each block k of b consecutive elements:  x'_blk = u_blk . H_b / sqrt(b)
+ *        (block-diagonal rotation for widths that are not one power of two,
+ *         [RQ] 2.1; b == n is the full rotation)
+ *   m = max_i |x'_i| over the whole row; scale = m / qmax, qmax = 2^(bits-1)-1
+ *   q_i = clamp(round_half_even(x'_i / scale), -qmax, qmax)   ([RQ] 2.2, [HQA] 1)
+ *   INT4 storage: two codes per byte, element 2j in the low nibble, 4-bit
+ *   two's complement ([QT] 2.2 gives the 4x size reduction; the nibble
+ *   order is this library's convention).
+ *   Inverse: v = q * scale_stored; x_hat_blk = (v_blk . H_b / sqrt(b)) * s
+ *        (the normalised H is orthogonal and symmetric, so it is its own
+ *         inverse: [MS] principle, [HQA] 1).
+ *
+ * Parity pins for every function are in tests/test_oracle_pins.py.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* Input / scale element types understood by the oracle (its own numbering). */
+#define HQO_F32 0
+#define HQO_BF16 1
+#define HQO_F16 2
+
+/* ---------------------------------------------------------------- helpers */
+
+static int is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+/* IEEE binary16 -> double, exact.  value = (1024+M) * 2^(E-25) for normals,
+ * M * 2^-24 for subnormals. */
+double hqo_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);
+    return sign ? -v : v;
+}
+
+/* double -> IEEE binary16 with one round-half-to-even step (no double
+ * rounding through float).  nearbyint() uses the default rounding mode,
+ * which is round-to-nearest-even. */
+uint16_t hqo_f64_to_f16(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v))
+        return sign | 0x7e00;
+    if (a >= 65520.0) /* halfway between 65504 and 2^16 rounds to even -> inf */
+        return sign | 0x7c00;
+    if (a < ldexp(1.0, -14)) { /* subnormal quantum 2^-24 */
+        double r = nearbyint(ldexp(a, 24));
+        return sign | (uint16_t)r; /* r == 1024 is the smallest normal */
+    }
+    int e2;
+    (void)frexp(a, &e2); /* a = f * 2^e2, f in [0.5, 1) */
+    int E = e2 - 1;      /* a = 1.m * 2^E */
+    double r = nearbyint(ldexp(a, 10 - E)); /* in [1024, 2048] */
+    if (r == 2048.0) {
+        r = 1024.0;
+        E += 1;
+    }
+    if (E > 15)
+        return sign | 0x7c00;
+    return sign | (uint16_t)((E + 15) << 10) | (uint16_t)(r - 1024.0);
+}
+
+/* bfloat16 -> double, exact (bf16 is the upper half of a binary32). */
+static double bf16_to_f64(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+int hqo_decode(const void *src, int dtype, int64_t count, double *dst)
+{
+    if (count < 0 || (count > 0 && (!src || !dst)))
+        return -1;
+    for (int64_t i = 0; i < count; ++i) {
+        if (dtype == HQO_F32)
+            dst[i] = (double)((const float *)src)[i];
+        else if (dtype == HQO_BF16)
+            dst[i] = bf16_to_f64(((const uint16_t *)src)[i]);
+        else if (dtype == HQO_F16)
+            dst[i] = hqo_f16_to_f64(((const uint16_t *)src)[i]);
+        else
+            return -1;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------ Sylvester matrix */
+
+/* Fills H (b*b, row-major) with the Sylvester Hadamard matrix of order b,
+ * entries +1/-1, by repeated doubling H_2m = [[H_m, H_m], [H_m, -H_m]]
+ * ([RQ] 2.1 prints H_2 and H_4 = H_2 (x) H_2; [HQA] 1 builds the same
+ * recursion).  Returns 0, or -1 if b is not a power of two. */
+int hqo_hadamard(int b, int8_t *H)
+{
+    if (!is_pow2(b) || !H)
+        return -1;
+    H[0] = 1;
+    for (int m = 1; m < b; m *= 2) {
+        for (int i = 0; i < m; ++i) {
+            for (int j = 0; j < m; ++j) {
+                int8_t v = H[(int64_t)i * b + j];
+                H[(int64_t)i * b + (j + m)] = v;
+                H[(int64_t)(i + m) * b + j] = v;
+                H[(int64_t)(i + m) * b + (j + m)] = (int8_t)-v;
+            }
+        }
+    }
+    return 0;
+}
+
+/* Builds Ht[i][j] = H[j][i] so that the matrix-vector product below walks
+ * memory contiguously.  (The Sylvester matrix is symmetric, but the oracle
+ * does not rely on that: it transposes explicitly.) */
+static int8_t *make_ht(int b)
+{
+    int8_t *H = (int8_t *)malloc((size_t)b * b);
+    int8_t *Ht = (int8_t *)malloc((size_t)b * b);
+    if (!H || !Ht || hqo_hadamard(b, H) != 0) {
+        free(H);
+        free(Ht);
+        return NULL;
+    }
+    for (int i = 0; i < b; ++i)
+        for (int j = 0; j < b; ++j)
+            Ht[(int64_t)i * b + j] = H[(int64_t)j * b + i];
+    free(H);
+    return Ht;
+}
+
+/* One row: out[kb+i] = sum_j (x[kb+j]*s[kb+j]) * H[j][i] / sqrt(b). */
+static void rotate_row(const double *x, const int8_t *s, int n, int b,
+                       const int8_t *Ht, double *u, double *out)
+{
+    double norm = sqrt((double)b);
+    for (int i = 0; i < n; ++i)
+        u[i] = s[i] < 0 ? -x[i] : x[i];
+    for (int k = 0; k < n; k += b) {
+        for (int i = 0; i < b; ++i) {
+            const int8_t *hrow = Ht + (int64_t)i * b;
+            double acc = 0.0;
+            for (int j = 0; j < b; ++j)
+                acc += u[k + j] * (double)hrow[j];
+            out[k + i] = acc / norm;
+        }
+    }
+}
+
+/* ---------------------------------------------------------- quantisation */
+
+static int qmax_of(int bits) { return (1 << (bits - 1)) - 1; }
+
+/* Quantises one rotated row.  Writes the packed codes, the stored scale and
+ * optionally the exact (fp64) scale and the pre-rounding values x'/scale. */
+static void quantize_row(const double *xr, int n, int bits, int scale_dtype,
+                         uint8_t *codes, void *scale_out, int64_t row,
+                         double *scale_exact, double *preround)
+{
+    int qmax = qmax_of(bits);
+    double m = 0.0;
+    for (int i = 0; i < n; ++i)
+        if (fabs(xr[i]) > m)
+            m = fabs(xr[i]);
+    double scale = m / (double)qmax;
+    if (scale_exact)
+        scale_exact[row] = scale;
+    if (scale_dtype == HQO_F32)
+        ((float *)scale_out)[row] = (float)scale; /* C cast: round to nearest even */
+    else
+        ((uint16_t *)scale_out)[row] = hqo_f64_to_f16(scale);
+
+    for (int i = 0; i < n; ++i) {
+        double r = (m > 0.0) ? xr[i] / scale : 0.0; /* all-zero row: codes 0 */
+        if (preround)
+            preround[(int64_t)row * n + i] = r;
+        double qd = nearbyint(r); /* round half to even */
+        if (qd > qmax)
+            qd = qmax;
+        if (qd < -qmax)
+            qd = -qmax;
+        int q = (int)qd;
+        if (bits == 8) {
+            codes[(int64_t)row * n + i] = (uint8_t)(int8_t)q;
+        } else {
+            uint8_t *byte = codes + (int64_t)row * (n / 2) + i / 2;
+            uint8_t nib = (uint8_t)(q & 0xf);
+            if ((i & 1) == 0)
+                *byte = nib;
+            else
+                *byte = (uint8_t)(*byte | (nib << 4));
+        }
+    }
+}
+
+static int unpack_code(const uint8_t *codes, int64_t row, int n, int bits, int i)
+{
+    if (bits == 8)
+        return (int)(int8_t)codes[row * n + i];
+    uint8_t byte = codes[row * (n / 2) + i / 2];
+    int nib = (i & 1) ? (byte >> 4) : (byte & 0xf);
+    return nib >= 8 ? nib - 16 : nib;
+}
+
+static double stored_scale(const void *scales, int scale_dtype, int64_t row)
+{
+    if (scale_dtype == HQO_F32)
+        return (double)((const float *)scales)[row];
+    return hqo_f16_to_f64(((const uint16_t *)scales)[row]);
+}
+
+/* ------------------------------------------------------------- threading */
+
+typedef struct {
+    int kind; /* 0 rotate, 1 rotate+quant, 2 dequant+inverse */
+    const void *x;
+    int x_dtype;
+    int64_t rows;
+    int n, b, bits, scale_dtype;
+    const int8_t *s;
+    const int8_t *Ht;
+    double *xr;
+    uint8_t *codes;
+    void *scales;
+    const uint8_t *codes_in;
+    const void *scales_in;
+    double *scale_exact, *preround, *y;
+    int64_t r0, r1;
+    int err;
+} job_t;
+
+static void *worker(void *arg)
+{
+    job_t *j = (job_t *)arg;
+    int n = j->n;
+    double *xin = (double *)malloc(sizeof(double) * n);
+    double *u = (double *)malloc(sizeof(double) * n);
+    double *out = (double *)malloc(sizeof(double) * n);
+    int8_t *ones = (int8_t *)malloc((size_t)n); /* unit signs for the inverse */
+    if (!xin || !u || !out || !ones) {
+        j->err = -2;
+        goto done;
+    }
+    memset(ones, 1, (size_t)n);
+    for (int64_t r = j->r0; r < j->r1; ++r) {
+        if (j->kind == 0) {
+            rotate_row((const double *)j->x + r * n, j->s, n, j->b, j->Ht, u,
+                       j->xr + r * n);
+        } else if (j->kind == 1) {
+            size_t esz = j->x_dtype == HQO_F32 ? 4 : 2;
+            hqo_decode((const char *)j->x + (size_t)r * n * esz, j->x_dtype, n, xin);
+            rotate_row(xin, j->s, n, j->b, j->Ht, u, out);
+            if (j->xr)
+                memcpy(j->xr + r * n, out, sizeof(double) * n);
+            quantize_row(out, n, j->bits, j->scale_dtype, j->codes, j->scales, r,
+                         j->scale_exact, j->preround);
+        } else {
+            /* v = q * scale_stored, then v.H/sqrt(b) per block, then * s. */
+            double sc = stored_scale(j->scales_in, j->scale_dtype, r);
+            for (int i = 0; i < n; ++i)
+                xin[i] = (double)unpack_code(j->codes_in, r, n, j->bits, i) * sc;
+            rotate_row(xin, ones, n, j->b, j->Ht, u, out);
+            for (int i = 0; i < n; ++i)
+                j->y[r * n + i] = j->s[i] < 0 ? -out[i] : out[i];
+        }
+    }
+done:
+    free(ones);
+    free(xin);
+    free(u);
+    free(out);
+    return NULL;
+}
+
+static int run_jobs(job_t *tmpl, int threads)
+{
+    if (tmpl->rows == 0)
+        return 0;
+    if (threads <= 0)
+        threads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (threads < 1)
+        threads = 1;
+    if ((int64_t)threads > tmpl->rows)
+        threads = (int)tmpl->rows;
+    tmpl->Ht = make_ht(tmpl->b);
+    if (!tmpl->Ht)
+        return -2;
+    job_t *jobs = (job_t *)calloc((size_t)threads, sizeof(job_t));
+    pthread_t *tids = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    int rc = 0;
+    if (!jobs || !tids) {
+        rc = -2;
+        goto out;
+    }
+    for (int t = 0; t < threads; ++t) {
+        jobs[t] = *tmpl;
+        jobs[t].r0 = tmpl->rows * t / threads;
+        jobs[t].r1 = tmpl->rows * (t + 1) / threads;
+        if (pthread_create(&tids[t], NULL, worker, &jobs[t]) != 0) {
+            jobs[t].err = -3;
+            tids[t] = 0;
+        }
+    }
+    for (int t = 0; t < threads; ++t) {
+        if (tids[t])
+            pthread_join(tids[t], NULL);
+        if (jobs[t].err)
+            rc = jobs[t].err;
+    }
+out:
+    free(jobs);
+    free(tids);
+    free((void *)tmpl->Ht);
+    return rc;
+}
+
+static int check_shape(int64_t rows, int n, int b, const int8_t *s)
+{
+    if (rows < 0 || n <= 0 || !is_pow2(b) || n % b != 0 || !s)
+        return -1;
+    return 0;
+}
+
+/* ------------------------------------------------------------ public API */
+
+/* Rotation only: xr = blockwise (x*s).H_b/sqrt(b), x already decoded to fp64. */
+int hqo_rotate(const double *x, int64_t rows, int n, int b, const int8_t *s,
+               double *xr, int threads)
+{
+    if (check_shape(rows, n, b, s) || (rows > 0 && (!x || !xr)))
+        return -1;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.kind = 0;
+    j.x = x;
+    j.rows = rows;
+    j.n = n;
+    j.b = b;
+    j.s = s;
+    j.xr = xr;
+    return run_jobs(&j, threads);
+}
+
+/* Rotation + quantisation straight from the raw input bytes.
+ * codes: [rows, n/2] (bits 4) or [rows, n] (bits 8);  scales: [rows] fp32
+ * or fp16 bits.  scale_exact [rows], preround [rows*n] and xr [rows*n] are
+ * optional diagnostics (NULL to skip). */
+int hqo_rotate_quant(const void *x, int x_dtype, int64_t rows, int n, int b,
+                     const int8_t *s, int bits, uint8_t *codes, void *scales,
+                     int scale_dtype, double *scale_exact, double *preround,
+                     double *xr, int threads)
+{
+    if (check_shape(rows, n, b, s))
+        return -1;
+    if (bits != 4 && bits != 8)
+        return -1;
+    if (bits == 4 && n % 2 != 0)
+        return -1;
+    if (x_dtype != HQO_F32 && x_dtype != HQO_BF16 && x_dtype != HQO_F16)
+        return -1;
+    if (scale_dtype != HQO_F32 && scale_dtype != HQO_F16)
+        return -1;
+    if (rows > 0 && (!x || !codes || !scales))
+        return -1;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.kind = 1;
+    j.x = x;
+    j.x_dtype = x_dtype;
+    j.rows = rows;
+    j.n = n;
+    j.b = b;
+    j.bits = bits;
+    j.scale_dtype = scale_dtype;
+    j.s = s;
+    j.codes = codes;
+    j.scales = scales;
+    j.scale_exact = scale_exact;
+    j.preround = preround;
+    j.xr = xr;
+    return run_jobs(&j, threads);
+}
+
+/* Dequantisation + inverse rotation: y = ((q*scale_stored) . H_b/sqrt(b)) * s. */
+int hqo_dequant_rotate_inv(const uint8_t *codes, const void *scales,
+                           int scale_dtype, int64_t rows, int n, int b,
+                           const int8_t *s, int bits, double *y, int threads)
+{
+    if (check_shape(rows, n, b, s))
+        return -1;
+    if (bits != 4 && bits != 8)
+        return -1;
+    if (bits == 4 && n % 2 != 0)
+        return -1;
+    if (scale_dtype != HQO_F32 && scale_dtype != HQO_F16)
+        return -1;
+    if (rows > 0 && (!codes || !scales || !y))
+        return -1;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.kind = 2;
+    j.codes_in = codes;
+    j.scales_in = scales;
+    j.scale_dtype = scale_dtype;
+    j.rows = rows;
+    j.n = n;
+    j.b = b;
+    j.bits = bits;
+    j.s = s;
+    j.y = y;
+    return run_jobs(&j, threads);
+}
+
+/* Number of worker threads a call with threads<=0 would use. */
+int hqo_default_threads(void) { return (int)sysconf(_SC_NPROCESSORS_ONLN); }

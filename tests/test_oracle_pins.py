@@ -1,0 +1,391 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: matrices
+printed on the pages, closed forms, textbook algorithms written here
+independently, library routines, exact invariants and brute force on tiny
+inputs.  Pages cited:
+  [HQA] "哈特曼旋转，轻量级QAT，流式注意力", section 1.
+  [RQ]  "旋转量化：大模型低比特量化中的离群值克星", sections 2.1 and 2.2.
+  [MS]  "QuaRot：基于旋转的离群值抑制算法说明", section "原理".
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.linalg import hadamard as scipy_hadamard
+
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _read_kv(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, *v = line.split()
+            out[k] = v
+    return out
+
+
+def _read_matrices(name):
+    mats, cur, key = {}, None, None
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line[0] == "H":
+                key = line
+                cur = mats.setdefault(key, [])
+            else:
+                cur.append([int(t) for t in line.split()])
+    return {k: np.array(v) for k, v in mats.items()}
+
+
+def textbook_fwht(v):
+    """In-place iterative fast Walsh-Hadamard transform (natural order),
+    written independently of the oracle: butterflies (a, b) -> (a+b, a-b)."""
+    v = np.array(v, dtype=np.float64)
+    h = 1
+    while h < len(v):
+        for i in range(0, len(v), 2 * h):
+            for j in range(i, i + h):
+                a, b = v[j], v[j + h]
+                v[j], v[j + h] = a + b, a - b
+        h *= 2
+    return v
+
+
+def ref_small(x, s, b):
+    """Blockwise textbook FWHT of (x*s), normalised by sqrt(b)."""
+    rows, n = x.shape
+    out = np.empty((rows, n))
+    for r in range(rows):
+        u = x[r] * s
+        for k in range(0, n, b):
+            out[r, k:k + b] = textbook_fwht(u[k:k + b]) / math.sqrt(b)
+    return out
+
+
+# ------------------------------------------------------------- H itself
+
+def test_h2_h4_match_printed_matrices():
+    m = _read_matrices("hadamard_h2_h4.txt")
+    assert np.array_equal(O.hadamard(2), m["H2"])
+    assert np.array_equal(O.hadamard(4), m["H4"])
+    # H4 = H2 (x) H2 as the page states
+    assert np.array_equal(O.hadamard(4), np.kron(m["H2"], m["H2"]))
+
+
+@pytest.mark.parametrize("b", [1 << k for k in range(13)])
+def test_sylvester_matches_scipy(b):
+    # scipy.linalg.hadamard is the library routine the page's snippet calls
+    assert np.array_equal(O.hadamard(b), scipy_hadamard(b))
+
+
+@pytest.mark.parametrize("b", [16, 128, 512])
+def test_closed_form_popcount(b):
+    i = np.arange(b)[:, None]
+    j = np.arange(b)[None, :]
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i & j)
+    assert np.array_equal(O.hadamard(b), np.where(pc % 2 == 0, 1, -1))
+
+
+@pytest.mark.parametrize("b", [1, 2, 8, 64, 256])
+def test_orthogonality(b):
+    # H.H^T = b.I, i.e. the normalised matrix is orthogonal ([HQA] 1, [MS])
+    H = O.hadamard(b).astype(np.int64)
+    assert np.array_equal(H @ H.T, b * np.eye(b, dtype=np.int64))
+
+
+def test_orthogonality_4096_sampled_rows():
+    H = O.hadamard(4096).astype(np.int64)
+    rng = np.random.default_rng(0)
+    idx = rng.choice(4096, size=24, replace=False)
+    G = H[idx] @ H.T
+    expect = np.zeros((24, 4096), dtype=np.int64)
+    expect[np.arange(24), idx] = 4096
+    assert np.array_equal(G, expect)
+
+
+# ------------------------------------------------------------ rotation
+
+@pytest.mark.parametrize("n,b", [(1, 1), (2, 2), (4, 4), (8, 8), (16, 16),
+                                 (16, 4), (16, 8), (8, 2), (16, 1), (12, 4)])
+def test_rotation_brute_force_small(n, b):
+    rng = np.random.default_rng(n * 131 + b)
+    x = rng.standard_normal((7, n))
+    s = np.where(rng.integers(0, 2, n) == 1, 1, -1).astype(np.int8)
+    got = O.rotate(x, s, b)
+    assert np.allclose(got, ref_small(x, s.astype(np.float64), b), rtol=0, atol=1e-12)
+
+
+def test_rotation_exhaustive_basis_16():
+    # every basis vector: column k of H/sqrt(16) times the sign s_k
+    n = 16
+    s = np.array([1, -1] * 8, dtype=np.int8)
+    got = O.rotate(np.eye(n), s, n)
+    H = scipy_hadamard(n) / 4.0
+    assert np.allclose(got, s[:, None] * H, atol=0)
+
+
+@pytest.mark.parametrize("n,b", [(4096, 4096), (11008, 128), (128, 128), (512, 64)])
+def test_l2_norm_preserved(n, b):
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, n)) * 3
+    s = np.where(rng.integers(0, 2, n) == 1, 1, -1).astype(np.int8)
+    y = O.rotate(x, s, b)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-12)
+
+
+def test_qk_inner_products_preserved():
+    # Q_rot . K_rot^T == Q . K^T when Q and K share the rotation ([HQA] 1)
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((9, 128))
+    k = rng.standard_normal((11, 128))
+    q[:, 5] *= 100
+    k[:, 5] *= 100
+    s = np.where(rng.integers(0, 2, 128) == 1, 1, -1).astype(np.int8)
+    qr, kr = O.rotate(q, s, 128), O.rotate(k, s, 128)
+    ref = q @ k.T
+    assert np.allclose(qr @ kr.T, ref, rtol=0, atol=1e-10 * np.abs(ref).max())
+
+
+def test_rotation_is_involution_up_to_signs():
+    # normalised H is symmetric and orthogonal: applying it twice returns
+    # x*s, and rotating with all +1 signs then multiplying by s undoes it
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((4, 256))
+    s = np.where(rng.integers(0, 2, 256) == 1, 1, -1).astype(np.int8)
+    ones = np.ones(256, dtype=np.int8)
+    y = O.rotate(x, s, 64)
+    back = O.rotate(y, ones, 64) * s
+    assert np.allclose(back, x, atol=1e-13)
+
+
+@pytest.mark.parametrize("k", [0, 123, 42, 4095, 2730])
+def test_spike_spreads_to_closed_form(k):
+    # [RQ] 2.2: a spike of 30 in 4096 coordinates spreads to 30/sqrt(4096)
+    # = 0.46875 exactly in every coordinate (the page rounds it to 0.47)
+    fx = _read_kv("spike_4096.txt")
+    n, spike = int(fx["n"][0]), float(fx["spike"][0])
+    printed, dec = float(fx["printed_magnitude"][0]), int(fx["printed_decimals"][0])
+    rng = np.random.default_rng(k)
+    s = np.where(rng.integers(0, 2, n) == 1, 1, -1).astype(np.int8)
+    x = np.zeros((1, n))
+    x[0, k] = spike
+    y = O.rotate(x, s, n)
+    assert np.all(np.abs(y) == 0.46875)
+    assert round(0.46875, dec) == printed
+    j = np.arange(n)
+    parity = np.vectorize(lambda v: bin(int(v)).count("1") % 2)(k & j)
+    assert np.array_equal(np.sign(y[0]), s[k] * np.where(parity == 0, 1.0, -1.0))
+    # quantised: every code is +-7, scale 0.46875/7, exact round trip
+    raw = x.astype(np.float32)
+    r = O.rotate_quant(raw, O.F32, n, s, 4, O.F32)
+    q = O.unpack_codes(r["codes"], 4, n)
+    assert np.array_equal(np.abs(q), np.full((1, n), 7))
+    assert r["scale_exact"][0] == 0.46875 / 7
+    back = O.dequant_rotate_inv(r["codes"], r["scales"], O.F32, n, s, 4, n)
+    assert np.allclose(back, x, atol=1e-6)
+
+
+def test_spike_blockwise_128():
+    n, b = 11008, 128
+    s = np.ones(n, dtype=np.int8)
+    x = np.zeros((1, n))
+    x[0, 300] = 30.0
+    y = O.rotate(x, s, b)
+    blk = 300 // b
+    assert np.allclose(np.abs(y[0, blk * b:(blk + 1) * b]), 30 / math.sqrt(128), rtol=1e-15)
+    mask = np.ones(n, bool)
+    mask[blk * b:(blk + 1) * b] = False
+    assert np.all(y[0, mask] == 0)
+
+
+# -------------------------------------------------------- quantisation
+
+def _brute_force_round(r, qmax):
+    """Nearest integer in [-qmax, qmax] by exhaustive search, ties to even."""
+    cands = np.arange(-qmax, qmax + 1)
+    out = np.empty(r.shape, dtype=np.int64)
+    for idx, v in np.ndenumerate(r):
+        d = np.abs(cands - v)
+        best = cands[d == d.min()]
+        out[idx] = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+    return out
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantisation_brute_force(bits):
+    # rows built so that x'/scale lands exactly on .5 ties and on integers
+    qmax = (1 << (bits - 1)) - 1
+    n = 16
+    s = np.ones(n, dtype=np.int8)
+    rng = np.random.default_rng(bits)
+    rows = []
+    for _ in range(12):
+        # choose the rotated vector directly: y = H/4 applied to target t
+        t = rng.integers(-2 * qmax, 2 * qmax + 1, size=n) / 2.0
+        t[rng.integers(0, n)] = qmax  # absmax equals qmax, so scale == 1 exactly
+        t = np.clip(t, -qmax, qmax)
+        rows.append(O.rotate(t[None, :], s, n)[0])  # involution: rotate(x)=t
+    x = np.array(rows, dtype=np.float32)
+    r = O.rotate_quant(x, O.F32, n, s, bits, O.F32, want_xr=True)
+    got = O.unpack_codes(r["codes"], bits, n)
+    ref = _brute_force_round(r["preround"], qmax)
+    assert np.array_equal(got, ref)
+    # a good share of the cases really were ties
+    frac = np.abs(r["preround"] - np.floor(r["preround"]))
+    assert np.sum(np.isclose(frac, 0.5, atol=1e-6)) > 20
+
+
+def test_int8_matches_numpy_round_and_clip():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((50, 128)).astype(np.float32)
+    x[:, 7] *= 100
+    s = np.where(rng.integers(0, 2, 128) == 1, 1, -1).astype(np.int8)
+    r = O.rotate_quant(x, O.F32, 128, s, 8, O.F32, want_xr=True)
+    scale = np.abs(r["xr"]).max(axis=1) / 127
+    ref = np.clip(np.round(r["xr"] / scale[:, None]), -127, 127)
+    assert np.array_equal(O.unpack_codes(r["codes"], 8, 128), ref.astype(np.int32))
+    assert np.array_equal(r["scales"], scale.astype(np.float32))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_absmax_gets_qmax_and_error_bound(bits):
+    qmax = (1 << (bits - 1)) - 1
+    raw, s = _rows(11, 40, 4096)
+    r = O.rotate_quant(raw, O.BF16, 4096, s, bits, O.F32, want_xr=True)
+    q = O.unpack_codes(r["codes"], bits, 4096)
+    xr = r["xr"]
+    am = np.argmax(np.abs(xr), axis=1)
+    assert np.array_equal(np.abs(q[np.arange(40), am]), np.full(40, qmax))
+    assert np.all(np.abs(q) <= qmax)
+    err = np.abs(q * r["scale_exact"][:, None] - xr)
+    assert np.all(err <= r["scale_exact"][:, None] / 2 * (1 + 1e-12))
+
+
+def test_scale_is_row_wide_not_per_block():
+    # one block carries a large outlier: the other 85 blocks of the row must
+    # use the row's scale, so none of their codes reaches qmax
+    n, b = 11008, 128
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((2, n)).astype(np.float32)
+    x[:, 700] = 500.0
+    s = np.ones(n, dtype=np.int8)
+    r = O.rotate_quant(x, O.F32, b, s, 4, O.F32)
+    q = O.unpack_codes(r["codes"], 4, n).reshape(2, 86, 128)
+    hot = 700 // b
+    assert np.all(np.abs(q[:, hot]).max(axis=1) == 7)
+    others = np.delete(q, hot, axis=1)
+    assert np.abs(others).max() <= 1
+
+
+def test_zero_row():
+    x = np.zeros((3, 128), dtype=np.float32)
+    s = np.ones(128, dtype=np.int8)
+    r = O.rotate_quant(x, O.F32, 128, s, 4, O.F16)
+    assert np.all(r["codes"] == 0) and np.all(r["scales"] == 0)
+    y = O.dequant_rotate_inv(r["codes"], r["scales"], O.F16, 128, s, 4, 128)
+    assert np.all(y == 0) and not np.any(np.isnan(y))
+
+
+def test_nibble_packing_fixture():
+    fx = _read_kv("nibble_packing.txt")
+    codes = np.array([int(v) for v in fx["codes"]])
+    want = np.array([int(v, 16) for v in fx["bytes"]], dtype=np.uint8)
+    # make a row whose codes are exactly `codes`: choose x' = codes (scale 1
+    # after placing +-7), rotate back with the involution
+    n = 8
+    s = np.ones(n, dtype=np.int8)
+    x = O.rotate(codes[None, :].astype(np.float64), s, n).astype(np.float32)
+    r = O.rotate_quant(x, O.F32, n, s, 4, O.F32)
+    assert np.array_equal(r["codes"][0], want)
+    assert np.array_equal(O.unpack_codes(want[None, :], 4, 8)[0], codes)
+
+
+# ------------------------------------------------------------ round trip
+
+def _rows(seed, rows, n, outliers=4):
+    rng = np.random.default_rng(seed)
+    s = np.where(rng.integers(0, 2, n) == 1, 1, -1).astype(np.int8)
+    x = rng.standard_normal((rows, n)).astype(np.float32)
+    x[:, rng.choice(n, outliers, replace=False)] *= 50
+    import torch
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return bits, s
+
+
+@pytest.mark.parametrize("n,b,bits,sd", [(4096, 4096, 4, O.F32), (128, 128, 4, O.F16),
+                                         (11008, 128, 4, O.F32), (128, 128, 8, O.F32)])
+def test_round_trip_error_bound(n, b, bits, sd):
+    raw, s = _rows(n + bits, 16, n)
+    x = O.decode(raw, O.BF16)
+    r = O.rotate_quant(raw, O.BF16, b, s, bits, sd)
+    y = O.dequant_rotate_inv(r["codes"], r["scales"], sd, b, s, bits, n)
+    sc = r["scales"].astype(np.float64)
+    # ||x_hat - x|| = ||q*scale_stored - x'|| <= sqrt(n)/2 * scale_exact
+    #                 + sqrt(n)*qmax*|scale_stored - scale_exact|
+    qmax = (1 << (bits - 1)) - 1
+    bound = math.sqrt(n) / 2 * r["scale_exact"] + math.sqrt(n) * qmax * np.abs(
+        sc - r["scale_exact"])
+    err = np.linalg.norm(y - x, axis=1)
+    assert np.all(err <= bound * (1 + 1e-9))
+
+
+def test_error_reduction_page_example():
+    # [RQ] 2.2 worked example: rotation cuts the 4-bit error many times over.
+    fx = _read_kv("quant_error_anchor.txt")
+    rng = np.random.default_rng(42)
+    w = rng.standard_normal((1, 4096)).astype(np.float32)
+    w[0, 123] = 30.0
+    ones = np.ones(4096, dtype=np.int8)
+    errs = []
+    for b in (1, 4096):
+        r = O.rotate_quant(w, O.F32, b, ones, 4, O.F32, want_xr=True)
+        q = O.unpack_codes(r["codes"], 4, 4096)
+        errs.append(float(np.mean(np.abs(r["xr"] - q * r["scales"].astype(np.float64)[:, None]))))
+    assert errs[1] < errs[0] / 4
+    assert errs[0] == pytest.approx(float(fx["unrotated"][0]), rel=1e-9)
+    assert errs[1] == pytest.approx(float(fx["rotated"][0]), rel=1e-9)
+
+
+# ------------------------------------------------------------ conversions
+
+def test_f16_conversion_matches_numpy():
+    rng = np.random.default_rng(1)
+    vals = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 5, 20000),
+        # exact ties of the fp16 grid (normal and subnormal), both parities
+        (np.arange(1024, 2048) + 0.5) * 2.0 ** -10,
+        (np.arange(0, 1024) + 0.5) * 2.0 ** -24,
+        [65504.0, 65519.99, 65520.0, 1e9, 0.0, -0.0, 2.0 ** -25, 2.0 ** -26],
+    ])
+    got = np.array([O.f64_to_f16_bits(v) for v in vals], dtype=np.uint16)
+    want = vals.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want)
+    back = np.array([O.f16_bits_to_f64(int(h)) for h in want])
+    assert np.array_equal(back, want.view(np.float16).astype(np.float64))
+
+
+def test_decode_bf16_and_f16():
+    import torch
+    rng = np.random.default_rng(2)
+    v = rng.standard_normal(1000).astype(np.float32) * 1000
+    t = torch.from_numpy(v).to(torch.bfloat16)
+    bits = t.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.decode(bits, O.BF16), t.to(torch.float64).numpy())
+    h = v.astype(np.float16)
+    assert np.array_equal(O.decode(h.view(np.uint16), O.F16), h.astype(np.float64))
+
+
+def test_fp16_scales_are_rounded_once_from_fp64():
+    raw, s = _rows(21, 64, 128)
+    r = O.rotate_quant(raw, O.BF16, 128, s, 4, O.F16)
+    assert np.array_equal(r["scales"], r["scale_exact"].astype(np.float16))
