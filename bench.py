@@ -1,0 +1,240 @@
+"""Benchmark of the fused rotate + INT4 quantise path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one hq_rotate_quant call over one whole batch of the workload
+(default: 16384 tokens x 4096 bf16, full 4096-point randomized Hadamard,
+per-token INT4, fp32 scales).  The inputs are resident in HBM before timing
+starts; steps cycle through several independent buffer sets whose total
+size is well above the 256 MB last-level cache, so every step streams from
+HBM.  Rank 0 prints one JSON line.
+
+`value` is GB/s of algorithmic traffic (input + codes + scales) per second of
+kernel time; `roofline` relates it to the 8 TB/s HBM peak; `cpu_baseline` is
+the CPU oracle timed on a bounded sample of the same workload.  The inverse
+path (dequantise + inverse rotation) and a same-size device copy are timed
+alongside for context.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+LLC_BYTES = 256 * 2 ** 20
+METRIC = "fused rotate+INT4-quant GB/s and % of HBM peak at 16384x4096 bf16"
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "hadamard_rotation_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters for the current
+    kernel sources, or None if no measurement matches them."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(workload, target_s: float = 12.0) -> dict:
+    """Time the CPU oracle on a bounded sample of the same workload."""
+    import numpy as np
+    from hadamard_rotation_amd import workloads as W
+    from oracle import oracle as O
+
+    w = W.WORKLOADS[workload]
+    per_row_mac = w.n * w.b
+    # probe on a few rows, then size the sample to about target_s seconds
+    probe_rows = max(1, int(2e8 // per_row_mac))
+    data = W.generate(workload, seed=42, tokens=max(1, probe_rows // w.unit + 1))
+    raw, s = data[w.tensors[0]], data["s"]
+    threads = O.default_threads()
+    t0 = time.perf_counter()
+    O.rotate_quant(raw[:probe_rows], w.x_dtype, w.b, s, w.bits, w.scale_dtype,
+                   threads=threads, want_preround=False)
+    dt = max(time.perf_counter() - t0, 1e-3)
+    rows = int(min(w.rows, max(probe_rows, probe_rows * target_s / dt)))
+    rows = max(threads, rows - rows % threads)
+    data = W.generate(workload, seed=42, tokens=(rows + w.unit - 1) // w.unit)
+    raw = data[w.tensors[0]][:rows]
+    t0 = time.perf_counter()
+    O.rotate_quant(raw, w.x_dtype, w.b, data["s"], w.bits, w.scale_dtype,
+                   threads=threads, want_preround=False)
+    dt = time.perf_counter() - t0
+    gbs = w.bytes_per_call(rows) / dt / 1e9
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {w.rows} rows of the same workload (seed 42), "
+                      f"{dt:.2f} s wall, explicit fp64 H_{w.b} product per block"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="hidden_4096")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the inverse-path and copy timings")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
+              "supported (rows are independent, so a multi-GPU run is the one-GPU "
+              "throughput per shard)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import hadamard_rotation_amd as hq
+    from hadamard_rotation_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    hq.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.WORKLOADS[args.workload]
+    data = W.generate(args.workload, seed=42)
+    raw, s_np = data[w.tensors[0]], data["s"]
+    rows, n = raw.shape
+    bytes_call = w.bytes_per_call(rows)
+    sets = max(4, int(np.ceil(3 * LLC_BYTES / bytes_call)))
+
+    x_dtype = {W.F32: torch.float32, W.BF16: torch.bfloat16, W.F16: torch.float16}[w.x_dtype]
+    if w.x_dtype == W.F32:
+        x0 = torch.from_numpy(raw).to(dev)
+    else:
+        x0 = torch.from_numpy(raw.view(np.int16)).to(dev).view(x_dtype)
+    s = torch.from_numpy(s_np).to(dev)
+    sd = torch.float32 if w.scale_dtype == W.F32 else torch.float16
+    xs = [x0.clone() for _ in range(sets)]
+    cw = n // 2 if w.bits == 4 else n
+    cdt = torch.uint8 if w.bits == 4 else torch.int8
+    codes = [torch.empty((rows, cw), dtype=cdt, device=dev) for _ in range(sets)]
+    scales = [torch.empty((rows,), dtype=sd, device=dev) for _ in range(sets)]
+    del x0
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        k = i % sets
+        hq.hq_rotate_quant(xs[k], s, w.b, w.bits, sd, codes=codes[k], scales=scales[k],
+                           stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    sec = ms / 1e3
+    value = bytes_call * args.steps / sec / 1e9
+    ms_step = ms / args.steps
+    launch_us = ms_step * 1e3  # one kernel launch per step
+
+    traffic = load_traffic(args.workload)
+    out = {
+        "metric": METRIC if args.workload == "hidden_4096" else
+        f"fused rotate+quant GB/s, workload {args.workload}",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {w.description}",
+            "rows": rows, "n": n, "b": w.b, "bits": w.bits,
+            "x_dtype": W.DTYPE_NAMES[w.x_dtype], "scale_dtype": W.DTYPE_NAMES[w.scale_dtype],
+            "bytes_per_call": bytes_call, "buffer_sets": sets,
+            "rows_per_s": round(rows * args.steps / sec, 1),
+            "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(bytes_call / (launch_us * 1e-6) / 1e9, 3),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(bytes_call / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel_us": round(launch_us, 3),
+        },
+    }
+
+    if not args.no_extras:
+        # inverse path on the same workload: codes + scales -> fp32 rows
+        ys = [torch.empty((rows, n), dtype=torch.float32, device=dev) for _ in range(2)]
+        for i in range(5):
+            hq.hq_dequant_rotate_inv(codes[i % sets], scales[i % sets], s, w.b, w.bits,
+                                     y=ys[i % 2], stream=stream)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        k_inv = max(10, args.steps // 4)
+        for i in range(k_inv):
+            hq.hq_dequant_rotate_inv(codes[i % sets], scales[i % sets], s, w.b, w.bits,
+                                     y=ys[i % 2], stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        inv_s = ev0.elapsed_time(ev1) / 1e3 / k_inv
+        inv_bytes = rows * (cw + (4 if w.scale_dtype == W.F32 else 2) + 4 * n)
+        out["inverse"] = {"us_per_call": round(inv_s * 1e6, 3),
+                          "GB/s": round(inv_bytes / inv_s / 1e9, 3),
+                          "bytes_per_call": inv_bytes, "out_dtype": "f32"}
+        del ys
+        # same-byte-count device copy as the achievable-bandwidth reference
+        nb = bytes_call // 2
+        src = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(sets)]
+        dst = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(sets)]
+        for i in range(5):
+            dst[i % sets].copy_(src[i % sets])
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(50):
+            dst[i % sets].copy_(src[i % sets])
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        cs = ev0.elapsed_time(ev1) / 1e3 / 50
+        out["copy_reference"] = {"bytes_moved": 2 * nb, "GB/s": round(2 * nb / cs / 1e9, 3)}
+        del src, dst
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

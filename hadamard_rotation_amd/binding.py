@@ -1,0 +1,200 @@
+"""Thin ctypes binding of libhq.so (C ABI in include/hq.h).
+
+The functions keep the C names.  They only marshal arguments: they check
+tensor placement, dtype, contiguity and shape, allocate outputs with torch
+when the caller passes none, pass raw device pointers plus torch's current
+HIP stream, and turn a non-OK status into an exception.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.  If the
+library is missing the first call raises.
+
+Pages cited: [RQ] "旋转量化：大模型低比特量化中的离群值克星" sections 2.1-2.2;
+[QT] "手把手教你用QuaRot实现LLM的4位量化：从原理到代码实践" section 2.1.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libhq.so")
+
+HQ_OK, HQ_EINVAL, HQ_EUNSUPPORTED, HQ_EHIP = 0, 1, 2, 3
+HQ_F32, HQ_BF16, HQ_F16 = 0, 1, 2
+
+_TORCH_TO_HQ = {torch.float32: HQ_F32, torch.bfloat16: HQ_BF16, torch.float16: HQ_F16}
+_HQ_TO_TORCH = {v: k for k, v in _TORCH_TO_HQ.items()}
+
+EXPORTS = ("hq_rotate_quant", "hq_dequant_rotate_inv", "hq_rotate", "hq_status_str",
+           "hq_last_hip_error", "hq_max_n", "hq_version")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class HQError(RuntimeError):
+    """A libhq call returned a status other than HQ_OK."""
+
+    def __init__(self, status: int, fn: str, detail: str = ""):
+        self.status = status
+        msg = f"{fn}: {status_str(status)}"
+        if detail:
+            msg += f" ({detail})"
+        super().__init__(msg)
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libhq.so (once) and declare its signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(
+                f"libhq.so not found at {p}: build it first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(p)
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        lib.hq_rotate_quant.argtypes = [P, I32, I64, I32, I32, P, I32, P, P, I32, P]
+        lib.hq_rotate_quant.restype = I32
+        lib.hq_dequant_rotate_inv.argtypes = [P, P, I32, I64, I32, I32, P, I32, P, I32, P]
+        lib.hq_dequant_rotate_inv.restype = I32
+        lib.hq_rotate.argtypes = [P, I32, I64, I32, I32, P, P, P]
+        lib.hq_rotate.restype = I32
+        lib.hq_status_str.argtypes = [I32]
+        lib.hq_status_str.restype = ctypes.c_char_p
+        lib.hq_last_hip_error.argtypes = []
+        lib.hq_last_hip_error.restype = ctypes.c_char_p
+        lib.hq_max_n.argtypes = []
+        lib.hq_max_n.restype = I32
+        lib.hq_version.argtypes = []
+        lib.hq_version.restype = I32
+        _lib = lib
+        return lib
+
+
+def status_str(status: int) -> str:
+    return load().hq_status_str(int(status)).decode()
+
+
+def hq_version() -> int:
+    return int(load().hq_version())
+
+
+def hq_max_n() -> int:
+    return int(load().hq_max_n())
+
+
+def _raise(status: int, fn: str):
+    if status == HQ_OK:
+        return
+    detail = load().hq_last_hip_error().decode()
+    if status == HQ_EINVAL:
+        raise ValueError(f"{fn}: {status_str(status)}")
+    if status == HQ_EUNSUPPORTED:
+        raise NotImplementedError(f"{fn}: {status_str(status)}")
+    raise HQError(status, fn, detail)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check_dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _rows_n(x: torch.Tensor, name: str):
+    if x.dim() != 2:
+        raise ValueError(f"{name} must be 2-D [rows, n]")
+    return x.shape[0], x.shape[1]
+
+
+def hq_rotate_quant(x: torch.Tensor, s: torch.Tensor, b: int, bits: int = 4,
+                    scale_dtype: torch.dtype = torch.float32,
+                    codes: torch.Tensor | None = None,
+                    scales: torch.Tensor | None = None, stream=None):
+    """Rotate + quantise rows of x.  Returns (codes, scales): codes uint8
+    [rows, n/2] (bits 4) or int8 [rows, n] (bits 8); scales [rows]."""
+    _check_dev(x, "x")
+    if x.dtype not in _TORCH_TO_HQ:
+        raise ValueError(f"x dtype {x.dtype} unsupported")
+    rows, n = _rows_n(x, "x")
+    _check_dev(s, "s", torch.int8, (n,))
+    if scale_dtype not in (torch.float32, torch.float16):
+        raise ValueError("scale_dtype must be float32 or float16")
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    cshape = (rows, n // 2) if bits == 4 else (rows, n)
+    cdtype = torch.uint8 if bits == 4 else torch.int8
+    if codes is None:
+        codes = torch.empty(cshape, dtype=cdtype, device=x.device)
+    _check_dev(codes, "codes", cdtype, cshape)
+    if scales is None:
+        scales = torch.empty((rows,), dtype=scale_dtype, device=x.device)
+    _check_dev(scales, "scales", scale_dtype, (rows,))
+    st = load().hq_rotate_quant(x.data_ptr(), _TORCH_TO_HQ[x.dtype], rows, n, int(b),
+                                s.data_ptr(), int(bits), codes.data_ptr(),
+                                scales.data_ptr(), _TORCH_TO_HQ[scale_dtype], _stream(stream))
+    _raise(st, "hq_rotate_quant")
+    return codes, scales
+
+
+def hq_dequant_rotate_inv(codes: torch.Tensor, scales: torch.Tensor, s: torch.Tensor,
+                          b: int, bits: int = 4, out_dtype: torch.dtype = torch.float32,
+                          y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Dequantise codes with their row scales and rotate back: y [rows, n]."""
+    _check_dev(codes, "codes")
+    rows, w = _rows_n(codes, "codes")
+    n = w * 2 if bits == 4 else w
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    if codes.dtype not in ((torch.uint8,) if bits == 4 else (torch.int8, torch.uint8)):
+        raise ValueError(f"codes dtype {codes.dtype} does not match bits={bits}")
+    _check_dev(scales, "scales", None, (rows,))
+    if scales.dtype not in (torch.float32, torch.float16):
+        raise ValueError("scales must be float32 or float16")
+    _check_dev(s, "s", torch.int8, (n,))
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    if y is None:
+        y = torch.empty((rows, n), dtype=out_dtype, device=codes.device)
+    _check_dev(y, "y", out_dtype, (rows, n))
+    st = load().hq_dequant_rotate_inv(codes.data_ptr(), scales.data_ptr(),
+                                      _TORCH_TO_HQ[scales.dtype], rows, n, int(b),
+                                      s.data_ptr(), int(bits), y.data_ptr(),
+                                      _TORCH_TO_HQ[out_dtype], _stream(stream))
+    _raise(st, "hq_dequant_rotate_inv")
+    return y
+
+
+def hq_rotate(x: torch.Tensor, s: torch.Tensor, b: int, y: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """Rotation only: fp32 [rows, n] rotated rows."""
+    _check_dev(x, "x")
+    if x.dtype not in _TORCH_TO_HQ:
+        raise ValueError(f"x dtype {x.dtype} unsupported")
+    rows, n = _rows_n(x, "x")
+    _check_dev(s, "s", torch.int8, (n,))
+    if y is None:
+        y = torch.empty((rows, n), dtype=torch.float32, device=x.device)
+    _check_dev(y, "y", torch.float32, (rows, n))
+    st = load().hq_rotate(x.data_ptr(), _TORCH_TO_HQ[x.dtype], rows, n, int(b),
+                          s.data_ptr(), y.data_ptr(), _stream(stream))
+    _raise(st, "hq_rotate")
+    return y

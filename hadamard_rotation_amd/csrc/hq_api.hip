@@ -1,0 +1,257 @@
+// hq_api.hip -- the C ABI of libhq.so (declared in include/hq.h): argument
+// validation, per-device property cache and dispatch to the kernels.
+//
+// Every check happens on the host before anything is enqueued, so an
+// invalid call writes nothing and launches nothing.  Calls with rows == 0
+// return HQ_OK without touching the HIP runtime.
+#include "hq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "hq_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxB = 4096;
+
+thread_local char g_hip_error[256] = "";
+
+struct DeviceSlot {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+    hq::DeviceInfo info{};
+};
+DeviceSlot g_devices[kMaxDevices];
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+hq_status hip_fail(hipError_t e, const char *where)
+{
+    std::snprintf(g_hip_error, sizeof g_hip_error, "%s: %s", where, hipGetErrorString(e));
+    return HQ_EHIP;
+}
+
+// Properties of the current device, queried once per device.
+hq_status current_device(const hq::DeviceInfo **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return hip_fail(hipErrorInvalidDevice, "device ordinal");
+    DeviceSlot &slot = g_devices[dev];
+    std::call_once(slot.once, [&]() {
+        int v = 0;
+        slot.err = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+        if (slot.err != hipSuccess)
+            return;
+        slot.info.cu_count = v;
+        slot.err = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+        if (slot.err != hipSuccess)
+            return;
+        slot.info.lds_per_block = v;
+    });
+    if (slot.err != hipSuccess)
+        return hip_fail(slot.err, "hipDeviceGetAttribute");
+    *out = &slot.info;
+    return HQ_OK;
+}
+
+int max_n_for(const hq::DeviceInfo &d)
+{
+    // the generic kernel stages a row in LDS as fp32 next to <= 256 B of its own
+    int by_lds = (d.lds_per_block - 256) / (int)sizeof(float);
+    int cap = 65536;
+    int m = by_lds < cap ? by_lds : cap;
+    return m & ~15;
+}
+
+// Checks shared by all entry points.  Pointer checks skip nulls when
+// rows == 0.
+hq_status check_shape(int64_t rows, int32_t n, int32_t b, const int8_t *s)
+{
+    if (rows < 0)
+        return HQ_EINVAL;
+    if (n < 16 || n % 16 != 0)
+        return HQ_EINVAL;
+    if (!is_pow2(b) || n % b != 0)
+        return HQ_EINVAL;
+    if (rows > 0 && !s)
+        return HQ_EINVAL;
+    if (s && !aligned(s, 16))
+        return HQ_EINVAL;
+    if (b > kMaxB)
+        return HQ_EUNSUPPORTED;
+    return HQ_OK;
+}
+
+bool valid_scale_dtype(int d) { return d == HQ_F32 || d == HQ_F16; }
+
+bool valid_in_dtype(int d) { return d == HQ_F32 || d == HQ_BF16 || d == HQ_F16; }
+
+hq_status dispatch(const hq::Request &r)
+{
+    const hq::DeviceInfo *dev = nullptr;
+    hq_status st = current_device(&dev);
+    if (st != HQ_OK)
+        return st;
+    if (r.n > max_n_for(*dev))
+        return HQ_EUNSUPPORTED;
+    hipError_t e;
+    if (hq::fast_available(r))
+        e = hq::launch_fast(r, *dev);
+    else
+        e = hq::launch_generic(r, *dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "kernel launch");
+    return HQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hq_status hq_rotate_quant(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
+                          int32_t b, const int8_t *s, int32_t bits, void *codes,
+                          void *scales, hq_dtype scale_dtype, void *stream)
+{
+    g_hip_error[0] = '\0';
+    hq_status st = check_shape(rows, n, b, s);
+    if (st == HQ_EINVAL)
+        return st;
+    if (!valid_in_dtype(x_dtype) || !valid_scale_dtype(scale_dtype))
+        return HQ_EINVAL;
+    if (bits != 4 && bits != 8)
+        return HQ_EINVAL;
+    if (rows > 0 && (!x || !codes || !scales))
+        return HQ_EINVAL;
+    if ((x && !aligned(x, 16)) || (codes && !aligned(codes, 16)))
+        return HQ_EINVAL;
+    if (scales && !aligned(scales, scale_dtype == HQ_F32 ? 4 : 2))
+        return HQ_EINVAL;
+    if (st != HQ_OK)
+        return st;
+    if (rows == 0)
+        return HQ_OK;
+    hq::Request r{};
+    r.op = hq::kRotateQuant;
+    r.x = x;
+    r.x_dtype = x_dtype;
+    r.rows = rows;
+    r.n = n;
+    r.b = b;
+    r.s = s;
+    r.bits = bits;
+    r.codes = codes;
+    r.scales = scales;
+    r.scale_dtype = scale_dtype;
+    r.stream = (hipStream_t)stream;
+    return dispatch(r);
+}
+
+hq_status hq_dequant_rotate_inv(const void *codes, const void *scales,
+                                hq_dtype scale_dtype, int64_t rows, int32_t n,
+                                int32_t b, const int8_t *s, int32_t bits, void *y,
+                                hq_dtype y_dtype, void *stream)
+{
+    g_hip_error[0] = '\0';
+    hq_status st = check_shape(rows, n, b, s);
+    if (st == HQ_EINVAL)
+        return st;
+    if (!valid_scale_dtype(scale_dtype) || (y_dtype != HQ_F32 && y_dtype != HQ_BF16))
+        return HQ_EINVAL;
+    if (bits != 4 && bits != 8)
+        return HQ_EINVAL;
+    if (rows > 0 && (!codes || !scales || !y))
+        return HQ_EINVAL;
+    if ((codes && !aligned(codes, 16)) || (y && !aligned(y, 16)))
+        return HQ_EINVAL;
+    if (scales && !aligned(scales, scale_dtype == HQ_F32 ? 4 : 2))
+        return HQ_EINVAL;
+    if (st != HQ_OK)
+        return st;
+    if (rows == 0)
+        return HQ_OK;
+    hq::Request r{};
+    r.op = hq::kDequantInv;
+    r.codes_in = codes;
+    r.scales_in = scales;
+    r.scale_dtype = scale_dtype;
+    r.rows = rows;
+    r.n = n;
+    r.b = b;
+    r.s = s;
+    r.bits = bits;
+    r.y = y;
+    r.y_dtype = y_dtype;
+    r.stream = (hipStream_t)stream;
+    return dispatch(r);
+}
+
+hq_status hq_rotate(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
+                    int32_t b, const int8_t *s, float *y, void *stream)
+{
+    g_hip_error[0] = '\0';
+    hq_status st = check_shape(rows, n, b, s);
+    if (st == HQ_EINVAL)
+        return st;
+    if (!valid_in_dtype(x_dtype))
+        return HQ_EINVAL;
+    if (rows > 0 && (!x || !y))
+        return HQ_EINVAL;
+    if ((x && !aligned(x, 16)) || (y && !aligned(y, 16)))
+        return HQ_EINVAL;
+    if (st != HQ_OK)
+        return st;
+    if (rows == 0)
+        return HQ_OK;
+    hq::Request r{};
+    r.op = hq::kRotate;
+    r.x = x;
+    r.x_dtype = x_dtype;
+    r.rows = rows;
+    r.n = n;
+    r.b = b;
+    r.s = s;
+    r.y = y;
+    r.y_dtype = HQ_F32;
+    r.bits = 4;
+    r.scale_dtype = HQ_F32;
+    r.stream = (hipStream_t)stream;
+    return dispatch(r);
+}
+
+const char *hq_status_str(int32_t status)
+{
+    switch (status) {
+    case HQ_OK: return "HQ_OK: success";
+    case HQ_EINVAL: return "HQ_EINVAL: invalid argument";
+    case HQ_EUNSUPPORTED: return "HQ_EUNSUPPORTED: valid request without a kernel in this build";
+    case HQ_EHIP: return "HQ_EHIP: HIP runtime error";
+    default: return "unknown hq_status";
+    }
+}
+
+const char *hq_last_hip_error(void) { return g_hip_error; }
+
+int32_t hq_max_n(void)
+{
+    const hq::DeviceInfo *dev = nullptr;
+    if (current_device(&dev) != HQ_OK)
+        return 0;
+    return max_n_for(*dev);
+}
+
+int32_t hq_version(void) { return 10000; }
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// hq_device.h -- device-side numeric helpers shared by every kernel of
+// libhq.so.  All arithmetic is IEEE binary32; the library is compiled with
+// -ffp-contract=off so that every fused multiply-add below is explicit.
+//
+// Pages cited: [RQ] "旋转量化：大模型低比特量化中的离群值克星" section 2.2
+// (symmetric absmax quantisation with round-to-nearest and clipping to
+// +-(2^(bits-1)-1)); [HQA] "哈特曼旋转，轻量级QAT，流式注意力" section 1 (scale
+// = max|x| / qmax).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <cstdint>
+
+namespace hq {
+
+// 1.5 * 2^23: adding it to a value v with |v| < 2^22 leaves round_half_even(v)
+// in the low mantissa bits, because the sum's unit in the last place is 1.
+constexpr float kRoundMagic = 12582912.0f;
+constexpr int kRoundMagicBits = 0x4B400000;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h)
+{
+    return __half2float(__ushort_as_half(h));
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16(float f)
+{
+    return __half_as_ushort(__float2half_rn(f));
+}
+
+// Quantisation code of an unnormalised rotated value y, given
+// inv = qmax / max|y| of its row: round_half_even(y * inv) with the product
+// kept exact inside one fma, clamped to [-qmax, qmax].  (y * inv equals
+// x'/scale because the 1/sqrt(b) normalisation cancels.)
+__device__ __forceinline__ int quant_code(float y, float inv, int qmax)
+{
+    float t = __builtin_fmaf(y, inv, kRoundMagic);
+    int q = (int)__float_as_uint(t) - kRoundMagicBits;
+    q = q > qmax ? qmax : q;
+    q = q < -qmax ? -qmax : q;
+    return q;
+}
+
+// Per-row constants of the quantiser.  m = max|y| over the row (unnormalised
+// rotated values); kq = 1 / (sqrt(b) * qmax) rounded to fp32 on the host.
+struct RowQuant {
+    float inv;    // qmax / m, or 0 for an all-zero row
+    float scale;  // m * kq = max|x'| / qmax
+};
+
+__device__ __forceinline__ RowQuant row_quant(float m, float kq, int qmax)
+{
+    RowQuant r;
+    r.inv = m > 0.0f ? (float)qmax / m : 0.0f;
+    r.scale = m * kq;
+    return r;
+}
+
+}  // namespace hq

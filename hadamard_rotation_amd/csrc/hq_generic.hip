@@ -1,0 +1,230 @@
+// hq_generic.hip -- generic path of libhq.so: one workgroup per row, the row
+// staged in LDS as fp32, the fast Walsh-Hadamard transform done stage by
+// stage in LDS.  It serves every supported (n, b) that the register-resident
+// kernels do not cover; it is simple rather than fast.
+//
+// Pages cited: [RQ] "旋转量化：大模型低比特量化中的离群值克星" section 2.1 (the
+// transform needs only additions and subtractions; blockwise rotation of
+// independent b-element blocks) and section 2.2 (absmax quantisation);
+// [QT] "手把手教你用QuaRot实现LLM的4位量化：从原理到代码实践" section 2.1 (sign
+// flip before the Hadamard matrix).
+//
+// Butterfly order: pairs (i, i+h) for h = 1, 2, 4, ..., b/2 with
+// (a, c) -> (a+c, a-c).  This is the Sylvester factorisation
+// H_b = H_2 (x) H_2 (x) ... (x) H_2, so the result comes out in natural order.
+#include "hq_device.h"
+#include "hq_internal.h"
+
+namespace hq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kStaticLds = 256;  // upper bound of the kernel's static LDS
+
+struct GenericArgs {
+    const void *x;
+    const void *codes_in;
+    const void *scales_in;
+    const int8_t *s;
+    void *codes;
+    void *scales;
+    void *y;
+    int64_t rows;
+    int n;
+    int log_b;
+    float kq;   // 1 / (sqrt(b) * qmax)
+    float rb;   // 1 / sqrt(b)
+};
+
+template <int IN>
+__device__ __forceinline__ float load_in(const void *x, int64_t idx)
+{
+    if constexpr (IN == kF32)
+        return ((const float *)x)[idx];
+    else if constexpr (IN == kBF16)
+        return bf16_to_f32(((const uint16_t *)x)[idx]);
+    else
+        return f16_to_f32(((const uint16_t *)x)[idx]);
+}
+
+__device__ float block_max(float v, float *red)
+{
+    for (int off = 32; off > 0; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off, 64));
+    int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0)
+        red[wave] = v;
+    __syncthreads();
+    float m = red[0];
+    for (int w = 1; w < kThreads / 64; ++w)
+        m = fmaxf(m, red[w]);
+    __syncthreads();
+    return m;
+}
+
+__device__ void fwht_lds(float *L, int n, int log_b)
+{
+    for (int lh = 0; lh < log_b; ++lh) {
+        __syncthreads();
+        int h = 1 << lh;
+        for (int p = threadIdx.x; p < (n >> 1); p += kThreads) {
+            int i = ((p >> lh) << (lh + 1)) | (p & (h - 1));
+            float a = L[i], c = L[i + h];
+            L[i] = a + c;
+            L[i + h] = a - c;
+        }
+    }
+    __syncthreads();
+}
+
+// OP = kRotateQuant / kRotate: IN is the input dtype, OUT_SC the scale dtype
+// (kRotateQuant only).  OP = kDequantInv: OUT_SC is the stored scale dtype,
+// IN the output dtype (kF32 or kBF16).
+template <int OP, int IN, int BITS, int SC>
+__global__ __launch_bounds__(kThreads) void generic_kernel(GenericArgs a)
+{
+    extern __shared__ float L[];
+    __shared__ float red[kThreads / 64];
+    const int n = a.n;
+    constexpr int qmax = (1 << (BITS - 1)) - 1;
+
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const int64_t base = row * (int64_t)n;
+        if constexpr (OP == kDequantInv) {
+            float sc;
+            if constexpr (SC == kF32)
+                sc = ((const float *)a.scales_in)[row];
+            else
+                sc = f16_to_f32(((const uint16_t *)a.scales_in)[row]);
+            for (int i = threadIdx.x; i < n; i += kThreads) {
+                int q;
+                if constexpr (BITS == 8) {
+                    q = ((const int8_t *)a.codes_in)[base + i];
+                } else {
+                    uint8_t byte = ((const uint8_t *)a.codes_in)[(base >> 1) + (i >> 1)];
+                    int nib = (i & 1) ? (byte >> 4) : (byte & 15);
+                    q = nib >= 8 ? nib - 16 : nib;
+                }
+                L[i] = (float)q;  // exact; the FWHT of integer codes stays exact
+            }
+            fwht_lds(L, n, a.log_b);
+            const float t = sc * a.rb;
+            for (int i = threadIdx.x; i < n; i += kThreads) {
+                float v = L[i] * t;
+                v = a.s[i] < 0 ? -v : v;
+                if constexpr (IN == kF32)
+                    ((float *)a.y)[base + i] = v;
+                else
+                    ((uint16_t *)a.y)[base + i] = f32_to_bf16(v);
+            }
+            __syncthreads();
+            continue;
+        } else {
+            for (int i = threadIdx.x; i < n; i += kThreads) {
+                float v = load_in<IN>(a.x, base + i);
+                L[i] = a.s[i] < 0 ? -v : v;
+            }
+            fwht_lds(L, n, a.log_b);
+            if constexpr (OP == kRotate) {
+                for (int i = threadIdx.x; i < n; i += kThreads)
+                    ((float *)a.y)[base + i] = L[i] * a.rb;
+                __syncthreads();
+            } else {
+                float m = 0.0f;
+                for (int i = threadIdx.x; i < n; i += kThreads)
+                    m = fmaxf(m, fabsf(L[i]));
+                m = block_max(m, red);
+                RowQuant rq = row_quant(m, a.kq, qmax);
+                if (threadIdx.x == 0) {
+                    if constexpr (SC == kF32)
+                        ((float *)a.scales)[row] = rq.scale;
+                    else
+                        ((uint16_t *)a.scales)[row] = f32_to_f16(rq.scale);
+                }
+                if constexpr (BITS == 8) {
+                    for (int i = threadIdx.x; i < n; i += kThreads)
+                        ((int8_t *)a.codes)[base + i] = (int8_t)quant_code(L[i], rq.inv, qmax);
+                } else {
+                    for (int j = threadIdx.x; j < (n >> 1); j += kThreads) {
+                        int q0 = quant_code(L[2 * j], rq.inv, qmax);
+                        int q1 = quant_code(L[2 * j + 1], rq.inv, qmax);
+                        ((uint8_t *)a.codes)[(base >> 1) + j] =
+                            (uint8_t)((q0 & 15) | ((q1 & 15) << 4));
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    }
+}
+
+template <int OP, int IN, int BITS, int SC>
+hipError_t go(const GenericArgs &ga, const Request &r, const DeviceInfo &dev)
+{
+    (void)dev;
+    int64_t grid = r.rows < (1 << 20) ? r.rows : (1 << 20);
+    size_t lds = (size_t)r.n * sizeof(float);
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void *)generic_kernel<OP, IN, BITS, SC>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL((generic_kernel<OP, IN, BITS, SC>), dim3((unsigned)grid),
+                       dim3(kThreads), lds, r.stream, ga);
+    return hipGetLastError();
+}
+
+template <int OP, int IN>
+hipError_t pick_bits(const GenericArgs &ga, const Request &r, const DeviceInfo &dev)
+{
+    if (r.bits == 4)
+        return r.scale_dtype == kF32 ? go<OP, IN, 4, kF32>(ga, r, dev)
+                                     : go<OP, IN, 4, kF16>(ga, r, dev);
+    return r.scale_dtype == kF32 ? go<OP, IN, 8, kF32>(ga, r, dev)
+                                 : go<OP, IN, 8, kF16>(ga, r, dev);
+}
+
+}  // namespace
+
+hipError_t launch_generic(const Request &r, const DeviceInfo &dev)
+{
+    GenericArgs ga{};
+    ga.x = r.x;
+    ga.codes_in = r.codes_in;
+    ga.scales_in = r.scales_in;
+    ga.s = r.s;
+    ga.codes = r.codes;
+    ga.scales = r.scales;
+    ga.y = r.y;
+    ga.rows = r.rows;
+    ga.n = r.n;
+    int lb = 0;
+    while ((1 << lb) < r.b)
+        ++lb;
+    ga.log_b = lb;
+    int qmax = r.bits == 8 ? 127 : 7;
+    ga.kq = (float)(1.0 / (__builtin_sqrt((double)r.b) * qmax));
+    ga.rb = (float)(1.0 / __builtin_sqrt((double)r.b));
+
+    size_t lds = (size_t)r.n * sizeof(float) + kStaticLds;
+    if ((int64_t)lds > dev.lds_per_block)
+        return hipErrorInvalidValue;
+
+    switch (r.op) {
+    case kRotateQuant:
+        if (r.x_dtype == kF32) return pick_bits<kRotateQuant, kF32>(ga, r, dev);
+        if (r.x_dtype == kBF16) return pick_bits<kRotateQuant, kBF16>(ga, r, dev);
+        return pick_bits<kRotateQuant, kF16>(ga, r, dev);
+    case kRotate:
+        if (r.x_dtype == kF32) return go<kRotate, kF32, 4, kF32>(ga, r, dev);
+        if (r.x_dtype == kBF16) return go<kRotate, kBF16, 4, kF32>(ga, r, dev);
+        return go<kRotate, kF16, 4, kF32>(ga, r, dev);
+    case kDequantInv:
+        if (r.y_dtype == kF32) return pick_bits<kDequantInv, kF32>(ga, r, dev);
+        return pick_bits<kDequantInv, kBF16>(ga, r, dev);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace hq

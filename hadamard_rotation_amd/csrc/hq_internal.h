@@ -1,0 +1,56 @@
+// hq_internal.h -- declarations shared by the host dispatcher and the kernel
+// translation units of libhq.so.  Not part of the public ABI (include/hq.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace hq {
+
+// Element types, numbered like the public hq_dtype.
+enum Dtype : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
+
+// Which path a launch computes.
+enum Op : int {
+    kRotateQuant = 0,  // x -> codes + scales
+    kRotate = 1,       // x -> fp32 rotated rows
+    kDequantInv = 2    // codes + scales -> rows (inverse rotation)
+};
+
+// Everything a launcher needs; validated by the host dispatcher beforehand.
+struct Request {
+    Op op;
+    const void *x;          // kRotateQuant / kRotate input rows
+    int x_dtype;
+    const void *codes_in;   // kDequantInv inputs
+    const void *scales_in;
+    int64_t rows;
+    int n;
+    int b;
+    const int8_t *s;
+    int bits;
+    void *codes;            // kRotateQuant outputs
+    void *scales;
+    int scale_dtype;        // kRotateQuant output / kDequantInv input
+    void *y;                // kRotate / kDequantInv output
+    int y_dtype;
+    hipStream_t stream;
+};
+
+// Per-device facts the dispatcher uses to choose and size launches.
+struct DeviceInfo {
+    int cu_count;
+    int lds_per_block;   // bytes of LDS one workgroup may allocate
+};
+
+// Generic path: any supported (n, b); one workgroup per row with the row
+// staged in LDS as fp32.  Requires 4*n <= dev.lds_per_block.
+hipError_t launch_generic(const Request &r, const DeviceInfo &dev);
+
+// Tuned register-resident paths.  fast_plan() says whether one exists for
+// the request; launch_fast() enqueues it.
+bool fast_available(const Request &r);
+hipError_t launch_fast(const Request &r, const DeviceInfo &dev);
+
+}  // namespace hq

@@ -1,0 +1,131 @@
+/*
+ * hq.h -- C ABI of libhq.so: randomized Hadamard rotation fused with symmetric
+ * per-row low-bit quantisation, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (pages cited by title and section):
+ *   [RQ] "旋转量化：大模型低比特量化中的离群值克星" (rotation-quantization blog)
+ *   [QT] "手把手教你用QuaRot实现LLM的4位量化：从原理到代码实践" (QuaRot tutorial)
+ *   [HQA] "哈特曼旋转，轻量级QAT，流式注意力" (Q&A post, section 1)
+ *   [MS] "QuaRot：基于旋转的离群值抑制算法说明" (msModelSlim QuaRot page)
+ *
+ *   Each row x (n contiguous elements) is flipped elementwise by a +-1 sign
+ *   vector s shared by all rows ([QT] 2.1: the "random Hadamard" transform),
+ *   then split into n/b consecutive blocks of b elements, and every block is
+ *   multiplied by the Sylvester Hadamard matrix H_b normalised by 1/sqrt(b)
+ *   ([RQ] 2.1: H_2 = [[1,1],[1,-1]], H_2m = H_2 (x) H_m; blockwise rotation
+ *   for widths that are not a power of two; b == n is the full rotation):
+ *
+ *       x'[kb+i] = sum_j x[kb+j] s[kb+j] H_b[j][i] / sqrt(b)
+ *
+ *   The row is then quantised symmetrically with one scale per row
+ *   ([HQA] 1, [RQ] 2.2):
+ *
+ *       scale = max_i |x'_i| / qmax,   qmax = 2^(bits-1) - 1  (7 or 127)
+ *       q_i   = clamp(round_half_even(x'_i / scale), -qmax, qmax)
+ *
+ *   and the inverse path dequantises and rotates back ([MS] principle: the
+ *   normalised H is orthogonal and symmetric, hence its own inverse):
+ *
+ *       x_hat[kb+i] = s[kb+i] * sum_j (q[kb+j] * scale) H_b[j][i] / sqrt(b)
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument except `stream` is a DEVICE pointer owned by the
+ *     caller.  The library allocates no memory and keeps no per-call state;
+ *     it caches a few device properties per device.  It is thread-safe.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL is the null stream).  On return with HQ_OK the work is enqueued.
+ *   - A row is n contiguous elements; rows are contiguous (row stride n).
+ *     Head-dim-innermost layouts ([B,H,S,D], [S,H,D]) are just rows of D.
+ *   - s: int8 [n]; an element < 0 means "negate", anything else "keep".
+ *     The caller supplies it; the library never draws random numbers.
+ *   - Supported shapes: b a power of two with 1 <= b <= 4096, n % b == 0,
+ *     n % 16 == 0, 16 <= n <= hq_max_n(); rows >= 0 (rows == 0 is a no-op).
+ *   - Alignment: x, codes, y and s must be 16-byte aligned; scales must be
+ *     aligned to their element size.
+ *   - Outputs must not overlap inputs.  Inputs are never modified.
+ *   - Every argument is validated on the host before anything is enqueued;
+ *     on any error nothing is written and nothing is launched.  No C++
+ *     exception crosses this boundary.
+ *   - Values of x that are NaN or infinite give unspecified codes/scales.
+ */
+#ifndef HQ_H
+#define HQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hq_status {
+    HQ_OK = 0,           /* enqueued (or nothing to do)                    */
+    HQ_EINVAL = 1,       /* invalid argument: null pointer, bad shape,
+                            dtype, bits, or misaligned pointer             */
+    HQ_EUNSUPPORTED = 2, /* valid request this build has no kernel for
+                            (n above hq_max_n(), b above 4096)             */
+    HQ_EHIP = 3          /* the HIP runtime reported an error (no device,
+                            launch failure); see hq_last_hip_error()       */
+} hq_status;
+
+typedef enum hq_dtype {
+    HQ_F32 = 0,  /* IEEE binary32 */
+    HQ_BF16 = 1, /* bfloat16      */
+    HQ_F16 = 2   /* IEEE binary16 */
+} hq_dtype;
+
+/*
+ * hq_rotate_quant -- fused rotation + symmetric quantisation (forward path).
+ *   x        [rows, n] input, element type x_dtype (HQ_F32, HQ_BF16, HQ_F16)
+ *   s        [n] int8 signs
+ *   bits     4 or 8
+ *   codes    bits == 4: [rows, n/2] uint8; element 2j in the low nibble,
+ *            2j+1 in the high nibble, 4-bit two's complement in [-7, 7].
+ *            bits == 8: [rows, n] int8 in [-127, 127].
+ *   scales   [rows], element type scale_dtype (HQ_F32 or HQ_F16), the stored
+ *            value of max|x'|/qmax rounded to nearest even.  A row of zeros
+ *            gets scale 0 and codes 0.
+ * Codes are computed from the unrounded scale, so they do not depend on
+ * scale_dtype.
+ */
+hq_status hq_rotate_quant(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
+                          int32_t b, const int8_t *s, int32_t bits, void *codes,
+                          void *scales, hq_dtype scale_dtype, void *stream);
+
+/*
+ * hq_dequant_rotate_inv -- dequantisation + inverse rotation (round trip).
+ *   codes, scales, scale_dtype, bits: as written by hq_rotate_quant
+ *   y        [rows, n] output, y_dtype HQ_F32 or HQ_BF16 (rounded to
+ *            nearest even)
+ */
+hq_status hq_dequant_rotate_inv(const void *codes, const void *scales,
+                                hq_dtype scale_dtype, int64_t rows, int32_t n,
+                                int32_t b, const int8_t *s, int32_t bits, void *y,
+                                hq_dtype y_dtype, void *stream);
+
+/*
+ * hq_rotate -- rotation only: y = x' as fp32 [rows, n] (no quantisation).
+ * Used to check the rotated values themselves and Q.K^T preservation
+ * ([HQA] 1: rotating Q and K with the same matrix keeps Q.K^T).
+ */
+hq_status hq_rotate(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
+                    int32_t b, const int8_t *s, float *y, void *stream);
+
+/* Static text for a status code (never NULL). */
+const char *hq_status_str(int32_t status);
+
+/* Text of the last HIP error seen by this thread inside the library (empty
+ * string if none).  Valid until the next library call on the same thread. */
+const char *hq_last_hip_error(void);
+
+/* Largest supported row width n on the current device (needs a device;
+ * returns 0 if none is present). */
+int32_t hq_max_n(void);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int32_t hq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HQ_H */

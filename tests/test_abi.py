@@ -1,0 +1,121 @@
+"""Host-side tests of the C ABI: the library loads, exports what include/hq.h
+declares, and rejects every invalid-argument class before touching the GPU.
+None of these calls reaches the HIP runtime (rows == 0 or invalid input)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hadamard_rotation_amd as hq
+from hadamard_rotation_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hq.h")
+
+A = ctypes.c_void_p(0x10000)      # 16-byte aligned, never dereferenced
+MIS = ctypes.c_void_p(0x10001)    # misaligned
+A2 = ctypes.c_void_p(0x10002)     # 2-byte aligned, not 4
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_header_symbols():
+    lib = hq.load()
+    syms = declared_symbols()
+    assert set(syms) == {"hq_rotate_quant", "hq_dequant_rotate_inv", "hq_rotate",
+                         "hq_status_str", "hq_last_hip_error", "hq_max_n", "hq_version"}
+    for name in syms:
+        assert hasattr(lib, name), name
+    assert set(B.EXPORTS) == set(syms)
+
+
+def test_status_strings():
+    for code, frag in ((0, "HQ_OK"), (1, "HQ_EINVAL"), (2, "HQ_EUNSUPPORTED"), (3, "HQ_EHIP"),
+                       (99, "unknown")):
+        assert frag in hq.status_str(code)
+    assert hq.hq_version() == 10000
+
+
+def rq(x=A, xd=1, rows=4, n=128, b=128, s=A, bits=4, codes=A, scales=A, sd=0):
+    return hq.load().hq_rotate_quant(x, xd, rows, n, b, s, bits, codes, scales, sd, None)
+
+
+def inv(codes=A, scales=A, sd=0, rows=4, n=128, b=128, s=A, bits=4, y=A, yd=0):
+    return hq.load().hq_dequant_rotate_inv(codes, scales, sd, rows, n, b, s, bits, y, yd, None)
+
+
+def rot(x=A, xd=1, rows=4, n=128, b=128, s=A, y=A):
+    return hq.load().hq_rotate(x, xd, rows, n, b, s, y, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(s=None), dict(codes=None), dict(scales=None),
+    dict(rows=-1), dict(n=0), dict(n=-128), dict(n=120), dict(n=8), dict(b=0), dict(b=3),
+    dict(b=96), dict(n=384, b=256), dict(bits=3), dict(bits=16), dict(xd=7), dict(sd=1),
+    dict(sd=9), dict(x=MIS), dict(s=MIS), dict(codes=MIS), dict(scales=A2),
+])
+def test_rotate_quant_einval(kw):
+    assert rq(**kw) == hq.HQ_EINVAL
+
+
+@pytest.mark.parametrize("kw", [
+    dict(codes=None), dict(scales=None), dict(y=None), dict(s=None), dict(rows=-5),
+    dict(n=100), dict(b=5), dict(bits=2), dict(sd=1), dict(yd=2), dict(yd=5),
+    dict(codes=MIS), dict(y=MIS), dict(scales=A2),
+])
+def test_dequant_einval(kw):
+    assert inv(**kw) == hq.HQ_EINVAL
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(y=None), dict(s=None), dict(rows=-1), dict(n=24), dict(b=6),
+    dict(xd=3), dict(x=MIS), dict(y=MIS),
+])
+def test_rotate_einval(kw):
+    assert rot(**kw) == hq.HQ_EINVAL
+
+
+def test_block_above_4096_unsupported():
+    assert rq(rows=1, n=8192, b=8192) == hq.HQ_EUNSUPPORTED
+    assert rot(rows=1, n=8192, b=8192) == hq.HQ_EUNSUPPORTED
+    assert inv(rows=1, n=8192, b=8192) == hq.HQ_EUNSUPPORTED
+    # an invalid argument still wins over "unsupported"
+    assert rq(rows=1, n=8192, b=8192, bits=5) == hq.HQ_EINVAL
+
+
+def test_zero_rows_is_noop_without_pointers():
+    assert rq(x=None, codes=None, scales=None, s=None, rows=0) == hq.HQ_OK
+    assert inv(codes=None, scales=None, y=None, s=None, rows=0) == hq.HQ_OK
+    assert rot(x=None, y=None, s=None, rows=0) == hq.HQ_OK
+    # shape checks still apply at rows == 0
+    assert rq(rows=0, n=100) == hq.HQ_EINVAL
+
+
+def test_binding_rejects_host_tensors_and_bad_layouts():
+    import torch
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    s = torch.ones(128, dtype=torch.int8)
+    with pytest.raises(ValueError, match="GPU"):
+        hq.hq_rotate_quant(x, s, 128)
+    with pytest.raises(ValueError, match="GPU"):
+        hq.hq_rotate(x, s, 128)
+    with pytest.raises(ValueError, match="GPU"):
+        hq.hq_dequant_rotate_inv(torch.zeros((4, 64), dtype=torch.uint8),
+                                 torch.zeros(4), s, 128)
+    with pytest.raises(TypeError):
+        hq.hq_rotate_quant(x.numpy() if False else [1, 2], s, 128)
+
+
+def test_product_package_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "hadamard_rotation_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), f
+                assert "hq_oracle" not in text and "liboracle" not in text, f
