@@ -1,0 +1,727 @@
+// hq_fast_impl.h -- the register-resident kernel template of libhq.so for
+// gfx950, included by the three translation units that instantiate it
+// (forward quantisation, rotation only, inverse).
+//
+// Pages cited: [RQ] "旋转量化：大模型低比特量化中的离群值克星" section 2.1 (the
+// Hadamard transform needs only additions and subtractions; rows whose width
+// is not a power of two are rotated in independent b-element blocks, e.g.
+// 4096 as 32 blocks of 128) and section 2.2 (per-row absmax scale, round and
+// clip); [QT] "手把手教你用QuaRot实现LLM的4位量化：从原理到代码实践" section 2.1
+// (sign flip, then Hadamard) and section 4.1 (the rotation belongs in the
+// kernel that reads the activations, not in a separate pass).
+//
+// Layout.  A lane owns UNITS "units" of 8 consecutive elements of a row (one
+// 16-byte load of bf16).  The lanes of one row segment hold consecutive
+// units, so a wave instruction reads 1 KB of contiguous memory; unit u of
+// lane l covers elements ((seg_base + u * LANES + l) * 8 + j), j = 0..7.
+// Element index bits are [j: 3][lane: log2 LANES][unit: log2 UNITS], and a
+// Hadamard block of b = 2^logb elements covers the low logb bits.  The fast
+// Walsh-Hadamard transform is one butterfly stage per index bit:
+//   j bits         between registers of one unit (bit 0 folded into the
+//                  widening v_dot2 of the input pair, which also applies
+//                  the sign vector)
+//   unit bits      between registers of two units
+//   lane bits 0..3 v_fmac_f32 with a DPP source (quad_perm, row_half_mirror,
+//                  row_ror:8): exchange and butterfly in one instruction
+//   lane bits 4, 5 v_permlane16_swap / v_permlane32_swap exchange the lane
+//                  bit with a unit bit already finished, after which the
+//                  butterfly is again between registers
+// LDS holds only the per-workgroup copy of the sign vector and, for rows
+// wider than one wave, the cross-wave absmax.
+//
+// The DPP stages compute acc_l += sigma_l * acc_partner(l): the difference
+// half of every butterfly comes out negated, and the pairs follow the basis
+// {1, 2, 7, 8} of the 16-lane index.  The result is still the Hadamard
+// transform of the block, but lane l ends up holding the natural output
+// chunk pi(l) times sign(l); the tables are in FastArgs (pi, neg) and the
+// store addresses and the quantisation multiplier absorb both.
+#pragma once
+
+#include "hq_device.h"
+#include "hq_internal.h"
+
+namespace hq {
+namespace fast {
+
+constexpr int kMaxWpr = 16;
+
+struct FastArgs {
+    const void *x;
+    const void *codes_in;
+    const void *scales_in;
+    const int8_t *s;
+    void *codes;
+    void *scales;
+    void *y;
+    int64_t rows;
+    int64_t groups;       // row groups in total (one workgroup iteration each)
+    int64_t chunk;        // consecutive row groups per workgroup
+    uint64_t pi;          // output chunk of lane l & 15 after the DPP stages
+    uint32_t neg;         // bit l set: lane l holds the negated value
+    int n;
+    int logb;             // used when the template's LOGB is -1
+    int log_lanes;        // used when the template's LOG_LANES is -1
+    int wpr;              // waves per row (LONG kernels)
+    int bits;             // 4 or 8
+    int scale_f16;        // scales stored as fp16 (else fp32)
+    float kq;             // 1 / (sqrt(b) * qmax)
+    float rb;             // 1 / sqrt(b)
+};
+
+// ------------------------------------------------------------ primitives
+
+// One DPP butterfly stage on 8 registers: v += sigma * v[partner lane].
+// "s_nop 4" first: a DPP read needs two wait states after a VALU write of
+// its source and five after an EXEC write; no instruction of the block
+// reads a register that an earlier instruction of the same block wrote.
+#define HQ_DPP8(CTRL)                                                                   \
+    asm volatile("s_nop 4\n\t"                                                          \
+                 "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+                 "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+                 "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+                 "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+                 "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+                 "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+                 "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
+                 "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"       \
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]),        \
+                   "+v"(v[5]), "+v"(v[6]), "+v"(v[7])                                   \
+                 : "v"(sigma))
+
+template <int STAGE>
+__device__ __forceinline__ void dpp_stage(float (&v)[8], float sigma)
+{
+    if constexpr (STAGE == 0)
+        HQ_DPP8("quad_perm:[1,0,3,2]");
+    else if constexpr (STAGE == 1)
+        HQ_DPP8("quad_perm:[2,3,0,1]");
+    else if constexpr (STAGE == 2)
+        HQ_DPP8("row_half_mirror");
+    else
+        HQ_DPP8("row_ror:8");
+}
+
+// First butterfly of an input pair fused with widening and the sign flip:
+// (s0*x0 + s1*x1, s0*x0 - s1*x1) from the packed pair w and the packed +-1
+// pair sg; neg_hi negates the high half of sg for the difference.
+template <int IN>
+__device__ __forceinline__ void dot2_pair(uint32_t w, uint32_t sg, float &a, float &b)
+{
+    if constexpr (IN == kBF16) {
+        asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(a) : "v"(w), "v"(sg));
+        asm("v_dot2_f32_bf16 %0, %1, %2, 0 neg_hi:[0,1,0]" : "=v"(b) : "v"(w), "v"(sg));
+    } else {
+        asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(a) : "v"(w), "v"(sg));
+        asm("v_dot2_f32_f16 %0, %1, %2, 0 neg_hi:[0,1,0]" : "=v"(b) : "v"(w), "v"(sg));
+    }
+}
+
+__device__ __forceinline__ void bfly(float &a, float &b)
+{
+    float t = a + b;
+    b = a - b;
+    a = t;
+}
+
+__device__ __forceinline__ float flip(float v, uint32_t sbit)
+{
+    return __uint_as_float(__float_as_uint(v) ^ (sbit << 31));
+}
+
+// Packs 8 INT4 codes: f[j] = 0x4B400008 + q_j with q_j in [-7, 7] (the +8
+// offset keeps every nibble free of borrows); element j lands in nibble j as
+// 4-bit two's complement.
+__device__ __forceinline__ uint32_t pack_int4(const uint32_t (&f)[8])
+{
+    uint32_t t01 = (f[1] << 4) + f[0];
+    uint32_t t23 = (f[3] << 4) + f[2];
+    uint32_t t45 = (f[5] << 4) + f[4];
+    uint32_t t67 = (f[7] << 4) + f[6];
+    uint32_t u0 = (t23 << 8) | t01;  // bytes 0,1 valid
+    uint32_t u1 = (t67 << 8) | t45;
+    uint32_t p = __builtin_amdgcn_perm(u1, u0, 0x05040100u);
+    return p ^ 0x88888888u;
+}
+
+// Packs 4 INT8 codes held as 0x4B400080 + q, q in [-127, 127].
+__device__ __forceinline__ uint32_t pack_int8(uint32_t f0, uint32_t f1, uint32_t f2, uint32_t f3)
+{
+    uint32_t u0 = (f1 << 8) | f0;
+    uint32_t u1 = (f3 << 8) | f2;
+    uint32_t p = __builtin_amdgcn_perm(u1, u0, 0x05040100u);
+    return p ^ 0x80808080u;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v)
+{
+    return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                        0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false)));
+}
+
+// max over the 2^log_lanes aligned lanes of one row segment
+__device__ __forceinline__ float segment_max(float v, int log_lanes)
+{
+    if (log_lanes > 0) v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
+    if (log_lanes > 1) v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
+    if (log_lanes > 2) v = dpp_max<0x141>(v);  // row_half_mirror
+    if (log_lanes > 3) v = dpp_max<0x128>(v);  // row_ror:8
+    if (log_lanes > 4) v = fmaxf(v, __shfl_xor(v, 16, 64));
+    if (log_lanes > 5) v = fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+// Raw input of one unit: 16 bytes of bf16/f16, 32 bytes of fp32, or 4/8
+// bytes of codes (inverse path).
+template <int OP, int IN>
+struct RawUnit {
+    uint32_t w[(OP != kDequantInv && IN == kF32) ? 8 : (OP == kDequantInv ? 2 : 4)];
+};
+
+// ----------------------------------------------------------------- kernel
+//
+// OP         kRotateQuant, kRotate or kDequantInv
+// IN         input dtype (forward) or output dtype (inverse: kF32 / kBF16)
+// UNITS      8-element units per lane and row (registers)
+// LOG_LANES  log2 lanes per row segment, or -1 for FastArgs::log_lanes
+// LOGB       log2 b, or -1 for FastArgs::logb
+// RPL        independent rows per lane per iteration (short rows)
+// LONG       a row spans FastArgs::wpr waves (LOG_LANES == 6, RPL == 1);
+//            units past the row end are loaded clamped and ignored
+#ifndef HQ_WAVES_PER_EU
+#define HQ_WAVES_PER_EU 1
+#endif
+#ifndef HQ_PREFETCH
+#define HQ_PREFETCH 1
+#endif
+template <int OP, int IN, int UNITS, int LOG_LANES, int LOGB, int RPL, bool LONG>
+__global__ __launch_bounds__(LONG && UNITS < 8 ? 1024 : 256)
+__attribute__((amdgpu_waves_per_eu(HQ_WAVES_PER_EU, 8))) void fast_kernel(FastArgs a)
+{
+    extern __shared__ __align__(16) uint32_t lds_sign[];  // sign material of one row width
+    __shared__ float red[2][kMaxWpr];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int log_lanes = LOG_LANES >= 0 ? LOG_LANES : a.log_lanes;
+    const int logb = LOGB >= 0 ? LOGB : a.logb;
+    const int lanes = 1 << log_lanes;
+    const int l = lane & (lanes - 1);  // lane within its row segment
+    const int units_row = a.n >> 3;
+
+    // ---- sign material -> LDS (row independent).  Forward: +-1 pairs in
+    // the input's 16-bit format, one word per element pair.  Inverse: the
+    // raw sign bytes.
+    if constexpr (OP == kDequantInv) {
+        for (int i = threadIdx.x; i < (a.n >> 2); i += blockDim.x)
+            lds_sign[i] = ((const uint32_t *)a.s)[i];
+    } else {
+        const uint32_t one = (IN == kF16) ? 0x3C00u : 0x3F80u;
+        for (int i = threadIdx.x; i < (a.n >> 1); i += blockDim.x) {
+            uint32_t two = ((const uint16_t *)a.s)[i];
+            uint32_t s0 = (two >> 7) & 1, s1 = (two >> 15) & 1;
+            lds_sign[i] = (one | (s0 << 15)) | ((one | (s1 << 15)) << 16);
+        }
+    }
+    __syncthreads();
+
+    // ---- stage plan (compile-time when LOGB and LOG_LANES are)
+    const int lane_bits = logb > 3 ? (logb - 3 < log_lanes ? logb - 3 : log_lanes) : 0;
+    const int n_dpp = lane_bits < 4 ? lane_bits : 4;
+    const bool swap16 = lane_bits > 4;
+    const bool swap32 = lane_bits > 5;
+    const int unit_bits = logb - 3 - log_lanes > 0 ? logb - 3 - log_lanes : 0;
+
+    const int l16 = lane & 15;
+    const float sig0 = ((l16 ^ (l16 >> 2)) & 1) ? -1.0f : 1.0f;
+    const float sig1 = (((l16 >> 1) ^ (l16 >> 2)) & 1) ? -1.0f : 1.0f;
+    const float sig2 = ((l16 >> 2) & 1) ? -1.0f : 1.0f;
+    const float sig3 = ((l16 >> 3) & 1) ? -1.0f : 1.0f;
+    const bool lane_neg = (a.neg >> l16) & 1;
+
+    // row segment geometry
+    const int seg = LONG ? wave : 0;
+    const int seg_base = seg * UNITS * 64;
+    const int rows_per_wave = LONG ? 0 : (64 >> log_lanes);
+    const int row_sub = LONG ? 0 : wave * rows_per_wave * RPL + (lane >> log_lanes);
+    const int rows_per_group = LONG ? 1 : (int)(blockDim.x >> 6) * rows_per_wave * RPL;
+
+    // unit index (within the row) read by unit u, and written after the
+    // DPP permutation and the permlane swaps
+    auto in_unit = [&](int u) { return seg_base + u * lanes + l; };
+    int pl = l;
+    if (n_dpp > 0) {
+        int c = (int)((a.pi >> (4 * l16)) & 15);
+        int mask = (1 << n_dpp) - 1;
+        pl = (l & ~mask) | (c & mask);
+    }
+    auto out_unit = [&](int u) {
+        int lo = pl, uo = u;
+        if (swap16) {
+            int lb = (lo >> 4) & 1, ub = uo & 1;
+            lo = (lo & ~16) | (ub << 4);
+            uo = (uo & ~1) | lb;
+        }
+        if (swap32) {
+            int lb = (lo >> 5) & 1, ub = (uo >> 1) & 1;
+            lo = (lo & ~32) | (ub << 5);
+            uo = (uo & ~2) | (lb << 1);
+        }
+        return seg_base + uo * lanes + lo;
+    };
+
+    const int64_t g_begin = (int64_t)blockIdx.x * a.chunk;
+    int64_t g_end = g_begin + a.chunk;
+    if (g_end > a.groups)
+        g_end = a.groups;
+    if (g_begin >= g_end)
+        return;
+
+    // rows of group g handled by this lane: row(g, k) = g*rows_per_group +
+    // row_sub + k*rows_per_wave
+    auto row_of = [&](int64_t g, int k) {
+        return g * rows_per_group + row_sub + (int64_t)k * rows_per_wave;
+    };
+    const int64_t last_row = a.rows - 1;
+
+    // ---- loads (addresses clamped to valid memory; results of rows or
+    // units past the end are never stored)
+    auto load = [&](int64_t g, RawUnit<OP, IN> (&raw)[RPL][UNITS]) {
+#pragma unroll
+        for (int k = 0; k < RPL; ++k) {
+            int64_t row = row_of(g, k);
+            row = row < last_row ? row : last_row;
+            // row base (wave-uniform when a wave holds one row) + lane offset
+            const int64_t re = row * (int64_t)a.n;
+#pragma unroll
+            for (int u = 0; u < UNITS; ++u) {
+                int un = in_unit(u);
+                if (LONG)
+                    un = un < units_row ? un : units_row - 1;
+                if constexpr (OP == kDequantInv) {
+                    if (a.bits == 4) {
+                        const uint8_t *rp = (const uint8_t *)a.codes_in + (re >> 1);
+                        raw[k][u].w[0] = *(const uint32_t *)(rp + un * 4);
+                        raw[k][u].w[1] = 0;
+                    } else {
+                        const int8_t *rp = (const int8_t *)a.codes_in + re;
+                        uint2 t = *(const uint2 *)(rp + un * 8);
+                        raw[k][u].w[0] = t.x;
+                        raw[k][u].w[1] = t.y;
+                    }
+                } else if constexpr (IN == kF32) {
+                    const float *rp = (const float *)a.x + re;
+                    const uint4 *src = (const uint4 *)(rp + un * 8);
+                    uint4 p = src[0], q = src[1];
+                    raw[k][u].w[0] = p.x; raw[k][u].w[1] = p.y;
+                    raw[k][u].w[2] = p.z; raw[k][u].w[3] = p.w;
+                    raw[k][u].w[4] = q.x; raw[k][u].w[5] = q.y;
+                    raw[k][u].w[6] = q.z; raw[k][u].w[7] = q.w;
+                } else {
+                    const uint16_t *rp = (const uint16_t *)a.x + re;
+                    uint4 p = *(const uint4 *)(rp + un * 8);
+                    raw[k][u].w[0] = p.x; raw[k][u].w[1] = p.y;
+                    raw[k][u].w[2] = p.z; raw[k][u].w[3] = p.w;
+                }
+            }
+        }
+    };
+
+    RawUnit<OP, IN> cur[RPL][UNITS];
+    if (HQ_PREFETCH)
+        load(g_begin, cur);
+
+    int parity = 0;
+    for (int64_t g = g_begin; g < g_end; ++g) {
+        float v[RPL][UNITS][8];
+        // An opaque zero added to the LDS sign-table index: it keeps the
+        // compiler from hoisting the (row-independent) table reads out of
+        // the loop, which would pin four registers per unit for good.
+        int lds_zero;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(lds_zero));
+
+        if (!HQ_PREFETCH)
+            load(g, cur);
+        // -------------------------------------------- widen + sign + bit 0
+#pragma unroll
+        for (int u = 0; u < UNITS; ++u) {
+            if constexpr (OP == kDequantInv) {
+#pragma unroll
+                for (int k = 0; k < RPL; ++k) {
+                    if (a.bits == 4) {
+                        uint32_t w = cur[k][u].w[0];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            v[k][u][j] = (float)((int32_t)(w << (28 - 4 * j)) >> 28);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            uint32_t word = cur[k][u].w[j >> 2];
+                            v[k][u][j] = (float)((int32_t)(word << (24 - 8 * (j & 3))) >> 24);
+                        }
+                    }
+                    if (logb > 0) {
+                        bfly(v[k][u][0], v[k][u][1]);
+                        bfly(v[k][u][2], v[k][u][3]);
+                        bfly(v[k][u][4], v[k][u][5]);
+                        bfly(v[k][u][6], v[k][u][7]);
+                    }
+                }
+            } else {
+                int su = in_unit(u);
+                if (LONG)
+                    su = su < units_row ? su : units_row - 1;
+                const uint4 sg = *(const uint4 *)&lds_sign[su * 4 + lds_zero];
+                const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
+#pragma unroll
+                for (int k = 0; k < RPL; ++k) {
+                    if constexpr (IN == kF32) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            v[k][u][j] = flip(__uint_as_float(cur[k][u].w[j]),
+                                              (sw[j >> 1] >> ((j & 1) ? 31 : 15)) & 1);
+                        if (logb > 0) {
+                            bfly(v[k][u][0], v[k][u][1]);
+                            bfly(v[k][u][2], v[k][u][3]);
+                            bfly(v[k][u][4], v[k][u][5]);
+                            bfly(v[k][u][6], v[k][u][7]);
+                        }
+                    } else if (logb > 0) {
+#pragma unroll
+                        for (int p = 0; p < 4; ++p)
+                            dot2_pair<IN>(cur[k][u].w[p], sw[p], v[k][u][2 * p], v[k][u][2 * p + 1]);
+                    } else {
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) {
+                            uint32_t w = cur[k][u].w[p];
+                            float lo, hi;
+                            if constexpr (IN == kBF16) {
+                                lo = bf16_lo(w);
+                                hi = bf16_hi(w);
+                            } else {
+                                lo = f16_to_f32((uint16_t)(w & 0xffff));
+                                hi = f16_to_f32((uint16_t)(w >> 16));
+                            }
+                            v[k][u][2 * p] = flip(lo, (sw[p] >> 15) & 1);
+                            v[k][u][2 * p + 1] = flip(hi, (sw[p] >> 31) & 1);
+                        }
+                    }
+                }
+            }
+        }
+
+        // ------------------------------------ prefetch the next row group
+        if (HQ_PREFETCH) {
+            int64_t gn = g + 1 < g_end ? g + 1 : g;
+            load(gn, cur);
+        }
+
+        // ------------------------------------------ in-unit stages (bits 1, 2)
+#pragma unroll
+        for (int k = 0; k < RPL; ++k)
+#pragma unroll
+            for (int u = 0; u < UNITS; ++u) {
+                if (logb > 1) {
+                    bfly(v[k][u][0], v[k][u][2]);
+                    bfly(v[k][u][1], v[k][u][3]);
+                    bfly(v[k][u][4], v[k][u][6]);
+                    bfly(v[k][u][5], v[k][u][7]);
+                }
+                if (logb > 2) {
+                    bfly(v[k][u][0], v[k][u][4]);
+                    bfly(v[k][u][1], v[k][u][5]);
+                    bfly(v[k][u][2], v[k][u][6]);
+                    bfly(v[k][u][3], v[k][u][7]);
+                }
+            }
+        // --------------------------------------------------- unit-bit stages
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            if ((1 << t) < UNITS && t < unit_bits) {
+#pragma unroll
+                for (int k = 0; k < RPL; ++k)
+#pragma unroll
+                    for (int u = 0; u < UNITS; ++u) {
+                        if ((u >> t) & 1)
+                            continue;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            bfly(v[k][u][j], v[k][u + (1 << t)][j]);
+                    }
+            }
+        }
+        // ----------------------------------------------- DPP lane stages 0..3
+#pragma unroll
+        for (int k = 0; k < RPL; ++k)
+#pragma unroll
+            for (int u = 0; u < UNITS; ++u) {
+                if (n_dpp > 0) dpp_stage<0>(v[k][u], sig0);
+                if (n_dpp > 1) dpp_stage<1>(v[k][u], sig1);
+                if (n_dpp > 2) dpp_stage<2>(v[k][u], sig2);
+                if (n_dpp > 3) dpp_stage<3>(v[k][u], sig3);
+            }
+        // ---------------------------------------- lane bits 4, 5 via permlane
+        if constexpr (UNITS >= 2) {
+            if (swap16) {
+#pragma unroll
+                for (int k = 0; k < RPL; ++k)
+#pragma unroll
+                    for (int u = 0; u < UNITS; u += 2)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            auto r = __builtin_amdgcn_permlane16_swap(
+                                __float_as_uint(v[k][u][j]), __float_as_uint(v[k][u + 1][j]),
+                                false, false);
+                            v[k][u][j] = __uint_as_float(r[0]);
+                            v[k][u + 1][j] = __uint_as_float(r[1]);
+                            bfly(v[k][u][j], v[k][u + 1][j]);
+                        }
+            }
+        }
+        if constexpr (UNITS >= 4) {
+            if (swap32) {
+#pragma unroll
+                for (int k = 0; k < RPL; ++k)
+#pragma unroll
+                    for (int u = 0; u < UNITS; ++u) {
+                        if (u & 2)
+                            continue;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            auto r = __builtin_amdgcn_permlane32_swap(
+                                __float_as_uint(v[k][u][j]), __float_as_uint(v[k][u + 2][j]),
+                                false, false);
+                            v[k][u][j] = __uint_as_float(r[0]);
+                            v[k][u + 2][j] = __uint_as_float(r[1]);
+                            bfly(v[k][u][j], v[k][u + 2][j]);
+                        }
+                    }
+            }
+        }
+
+        // ------------------------------------------------------------ outputs
+#pragma unroll
+        for (int k = 0; k < RPL; ++k) {
+            const int64_t row = row_of(g, k);
+            const bool row_ok = row < a.rows;
+            const int64_t rbase = row * (int64_t)a.n;
+
+            if constexpr (OP == kRotate) {
+                const float m = lane_neg ? -a.rb : a.rb;
+                if (row_ok) {
+#pragma unroll
+                    for (int u = 0; u < UNITS; ++u) {
+                        const int ou = out_unit(u);
+                        if (LONG && ou >= units_row)
+                            continue;
+                        float4 *dst = (float4 *)((float *)a.y + rbase + (int64_t)ou * 8);
+                        dst[0] = make_float4(v[k][u][0] * m, v[k][u][1] * m, v[k][u][2] * m,
+                                             v[k][u][3] * m);
+                        dst[1] = make_float4(v[k][u][4] * m, v[k][u][5] * m, v[k][u][6] * m,
+                                             v[k][u][7] * m);
+                    }
+                }
+            } else if constexpr (OP == kDequantInv) {
+                float sc = 0.0f;
+                const int64_t rr = row < last_row ? row : last_row;
+                if (a.scale_f16)
+                    sc = f16_to_f32(((const uint16_t *)a.scales_in)[rr]);
+                else
+                    sc = ((const float *)a.scales_in)[rr];
+                float t = sc * a.rb;
+                t = lane_neg ? -t : t;
+                if (row_ok) {
+#pragma unroll
+                    for (int u = 0; u < UNITS; ++u) {
+                        const int ou = out_unit(u);
+                        if (LONG && ou >= units_row)
+                            continue;
+                        const uint2 sb = *(const uint2 *)&lds_sign[ou * 2 + lds_zero];
+                        float o[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            uint32_t word = j < 4 ? sb.x : sb.y;
+                            o[j] = flip(v[k][u][j] * t, (word >> (8 * (j & 3) + 7)) & 1);
+                        }
+                        if constexpr (IN == kF32) {
+                            float4 *dst = (float4 *)((float *)a.y + rbase + (int64_t)ou * 8);
+                            dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+                            dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+                        } else {
+                            uint4 pk;
+                            pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+                            pk.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+                            pk.z = (uint32_t)f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
+                            pk.w = (uint32_t)f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
+                            *(uint4 *)((uint16_t *)a.y + rbase + (int64_t)ou * 8) = pk;
+                        }
+                    }
+                }
+            } else {
+                // absmax of the row (units past the end of a long row excluded)
+                float m = 0.0f;
+#pragma unroll
+                for (int u = 0; u < UNITS; ++u) {
+                    float mu = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < 8; j += 2)
+                        mu = fmaxf(fmaxf(mu, fabsf(v[k][u][j])), fabsf(v[k][u][j + 1]));
+                    // after the permlane swaps register u holds the data of
+                    // output unit out_unit(u): that decides whether it lies
+                    // past the end of the row
+                    if (LONG)
+                        mu = out_unit(u) < units_row ? mu : 0.0f;
+                    m = fmaxf(m, mu);
+                }
+                m = segment_max(m, log_lanes);
+                if constexpr (LONG) {
+                    if (a.wpr > 1) {
+                        if (lane == 0)
+                            red[parity][wave] = m;
+                        __syncthreads();
+                        m = red[parity][0];
+                        for (int w2 = 1; w2 < a.wpr; ++w2)
+                            m = fmaxf(m, red[parity][w2]);
+                        parity ^= 1;
+                    }
+                }
+                const int qmax = a.bits == 4 ? 7 : 127;
+                RowQuant rq = row_quant(m, a.kq, qmax);
+                if (row_ok && l == 0 && seg == 0) {
+                    if (a.scale_f16)
+                        ((uint16_t *)a.scales)[row] = f32_to_f16(rq.scale);
+                    else
+                        ((float *)a.scales)[row] = rq.scale;
+                }
+                const float inv = lane_neg ? -rq.inv : rq.inv;
+                if (a.bits == 4) {
+                    if (row_ok) {
+#pragma unroll
+                        for (int u = 0; u < UNITS; ++u) {
+                            uint32_t f[8];
+#pragma unroll
+                            for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 8
+                                f[j] = __float_as_uint(__builtin_fmaf(v[k][u][j], inv, 12582920.0f));
+                            const int ou = out_unit(u);
+                            if (LONG && ou >= units_row)
+                                continue;
+                            *(uint32_t *)((uint8_t *)a.codes + (rbase >> 1) + (int64_t)ou * 4) =
+                                pack_int4(f);
+                        }
+                    }
+                } else {
+                    if (row_ok) {
+#pragma unroll
+                        for (int u = 0; u < UNITS; ++u) {
+                            uint32_t f[8];
+#pragma unroll
+                            for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 128
+                                f[j] = __float_as_uint(__builtin_fmaf(v[k][u][j], inv, 12583040.0f));
+                            const int ou = out_unit(u);
+                            if (LONG && ou >= units_row)
+                                continue;
+                            uint2 pk = make_uint2(pack_int8(f[0], f[1], f[2], f[3]),
+                                                  pack_int8(f[4], f[5], f[6], f[7]));
+                            *(uint2 *)((int8_t *)a.codes + rbase + (int64_t)ou * 8) = pk;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- launching
+
+struct Plan {
+    int units;      // 1, 2, 4 or 8
+    int log_lanes;  // 0..6
+    int logb;       // log2 b
+    int rpl;        // rows per lane per iteration
+    int wpr;        // waves per row (> 1: long rows)
+    bool is_long;
+};
+
+bool make_plan(int n, int b, Plan &p);
+void fill_args(FastArgs &fa, const Request &r, const Plan &p);
+int occupancy_blocks(const void *fn, int threads, size_t lds);
+
+template <int OP, int IN, int UNITS, int LOG_LANES, int LOGB, int RPL, bool LONG>
+hipError_t launch_one(FastArgs fa, const Plan &p, const Request &r, const DeviceInfo &dev)
+{
+    const int threads = LONG ? 64 * p.wpr : 256;
+    const int rows_per_group = LONG ? 1 : 4 * (64 >> p.log_lanes) * RPL;
+    fa.groups = (r.rows + rows_per_group - 1) / rows_per_group;
+    const size_t lds = OP == kDequantInv ? (size_t)r.n : (size_t)r.n * 2;
+    auto fn = fast_kernel<OP, IN, UNITS, LOG_LANES, LOGB, RPL, LONG>;
+    const int occ = occupancy_blocks((const void *)fn, threads, lds);
+    const int64_t max_grid = (int64_t)dev.cu_count * occ;
+    int64_t grid = fa.groups < max_grid ? fa.groups : max_grid;
+    fa.chunk = (fa.groups + grid - 1) / grid;
+    grid = (fa.groups + fa.chunk - 1) / fa.chunk;
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), lds, r.stream, fa);
+    return hipGetLastError();
+}
+
+// Specialised instantiations for one (OP, IN); anything else runs the
+// variant with a run-time stage plan.
+template <int OP, int IN>
+hipError_t dispatch_op(const Request &r, const DeviceInfo &dev)
+{
+    Plan p;
+    if (!make_plan(r.n, r.b, p))
+        return hipErrorInvalidValue;
+    FastArgs fa{};
+    fill_args(fa, r, p);
+    if (p.is_long) {
+        if (p.logb == 7) {
+            switch (p.units) {
+            case 1: return launch_one<OP, IN, 1, 6, 7, 1, true>(fa, p, r, dev);
+            case 2: return launch_one<OP, IN, 2, 6, 7, 1, true>(fa, p, r, dev);
+            case 4: return launch_one<OP, IN, 4, 6, 7, 1, true>(fa, p, r, dev);
+            default: break;
+            }
+        }
+        switch (p.units) {
+        case 1: return launch_one<OP, IN, 1, 6, -1, 1, true>(fa, p, r, dev);
+        case 2: return launch_one<OP, IN, 2, 6, -1, 1, true>(fa, p, r, dev);
+        case 4: return launch_one<OP, IN, 4, 6, -1, 1, true>(fa, p, r, dev);
+        default: return launch_one<OP, IN, 8, 6, -1, 1, true>(fa, p, r, dev);
+        }
+    }
+    const int n = r.n;
+    if (p.logb == 7 || (1 << p.logb) == n) {
+        const bool full = (1 << p.logb) == n;
+        switch (n) {
+        case 16: return launch_one<OP, IN, 1, 1, 4, 4, false>(fa, p, r, dev);
+        case 32: return launch_one<OP, IN, 1, 2, 5, 4, false>(fa, p, r, dev);
+        case 64: return launch_one<OP, IN, 1, 3, 6, 4, false>(fa, p, r, dev);
+        case 128: return launch_one<OP, IN, 1, 4, 7, 4, false>(fa, p, r, dev);
+        case 256:
+            return full ? launch_one<OP, IN, 2, 4, 8, 2, false>(fa, p, r, dev)
+                        : launch_one<OP, IN, 2, 4, 7, 2, false>(fa, p, r, dev);
+        case 512:
+            return full ? launch_one<OP, IN, 4, 4, 9, 1, false>(fa, p, r, dev)
+                        : launch_one<OP, IN, 4, 4, 7, 1, false>(fa, p, r, dev);
+        case 1024:
+            return full ? launch_one<OP, IN, 8, 4, 10, 1, false>(fa, p, r, dev)
+                        : launch_one<OP, IN, 8, 4, 7, 1, false>(fa, p, r, dev);
+        case 2048:
+            return full ? launch_one<OP, IN, 8, 5, 11, 1, false>(fa, p, r, dev)
+                        : launch_one<OP, IN, 8, 5, 7, 1, false>(fa, p, r, dev);
+        case 4096:
+            return full ? launch_one<OP, IN, 8, 6, 12, 1, false>(fa, p, r, dev)
+                        : launch_one<OP, IN, 8, 6, 7, 1, false>(fa, p, r, dev);
+        default: break;
+        }
+    }
+    switch (p.units) {
+    case 1: return launch_one<OP, IN, 1, -1, -1, 1, false>(fa, p, r, dev);
+    case 2: return launch_one<OP, IN, 2, -1, -1, 1, false>(fa, p, r, dev);
+    case 4: return launch_one<OP, IN, 4, -1, -1, 1, false>(fa, p, r, dev);
+    default: return launch_one<OP, IN, 8, -1, -1, 1, false>(fa, p, r, dev);
+    }
+}
+
+}  // namespace fast
+}  // namespace hq
