@@ -45,6 +45,17 @@ namespace fast {
 
 constexpr int kMaxWpr = 16;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Loads of data that is read exactly once: the non-temporal hint keeps the
+// streamed rows from displacing other lines in the caches.
+template <class T>
+__device__ __forceinline__ T stream_load(const T *p)
+{
+    return __builtin_nontemporal_load(p);
+}
+
 struct FastArgs {
     const void *x;
     const void *codes_in;
@@ -54,8 +65,7 @@ struct FastArgs {
     void *scales;
     void *y;
     int64_t rows;
-    int64_t groups;       // row groups in total (one workgroup iteration each)
-    int64_t chunk;        // consecutive row groups per workgroup
+    int64_t groups;       // row groups in total (see the work split)
     uint64_t pi;          // output chunk of lane l & 15 after the DPP stages
     uint32_t neg;         // bit l set: lane l holds the negated value
     int n;
@@ -70,35 +80,43 @@ struct FastArgs {
 
 // ------------------------------------------------------------ primitives
 
-// One DPP butterfly stage on 8 registers: v += sigma * v[partner lane].
-// "s_nop 4" first: a DPP read needs two wait states after a VALU write of
-// its source and five after an EXEC write; no instruction of the block
-// reads a register that an earlier instruction of the same block wrote.
-#define HQ_DPP8(CTRL)                                                                   \
-    asm volatile("s_nop 4\n\t"                                                          \
-                 "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
-                 "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
-                 "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
-                 "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
-                 "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
-                 "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
-                 "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"   \
-                 "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"       \
-                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]),        \
-                   "+v"(v[5]), "+v"(v[6]), "+v"(v[7])                                   \
-                 : "v"(sigma))
+// The DPP butterfly stages of one unit: for every stage t < NST and every
+// register, v += sigma_t * v[partner lane of stage t].  One asm block per
+// unit, opened by "s_nop 4": a DPP read needs two wait states after a VALU
+// write of its source and five after an EXEC write.  Inside the block each
+// register is read again only eight instructions after it was written.
+#define HQ_DPP_ROW(C, S)                                                      \
+    "v_fmac_f32_dpp %0, %0, %" S " " C " row_mask:0xf bank_mask:0xf\n\t"      \
+    "v_fmac_f32_dpp %1, %1, %" S " " C " row_mask:0xf bank_mask:0xf\n\t"      \
+    "v_fmac_f32_dpp %2, %2, %" S " " C " row_mask:0xf bank_mask:0xf\n\t"      \
+    "v_fmac_f32_dpp %3, %3, %" S " " C " row_mask:0xf bank_mask:0xf\n\t"      \
+    "v_fmac_f32_dpp %4, %4, %" S " " C " row_mask:0xf bank_mask:0xf\n\t"      \
+    "v_fmac_f32_dpp %5, %5, %" S " " C " row_mask:0xf bank_mask:0xf\n\t"      \
+    "v_fmac_f32_dpp %6, %6, %" S " " C " row_mask:0xf bank_mask:0xf\n\t"      \
+    "v_fmac_f32_dpp %7, %7, %" S " " C " row_mask:0xf bank_mask:0xf\n\t"
+#define HQ_DPP_C0 "quad_perm:[1,0,3,2]"
+#define HQ_DPP_C1 "quad_perm:[2,3,0,1]"
+#define HQ_DPP_C2 "row_half_mirror"
+#define HQ_DPP_C3 "row_ror:8"
+#define HQ_DPP_OPS                                                             \
+    : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), \
+      "+v"(v[6]), "+v"(v[7])                                                  \
+    : "v"(s0), "v"(s1), "v"(s2), "v"(s3)
 
-template <int STAGE>
-__device__ __forceinline__ void dpp_stage(float (&v)[8], float sigma)
+template <int NST>
+__device__ __forceinline__ void dpp_stages(float (&v)[8], float s0, float s1, float s2, float s3)
 {
-    if constexpr (STAGE == 0)
-        HQ_DPP8("quad_perm:[1,0,3,2]");
-    else if constexpr (STAGE == 1)
-        HQ_DPP8("quad_perm:[2,3,0,1]");
-    else if constexpr (STAGE == 2)
-        HQ_DPP8("row_half_mirror");
-    else
-        HQ_DPP8("row_ror:8");
+    if constexpr (NST == 1)
+        asm volatile("s_nop 4\n\t" HQ_DPP_ROW(HQ_DPP_C0, "8") HQ_DPP_OPS);
+    else if constexpr (NST == 2)
+        asm volatile("s_nop 4\n\t" HQ_DPP_ROW(HQ_DPP_C0, "8") HQ_DPP_ROW(HQ_DPP_C1, "9")
+                     HQ_DPP_OPS);
+    else if constexpr (NST == 3)
+        asm volatile("s_nop 4\n\t" HQ_DPP_ROW(HQ_DPP_C0, "8") HQ_DPP_ROW(HQ_DPP_C1, "9")
+                         HQ_DPP_ROW(HQ_DPP_C2, "10") HQ_DPP_OPS);
+    else if constexpr (NST == 4)
+        asm volatile("s_nop 4\n\t" HQ_DPP_ROW(HQ_DPP_C0, "8") HQ_DPP_ROW(HQ_DPP_C1, "9")
+                         HQ_DPP_ROW(HQ_DPP_C2, "10") HQ_DPP_ROW(HQ_DPP_C3, "11") HQ_DPP_OPS);
 }
 
 // First butterfly of an input pair fused with widening and the sign flip:
@@ -128,28 +146,34 @@ __device__ __forceinline__ float flip(float v, uint32_t sbit)
     return __uint_as_float(__float_as_uint(v) ^ (sbit << 31));
 }
 
+// (a | b) ^ c in one v_bitop3_b32.  The constant sits in the middle operand,
+// which makes the truth table the same whichever operand the hardware takes
+// as the most significant index bit.
+__device__ __forceinline__ uint32_t or_xor(uint32_t a, uint32_t b, uint32_t c)
+{
+    return __builtin_amdgcn_bitop3_b32(a, c, b, 0x36);
+}
+
 // Packs 8 INT4 codes: f[j] = 0x4B400008 + q_j with q_j in [-7, 7] (the +8
-// offset keeps every nibble free of borrows); element j lands in nibble j as
-// 4-bit two's complement.
+// offset keeps every nibble free of borrows, and byte 1 of every f is 0);
+// element j lands in nibble j as 4-bit two's complement.
 __device__ __forceinline__ uint32_t pack_int4(const uint32_t (&f)[8])
 {
-    uint32_t t01 = (f[1] << 4) + f[0];
-    uint32_t t23 = (f[3] << 4) + f[2];
-    uint32_t t45 = (f[5] << 4) + f[4];
-    uint32_t t67 = (f[7] << 4) + f[6];
-    uint32_t u0 = (t23 << 8) | t01;  // bytes 0,1 valid
-    uint32_t u1 = (t67 << 8) | t45;
-    uint32_t p = __builtin_amdgcn_perm(u1, u0, 0x05040100u);
-    return p ^ 0x88888888u;
+    const uint32_t t01 = (f[1] << 4) + f[0];  // byte 0 = (q1+8)<<4 | (q0+8)
+    const uint32_t t23 = (f[3] << 4) + f[2];
+    const uint32_t t45 = (f[5] << 4) + f[4];
+    const uint32_t t67 = (f[7] << 4) + f[6];
+    const uint32_t lo = __builtin_amdgcn_perm(t23, t01, 0x0c0c0400u);  // [t01.b0, t23.b0, 0, 0]
+    const uint32_t hi = __builtin_amdgcn_perm(t67, t45, 0x04000c0cu);  // [0, 0, t45.b0, t67.b0]
+    return or_xor(lo, hi, 0x88888888u);
 }
 
 // Packs 4 INT8 codes held as 0x4B400080 + q, q in [-127, 127].
 __device__ __forceinline__ uint32_t pack_int8(uint32_t f0, uint32_t f1, uint32_t f2, uint32_t f3)
 {
-    uint32_t u0 = (f1 << 8) | f0;
-    uint32_t u1 = (f3 << 8) | f2;
-    uint32_t p = __builtin_amdgcn_perm(u1, u0, 0x05040100u);
-    return p ^ 0x80808080u;
+    const uint32_t lo = __builtin_amdgcn_perm(f1, f0, 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(f3, f2, 0x04000c0cu);
+    return or_xor(lo, hi, 0x80808080u);
 }
 
 template <int CTRL>
@@ -188,15 +212,9 @@ struct RawUnit {
 // RPL        independent rows per lane per iteration (short rows)
 // LONG       a row spans FastArgs::wpr waves (LOG_LANES == 6, RPL == 1);
 //            units past the row end are loaded clamped and ignored
-#ifndef HQ_WAVES_PER_EU
-#define HQ_WAVES_PER_EU 1
-#endif
-#ifndef HQ_PREFETCH
-#define HQ_PREFETCH 1
-#endif
 template <int OP, int IN, int UNITS, int LOG_LANES, int LOGB, int RPL, bool LONG>
-__global__ __launch_bounds__(LONG && UNITS < 8 ? 1024 : 256)
-__attribute__((amdgpu_waves_per_eu(HQ_WAVES_PER_EU, 8))) void fast_kernel(FastArgs a)
+__global__ __launch_bounds__(UNITS < 8 ? 1024 : (LONG ? 256 : 768))
+void fast_kernel(FastArgs a)
 {
     extern __shared__ __align__(16) uint32_t lds_sign[];  // sign material of one row width
     __shared__ float red[2][kMaxWpr];
@@ -208,22 +226,6 @@ __attribute__((amdgpu_waves_per_eu(HQ_WAVES_PER_EU, 8))) void fast_kernel(FastAr
     const int lanes = 1 << log_lanes;
     const int l = lane & (lanes - 1);  // lane within its row segment
     const int units_row = a.n >> 3;
-
-    // ---- sign material -> LDS (row independent).  Forward: +-1 pairs in
-    // the input's 16-bit format, one word per element pair.  Inverse: the
-    // raw sign bytes.
-    if constexpr (OP == kDequantInv) {
-        for (int i = threadIdx.x; i < (a.n >> 2); i += blockDim.x)
-            lds_sign[i] = ((const uint32_t *)a.s)[i];
-    } else {
-        const uint32_t one = (IN == kF16) ? 0x3C00u : 0x3F80u;
-        for (int i = threadIdx.x; i < (a.n >> 1); i += blockDim.x) {
-            uint32_t two = ((const uint16_t *)a.s)[i];
-            uint32_t s0 = (two >> 7) & 1, s1 = (two >> 15) & 1;
-            lds_sign[i] = (one | (s0 << 15)) | ((one | (s1 << 15)) << 16);
-        }
-    }
-    __syncthreads();
 
     // ---- stage plan (compile-time when LOGB and LOG_LANES are)
     const int lane_bits = logb > 3 ? (logb - 3 < log_lanes ? logb - 3 : log_lanes) : 0;
@@ -243,44 +245,62 @@ __attribute__((amdgpu_waves_per_eu(HQ_WAVES_PER_EU, 8))) void fast_kernel(FastAr
     const int seg = LONG ? wave : 0;
     const int seg_base = seg * UNITS * 64;
     const int rows_per_wave = LONG ? 0 : (64 >> log_lanes);
-    const int row_sub = LONG ? 0 : wave * rows_per_wave * RPL + (lane >> log_lanes);
-    const int rows_per_group = LONG ? 1 : (int)(blockDim.x >> 6) * rows_per_wave * RPL;
+    // Work split.  Long rows: the waves of a workgroup share each row.
+    // Short rows: a wave works alone on "wave groups" of
+    // rows_per_wave * RPL consecutive rows, and each workgroup (one per CU,
+    // holding all of that CU's waves) hands its share of the groups out
+    // through an LDS counter:
+    // the SIMD arbiter favours older waves, so a static split per wave
+    // would leave the youngest waves with most of their rows at the end.
+    __shared__ int pool_next;
+    const int row_sub = LONG ? 0 : (lane >> log_lanes);
+    const int rows_per_group = LONG ? 1 : rows_per_wave * RPL;
+    // Workgroup b owns groups b, b + grid, b + 2*grid, ... (strided: speed
+    // differences between CUs and address ranges average out).
+    const int64_t pool_size = (a.groups - blockIdx.x + gridDim.x - 1) / gridDim.x;
+    const int nwaves = blockDim.x >> 6;
+    // the first group of every wave is fixed (no LDS round trip before the
+    // first load); the counter starts after them
+    const int64_t first = LONG ? 0 : wave;
+    const bool has_work = first < pool_size;
+    if (threadIdx.x == 0)
+        pool_next = nwaves;
+    auto grab = [&]() -> int64_t {
+        int v = 0;
+        if (lane == 0)
+            v = atomicAdd(&pool_next, 1);
+        return __builtin_amdgcn_readfirstlane(v);
+    };
 
     // unit index (within the row) read by unit u, and written after the
     // DPP permutation and the permlane swaps
     auto in_unit = [&](int u) { return seg_base + u * lanes + l; };
     int pl = l;
     if (n_dpp > 0) {
-        int c = (int)((a.pi >> (4 * l16)) & 15);
-        int mask = (1 << n_dpp) - 1;
+        const int c = (int)((a.pi >> (4 * l16)) & 15);
+        const int mask = (1 << n_dpp) - 1;
         pl = (l & ~mask) | (c & mask);
     }
     auto out_unit = [&](int u) {
         int lo = pl, uo = u;
-        if (swap16) {
-            int lb = (lo >> 4) & 1, ub = uo & 1;
+        if (swap16) {  // lane bit 4 <-> unit bit 0
+            const int lb = (lo >> 4) & 1, ub = uo & 1;
             lo = (lo & ~16) | (ub << 4);
             uo = (uo & ~1) | lb;
         }
-        if (swap32) {
-            int lb = (lo >> 5) & 1, ub = (uo >> 1) & 1;
+        if (swap32) {  // lane bit 5 <-> unit bit 1
+            const int lb = (lo >> 5) & 1, ub = (uo >> 1) & 1;
             lo = (lo & ~32) | (ub << 5);
             uo = (uo & ~2) | (lb << 1);
         }
         return seg_base + uo * lanes + lo;
     };
 
-    const int64_t g_begin = (int64_t)blockIdx.x * a.chunk;
-    int64_t g_end = g_begin + a.chunk;
-    if (g_end > a.groups)
-        g_end = a.groups;
-    if (g_begin >= g_end)
-        return;
-
-    // rows of group g handled by this lane: row(g, k) = g*rows_per_group +
-    // row_sub + k*rows_per_wave
+    // rows of (pool-relative) group g handled by this lane:
+    // row(g, k) = (b + g*grid)*rows_per_group + k*rows_per_wave + row_sub
     auto row_of = [&](int64_t g, int k) {
-        return g * rows_per_group + row_sub + (int64_t)k * rows_per_wave;
+        return ((int64_t)blockIdx.x + g * gridDim.x) * rows_per_group + row_sub +
+               (int64_t)k * rows_per_wave;
     };
     const int64_t last_row = a.rows - 1;
 
@@ -301,47 +321,99 @@ __attribute__((amdgpu_waves_per_eu(HQ_WAVES_PER_EU, 8))) void fast_kernel(FastAr
                 if constexpr (OP == kDequantInv) {
                     if (a.bits == 4) {
                         const uint8_t *rp = (const uint8_t *)a.codes_in + (re >> 1);
-                        raw[k][u].w[0] = *(const uint32_t *)(rp + un * 4);
+                        raw[k][u].w[0] = stream_load((const uint32_t *)(rp + un * 4));
                         raw[k][u].w[1] = 0;
                     } else {
                         const int8_t *rp = (const int8_t *)a.codes_in + re;
-                        uint2 t = *(const uint2 *)(rp + un * 8);
-                        raw[k][u].w[0] = t.x;
-                        raw[k][u].w[1] = t.y;
+                        u32x2 t = stream_load((const u32x2 *)(rp + un * 8));
+                        raw[k][u].w[0] = t[0];
+                        raw[k][u].w[1] = t[1];
                     }
                 } else if constexpr (IN == kF32) {
                     const float *rp = (const float *)a.x + re;
-                    const uint4 *src = (const uint4 *)(rp + un * 8);
-                    uint4 p = src[0], q = src[1];
-                    raw[k][u].w[0] = p.x; raw[k][u].w[1] = p.y;
-                    raw[k][u].w[2] = p.z; raw[k][u].w[3] = p.w;
-                    raw[k][u].w[4] = q.x; raw[k][u].w[5] = q.y;
-                    raw[k][u].w[6] = q.z; raw[k][u].w[7] = q.w;
+                    const u32x4 *src = (const u32x4 *)(rp + un * 8);
+                    u32x4 p = stream_load(src), q = stream_load(src + 1);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        raw[k][u].w[t] = p[t];
+                        raw[k][u].w[4 + t] = q[t];
+                    }
                 } else {
                     const uint16_t *rp = (const uint16_t *)a.x + re;
-                    uint4 p = *(const uint4 *)(rp + un * 8);
-                    raw[k][u].w[0] = p.x; raw[k][u].w[1] = p.y;
-                    raw[k][u].w[2] = p.z; raw[k][u].w[3] = p.w;
+                    u32x4 p = stream_load((const u32x4 *)(rp + un * 8));
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        raw[k][u].w[t] = p[t];
                 }
             }
         }
     };
 
+    // ---- sign material -> LDS (row independent).  The sign vector is
+    // requested before the first row group so that the table does not wait
+    // behind the grid's initial burst of row loads; the LDS writes and the
+    // barrier follow once the row loads are in flight.  Forward: +-1 pairs
+    // in the input's 16-bit format, one word per element pair.  Inverse:
+    // the raw sign bytes.  One pass of kSignChunks 16-sign chunks per
+    // thread covers every row width the plans produce (n <= 1024 per wave
+    // of the workgroup times kSignChunks * 16 / 16).
+    constexpr int kSignChunks = 4;
+    uint4 sraw[kSignChunks];
+#pragma unroll
+    for (int q = 0; q < kSignChunks; ++q) {
+        const int c = threadIdx.x + q * blockDim.x;
+        sraw[q] = c < (a.n >> 4) ? ((const uint4 *)a.s)[c] : make_uint4(0, 0, 0, 0);
+    }
+
+    // The first row group is loaded unconditionally (a wave without work
+    // loads group 0 and ignores it), which keeps the count of loads in
+    // flight static, so the sign table below waits only for its own loads.
     RawUnit<OP, IN> cur[RPL][UNITS];
-    if (HQ_PREFETCH)
-        load(g_begin, cur);
+    load(has_work ? first : 0, cur);
+
+#pragma unroll
+    for (int q = 0; q < kSignChunks; ++q) {
+        const int c = threadIdx.x + q * blockDim.x;
+        if (c < (a.n >> 4)) {
+            const uint4 w = sraw[q];
+            if constexpr (OP == kDequantInv) {
+                ((uint4 *)lds_sign)[c] = w;
+            } else {
+                const uint32_t one = (IN == kF16) ? 0x3C00u : 0x3F80u;
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+                uint32_t o[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const uint32_t two = ww[t >> 1] >> ((t & 1) * 16);
+                    const uint32_t s0 = (two >> 7) & 1, s1 = (two >> 15) & 1;
+                    o[t] = (one | (s0 << 15)) | ((one | (s1 << 15)) << 16);
+                }
+                ((uint4 *)lds_sign)[2 * c] = make_uint4(o[0], o[1], o[2], o[3]);
+                ((uint4 *)lds_sign)[2 * c + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+            }
+        }
+    }
+    // LDS-only release: the barrier must not wait for the row loads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
     int parity = 0;
-    for (int64_t g = g_begin; g < g_end; ++g) {
+    int64_t g = first;
+    while (g < pool_size) {
         float v[RPL][UNITS][8];
-        // An opaque zero added to the LDS sign-table index: it keeps the
-        // compiler from hoisting the (row-independent) table reads out of
-        // the loop, which would pin four registers per unit for good.
-        int lds_zero;
-        asm volatile("v_mov_b32 %0, 0" : "=v"(lds_zero));
-
-        if (!HQ_PREFETCH)
-            load(g, cur);
+        // next group: the following one for long rows (every wave of the
+        // workgroup walks the same rows), else a fresh one from the pool;
+        // requested now, used at the prefetch below
+        const int64_t g_next = LONG ? g + 1 : grab();
+        // The lane's word offset in the sign table, passed through an empty
+        // asm each row: the compiler cannot hoist the (row-independent)
+        // table reads out of the loop, which would pin four registers per
+        // unit, and the per-unit offsets stay immediate.
+        int sofs = (seg_base + l) * 4;
+        asm volatile("" : "+v"(sofs));
+        int zofs = 0;  // the same for the inverse path's output-position signs
+        asm volatile("" : "+v"(zofs));
         // -------------------------------------------- widen + sign + bit 0
 #pragma unroll
         for (int u = 0; u < UNITS; ++u) {
@@ -368,10 +440,11 @@ __attribute__((amdgpu_waves_per_eu(HQ_WAVES_PER_EU, 8))) void fast_kernel(FastAr
                     }
                 }
             } else {
-                int su = in_unit(u);
+                int sidx = sofs + u * lanes * 4;  // = in_unit(u) * 4
                 if (LONG)
-                    su = su < units_row ? su : units_row - 1;
-                const uint4 sg = *(const uint4 *)&lds_sign[su * 4 + lds_zero];
+                    sidx = sidx < units_row * 4 ? sidx : (units_row - 1) * 4;
+                const uint4 sg =
+                    *(const uint4 *)__builtin_assume_aligned(&lds_sign[sidx], 16);
                 const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
 #pragma unroll
                 for (int k = 0; k < RPL; ++k) {
@@ -411,10 +484,8 @@ __attribute__((amdgpu_waves_per_eu(HQ_WAVES_PER_EU, 8))) void fast_kernel(FastAr
         }
 
         // ------------------------------------ prefetch the next row group
-        if (HQ_PREFETCH) {
-            int64_t gn = g + 1 < g_end ? g + 1 : g;
-            load(gn, cur);
-        }
+        if (g_next < pool_size)  // wave-uniform
+            load(g_next, cur);
 
         // ------------------------------------------ in-unit stages (bits 1, 2)
 #pragma unroll
@@ -455,10 +526,13 @@ __attribute__((amdgpu_waves_per_eu(HQ_WAVES_PER_EU, 8))) void fast_kernel(FastAr
         for (int k = 0; k < RPL; ++k)
 #pragma unroll
             for (int u = 0; u < UNITS; ++u) {
-                if (n_dpp > 0) dpp_stage<0>(v[k][u], sig0);
-                if (n_dpp > 1) dpp_stage<1>(v[k][u], sig1);
-                if (n_dpp > 2) dpp_stage<2>(v[k][u], sig2);
-                if (n_dpp > 3) dpp_stage<3>(v[k][u], sig3);
+                switch (n_dpp) {
+                case 1: dpp_stages<1>(v[k][u], sig0, sig1, sig2, sig3); break;
+                case 2: dpp_stages<2>(v[k][u], sig0, sig1, sig2, sig3); break;
+                case 3: dpp_stages<3>(v[k][u], sig0, sig1, sig2, sig3); break;
+                case 4: dpp_stages<4>(v[k][u], sig0, sig1, sig2, sig3); break;
+                default: break;
+                }
             }
         // ---------------------------------------- lane bits 4, 5 via permlane
         if constexpr (UNITS >= 2) {
@@ -536,7 +610,7 @@ __attribute__((amdgpu_waves_per_eu(HQ_WAVES_PER_EU, 8))) void fast_kernel(FastAr
                         const int ou = out_unit(u);
                         if (LONG && ou >= units_row)
                             continue;
-                        const uint2 sb = *(const uint2 *)&lds_sign[ou * 2 + lds_zero];
+                        const uint2 sb = *(const uint2 *)&lds_sign[ou * 2 + zofs];
                         float o[8];
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
@@ -578,7 +652,10 @@ __attribute__((amdgpu_waves_per_eu(HQ_WAVES_PER_EU, 8))) void fast_kernel(FastAr
                     if (a.wpr > 1) {
                         if (lane == 0)
                             red[parity][wave] = m;
-                        __syncthreads();
+                        // LDS-only: the barrier must not drain the prefetch
+                        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                        __builtin_amdgcn_s_barrier();
+                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
                         m = red[parity][0];
                         for (int w2 = 1; w2 < a.wpr; ++w2)
                             m = fmaxf(m, red[parity][w2]);
@@ -628,6 +705,7 @@ __attribute__((amdgpu_waves_per_eu(HQ_WAVES_PER_EU, 8))) void fast_kernel(FastAr
                 }
             }
         }
+        g = g_next;
     }
 }
 
@@ -649,16 +727,27 @@ int occupancy_blocks(const void *fn, int threads, size_t lds);
 template <int OP, int IN, int UNITS, int LOG_LANES, int LOGB, int RPL, bool LONG>
 hipError_t launch_one(FastArgs fa, const Plan &p, const Request &r, const DeviceInfo &dev)
 {
-    const int threads = LONG ? 64 * p.wpr : 256;
-    const int rows_per_group = LONG ? 1 : 4 * (64 >> p.log_lanes) * RPL;
+    // groups: rows of one workgroup iteration (LONG) or of one wave
+    // iteration (short rows)
+    const int rows_per_group = LONG ? 1 : (64 >> p.log_lanes) * RPL;
     fa.groups = (r.rows + rows_per_group - 1) / rows_per_group;
     const size_t lds = OP == kDequantInv ? (size_t)r.n : (size_t)r.n * 2;
     auto fn = fast_kernel<OP, IN, UNITS, LOG_LANES, LOGB, RPL, LONG>;
-    const int occ = occupancy_blocks((const void *)fn, threads, lds);
-    const int64_t max_grid = (int64_t)dev.cu_count * occ;
-    int64_t grid = fa.groups < max_grid ? fa.groups : max_grid;
-    fa.chunk = (fa.groups + grid - 1) / grid;
-    grid = (fa.groups + fa.chunk - 1) / fa.chunk;
+    int threads, grid_per_cu;
+    if (LONG) {
+        threads = 64 * p.wpr;
+        grid_per_cu = occupancy_blocks((const void *)fn, threads, lds);
+    } else {
+        // every wave the CU can hold, in as few workgroups as the
+        // 1024-thread (768 for the widest rows) limit allows
+        const int max_threads = UNITS < 8 ? 1024 : 768;
+        const int waves_cu = 4 * occupancy_blocks((const void *)fn, 256, lds);
+        grid_per_cu = (waves_cu * 64 + max_threads - 1) / max_threads;
+        threads = 64 * (waves_cu / grid_per_cu);
+    }
+    int64_t grid = (int64_t)dev.cu_count * grid_per_cu;
+    if (grid > fa.groups)
+        grid = fa.groups;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), lds, r.stream, fa);
     return hipGetLastError();
 }
