@@ -34,6 +34,12 @@ LLC_BYTES = 256 * 2 ** 20
 METRIC = "fused rotate+INT4-quant GB/s and % of HBM peak at 16384x4096 bf16"
 
 
+def copy_bytes_for(bytes_call: int) -> int:
+    """Size of the plain device copy timed beside the kernel (it moves the
+    same number of bytes: half read, half written)."""
+    return bytes_call // 2
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "hadamard_rotation_amd", "csrc", "*"))):
@@ -41,6 +47,47 @@ def source_hash() -> str:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def _csv_means(path: str, counter: str) -> dict:
+    """Mean per dispatch of `counter` for every (kernel name, grid size) in a
+    rocprofv3 counter_collection CSV, with the dispatch count."""
+    import csv
+    acc: dict = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], int(r["Grid_Size"]))
+            acc.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_bytes: int) -> dict:
+    """HBM bytes per launch of the dominant hq kernel from two rocprofv3
+    --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; both in KiB per
+    dispatch), each scaled by what the same counter reads for the plain
+    device copy of `copy_bytes` bytes that the script also times (the
+    copy launch repeated most often; other copies, e.g. buffer clones,
+    have other grid sizes)."""
+    fetch = _csv_means(fetch_csv, "FETCH_SIZE")
+    write = _csv_means(write_csv, "WRITE_SIZE")
+    copy_key = max((k for k in fetch if "copyBuffer" in k[0]), key=lambda k: fetch[k][1])
+    kern_key = max((k for k in fetch if "hq::" in k[0]), key=lambda k: fetch[k][0] * fetch[k][1])
+    f_scale = copy_bytes / (fetch[copy_key][0] * 1024.0)
+    w_scale = copy_bytes / (write[copy_key][0] * 1024.0)
+    fb = fetch[kern_key][0] * 1024.0 * f_scale
+    wb = write[kern_key][0] * 1024.0 * w_scale
+    out = {"workload": workload, "kernel": kern_key[0], "source_hash": source_hash(),
+           "fetch_kib_raw": fetch[kern_key][0], "write_kib_raw": write[kern_key][0],
+           "copy_bytes": copy_bytes, "copy_grid": copy_key[1],
+           "copy_fetch_kib_raw": fetch[copy_key][0], "copy_write_kib_raw": write[copy_key][0],
+           "fetch_scale": f_scale, "write_scale": w_scale, "fetch_bytes": fb,
+           "write_bytes": wb, "bytes_per_launch": fb + wb}
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
 
 
 def load_traffic(workload: str):
@@ -57,24 +104,24 @@ def load_traffic(workload: str):
 
 
 def cpu_baseline(workload, target_s: float = 12.0) -> dict:
-    """Time the CPU oracle on a bounded sample of the same workload."""
-    import numpy as np
+    """Time the CPU oracle (as it stands, all host cores) on a bounded sample
+    of the same workload: a probe of about 3e9 multiply-adds sizes the
+    sample to roughly target_s seconds, capped at the whole workload."""
     from hadamard_rotation_amd import workloads as W
     from oracle import oracle as O
 
     w = W.WORKLOADS[workload]
-    per_row_mac = w.n * w.b
-    # probe on a few rows, then size the sample to about target_s seconds
-    probe_rows = max(1, int(2e8 // per_row_mac))
-    data = W.generate(workload, seed=42, tokens=max(1, probe_rows // w.unit + 1))
-    raw, s = data[w.tensors[0]], data["s"]
     threads = O.default_threads()
+    per_row_mac = w.n * w.b
+    probe_rows = max(threads, min(w.rows, int(3e9 // per_row_mac)))
+    data = W.generate(workload, seed=42, tokens=(probe_rows + w.unit - 1) // w.unit)
+    raw, s = data[w.tensors[0]][:probe_rows], data["s"]
     t0 = time.perf_counter()
-    O.rotate_quant(raw[:probe_rows], w.x_dtype, w.b, s, w.bits, w.scale_dtype,
-                   threads=threads, want_preround=False)
+    O.rotate_quant(raw, w.x_dtype, w.b, s, w.bits, w.scale_dtype, threads=threads,
+                   want_preround=False)
     dt = max(time.perf_counter() - t0, 1e-3)
-    rows = int(min(w.rows, max(probe_rows, probe_rows * target_s / dt)))
-    rows = max(threads, rows - rows % threads)
+    rows = int(min(w.rows, probe_rows * target_s / dt))
+    rows = max(probe_rows, rows - rows % w.unit)
     data = W.generate(workload, seed=42, tokens=(rows + w.unit - 1) // w.unit)
     raw = data[w.tensors[0]][:rows]
     t0 = time.perf_counter()
@@ -83,8 +130,9 @@ def cpu_baseline(workload, target_s: float = 12.0) -> dict:
     dt = time.perf_counter() - t0
     gbs = w.bytes_per_call(rows) / dt / 1e9
     return {"value": round(gbs, 6), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {w.rows} rows of the same workload (seed 42), "
-                      f"{dt:.2f} s wall, explicit fp64 H_{w.b} product per block"}
+            "sample": f"{rows} of {w.rows} rows of the same workload (seed 42, same "
+                      f"generator), {dt:.2f} s wall on {threads} threads; explicit fp64 "
+                      f"H_{w.b} product per block, scalar quantisation"}
 
 
 def main(argv=None):
@@ -96,7 +144,18 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the inverse-path and copy timings")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
+                         "WRITE_SIZE) into profiles/traffic_<workload>.json and exit")
     args = ap.parse_args(argv)
+
+    if args.traffic:
+        from hadamard_rotation_amd import workloads as W
+        w = W.WORKLOADS[args.workload]
+        out = write_traffic(args.workload, args.traffic[0], args.traffic[1],
+                            copy_bytes_for(w.bytes_per_call()))
+        print(json.dumps(out))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
@@ -121,7 +180,7 @@ def main(argv=None):
     raw, s_np = data[w.tensors[0]], data["s"]
     rows, n = raw.shape
     bytes_call = w.bytes_per_call(rows)
-    sets = max(4, int(np.ceil(3 * LLC_BYTES / bytes_call)))
+    sets = min(64, max(4, int(np.ceil(3 * LLC_BYTES / bytes_call))))
 
     x_dtype = {W.F32: torch.float32, W.BF16: torch.bfloat16, W.F16: torch.float16}[w.x_dtype]
     if w.x_dtype == W.F32:
@@ -215,7 +274,7 @@ def main(argv=None):
                           "bytes_per_call": inv_bytes, "out_dtype": "f32"}
         del ys
         # same-byte-count device copy as the achievable-bandwidth reference
-        nb = bytes_call // 2
+        nb = copy_bytes_for(bytes_call)
         src = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(sets)]
         dst = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(sets)]
         for i in range(5):
