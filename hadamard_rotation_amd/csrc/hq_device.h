@@ -58,16 +58,29 @@ __device__ __forceinline__ int quant_code(float y, float inv, int qmax)
 // Per-row constants of the quantiser.  m = max|y| over the row (unnormalised
 // rotated values); kq = 1 / (sqrt(b) * qmax) rounded to fp32 on the host.
 struct RowQuant {
-    float inv;    // qmax / m, or 0 for an all-zero row
+    float inv;    // qmax / m, or 0 for a row treated as zero
     float scale;  // m * kq = max|x'| / qmax
 };
 
+// Rows whose absmax is below this are treated as all-zero rows (scale 0,
+// codes 0): qmax / m would overflow fp32 for them.
+constexpr float kTinyRow = 0x1p-120f;
+
+// inv = qmax / m from the hardware reciprocal refined by one residual step
+// (within about half an ulp of the correctly rounded quotient for normal m;
+// a handful of instructions instead of the full IEEE division sequence,
+// which every lane of a row would otherwise run).
 __device__ __forceinline__ RowQuant row_quant(float m, float kq, int qmax)
 {
-    RowQuant r;
-    r.inv = m > 0.0f ? (float)qmax / m : 0.0f;
-    r.scale = m * kq;
-    return r;
+    const float fq = (float)qmax;
+    const bool live = m >= kTinyRow;
+    const float r = __builtin_amdgcn_rcpf(live ? m : 1.0f);
+    const float q0 = fq * r;
+    const float e = __builtin_fmaf(-m, q0, fq);
+    RowQuant rq;
+    rq.inv = live ? __builtin_fmaf(e, r, q0) : 0.0f;
+    rq.scale = live ? m * kq : 0.0f;
+    return rq;
 }
 
 }  // namespace hq

@@ -134,6 +134,33 @@ __device__ __forceinline__ void dot2_pair(uint32_t w, uint32_t sg, float &a, flo
     }
 }
 
+// The first two butterfly stages of four inputs (pairs wl = (x0, x1) and
+// wh = (x2, x3) with sign pairs sl, sh), widened and sign-flipped, in six
+// dot products instead of four products and four add/subs: with
+// B = s2x2 + s3x3 and B' = s2x2 - s3x3 (accumulator operand C, negated by
+// neg_lo where needed)
+//   y0 = s0x0 + s1x1 + B,  y1 = s0x0 - s1x1 + B',
+//   y2 = s0x0 + s1x1 - B,  y3 = s0x0 - s1x1 - B'   (rows of H_4).
+#define HQ_DOT2_QUAD(OPC)                                                                   \
+    asm(OPC " %0, %1, %2, 0" : "=v"(B) : "v"(wh), "v"(sh));                                 \
+    asm(OPC " %0, %1, %2, 0 neg_hi:[0,1,0]" : "=v"(Bn) : "v"(wh), "v"(sh));                 \
+    asm(OPC " %0, %1, %2, %3" : "=v"(y0) : "v"(wl), "v"(sl), "v"(B));                       \
+    asm(OPC " %0, %1, %2, %3 neg_hi:[0,1,0]" : "=v"(y1) : "v"(wl), "v"(sl), "v"(Bn));       \
+    asm(OPC " %0, %1, %2, %3 neg_lo:[0,0,1]" : "=v"(y2) : "v"(wl), "v"(sl), "v"(B));        \
+    asm(OPC " %0, %1, %2, %3 neg_lo:[0,0,1] neg_hi:[0,1,0]" : "=v"(y3) : "v"(wl), "v"(sl), "v"(Bn))
+
+template <int IN>
+__device__ __forceinline__ void dot2_quad(uint32_t wl, uint32_t wh, uint32_t sl, uint32_t sh,
+                                          float &y0, float &y1, float &y2, float &y3)
+{
+    float B, Bn;
+    if constexpr (IN == kBF16) {
+        HQ_DOT2_QUAD("v_dot2_f32_bf16");
+    } else {
+        HQ_DOT2_QUAD("v_dot2_f32_f16");
+    }
+}
+
 __device__ __forceinline__ void bfly(float &a, float &b)
 {
     float t = a + b;
@@ -177,21 +204,33 @@ __device__ __forceinline__ uint32_t pack_int8(uint32_t f0, uint32_t f1, uint32_t
 }
 
 template <int CTRL>
-__device__ __forceinline__ float dpp_max(float v)
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v)
 {
-    return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                        0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false)));
+    // every source lane of these patterns exists, so bound_ctrl changes
+    // nothing; it lets the compiler fuse the move into v_max_u32_dpp
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, true);
+    return v > o ? v : o;
 }
 
-// max over the 2^log_lanes aligned lanes of one row segment
-__device__ __forceinline__ float segment_max(float v, int log_lanes)
+// max over the 2^log_lanes aligned lanes of one row segment.  The values are
+// |y| as bit patterns: for non-negative floats the integer order is the
+// float order, and integer max needs no NaN canonicalisation.
+__device__ __forceinline__ uint32_t segment_max(uint32_t v, int log_lanes)
 {
     if (log_lanes > 0) v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
     if (log_lanes > 1) v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
     if (log_lanes > 2) v = dpp_max<0x141>(v);  // row_half_mirror
     if (log_lanes > 3) v = dpp_max<0x128>(v);  // row_ror:8
-    if (log_lanes > 4) v = fmaxf(v, __shfl_xor(v, 16, 64));
-    if (log_lanes > 5) v = fmaxf(v, __shfl_xor(v, 32, 64));
+    if (log_lanes > 4) {
+        // with both operands equal, the swap hands every lane the value of
+        // its partner 16 lanes away in one of the two results
+        auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = r[0] > r[1] ? r[0] : r[1];
+    }
+    if (log_lanes > 5) {
+        auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = r[0] > r[1] ? r[0] : r[1];
+    }
     return v;
 }
 
@@ -217,7 +256,7 @@ __global__ __launch_bounds__(UNITS < 8 ? 1024 : (LONG ? 256 : 768))
 void fast_kernel(FastArgs a)
 {
     extern __shared__ __align__(16) uint32_t lds_sign[];  // sign material of one row width
-    __shared__ float red[2][kMaxWpr];
+    __shared__ uint32_t red[2][kMaxWpr];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -296,42 +335,46 @@ void fast_kernel(FastArgs a)
         return seg_base + uo * lanes + lo;
     };
 
-    // rows of (pool-relative) group g handled by this lane:
-    // row(g, k) = (b + g*grid)*rows_per_group + k*rows_per_wave + row_sub
-    auto row_of = [&](int64_t g, int k) {
-        return ((int64_t)blockIdx.x + g * gridDim.x) * rows_per_group + row_sub +
-               (int64_t)k * rows_per_wave;
+    // Rows of (pool-relative) group g: the group starts at the wave-uniform
+    // row (b + g*grid)*rows_per_group, and this lane's k-th row is
+    // lane_row(k) rows further.  Addresses are a wave-uniform 64-bit group
+    // base plus 32-bit per-lane offsets.
+    auto group_row0 = [&](int64_t g) {
+        return ((int64_t)blockIdx.x + g * gridDim.x) * rows_per_group;
     };
-    const int64_t last_row = a.rows - 1;
+    auto lane_row = [&](int k) { return row_sub + k * rows_per_wave; };
 
     // ---- loads (addresses clamped to valid memory; results of rows or
     // units past the end are never stored)
     auto load = [&](int64_t g, RawUnit<OP, IN> (&raw)[RPL][UNITS]) {
+        const int64_t r0 = group_row0(g);
+        const int64_t left = a.rows - 1 - r0;  // rows after r0 in the tensor
+        const int lim = left < rows_per_group ? (int)left : rows_per_group;
+        const int64_t e0 = r0 * (int64_t)a.n;  // wave-uniform
 #pragma unroll
         for (int k = 0; k < RPL; ++k) {
-            int64_t row = row_of(g, k);
-            row = row < last_row ? row : last_row;
-            // row base (wave-uniform when a wave holds one row) + lane offset
-            const int64_t re = row * (int64_t)a.n;
+            int lr = lane_row(k);
+            lr = lr < lim ? lr : lim;  // clamp into the tensor
 #pragma unroll
             for (int u = 0; u < UNITS; ++u) {
                 int un = in_unit(u);
                 if (LONG)
                     un = un < units_row ? un : units_row - 1;
+                const int eo = lr * a.n + un * 8;  // per-lane element offset
                 if constexpr (OP == kDequantInv) {
                     if (a.bits == 4) {
-                        const uint8_t *rp = (const uint8_t *)a.codes_in + (re >> 1);
-                        raw[k][u].w[0] = stream_load((const uint32_t *)(rp + un * 4));
+                        const uint8_t *gp = (const uint8_t *)a.codes_in + (e0 >> 1);
+                        raw[k][u].w[0] = stream_load((const uint32_t *)(gp + (eo >> 1)));
                         raw[k][u].w[1] = 0;
                     } else {
-                        const int8_t *rp = (const int8_t *)a.codes_in + re;
-                        u32x2 t = stream_load((const u32x2 *)(rp + un * 8));
+                        const int8_t *gp = (const int8_t *)a.codes_in + e0;
+                        u32x2 t = stream_load((const u32x2 *)(gp + eo));
                         raw[k][u].w[0] = t[0];
                         raw[k][u].w[1] = t[1];
                     }
                 } else if constexpr (IN == kF32) {
-                    const float *rp = (const float *)a.x + re;
-                    const u32x4 *src = (const u32x4 *)(rp + un * 8);
+                    const float *gp = (const float *)a.x + e0;
+                    const u32x4 *src = (const u32x4 *)(gp + eo);
                     u32x4 p = stream_load(src), q = stream_load(src + 1);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
@@ -339,8 +382,8 @@ void fast_kernel(FastArgs a)
                         raw[k][u].w[4 + t] = q[t];
                     }
                 } else {
-                    const uint16_t *rp = (const uint16_t *)a.x + re;
-                    u32x4 p = stream_load((const u32x4 *)(rp + un * 8));
+                    const uint16_t *gp = (const uint16_t *)a.x + e0;
+                    u32x4 p = stream_load((const u32x4 *)(gp + eo));
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
                         raw[k][u].w[t] = p[t];
@@ -397,6 +440,22 @@ void fast_kernel(FastArgs a)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+    // Loads and stores share one completion counter, and with both kinds
+    // in flight the compiler can only wait for all of them.  An empty asm
+    // that reads and rewrites the loaded registers fixes where that wait
+    // happens: the loop below never waits for the loads at its top (where
+    // the previous group's stores were just issued).
+    auto take_delivery = [&](RawUnit<OP, IN> (&raw)[RPL][UNITS]) {
+#pragma unroll
+        for (int k = 0; k < RPL; ++k)
+#pragma unroll
+            for (int u = 0; u < UNITS; ++u)
+#pragma unroll
+                for (int t = 0; t < (int)(sizeof(raw[k][u].w) / 4); ++t)
+                    asm volatile("" : "+v"(raw[k][u].w[t]));
+    };
+    take_delivery(cur);
 
     int parity = 0;
     int64_t g = first;
@@ -459,6 +518,11 @@ void fast_kernel(FastArgs a)
                             bfly(v[k][u][4], v[k][u][5]);
                             bfly(v[k][u][6], v[k][u][7]);
                         }
+                    } else if (logb > 1) {
+                        dot2_quad<IN>(cur[k][u].w[0], cur[k][u].w[1], sw[0], sw[1], v[k][u][0],
+                                      v[k][u][1], v[k][u][2], v[k][u][3]);
+                        dot2_quad<IN>(cur[k][u].w[2], cur[k][u].w[3], sw[2], sw[3], v[k][u][4],
+                                      v[k][u][5], v[k][u][6], v[k][u][7]);
                     } else if (logb > 0) {
 #pragma unroll
                         for (int p = 0; p < 4; ++p)
@@ -488,11 +552,13 @@ void fast_kernel(FastArgs a)
             load(g_next, cur);
 
         // ------------------------------------------ in-unit stages (bits 1, 2)
+        // (bit 1 of 16-bit input is already folded into dot2_quad)
+        constexpr bool kQuad = OP != kDequantInv && IN != kF32;
 #pragma unroll
         for (int k = 0; k < RPL; ++k)
 #pragma unroll
             for (int u = 0; u < UNITS; ++u) {
-                if (logb > 1) {
+                if (!kQuad && logb > 1) {
                     bfly(v[k][u][0], v[k][u][2]);
                     bfly(v[k][u][1], v[k][u][3]);
                     bfly(v[k][u][4], v[k][u][6]);
@@ -573,12 +639,21 @@ void fast_kernel(FastArgs a)
             }
         }
 
+        // Take delivery of the prefetched group here, before this group's
+        // stores: the wait covers loads issued a group's compute ago and
+        // the previous group's stores, not stores issued just before.
+        take_delivery(cur);
+
         // ------------------------------------------------------------ outputs
 #pragma unroll
         for (int k = 0; k < RPL; ++k) {
-            const int64_t row = row_of(g, k);
-            const bool row_ok = row < a.rows;
-            const int64_t rbase = row * (int64_t)a.n;
+            const int64_t r0 = group_row0(g);
+            const int64_t left = a.rows - 1 - r0;  // wave-uniform
+            const int lim = left < rows_per_group ? (int)left : rows_per_group;
+            const int lr = lane_row(k);
+            const bool row_ok = lr <= lim;
+            const int64_t e0 = r0 * (int64_t)a.n;  // wave-uniform
+            const int ro = lr * a.n;              // per-lane row offset
 
             if constexpr (OP == kRotate) {
                 const float m = lane_neg ? -a.rb : a.rb;
@@ -588,7 +663,7 @@ void fast_kernel(FastArgs a)
                         const int ou = out_unit(u);
                         if (LONG && ou >= units_row)
                             continue;
-                        float4 *dst = (float4 *)((float *)a.y + rbase + (int64_t)ou * 8);
+                        float4 *dst = (float4 *)((float *)a.y + e0 + (ro + ou * 8));
                         dst[0] = make_float4(v[k][u][0] * m, v[k][u][1] * m, v[k][u][2] * m,
                                              v[k][u][3] * m);
                         dst[1] = make_float4(v[k][u][4] * m, v[k][u][5] * m, v[k][u][6] * m,
@@ -597,11 +672,11 @@ void fast_kernel(FastArgs a)
                 }
             } else if constexpr (OP == kDequantInv) {
                 float sc = 0.0f;
-                const int64_t rr = row < last_row ? row : last_row;
+                const int lc = lr < lim ? lr : lim;  // clamped into the tensor
                 if (a.scale_f16)
-                    sc = f16_to_f32(((const uint16_t *)a.scales_in)[rr]);
+                    sc = f16_to_f32(((const uint16_t *)a.scales_in + r0)[lc]);
                 else
-                    sc = ((const float *)a.scales_in)[rr];
+                    sc = ((const float *)a.scales_in + r0)[lc];
                 float t = sc * a.rb;
                 t = lane_neg ? -t : t;
                 if (row_ok) {
@@ -618,7 +693,7 @@ void fast_kernel(FastArgs a)
                             o[j] = flip(v[k][u][j] * t, (word >> (8 * (j & 3) + 7)) & 1);
                         }
                         if constexpr (IN == kF32) {
-                            float4 *dst = (float4 *)((float *)a.y + rbase + (int64_t)ou * 8);
+                            float4 *dst = (float4 *)((float *)a.y + e0 + (ro + ou * 8));
                             dst[0] = make_float4(o[0], o[1], o[2], o[3]);
                             dst[1] = make_float4(o[4], o[5], o[6], o[7]);
                         } else {
@@ -627,12 +702,14 @@ void fast_kernel(FastArgs a)
                             pk.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
                             pk.z = (uint32_t)f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
                             pk.w = (uint32_t)f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
-                            *(uint4 *)((uint16_t *)a.y + rbase + (int64_t)ou * 8) = pk;
+                            *(uint4 *)((uint16_t *)a.y + e0 + (ro + ou * 8)) = pk;
                         }
                     }
                 }
             } else {
-                // absmax of the row (units past the end of a long row excluded)
+                // absmax of the row (units past the end of a long row
+                // excluded); across lanes on the bit pattern of the
+                // non-negative maximum
                 float m = 0.0f;
 #pragma unroll
                 for (int u = 0; u < UNITS; ++u) {
@@ -647,28 +724,28 @@ void fast_kernel(FastArgs a)
                         mu = out_unit(u) < units_row ? mu : 0.0f;
                     m = fmaxf(m, mu);
                 }
-                m = segment_max(m, log_lanes);
+                uint32_t mb = segment_max(__float_as_uint(m), log_lanes);
                 if constexpr (LONG) {
                     if (a.wpr > 1) {
                         if (lane == 0)
-                            red[parity][wave] = m;
+                            red[parity][wave] = mb;
                         // LDS-only: the barrier must not drain the prefetch
                         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
                         __builtin_amdgcn_s_barrier();
                         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-                        m = red[parity][0];
+                        mb = red[parity][0];
                         for (int w2 = 1; w2 < a.wpr; ++w2)
-                            m = fmaxf(m, red[parity][w2]);
+                            mb = mb > red[parity][w2] ? mb : red[parity][w2];
                         parity ^= 1;
                     }
                 }
                 const int qmax = a.bits == 4 ? 7 : 127;
-                RowQuant rq = row_quant(m, a.kq, qmax);
+                RowQuant rq = row_quant(__uint_as_float(mb), a.kq, qmax);
                 if (row_ok && l == 0 && seg == 0) {
                     if (a.scale_f16)
-                        ((uint16_t *)a.scales)[row] = f32_to_f16(rq.scale);
+                        ((uint16_t *)a.scales + r0)[lr] = f32_to_f16(rq.scale);
                     else
-                        ((float *)a.scales)[row] = rq.scale;
+                        ((float *)a.scales + r0)[lr] = rq.scale;
                 }
                 const float inv = lane_neg ? -rq.inv : rq.inv;
                 if (a.bits == 4) {
@@ -682,7 +759,7 @@ void fast_kernel(FastArgs a)
                             const int ou = out_unit(u);
                             if (LONG && ou >= units_row)
                                 continue;
-                            *(uint32_t *)((uint8_t *)a.codes + (rbase >> 1) + (int64_t)ou * 4) =
+                            *(uint32_t *)((uint8_t *)a.codes + (e0 >> 1) + ((ro >> 1) + ou * 4)) =
                                 pack_int4(f);
                         }
                     }
@@ -699,7 +776,7 @@ void fast_kernel(FastArgs a)
                                 continue;
                             uint2 pk = make_uint2(pack_int8(f[0], f[1], f[2], f[3]),
                                                   pack_int8(f[4], f[5], f[6], f[7]));
-                            *(uint2 *)((int8_t *)a.codes + rbase + (int64_t)ou * 8) = pk;
+                            *(uint2 *)((int8_t *)a.codes + e0 + (ro + ou * 8)) = pk;
                         }
                     }
                 }

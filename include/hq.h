@@ -83,7 +83,9 @@ typedef enum hq_dtype {
  *            bits == 8: [rows, n] int8 in [-127, 127].
  *   scales   [rows], element type scale_dtype (HQ_F32 or HQ_F16), the stored
  *            value of max|x'|/qmax rounded to nearest even.  A row of zeros
- *            gets scale 0 and codes 0.
+ *            gets scale 0 and codes 0, and so does a row whose unnormalised
+ *            maximum max|(x*s) H_b| is below 2^-120 (every |x| below about
+ *            1e-37): for such a row qmax/max would overflow binary32.
  * Codes are computed from the unrounded scale, so they do not depend on
  * scale_dtype.
  */

@@ -173,6 +173,26 @@ def test_zero_rows_and_spikes():
         assert np.allclose(y[1], raw[1], atol=1e-6)
 
 
+def test_tiny_rows_flush_to_zero():
+    # A row whose unnormalised rotated maximum is below 2^-120 is stored as
+    # a zero row (the library's documented contract: qmax / max would
+    # overflow binary32).  Just above that, rows follow the oracle.
+    # (32768, 4096) takes the generic LDS kernel, the others the fast one.
+    for n, b in ((128, 128), (4096, 4096), (11008, 128), (32768, 4096)):
+        raw = np.zeros((4, n), dtype=np.float32)
+        raw[0, 5] = 1e-38            # flushed
+        raw[1, n - 3] = -2.0 ** -119  # kept: maximum 2^-119
+        raw[2, :] = 2.0 ** -110       # kept
+        raw[3, 7] = 1.0
+        s = np.where(np.arange(n) % 5 == 0, -1, 1).astype(np.int8)
+        for bits in (4, 8):
+            codes, scales = G.gpu_rotate_quant(raw, W.F32, s, b, bits, W.F32)
+            assert scales[0] == 0 and np.all(codes[0] == 0), (n, bits)
+            ref = O.rotate_quant(raw[1:], W.F32, b, s, bits, W.F32)
+            P.check_codes(codes[1:], ref, bits, n, what=f"tiny n={n} bits={bits}")
+            P.check_scales(scales[1:], ref, W.F32, what=f"tiny n={n} bits={bits}")
+
+
 def test_rows_zero_is_noop():
     import torch
     import hadamard_rotation_amd as hq
