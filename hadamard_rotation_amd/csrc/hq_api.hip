@@ -108,7 +108,9 @@ hq_status dispatch(const hq::Request &r)
     if (r.n > max_n_for(*dev))
         return HQ_EUNSUPPORTED;
     hipError_t e;
-    if (hq::fast_available(r))
+    if (hq::mfma_available(r))
+        e = hq::launch_mfma(r, *dev);
+    else if (hq::fast_available(r))
         e = hq::launch_fast(r, *dev);
     else
         e = hq::launch_generic(r, *dev);

@@ -109,6 +109,16 @@ bool make_plan(int n, int b, Plan &p)
     return true;
 }
 
+void dpp_tables(int n_dpp, uint64_t &pi, uint32_t &neg)
+{
+    pi = 0;
+    neg = 0;
+    for (int i = 0; i < 16; ++i) {
+        pi |= (uint64_t)kPi[n_dpp][i] << (4 * i);
+        neg |= (kSign[n_dpp][i] < 0 ? 1u : 0u) << i;
+    }
+}
+
 void fill_args(FastArgs &fa, const Request &r, const Plan &p)
 {
     fa.x = r.x;
@@ -127,14 +137,7 @@ void fill_args(FastArgs &fa, const Request &r, const Plan &p)
     fa.scale_f16 = r.scale_dtype == kF16;
     const int lane_bits = p.logb > 3 ? (p.logb - 3 < p.log_lanes ? p.logb - 3 : p.log_lanes) : 0;
     const int n_dpp = lane_bits < 4 ? lane_bits : 4;
-    uint64_t pi = 0;
-    uint32_t neg = 0;
-    for (int i = 0; i < 16; ++i) {
-        pi |= (uint64_t)kPi[n_dpp][i] << (4 * i);
-        neg |= (kSign[n_dpp][i] < 0 ? 1u : 0u) << i;
-    }
-    fa.pi = pi;
-    fa.neg = neg;
+    dpp_tables(n_dpp, fa.pi, fa.neg);
     const int qmax = r.bits == 8 ? 127 : 7;
     fa.kq = (float)(1.0 / (__builtin_sqrt((double)r.b) * qmax));
     fa.rb = (float)(1.0 / __builtin_sqrt((double)r.b));

@@ -798,6 +798,9 @@ struct Plan {
 };
 
 bool make_plan(int n, int b, Plan &p);
+// Output chunk (4 bits per lane) and negation mask (1 bit per lane) of the
+// 16 lanes of a DPP row after n_dpp = 0..4 DPP butterfly stages.
+void dpp_tables(int n_dpp, uint64_t &pi, uint32_t &neg);
 void fill_args(FastArgs &fa, const Request &r, const Plan &p);
 int occupancy_blocks(const void *fn, int threads, size_t lds);
 

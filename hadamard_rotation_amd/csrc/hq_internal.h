@@ -53,4 +53,9 @@ hipError_t launch_generic(const Request &r, const DeviceInfo &dev);
 bool fast_available(const Request &r);
 hipError_t launch_fast(const Request &r, const DeviceInfo &dev);
 
+// Matrix-core paths (16-bit input, forward): mfma_available() says whether
+// one exists for the request; launch_mfma() enqueues it.
+bool mfma_available(const Request &r);
+hipError_t launch_mfma(const Request &r, const DeviceInfo &dev);
+
 }  // namespace hq

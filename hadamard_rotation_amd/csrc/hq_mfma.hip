@@ -1,0 +1,98 @@
+// hq_mfma.hip -- host side of the matrix-core kernels: which requests they
+// take, argument setup and dispatch to the per-path translation units
+// (hq_mfma_rq.hip, hq_mfma_rot.hip).  The kernel template is in
+// hq_mfma_impl.h.
+#include <mutex>
+
+#include "hq_mfma_impl.h"
+
+namespace hq {
+namespace mfma {
+
+namespace {
+
+int ilog2(int v)
+{
+    int r = 0;
+    while ((1 << r) < v)
+        ++r;
+    return r;
+}
+
+struct OccEntry {
+    const void *fn;
+    size_t lds;
+    int waves;
+};
+std::mutex g_occ_mu;
+OccEntry g_occ[256];
+int g_occ_used = 0;
+
+}  // namespace
+
+// Power-of-two rows of 32..4096 elements in a 16-bit type, rotated whole or
+// in 128-element blocks, forward paths only.
+bool plan_ok(const Request &r)
+{
+    if (r.op != kRotateQuant && r.op != kRotate)
+        return false;
+    if (r.x_dtype != kBF16 && r.x_dtype != kF16)
+        return false;
+    if (r.n < 32 || r.n > 4096 || (r.n & (r.n - 1)) != 0)
+        return false;
+    return r.b == r.n || (r.b == 128 && r.n >= 256);
+}
+
+void fill_args(MfmaArgs &ma, const Request &r, int tiles_per_group)
+{
+    ma.x = r.x;
+    ma.s = r.s;
+    ma.codes = r.codes;
+    ma.scales = r.scales;
+    ma.y = r.y;
+    ma.rows = r.rows;
+    ma.total = r.rows * (int64_t)r.n;
+    const int64_t per_group = (int64_t)tiles_per_group * 512;
+    ma.groups = (ma.total + per_group - 1) / per_group;
+    const int logb = ilog2(r.b);
+    const int n_dpp = logb - 5 < 4 ? logb - 5 : 4;
+    fast::dpp_tables(n_dpp, ma.pi, ma.neg);
+    ma.n = r.n;
+    ma.bits = r.bits;
+    ma.scale_f16 = r.scale_dtype == kF16;
+    const int qmax = r.bits == 8 ? 127 : 7;
+    ma.kq = (float)(1.0 / (__builtin_sqrt((double)r.b) * qmax));
+    ma.rb = (float)(1.0 / __builtin_sqrt((double)r.b));
+}
+
+int occupancy_waves(const void *fn, size_t lds)
+{
+    std::lock_guard<std::mutex> lk(g_occ_mu);
+    for (int i = 0; i < g_occ_used; ++i)
+        if (g_occ[i].fn == fn && g_occ[i].lds == lds)
+            return g_occ[i].waves;
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 256, lds) != hipSuccess || nb < 1)
+        nb = 1;
+    const int waves = 4 * nb;
+    if (g_occ_used < (int)(sizeof g_occ / sizeof g_occ[0]))
+        g_occ[g_occ_used++] = OccEntry{fn, lds, waves};
+    return waves;
+}
+
+hipError_t launch_rq(const Request &r, const DeviceInfo &dev);
+hipError_t launch_rot(const Request &r, const DeviceInfo &dev);
+
+}  // namespace mfma
+
+bool mfma_available(const Request &r)
+{
+    return mfma::plan_ok(r);
+}
+
+hipError_t launch_mfma(const Request &r, const DeviceInfo &dev)
+{
+    return r.op == kRotate ? mfma::launch_rot(r, dev) : mfma::launch_rq(r, dev);
+}
+
+}  // namespace hq

@@ -1,0 +1,427 @@
+// hq_mfma_impl.h -- the matrix-core kernel template of libhq.so for gfx950:
+// rotation (+ quantisation) of 16-bit rows with the first five butterfly
+// stages of every block done as one exact 32-point product on the MFMA
+// unit, the rest as in the register-resident kernel.
+//
+// Pages cited: [RQ] "旋转量化：大模型低比特量化中的离群值克星" section 2.1 (the
+// Hadamard matrix of order 2^k is the Kronecker product of H_2 factors,
+// H_2n = [[H_n, H_n], [H_n, -H_n]], so an index-bit subset of the transform
+// can be done as a dense product of a smaller Hadamard matrix; blockwise
+// rotation for widths that are not one block) and section 2.2 (per-row
+// absmax scale, round and clip); [QT] "手把手教你用QuaRot实现LLM的4位量化：从原
+// 理到代码实践" section 2.1 (signs, then Hadamard).
+//
+// Why a matrix unit in a memory-bound path.  The butterfly kernel needs
+// about 16 VALU instructions per element for 4096-point rows, and wave64
+// VALU issue (not HBM) is what limits it.  A 32-point Hadamard transform of
+// 16-bit data is exact on the matrix core: every product of an input with
+// +-1 is exact, and the 32-term sums are accumulated in fp32 like the
+// butterflies' own adds.  One v_mfma_f32_16x16x32 on 8 inputs per lane
+// replaces the widening, the sign flip (now one XOR per pair) and five
+// butterfly stages, i.e. about 6.5 VALU instructions per element, with
+// about one eighth of an MFMA issue slot.  Later stages stay fp32 on the
+// VALU (their inputs are fp32 and the matrix core would round them).
+//
+// Tile layout.  The rows are viewed as one stream of 512-element tiles
+// (rows of n < 512 elements pack 512/n rows per tile; rows of n >= 512
+// elements are n/512 whole tiles).  In a tile, lane l (L0..L5 its bits)
+// loads the 16 bytes of elements P = j + 8*(L4 + 2*L5) + 32*(l & 15),
+// j = 0..7, so a wave load covers 1 KB of contiguous memory.  For the
+// 16x16x32 product the tile is the B operand: k = j + 8*(l >> 4) runs over
+// the element bits P0..P4, the column n = l & 15 over P5..P8.  The A
+// operand is a 16-row slice of H_32 (two slices, h = 0, 1, give the 32
+// outputs); output row m of slice h is the transformed index
+// Q = (m & 3) + 4*h + 8*(m >> 2) in the bits P0..P4, so the lane ends up
+// with 8 consecutive outputs (j' = (m & 3) + 4*h) at the same lane
+// position: its codes are one 32-bit store.
+//
+// Block bits above P4: P5..P8 live on lane bits 0..3 and are finished with
+// the DPP butterflies of the register-resident kernel (same sign tracking
+// and output permutation); bits above P8 (b > 512) are tile bits and are
+// finished between registers.  Rows narrower than 512 elements keep their
+// row index in the high lane bits.
+#pragma once
+
+#include "hq_fast_impl.h"
+
+namespace hq {
+namespace mfma {
+
+using fast::u32x2;
+using fast::u32x4;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct MfmaArgs {
+    const void *x;
+    const int8_t *s;
+    void *codes;
+    void *scales;
+    void *y;
+    int64_t rows;
+    int64_t total;    // rows * n elements
+    int64_t groups;   // groups of T tiles
+    uint64_t pi;      // output chunk of lane l & 15 after the DPP stages
+    uint32_t neg;     // bit l set: lane l holds the negated value
+    int n;
+    int bits;
+    int scale_f16;
+    float kq;         // 1 / (sqrt(b) * qmax)
+    float rb;         // 1 / sqrt(b)
+};
+
+// 16x16x32 product of the +-1 slice a with the 16-bit tile b (fp32 sums).
+template <int IN>
+__device__ __forceinline__ f32x4 hmma(u32x4 a, u32x4 b)
+{
+    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (IN == kBF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), z, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), z, 0, 0, 0);
+}
+
+// Row maximum over the lanes of one row: P3, P4 (lane bits 4, 5) always,
+// and lane bits 0 .. NDPP-1 (P5 ..) for rows wider than 32 elements.  The
+// values are bit patterns of non-negative floats.
+template <int NDPP>
+__device__ __forceinline__ uint32_t row_lane_max(uint32_t v)
+{
+    if constexpr (NDPP > 0) v = fast::dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
+    if constexpr (NDPP > 1) v = fast::dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
+    if constexpr (NDPP > 2) v = fast::dpp_max<0x141>(v);  // row_half_mirror
+    if constexpr (NDPP > 3) v = fast::dpp_max<0x128>(v);  // row_ror:8
+    auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = r16[0] > r16[1] ? r16[0] : r16[1];
+    auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return r32[0] > r32[1] ? r32[0] : r32[1];
+}
+
+// OP    kRotateQuant or kRotate
+// IN    kBF16 or kF16
+// T     tiles per wave and iteration
+// LOGB  log2 b, 5..12
+// LOGN  log2 n, LOGB..12
+template <int OP, int IN, int T, int LOGB, int LOGN>
+__global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
+{
+    extern __shared__ __align__(16) u32x4 lds_mask[];  // n > 512: [tile of row][lane]
+    constexpr int D = LOGB - 5 < 4 ? LOGB - 5 : 4;      // DPP stages (lane bits 0..D-1)
+    constexpr int R = LOGB > 9 ? LOGB - 9 : 0;          // tile-bit stages
+    constexpr int TPR = LOGN > 9 ? 1 << (LOGN - 9) : 1; // tiles per row
+    static_assert(T % TPR == 0, "a group holds whole rows");
+    static_assert(LOGB >= 5 && LOGB <= LOGN && LOGN <= 12, "plan");
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int l16 = lane & 15;
+    const int lane_off = 8 * (lane >> 4) + 32 * l16;  // element offset in a tile
+
+    // DPP sign functionals and output permutation (as in the butterfly kernel)
+    const float sig0 = ((l16 ^ (l16 >> 2)) & 1) ? -1.0f : 1.0f;
+    const float sig1 = (((l16 >> 1) ^ (l16 >> 2)) & 1) ? -1.0f : 1.0f;
+    const float sig2 = ((l16 >> 2) & 1) ? -1.0f : 1.0f;
+    const float sig3 = ((l16 >> 3) & 1) ? -1.0f : 1.0f;
+    const bool lane_neg = (a.neg >> l16) & 1;
+    int pl = l16;
+    if constexpr (D > 0) {
+        const int c = (int)((a.pi >> (4 * l16)) & 15);
+        constexpr int mask = (1 << D) - 1;
+        pl = (l16 & ~mask) | (c & mask);
+    }
+    const int out_off = 8 * (lane >> 4) + 32 * pl;  // element offset of the 8 outputs
+
+    // The two +-1 slices of H_32 as A operands: lane l holds row m = l & 15
+    // at k = 8*(l >> 4) + j; row m of slice h is output Q(m, h).
+    u32x4 amat[2];
+    {
+        const uint32_t one = IN == kF16 ? 0x3C00u : 0x3F80u;
+        const int m = l16;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int q = (m & 3) | (h << 2) | ((m >> 2) << 3);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int k = 8 * (lane >> 4) + 2 * c + e;
+                    const uint32_t sgn = __builtin_popcount(q & k) & 1;
+                    w |= (one | (sgn << 15)) << (16 * e);
+                }
+                amat[h][c] = w;
+            }
+        }
+    }
+
+    // ---- work split: one persistent workgroup per CU hands out groups of
+    // T tiles through an LDS counter (groups strided across workgroups)
+    __shared__ int pool_next;
+    const int64_t pool_size = (a.groups - blockIdx.x + gridDim.x - 1) / gridDim.x;
+    const int nwaves = blockDim.x >> 6;
+    const int64_t first = wave;
+    const bool has_work = first < pool_size;
+    if (threadIdx.x == 0)
+        pool_next = nwaves;
+    auto grab = [&]() -> int64_t {
+        int v = 0;
+        if (lane == 0)
+            v = atomicAdd(&pool_next, 1);
+        return __builtin_amdgcn_readfirstlane(v);
+    };
+    // first element of group g (wave-uniform)
+    auto group_elem0 = [&](int64_t g) {
+        return ((int64_t)blockIdx.x + g * gridDim.x) * (int64_t)(T * 512);
+    };
+
+    auto load = [&](int64_t g, u32x4 (&raw)[T]) {
+        const int64_t e0 = group_elem0(g);
+        const int64_t left = a.total - 8 - e0;  // >= 0 for every group
+        const int lim = left < T * 512 ? (int)left : T * 512;
+        const uint16_t *gp = (const uint16_t *)a.x + e0;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            int eo = t * 512 + lane_off;
+            eo = eo < lim ? eo : lim;  // the ragged end reads valid memory
+            raw[t] = fast::stream_load((const u32x4 *)(gp + eo));
+        }
+    };
+
+    // ---- sign masks (bit 15 of each 16-bit element).  Rows of up to 512
+    // elements: the lane's 8 row positions are the same in every tile, so
+    // the masks live in 4 registers.  Wider rows: one 16-byte mask per
+    // (tile of the row, lane) in LDS.
+    u32x4 smask = {0, 0, 0, 0};
+    if constexpr (TPR == 1) {
+        const int p = lane_off & ((1 << LOGN) - 1);
+        const u32x2 sb = *(const u32x2 *)(a.s + p);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t w = sb[c >> 1] >> (16 * (c & 1));
+            smask[c] = ((w >> 7) & 1) << 15 | ((w >> 15) & 1) << 31;
+        }
+    }
+
+    u32x4 cur[T];
+    load(has_work ? first : 0, cur);
+
+    if constexpr (TPR > 1) {
+        for (int idx = threadIdx.x; idx < TPR * 64; idx += blockDim.x) {
+            const int ln = idx & 63;
+            const int p = (idx >> 6) * 512 + 8 * (ln >> 4) + 32 * (ln & 15);
+            const u32x2 sb = *(const u32x2 *)(a.s + p);
+            u32x4 m;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t w = sb[c >> 1] >> (16 * (c & 1));
+                m[c] = ((w >> 7) & 1) << 15 | ((w >> 15) & 1) << 31;
+            }
+            lds_mask[idx] = m;
+        }
+    }
+    // LDS-only release: the barrier must not wait for the row loads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+    // Loads and stores share one completion counter; this empty asm fixes
+    // where the wait for a prefetch happens (see the butterfly kernel).
+    auto take_delivery = [&](u32x4 (&raw)[T]) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                asm volatile("" : "+v"(raw[t][c]));
+    };
+    take_delivery(cur);
+
+    int64_t g = first;
+    while (g < pool_size) {
+        const int64_t g_next = grab();
+        float v[T][8];
+        // ------------------------------------------ signs + 32-point product
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            u32x4 m = smask;
+            if constexpr (TPR > 1) {
+                int mofs = (t % TPR) * 64 + lane;
+                asm volatile("" : "+v"(mofs));  // keep the read in the loop
+                m = lds_mask[mofs];
+            }
+            u32x4 b;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                b[c] = cur[t][c] ^ m[c];
+            const f32x4 d0 = hmma<IN>(amat[0], b);
+            const f32x4 d1 = hmma<IN>(amat[1], b);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[t][i] = d0[i];
+                v[t][4 + i] = d1[i];
+            }
+        }
+        // ------------------------------------ prefetch the next tile group
+        if (g_next < pool_size)  // wave-uniform
+            load(g_next, cur);
+
+        // ------------------------------------------ tile-bit stages (b > 512)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                if ((t >> r) & 1)
+                    continue;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    fast::bfly(v[t][j], v[t + (1 << r)][j]);
+            }
+
+        // ------------------------------------- DPP stages (lane bits 0..D-1)
+        if constexpr (D > 0) {
+            // The DPP blocks are inline asm, which the compiler does not pad
+            // against the matrix unit's write latency.  Every product result
+            // is first passed through an empty asm (in program order), then
+            // 20 wait states cover the longest MFMA-write -> VALU hazard.
+            if constexpr (R == 0) {
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        asm volatile("" : "+v"(v[t][j]));
+                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::);
+            }
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                fast::dpp_stages<D>(v[t], sig0, sig1, sig2, sig3);
+        }
+
+        // Take delivery of the prefetched group before this group's stores.
+        take_delivery(cur);
+
+        // ------------------------------------------------------------ outputs
+        const int64_t e0 = group_elem0(g);
+        if constexpr (OP == kRotate) {
+            const float mul = lane_neg ? -a.rb : a.rb;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const int eo = t * 512 + out_off;
+                if (e0 + eo < a.total) {
+                    float4 *dst = (float4 *)((float *)a.y + e0 + eo);
+                    dst[0] = make_float4(v[t][0] * mul, v[t][1] * mul, v[t][2] * mul, v[t][3] * mul);
+                    dst[1] = make_float4(v[t][4] * mul, v[t][5] * mul, v[t][6] * mul, v[t][7] * mul);
+                }
+            }
+        } else {
+            const int qmax = a.bits == 4 ? 7 : 127;
+#pragma unroll
+            for (int rr = 0; rr < T / TPR; ++rr) {
+                // tiles t0 .. t0+TPR-1 hold RPT rows (TPR == 1) or one row
+                const int t0 = rr * TPR;
+                float m = 0.0f;
+#pragma unroll
+                for (int t = t0; t < t0 + TPR; ++t)
+#pragma unroll
+                    for (int j = 0; j < 8; j += 2)
+                        m = fmaxf(fmaxf(m, fabsf(v[t][j])), fabsf(v[t][j + 1]));
+                constexpr int NDPP = LOGN - 5 < 4 ? LOGN - 5 : 4;
+                const uint32_t mb = row_lane_max<NDPP>(__float_as_uint(m));
+                const RowQuant rq = row_quant(__uint_as_float(mb), a.kq, qmax);
+                // the lane's row: first element of its outputs / n
+                const int64_t row = (e0 + t0 * 512 + out_off) >> LOGN;
+                const bool row_ok = row < a.rows;
+                // one lane per row writes the scale: lane bits 4, 5 and the
+                // row-internal low lane bits all zero
+                constexpr int row_lanes_mask = (1 << NDPP) - 1;
+                if (row_ok && lane < 16 && (l16 & row_lanes_mask) == 0) {
+                    if (a.scale_f16)
+                        ((uint16_t *)a.scales)[row] = f32_to_f16(rq.scale);
+                    else
+                        ((float *)a.scales)[row] = rq.scale;
+                }
+                const float inv = lane_neg ? -rq.inv : rq.inv;
+                if (row_ok) {
+#pragma unroll
+                    for (int t = t0; t < t0 + TPR; ++t) {
+                        const int eo = t * 512 + out_off;
+                        if (a.bits == 4) {
+                            uint32_t f[8];
+#pragma unroll
+                            for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 8
+                                f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv, 12582920.0f));
+                            *(uint32_t *)((uint8_t *)a.codes + (e0 >> 1) + (eo >> 1)) =
+                                fast::pack_int4(f);
+                        } else {
+                            uint32_t f[8];
+#pragma unroll
+                            for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 128
+                                f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv, 12583040.0f));
+                            *(uint2 *)((int8_t *)a.codes + e0 + eo) =
+                                make_uint2(fast::pack_int8(f[0], f[1], f[2], f[3]),
+                                           fast::pack_int8(f[4], f[5], f[6], f[7]));
+                        }
+                    }
+                }
+            }
+        }
+        g = g_next;
+    }
+}
+
+}  // namespace mfma
+}  // namespace hq
+
+namespace hq {
+namespace mfma {
+
+// Host side (hq_mfma.hip): plan check, argument setup and the launch.
+bool plan_ok(const Request &r);
+void fill_args(MfmaArgs &ma, const Request &r, int tiles_per_group);
+int occupancy_waves(const void *fn, size_t lds);
+
+template <int OP, int IN, int T, int LOGB, int LOGN>
+hipError_t launch_one(const Request &r, const DeviceInfo &dev)
+{
+    MfmaArgs ma;
+    fill_args(ma, r, T);
+    constexpr int TPR = LOGN > 9 ? 1 << (LOGN - 9) : 1;
+    const size_t lds = TPR > 1 ? (size_t)TPR * 64 * 16 : 0;
+    auto fn = mfma_kernel<OP, IN, T, LOGB, LOGN>;
+    // every wave the CU can hold, in as few workgroups as the thread limit
+    // of the kernel allows
+    const int max_threads = T < 8 ? 1024 : 768;
+    const int waves_cu = occupancy_waves((const void *)fn, lds);
+    const int grid_per_cu = (waves_cu * 64 + max_threads - 1) / max_threads;
+    const int threads = 64 * (waves_cu / grid_per_cu);
+    int64_t grid = (int64_t)dev.cu_count * grid_per_cu;
+    if (grid > ma.groups)
+        grid = ma.groups;
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), lds, r.stream, ma);
+    return hipGetLastError();
+}
+
+// Full rotations of n = 32..4096 and 128-blocks of n = 256..4096.
+template <int OP, int IN>
+hipError_t dispatch_op(const Request &r, const DeviceInfo &dev)
+{
+    const bool full = r.b == r.n;
+    switch (r.n) {
+    case 32: return launch_one<OP, IN, 4, 5, 5>(r, dev);
+    case 64: return launch_one<OP, IN, 4, 6, 6>(r, dev);
+    case 128: return launch_one<OP, IN, 4, 7, 7>(r, dev);
+    case 256: return full ? launch_one<OP, IN, 4, 8, 8>(r, dev) : launch_one<OP, IN, 4, 7, 8>(r, dev);
+    case 512: return full ? launch_one<OP, IN, 4, 9, 9>(r, dev) : launch_one<OP, IN, 4, 7, 9>(r, dev);
+    case 1024:
+        return full ? launch_one<OP, IN, 8, 10, 10>(r, dev) : launch_one<OP, IN, 8, 7, 10>(r, dev);
+    case 2048:
+        return full ? launch_one<OP, IN, 8, 11, 11>(r, dev) : launch_one<OP, IN, 8, 7, 11>(r, dev);
+    default:
+        return full ? launch_one<OP, IN, 8, 12, 12>(r, dev) : launch_one<OP, IN, 8, 7, 12>(r, dev);
+    }
+}
+
+}  // namespace mfma
+}  // namespace hq
