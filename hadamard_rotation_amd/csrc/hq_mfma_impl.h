@@ -390,13 +390,14 @@ hipError_t launch_one(const Request &r, const DeviceInfo &dev)
     constexpr int TPR = LOGN > 9 ? 1 << (LOGN - 9) : 1;
     const size_t lds = TPR > 1 ? (size_t)TPR * 64 * 16 : 0;
     auto fn = mfma_kernel<OP, IN, T, LOGB, LOGN>;
-    // every wave the CU can hold, in as few workgroups as the thread limit
-    // of the kernel allows
+    // One workgroup per CU with every wave the CU can hold, at most 16
+    // (measured on the 128-wide K/V rows: 16 waves per CU beat 20 by 10 %).
     const int max_threads = T < 8 ? 1024 : 768;
-    const int waves_cu = occupancy_waves((const void *)fn, lds);
-    const int grid_per_cu = (waves_cu * 64 + max_threads - 1) / max_threads;
-    const int threads = 64 * (waves_cu / grid_per_cu);
-    int64_t grid = (int64_t)dev.cu_count * grid_per_cu;
+    int waves_cu = occupancy_waves((const void *)fn, lds);
+    if (waves_cu > max_threads / 64)
+        waves_cu = max_threads / 64;
+    const int threads = 64 * waves_cu;
+    int64_t grid = dev.cu_count;
     if (grid > ma.groups)
         grid = ma.groups;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), lds, r.stream, ma);
@@ -404,16 +405,33 @@ hipError_t launch_one(const Request &r, const DeviceInfo &dev)
 }
 
 // Full rotations of n = 32..4096 and 128-blocks of n = 256..4096.
+// Rows of up to 512 elements take groups of 4 tiles, or of 2 tiles when
+// that would leave fewer than 4 groups per wave (the last round of groups
+// then idles less of the machine; measured on 131072 x 128).
+template <int OP, int IN, int T>
+hipError_t dispatch_short(const Request &r, const DeviceInfo &dev)
+{
+    const bool full = r.b == r.n;
+    switch (r.n) {
+    case 32: return launch_one<OP, IN, T, 5, 5>(r, dev);
+    case 64: return launch_one<OP, IN, T, 6, 6>(r, dev);
+    case 128: return launch_one<OP, IN, T, 7, 7>(r, dev);
+    case 256: return full ? launch_one<OP, IN, T, 8, 8>(r, dev) : launch_one<OP, IN, T, 7, 8>(r, dev);
+    default: return full ? launch_one<OP, IN, T, 9, 9>(r, dev) : launch_one<OP, IN, T, 7, 9>(r, dev);
+    }
+}
+
 template <int OP, int IN>
 hipError_t dispatch_op(const Request &r, const DeviceInfo &dev)
 {
     const bool full = r.b == r.n;
+    if (r.n <= 512) {
+        const int64_t groups4 = (r.rows * (int64_t)r.n + 4 * 512 - 1) / (4 * 512);
+        if (groups4 < (int64_t)dev.cu_count * 16 * 4)
+            return dispatch_short<OP, IN, 2>(r, dev);
+        return dispatch_short<OP, IN, 4>(r, dev);
+    }
     switch (r.n) {
-    case 32: return launch_one<OP, IN, 4, 5, 5>(r, dev);
-    case 64: return launch_one<OP, IN, 4, 6, 6>(r, dev);
-    case 128: return launch_one<OP, IN, 4, 7, 7>(r, dev);
-    case 256: return full ? launch_one<OP, IN, 4, 8, 8>(r, dev) : launch_one<OP, IN, 4, 7, 8>(r, dev);
-    case 512: return full ? launch_one<OP, IN, 4, 9, 9>(r, dev) : launch_one<OP, IN, 4, 7, 9>(r, dev);
     case 1024:
         return full ? launch_one<OP, IN, 8, 10, 10>(r, dev) : launch_one<OP, IN, 8, 7, 10>(r, dev);
     case 2048:

@@ -118,11 +118,12 @@ def test_qk_inner_products_preserved():
 
 # ----------------------------------------------------------------- shapes
 
-SHAPES = [  # (n, b): generic and tuned paths, blockwise and full
-    (16, 1), (16, 2), (16, 16), (32, 4), (64, 8), (128, 32), (128, 128), (256, 256),
-    (512, 64), (512, 512), (1024, 1024), (2048, 128), (2048, 2048), (4096, 64),
-    (4096, 256), (4096, 1024), (4096, 4096), (8192, 4096), (11008, 16), (11008, 128),
-    (11008, 256), (16384, 4096),
+SHAPES = [  # (n, b): generic, butterfly and matrix-core paths, blockwise and full
+    (16, 1), (16, 2), (16, 16), (32, 4), (32, 32), (64, 8), (64, 64), (128, 32),
+    (128, 128), (256, 128), (256, 256), (512, 64), (512, 128), (512, 512), (1024, 128),
+    (1024, 1024), (2048, 128), (2048, 2048), (4096, 64), (4096, 128), (4096, 256),
+    (4096, 1024), (4096, 4096), (8192, 4096), (11008, 16), (11008, 128), (11008, 256),
+    (16384, 4096),
 ]
 
 
