@@ -40,9 +40,17 @@ def copy_bytes_for(bytes_call: int) -> int:
     return bytes_call // 2
 
 
+# The sources the rotate + quantise launch of 16-bit rows is built from
+# (dispatch, shared primitives, the matrix-core kernel and its host side).
+TRAFFIC_SOURCES = ("hq_api.hip", "hq_internal.h", "hq_device.h", "hq_fast_impl.h",
+                   "hq_mfma_impl.h", "hq_mfma.hip", "hq_mfma_rq.hip")
+
+
 def source_hash() -> str:
+    """Hash of the kernel sources a stored traffic measurement belongs to."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "hadamard_rotation_amd", "csrc", "*"))):
+    for name in TRAFFIC_SOURCES:
+        p = os.path.join(ROOT, "hadamard_rotation_amd", "csrc", name)
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
