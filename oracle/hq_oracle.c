@@ -28,10 +28,16 @@
  *         [RQ] 2.1; b == n is the full rotation)
  *   m = max_i |x'_i| over the whole row; scale = m / qmax, qmax = 2^(bits-1)-1
  *   q_i = clamp(round_half_even(x'_i / scale), -qmax, qmax)   ([RQ] 2.2, [HQA] 1)
+ *   Group-wise scales: the same, with m taken over each run of `group`
+ *   consecutive elements of the rotated row and one scale per run, stored
+ *   row by row ([RQ] 6.2 recommends group size 128 for 4 bits; [QT] 4.2
+ *   keeps the scales of one group together).  group == n is the per-row
+ *   case above.
  *   INT4 storage: two codes per byte, element 2j in the low nibble, 4-bit
  *   two's complement ([QT] 2.2 gives the 4x size reduction; the nibble
  *   order is this library's convention).
- *   Inverse: v = q * scale_stored; x_hat_blk = (v_blk . H_b / sqrt(b)) * s
+ *   Inverse: v = q * scale_stored (the scale of the element's group);
+ *        x_hat_blk = (v_blk . H_b / sqrt(b)) * s
  *        (the normalised H is orthogonal and symmetric, so it is its own
  *         inverse: [MS] principle, [HQA] 1).
  *
@@ -189,44 +195,51 @@ static void rotate_row(const double *x, const int8_t *s, int n, int b,
 
 static int qmax_of(int bits) { return (1 << (bits - 1)) - 1; }
 
-/* Quantises one rotated row.  Writes the packed codes, the stored scale and
- * optionally the exact (fp64) scale and the pre-rounding values x'/scale. */
-static void quantize_row(const double *xr, int n, int bits, int scale_dtype,
+/* Quantises one rotated row in groups of `group` consecutive elements (one
+ * scale each; group == n is one scale per row).  Writes the packed codes,
+ * the stored scales [row * (n/group) + k] and optionally the exact (fp64)
+ * scales (same index) and the pre-rounding values x'/scale. */
+static void quantize_row(const double *xr, int n, int group, int bits, int scale_dtype,
                          uint8_t *codes, void *scale_out, int64_t row,
                          double *scale_exact, double *preround)
 {
     int qmax = qmax_of(bits);
-    double m = 0.0;
-    for (int i = 0; i < n; ++i)
-        if (fabs(xr[i]) > m)
-            m = fabs(xr[i]);
-    double scale = m / (double)qmax;
-    if (scale_exact)
-        scale_exact[row] = scale;
-    if (scale_dtype == HQO_F32)
-        ((float *)scale_out)[row] = (float)scale; /* C cast: round to nearest even */
-    else
-        ((uint16_t *)scale_out)[row] = hqo_f64_to_f16(scale);
+    int ngroups = n / group;
+    for (int k = 0; k < ngroups; ++k) {
+        int i0 = k * group;
+        int64_t si = row * ngroups + k;
+        double m = 0.0;
+        for (int i = i0; i < i0 + group; ++i)
+            if (fabs(xr[i]) > m)
+                m = fabs(xr[i]);
+        double scale = m / (double)qmax;
+        if (scale_exact)
+            scale_exact[si] = scale;
+        if (scale_dtype == HQO_F32)
+            ((float *)scale_out)[si] = (float)scale; /* C cast: round to nearest even */
+        else
+            ((uint16_t *)scale_out)[si] = hqo_f64_to_f16(scale);
 
-    for (int i = 0; i < n; ++i) {
-        double r = (m > 0.0) ? xr[i] / scale : 0.0; /* all-zero row: codes 0 */
-        if (preround)
-            preround[(int64_t)row * n + i] = r;
-        double qd = nearbyint(r); /* round half to even */
-        if (qd > qmax)
-            qd = qmax;
-        if (qd < -qmax)
-            qd = -qmax;
-        int q = (int)qd;
-        if (bits == 8) {
-            codes[(int64_t)row * n + i] = (uint8_t)(int8_t)q;
-        } else {
-            uint8_t *byte = codes + (int64_t)row * (n / 2) + i / 2;
-            uint8_t nib = (uint8_t)(q & 0xf);
-            if ((i & 1) == 0)
-                *byte = nib;
-            else
-                *byte = (uint8_t)(*byte | (nib << 4));
+        for (int i = i0; i < i0 + group; ++i) {
+            double r = (m > 0.0) ? xr[i] / scale : 0.0; /* all-zero group: codes 0 */
+            if (preround)
+                preround[(int64_t)row * n + i] = r;
+            double qd = nearbyint(r); /* round half to even */
+            if (qd > qmax)
+                qd = qmax;
+            if (qd < -qmax)
+                qd = -qmax;
+            int q = (int)qd;
+            if (bits == 8) {
+                codes[(int64_t)row * n + i] = (uint8_t)(int8_t)q;
+            } else {
+                uint8_t *byte = codes + (int64_t)row * (n / 2) + i / 2;
+                uint8_t nib = (uint8_t)(q & 0xf);
+                if ((i & 1) == 0)
+                    *byte = nib;
+                else
+                    *byte = (uint8_t)(*byte | (nib << 4));
+            }
         }
     }
 }
@@ -240,11 +253,11 @@ static int unpack_code(const uint8_t *codes, int64_t row, int n, int bits, int i
     return nib >= 8 ? nib - 16 : nib;
 }
 
-static double stored_scale(const void *scales, int scale_dtype, int64_t row)
+static double stored_scale(const void *scales, int scale_dtype, int64_t index)
 {
     if (scale_dtype == HQO_F32)
-        return (double)((const float *)scales)[row];
-    return hqo_f16_to_f64(((const uint16_t *)scales)[row]);
+        return (double)((const float *)scales)[index];
+    return hqo_f16_to_f64(((const uint16_t *)scales)[index]);
 }
 
 /* ------------------------------------------------------------- threading */
@@ -254,7 +267,7 @@ typedef struct {
     const void *x;
     int x_dtype;
     int64_t rows;
-    int n, b, bits, scale_dtype;
+    int n, b, group, bits, scale_dtype;
     const int8_t *s;
     const int8_t *Ht;
     double *xr;
@@ -290,13 +303,17 @@ static void *worker(void *arg)
             rotate_row(xin, j->s, n, j->b, j->Ht, u, out);
             if (j->xr)
                 memcpy(j->xr + r * n, out, sizeof(double) * n);
-            quantize_row(out, n, j->bits, j->scale_dtype, j->codes, j->scales, r,
+            quantize_row(out, n, j->group, j->bits, j->scale_dtype, j->codes, j->scales, r,
                          j->scale_exact, j->preround);
         } else {
-            /* v = q * scale_stored, then v.H/sqrt(b) per block, then * s. */
-            double sc = stored_scale(j->scales_in, j->scale_dtype, r);
-            for (int i = 0; i < n; ++i)
+            /* v = q * scale_stored (of the element's group), then v.H/sqrt(b)
+             * per block, then * s. */
+            int ngroups = n / j->group;
+            for (int i = 0; i < n; ++i) {
+                double sc = stored_scale(j->scales_in, j->scale_dtype,
+                                         r * ngroups + i / j->group);
                 xin[i] = (double)unpack_code(j->codes_in, r, n, j->bits, i) * sc;
+            }
             rotate_row(xin, ones, n, j->b, j->Ht, u, out);
             for (int i = 0; i < n; ++i)
                 j->y[r * n + i] = j->s[i] < 0 ? -out[i] : out[i];
@@ -379,16 +396,19 @@ int hqo_rotate(const double *x, int64_t rows, int n, int b, const int8_t *s,
     return run_jobs(&j, threads);
 }
 
-/* Rotation + quantisation straight from the raw input bytes.
- * codes: [rows, n/2] (bits 4) or [rows, n] (bits 8);  scales: [rows] fp32
- * or fp16 bits.  scale_exact [rows], preround [rows*n] and xr [rows*n] are
- * optional diagnostics (NULL to skip). */
-int hqo_rotate_quant(const void *x, int x_dtype, int64_t rows, int n, int b,
-                     const int8_t *s, int bits, uint8_t *codes, void *scales,
-                     int scale_dtype, double *scale_exact, double *preround,
-                     double *xr, int threads)
+/* Rotation + quantisation straight from the raw input bytes, one scale per
+ * run of `group` consecutive rotated elements (group must divide n).
+ * codes: [rows, n/2] (bits 4) or [rows, n] (bits 8);  scales: [rows, n/group]
+ * fp32 or fp16 bits.  scale_exact [rows, n/group], preround [rows*n] and
+ * xr [rows*n] are optional diagnostics (NULL to skip). */
+int hqo_rotate_quant_g(const void *x, int x_dtype, int64_t rows, int n, int b,
+                       const int8_t *s, int bits, int group, uint8_t *codes, void *scales,
+                       int scale_dtype, double *scale_exact, double *preround,
+                       double *xr, int threads)
 {
     if (check_shape(rows, n, b, s))
+        return -1;
+    if (group <= 0 || n % group != 0 || (bits == 4 && group % 2 != 0))
         return -1;
     if (bits != 4 && bits != 8)
         return -1;
@@ -408,6 +428,7 @@ int hqo_rotate_quant(const void *x, int x_dtype, int64_t rows, int n, int b,
     j.rows = rows;
     j.n = n;
     j.b = b;
+    j.group = group;
     j.bits = bits;
     j.scale_dtype = scale_dtype;
     j.s = s;
@@ -419,12 +440,25 @@ int hqo_rotate_quant(const void *x, int x_dtype, int64_t rows, int n, int b,
     return run_jobs(&j, threads);
 }
 
-/* Dequantisation + inverse rotation: y = ((q*scale_stored) . H_b/sqrt(b)) * s. */
-int hqo_dequant_rotate_inv(const uint8_t *codes, const void *scales,
-                           int scale_dtype, int64_t rows, int n, int b,
-                           const int8_t *s, int bits, double *y, int threads)
+/* Per-row scales: the group-wise function with group == n. */
+int hqo_rotate_quant(const void *x, int x_dtype, int64_t rows, int n, int b,
+                     const int8_t *s, int bits, uint8_t *codes, void *scales,
+                     int scale_dtype, double *scale_exact, double *preround,
+                     double *xr, int threads)
+{
+    return hqo_rotate_quant_g(x, x_dtype, rows, n, b, s, bits, n, codes, scales,
+                              scale_dtype, scale_exact, preround, xr, threads);
+}
+
+/* Dequantisation + inverse rotation with group-wise scales [rows, n/group]:
+ * y = ((q*scale_stored) . H_b/sqrt(b)) * s. */
+int hqo_dequant_rotate_inv_g(const uint8_t *codes, const void *scales,
+                             int scale_dtype, int64_t rows, int n, int b,
+                             const int8_t *s, int bits, int group, double *y, int threads)
 {
     if (check_shape(rows, n, b, s))
+        return -1;
+    if (group <= 0 || n % group != 0 || (bits == 4 && group % 2 != 0))
         return -1;
     if (bits != 4 && bits != 8)
         return -1;
@@ -443,10 +477,20 @@ int hqo_dequant_rotate_inv(const uint8_t *codes, const void *scales,
     j.rows = rows;
     j.n = n;
     j.b = b;
+    j.group = group;
     j.bits = bits;
     j.s = s;
     j.y = y;
     return run_jobs(&j, threads);
+}
+
+/* Per-row scales: the group-wise inverse with group == n. */
+int hqo_dequant_rotate_inv(const uint8_t *codes, const void *scales,
+                           int scale_dtype, int64_t rows, int n, int b,
+                           const int8_t *s, int bits, double *y, int threads)
+{
+    return hqo_dequant_rotate_inv_g(codes, scales, scale_dtype, rows, n, b, s, bits, n, y,
+                                    threads);
 }
 
 /* Number of worker threads a call with threads<=0 would use. */

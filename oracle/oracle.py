@@ -55,14 +55,17 @@ def _load():
         lib.hqo_decode.argtypes = [P, I, L, P]
         lib.hqo_rotate.argtypes = [P, L, I, I, P, P, I]
         lib.hqo_rotate_quant.argtypes = [P, I, L, I, I, P, I, P, P, I, P, P, P, I]
+        lib.hqo_rotate_quant_g.argtypes = [P, I, L, I, I, P, I, I, P, P, I, P, P, P, I]
         lib.hqo_dequant_rotate_inv.argtypes = [P, P, I, L, I, I, P, I, P, I]
+        lib.hqo_dequant_rotate_inv_g.argtypes = [P, P, I, L, I, I, P, I, I, P, I]
         lib.hqo_f64_to_f16.argtypes = [ctypes.c_double]
         lib.hqo_f64_to_f16.restype = ctypes.c_uint16
         lib.hqo_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.hqo_f16_to_f64.restype = ctypes.c_double
         lib.hqo_default_threads.restype = ctypes.c_int
         for f in (lib.hqo_hadamard, lib.hqo_decode, lib.hqo_rotate,
-                  lib.hqo_rotate_quant, lib.hqo_dequant_rotate_inv):
+                  lib.hqo_rotate_quant, lib.hqo_rotate_quant_g,
+                  lib.hqo_dequant_rotate_inv, lib.hqo_dequant_rotate_inv_g):
             f.restype = ctypes.c_int
         _lib = lib
         return lib
@@ -121,26 +124,30 @@ def rotate(x: np.ndarray, s: np.ndarray, b: int, threads: int = 0) -> np.ndarray
 
 def rotate_quant(raw: np.ndarray, x_dtype: int, b: int, s: np.ndarray, bits: int,
                  scale_dtype: int, threads: int = 0, want_xr: bool = False,
-                 want_preround: bool = True) -> dict:
-    """Rotation + symmetric per-row quantisation of raw rows [rows, n].
+                 want_preround: bool = True, group: int | None = None) -> dict:
+    """Rotation + symmetric quantisation of raw rows [rows, n], one scale per
+    row (group None) or per run of `group` consecutive rotated elements.
 
     Returns a dict with
       codes        uint8 [rows, n/2] (bits 4) or [rows, n] (bits 8)
-      scales       stored scales: float32, or float16 when scale_dtype is F16
-      scale_exact  float64 [rows], absmax/qmax before storage rounding
+      scales       stored scales: float32, or float16 when scale_dtype is F16;
+                   [rows] per row, [rows, n/group] per group
+      scale_exact  float64, same shape: absmax/qmax before storage rounding
       preround     float64 [rows, n], x'/scale_exact (if want_preround)
       xr           float64 [rows, n], the rotated row (if want_xr)
     """
     raw = np.ascontiguousarray(raw)
     s = np.ascontiguousarray(s, dtype=np.int8)
     rows, n = raw.shape
+    g = n if group is None else int(group)
+    sshape = (rows,) if group is None else (rows, n // g if g > 0 else 0)
     codes = np.empty((rows, n // 2 if bits == 4 else n), dtype=np.uint8)
-    scales = np.empty(rows, dtype=np.float32 if scale_dtype == F32 else np.uint16)
-    scale_exact = np.empty(rows, dtype=np.float64)
+    scales = np.empty(sshape, dtype=np.float32 if scale_dtype == F32 else np.uint16)
+    scale_exact = np.empty(sshape, dtype=np.float64)
     pre = np.empty((rows, n), dtype=np.float64) if want_preround else None
     xr = np.empty((rows, n), dtype=np.float64) if want_xr else None
-    rc = _load().hqo_rotate_quant(
-        _ptr(raw), int(x_dtype), rows, n, int(b), _ptr(s), int(bits), _ptr(codes),
+    rc = _load().hqo_rotate_quant_g(
+        _ptr(raw), int(x_dtype), rows, n, int(b), _ptr(s), int(bits), g, _ptr(codes),
         _ptr(scales), int(scale_dtype), _ptr(scale_exact),
         _ptr(pre) if pre is not None else None,
         _ptr(xr) if xr is not None else None, threads)
@@ -153,18 +160,20 @@ def rotate_quant(raw: np.ndarray, x_dtype: int, b: int, s: np.ndarray, bits: int
 
 def dequant_rotate_inv(codes: np.ndarray, scales: np.ndarray, scale_dtype: int,
                        b: int, s: np.ndarray, bits: int, n: int,
-                       threads: int = 0) -> np.ndarray:
-    """y = ((q*scale_stored).H_b/sqrt(b)) * s, float64 [rows, n]."""
+                       threads: int = 0, group: int | None = None) -> np.ndarray:
+    """y = ((q*scale_stored).H_b/sqrt(b)) * s, float64 [rows, n]; scales per
+    row (group None) or [rows, n/group] per group."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales)
     if scale_dtype == F16:
         scales = scales.view(np.uint16)
     s = np.ascontiguousarray(s, dtype=np.int8)
     rows = codes.shape[0]
+    g = int(n) if group is None else int(group)
     y = np.empty((rows, n), dtype=np.float64)
-    rc = _load().hqo_dequant_rotate_inv(_ptr(codes), _ptr(scales), int(scale_dtype),
-                                        rows, int(n), int(b), _ptr(s), int(bits),
-                                        _ptr(y), threads)
+    rc = _load().hqo_dequant_rotate_inv_g(_ptr(codes), _ptr(scales), int(scale_dtype),
+                                          rows, int(n), int(b), _ptr(s), int(bits), g,
+                                          _ptr(y), threads)
     _check(rc, "dequant_rotate_inv")
     return y
 

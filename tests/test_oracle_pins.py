@@ -389,3 +389,123 @@ def test_fp16_scales_are_rounded_once_from_fp64():
     raw, s = _rows(21, 64, 128)
     r = O.rotate_quant(raw, O.BF16, 128, s, 4, O.F16)
     assert np.array_equal(r["scales"], r["scale_exact"].astype(np.float16))
+
+
+# ------------------------------------------------------- group-wise scales
+# [RQ] section 6.2 recommends one scale per group of 128 elements for 4 bits;
+# [QT] section 4.2 keeps a group's scales together.  Groups are runs of
+# `group` consecutive elements of the rotated row.
+
+def _popcount_sign(p, i):
+    return -1.0 if bin(p & i).count("1") % 2 else 1.0
+
+
+@pytest.mark.parametrize("group", [32, 64, 128, 256])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_group_spike_closed_form(group, bits):
+    # one spike A at position p, full rotation of n = 256: every rotated
+    # element is s_p * A * H[p, i] / 16 (closed form of the Sylvester row),
+    # so every group has scale A / (16 qmax) and codes +-qmax
+    n, p, A = 256, 77, 112.0
+    qmax = 7 if bits == 4 else 127
+    s = np.where(np.arange(n) % 3 == 1, -1, 1).astype(np.int8)
+    x = np.zeros((1, n), dtype=np.float32)
+    x[0, p] = A
+    r = O.rotate_quant(x, O.F32, n, s, bits, O.F32, group=group)
+    assert r["scales"].shape == (1, n // group)
+    assert np.allclose(r["scale_exact"], A / 16 / qmax, rtol=0, atol=1e-15)
+    want = np.array([qmax * s[p] * _popcount_sign(p, i) for i in range(n)])
+    assert np.array_equal(O.unpack_codes(r["codes"], bits, n)[0], want)
+
+
+@pytest.mark.parametrize("n,b", [(256, 256), (512, 128), (384, 128)])
+def test_group_equal_to_row_is_per_row(n, b):
+    raw = np.random.default_rng(3).standard_normal((9, n)).astype(np.float32)
+    s = np.where(np.random.default_rng(4).integers(0, 2, n) == 1, 1, -1).astype(np.int8)
+    for bits, sd in ((4, O.F32), (8, O.F16)):
+        a = O.rotate_quant(raw, O.F32, b, s, bits, sd)
+        g = O.rotate_quant(raw, O.F32, b, s, bits, sd, group=n)
+        assert np.array_equal(a["codes"], g["codes"])
+        assert np.array_equal(a["scales"], g["scales"][:, 0])
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_group_equal_to_block_reduces_to_per_row(bits):
+    # with group == b, a row of n/b blocks is n/b independent rows of b
+    # elements (sign vector sliced per block): the per-row function (pinned
+    # above) on the reshaped tensor gives the same codes and scales
+    rows, n, b = 5, 512, 128
+    raw = np.random.default_rng(5).standard_normal((rows, n)).astype(np.float32)
+    raw[:, 17] *= 40
+    s = np.where(np.random.default_rng(6).integers(0, 2, n) == 1, 1, -1).astype(np.int8)
+    g = O.rotate_quant(raw, O.F32, b, s, bits, O.F32, group=b)
+    codes = O.unpack_codes(g["codes"], bits, n)
+    for k in range(n // b):
+        part = np.ascontiguousarray(raw[:, k * b:(k + 1) * b])
+        r = O.rotate_quant(part, O.F32, b, s[k * b:(k + 1) * b], bits, O.F32)
+        assert np.array_equal(O.unpack_codes(r["codes"], bits, b), codes[:, k * b:(k + 1) * b])
+        assert np.array_equal(r["scales"], g["scales"][:, k])
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_group_error_bound_and_qmax(group):
+    # inside every group: |x' - q*scale| <= scale/2, and the group's largest
+    # element gets +-qmax
+    n, b = 1024, 1024
+    raw = np.random.default_rng(7).standard_t(4, (6, n)).astype(np.float32)
+    s = np.where(np.random.default_rng(8).integers(0, 2, n) == 1, 1, -1).astype(np.int8)
+    r = O.rotate_quant(raw, O.F32, b, s, 4, O.F32, group=group, want_xr=True)
+    q = O.unpack_codes(r["codes"], 4, n).reshape(6, n // group, group)
+    xr = r["xr"].reshape(6, n // group, group)
+    sc = r["scale_exact"][:, :, None]
+    assert np.all(np.abs(xr - q * sc) <= sc / 2 * (1 + 1e-12))
+    assert np.all(np.abs(q).max(axis=2) == 7)
+    # and the groups really differ: a per-row scale would be the largest
+    assert np.any(r["scale_exact"] < r["scale_exact"].max(axis=1, keepdims=True))
+
+
+def test_group_zero_group_in_live_row():
+    # blockwise b = group = 128: a zero block is a zero group (scale 0,
+    # codes 0) while its neighbours are not
+    n, b = 512, 128
+    x = np.random.default_rng(9).standard_normal((2, n)).astype(np.float32)
+    x[:, 128:256] = 0
+    s = np.ones(n, dtype=np.int8)
+    r = O.rotate_quant(x, O.F32, b, s, 4, O.F32, group=128)
+    assert np.all(r["scales"][:, 1] == 0) and np.all(r["scales"][:, [0, 2, 3]] > 0)
+    assert np.all(O.unpack_codes(r["codes"], 4, n)[:, 128:256] == 0)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_group_inverse_uses_each_groups_scale(bits):
+    # codes all +1 and one scale v_k per group, b = group = 64: each block of
+    # v = q*scale is constant, and a constant block c maps to c*sqrt(b) at its
+    # first position and 0 elsewhere (column sums of H_b), times the sign
+    n, b = 256, 64
+    ng = n // b
+    q = np.ones((1, n), dtype=np.int32)
+    if bits == 4:
+        codes = ((q[:, 0::2] & 0xF) | ((q[:, 1::2] & 0xF) << 4)).astype(np.uint8)
+    else:
+        codes = q.astype(np.int8).view(np.uint8)
+    scales = np.array([[0.5, 2.0, -0.0, 3.25]], dtype=np.float32)
+    s = np.where(np.arange(n) % 2 == 0, -1, 1).astype(np.int8)
+    y = O.dequant_rotate_inv(codes, scales, O.F32, b, s, bits, n, group=b)
+    want = np.zeros((1, n))
+    for k in range(ng):
+        want[0, k * b] = scales[0, k] * math.sqrt(b) * s[k * b]
+    assert np.allclose(y, want, rtol=0, atol=1e-12)
+
+
+def test_group_round_trip_of_grid_row_is_exact():
+    # the spike row of test_group_spike_closed_form lies on the grid (scale
+    # exactly 1 in fp32): group-wise forward then inverse returns the spike
+    n, p, A = 256, 77, 112.0
+    s = np.where(np.arange(n) % 3 == 1, -1, 1).astype(np.int8)
+    x = np.zeros((1, n), dtype=np.float32)
+    x[0, p] = A
+    for group in (32, 128, 256):
+        r = O.rotate_quant(x, O.F32, n, s, 4, O.F32, group=group)
+        assert np.all(r["scales"] == 1.0)
+        y = O.dequant_rotate_inv(r["codes"], r["scales"], O.F32, n, s, 4, n, group=group)
+        assert np.allclose(y, x, rtol=0, atol=1e-12)
