@@ -1,10 +1,12 @@
 """Benchmark of the fused rotate + INT4 quantise path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--group G]
 
 One step is one hq_rotate_quant call over one whole batch of the workload
 (default: 16384 tokens x 4096 bf16, full 4096-point randomized Hadamard,
-per-token INT4, fp32 scales).  The inputs are resident in HBM before timing
+per-token INT4, fp32 scales; --group G times hq_rotate_quant_grouped with one
+scale per G rotated elements instead).  The inputs are resident in HBM before timing
 starts; steps cycle through several independent buffer sets whose total
 size is well above the 256 MB last-level cache, so every step streams from
 HBM.  Rank 0 prints one JSON line.
@@ -149,6 +151,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="hidden_4096")
+    ap.add_argument("--group", type=int, default=None,
+                    help="group-wise scales: one per GROUP rotated elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the inverse-path and copy timings")
@@ -187,7 +191,8 @@ def main(argv=None):
     data = W.generate(args.workload, seed=42)
     raw, s_np = data[w.tensors[0]], data["s"]
     rows, n = raw.shape
-    bytes_call = w.bytes_per_call(rows)
+    g = args.group
+    bytes_call = w.bytes_per_call(rows, g)
     sets = min(64, max(4, int(np.ceil(3 * LLC_BYTES / bytes_call))))
 
     x_dtype = {W.F32: torch.float32, W.BF16: torch.bfloat16, W.F16: torch.float16}[w.x_dtype]
@@ -201,14 +206,26 @@ def main(argv=None):
     cw = n // 2 if w.bits == 4 else n
     cdt = torch.uint8 if w.bits == 4 else torch.int8
     codes = [torch.empty((rows, cw), dtype=cdt, device=dev) for _ in range(sets)]
-    scales = [torch.empty((rows,), dtype=sd, device=dev) for _ in range(sets)]
+    sshape = (rows,) if g is None else (rows, n // g)
+    scales = [torch.empty(sshape, dtype=sd, device=dev) for _ in range(sets)]
     del x0
     stream = torch.cuda.current_stream()
 
     def step(i):
         k = i % sets
-        hq.hq_rotate_quant(xs[k], s, w.b, w.bits, sd, codes=codes[k], scales=scales[k],
-                           stream=stream)
+        if g is None:
+            hq.hq_rotate_quant(xs[k], s, w.b, w.bits, sd, codes=codes[k], scales=scales[k],
+                               stream=stream)
+        else:
+            hq.hq_rotate_quant_grouped(xs[k], s, w.b, g, w.bits, sd, codes=codes[k],
+                                       scales=scales[k], stream=stream)
+
+    def inverse(k, y):
+        if g is None:
+            hq.hq_dequant_rotate_inv(codes[k], scales[k], s, w.b, w.bits, y=y, stream=stream)
+        else:
+            hq.hq_dequant_rotate_inv_grouped(codes[k], scales[k], s, w.b, g, w.bits, y=y,
+                                             stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -227,10 +244,15 @@ def main(argv=None):
     ms_step = ms / args.steps
     launch_us = ms_step * 1e3  # one kernel launch per step
 
-    traffic = load_traffic(args.workload)
+    traffic = load_traffic(args.workload) if g is None else None
+    if g is not None:
+        metric = f"fused rotate+quant GB/s, workload {args.workload}, group {g}"
+    elif args.workload == "hidden_4096":
+        metric = METRIC
+    else:
+        metric = f"fused rotate+quant GB/s, workload {args.workload}"
     out = {
-        "metric": METRIC if args.workload == "hidden_4096" else
-        f"fused rotate+quant GB/s, workload {args.workload}",
+        "metric": metric,
         "value": round(value, 3),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -244,7 +266,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": f"{args.workload}: {w.description}",
-            "rows": rows, "n": n, "b": w.b, "bits": w.bits,
+            "rows": rows, "n": n, "b": w.b, "bits": w.bits, "group": g or n,
             "x_dtype": W.DTYPE_NAMES[w.x_dtype], "scale_dtype": W.DTYPE_NAMES[w.scale_dtype],
             "bytes_per_call": bytes_call, "buffer_sets": sets,
             "rows_per_s": round(rows * args.steps / sec, 1),
@@ -265,18 +287,17 @@ def main(argv=None):
         # inverse path on the same workload: codes + scales -> fp32 rows
         ys = [torch.empty((rows, n), dtype=torch.float32, device=dev) for _ in range(2)]
         for i in range(5):
-            hq.hq_dequant_rotate_inv(codes[i % sets], scales[i % sets], s, w.b, w.bits,
-                                     y=ys[i % 2], stream=stream)
+            inverse(i % sets, ys[i % 2])
         torch.cuda.synchronize()
         ev0.record(stream)
         k_inv = max(10, args.steps // 4)
         for i in range(k_inv):
-            hq.hq_dequant_rotate_inv(codes[i % sets], scales[i % sets], s, w.b, w.bits,
-                                     y=ys[i % 2], stream=stream)
+            inverse(i % sets, ys[i % 2])
         ev1.record(stream)
         torch.cuda.synchronize()
         inv_s = ev0.elapsed_time(ev1) / 1e3 / k_inv
-        inv_bytes = rows * (cw + (4 if w.scale_dtype == W.F32 else 2) + 4 * n)
+        n_sc = 1 if g is None else n // g
+        inv_bytes = rows * (cw + (4 if w.scale_dtype == W.F32 else 2) * n_sc + 4 * n)
         out["inverse"] = {"us_per_call": round(inv_s * 1e6, 3),
                           "GB/s": round(inv_bytes / inv_s / 1e9, 3),
                           "bytes_per_call": inv_bytes, "out_dtype": "f32"}
@@ -297,7 +318,7 @@ def main(argv=None):
         out["copy_reference"] = {"bytes_moved": 2 * nb, "GB/s": round(2 * nb / cs / 1e9, 3)}
         del src, dst
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and g is None:
         out["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(out), flush=True)
     return 0

@@ -26,7 +26,8 @@ HQ_F32, HQ_BF16, HQ_F16 = 0, 1, 2
 _TORCH_TO_HQ = {torch.float32: HQ_F32, torch.bfloat16: HQ_BF16, torch.float16: HQ_F16}
 _HQ_TO_TORCH = {v: k for k, v in _TORCH_TO_HQ.items()}
 
-EXPORTS = ("hq_rotate_quant", "hq_dequant_rotate_inv", "hq_rotate", "hq_status_str",
+EXPORTS = ("hq_rotate_quant", "hq_dequant_rotate_inv", "hq_rotate_quant_grouped",
+           "hq_dequant_rotate_inv_grouped", "hq_rotate", "hq_status_str",
            "hq_last_hip_error", "hq_max_n", "hq_version")
 
 _lock = threading.Lock()
@@ -61,6 +62,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.hq_rotate_quant.restype = I32
         lib.hq_dequant_rotate_inv.argtypes = [P, P, I32, I64, I32, I32, P, I32, P, I32, P]
         lib.hq_dequant_rotate_inv.restype = I32
+        lib.hq_rotate_quant_grouped.argtypes = [P, I32, I64, I32, I32, P, I32, I32, P, P, I32, P]
+        lib.hq_rotate_quant_grouped.restype = I32
+        lib.hq_dequant_rotate_inv_grouped.argtypes = [P, P, I32, I64, I32, I32, P, I32, I32, P,
+                                                      I32, P]
+        lib.hq_dequant_rotate_inv_grouped.restype = I32
         lib.hq_rotate.argtypes = [P, I32, I64, I32, I32, P, P, P]
         lib.hq_rotate.restype = I32
         lib.hq_status_str.argtypes = [I32]
@@ -131,6 +137,19 @@ def hq_rotate_quant(x: torch.Tensor, s: torch.Tensor, b: int, bits: int = 4,
                     scales: torch.Tensor | None = None, stream=None):
     """Rotate + quantise rows of x.  Returns (codes, scales): codes uint8
     [rows, n/2] (bits 4) or int8 [rows, n] (bits 8); scales [rows]."""
+    return _rotate_quant(x, s, b, bits, None, scale_dtype, codes, scales, stream)
+
+
+def hq_rotate_quant_grouped(x: torch.Tensor, s: torch.Tensor, b: int, group: int,
+                            bits: int = 4, scale_dtype: torch.dtype = torch.float32,
+                            codes: torch.Tensor | None = None,
+                            scales: torch.Tensor | None = None, stream=None):
+    """Rotate + quantise with one scale per `group` consecutive rotated
+    elements.  Returns (codes, scales) with scales [rows, n/group]."""
+    return _rotate_quant(x, s, b, bits, int(group), scale_dtype, codes, scales, stream)
+
+
+def _rotate_quant(x, s, b, bits, group, scale_dtype, codes, scales, stream):
     _check_dev(x, "x")
     if x.dtype not in _TORCH_TO_HQ:
         raise ValueError(f"x dtype {x.dtype} unsupported")
@@ -145,13 +164,22 @@ def hq_rotate_quant(x: torch.Tensor, s: torch.Tensor, b: int, bits: int = 4,
     if codes is None:
         codes = torch.empty(cshape, dtype=cdtype, device=x.device)
     _check_dev(codes, "codes", cdtype, cshape)
+    sshape = (rows,) if group is None else (rows, n // group if group > 0 else 0)
     if scales is None:
-        scales = torch.empty((rows,), dtype=scale_dtype, device=x.device)
-    _check_dev(scales, "scales", scale_dtype, (rows,))
-    st = load().hq_rotate_quant(x.data_ptr(), _TORCH_TO_HQ[x.dtype], rows, n, int(b),
-                                s.data_ptr(), int(bits), codes.data_ptr(),
-                                scales.data_ptr(), _TORCH_TO_HQ[scale_dtype], _stream(stream))
-    _raise(st, "hq_rotate_quant")
+        scales = torch.empty(sshape, dtype=scale_dtype, device=x.device)
+    _check_dev(scales, "scales", scale_dtype, sshape)
+    if group is None:
+        st = load().hq_rotate_quant(x.data_ptr(), _TORCH_TO_HQ[x.dtype], rows, n, int(b),
+                                    s.data_ptr(), int(bits), codes.data_ptr(),
+                                    scales.data_ptr(), _TORCH_TO_HQ[scale_dtype],
+                                    _stream(stream))
+        _raise(st, "hq_rotate_quant")
+    else:
+        st = load().hq_rotate_quant_grouped(x.data_ptr(), _TORCH_TO_HQ[x.dtype], rows, n,
+                                            int(b), s.data_ptr(), int(bits), group,
+                                            codes.data_ptr(), scales.data_ptr(),
+                                            _TORCH_TO_HQ[scale_dtype], _stream(stream))
+        _raise(st, "hq_rotate_quant_grouped")
     return codes, scales
 
 
@@ -159,6 +187,19 @@ def hq_dequant_rotate_inv(codes: torch.Tensor, scales: torch.Tensor, s: torch.Te
                           b: int, bits: int = 4, out_dtype: torch.dtype = torch.float32,
                           y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Dequantise codes with their row scales and rotate back: y [rows, n]."""
+    return _dequant_inv(codes, scales, s, b, bits, None, out_dtype, y, stream)
+
+
+def hq_dequant_rotate_inv_grouped(codes: torch.Tensor, scales: torch.Tensor, s: torch.Tensor,
+                                  b: int, group: int, bits: int = 4,
+                                  out_dtype: torch.dtype = torch.float32,
+                                  y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Dequantise codes with their group scales [rows, n/group] and rotate
+    back: y [rows, n]."""
+    return _dequant_inv(codes, scales, s, b, bits, int(group), out_dtype, y, stream)
+
+
+def _dequant_inv(codes, scales, s, b, bits, group, out_dtype, y, stream):
     _check_dev(codes, "codes")
     rows, w = _rows_n(codes, "codes")
     n = w * 2 if bits == 4 else w
@@ -166,7 +207,8 @@ def hq_dequant_rotate_inv(codes: torch.Tensor, scales: torch.Tensor, s: torch.Te
         raise ValueError("bits must be 4 or 8")
     if codes.dtype not in ((torch.uint8,) if bits == 4 else (torch.int8, torch.uint8)):
         raise ValueError(f"codes dtype {codes.dtype} does not match bits={bits}")
-    _check_dev(scales, "scales", None, (rows,))
+    sshape = (rows,) if group is None else (rows, n // group if group > 0 else 0)
+    _check_dev(scales, "scales", None, sshape)
     if scales.dtype not in (torch.float32, torch.float16):
         raise ValueError("scales must be float32 or float16")
     _check_dev(s, "s", torch.int8, (n,))
@@ -175,11 +217,18 @@ def hq_dequant_rotate_inv(codes: torch.Tensor, scales: torch.Tensor, s: torch.Te
     if y is None:
         y = torch.empty((rows, n), dtype=out_dtype, device=codes.device)
     _check_dev(y, "y", out_dtype, (rows, n))
-    st = load().hq_dequant_rotate_inv(codes.data_ptr(), scales.data_ptr(),
-                                      _TORCH_TO_HQ[scales.dtype], rows, n, int(b),
-                                      s.data_ptr(), int(bits), y.data_ptr(),
-                                      _TORCH_TO_HQ[out_dtype], _stream(stream))
-    _raise(st, "hq_dequant_rotate_inv")
+    if group is None:
+        st = load().hq_dequant_rotate_inv(codes.data_ptr(), scales.data_ptr(),
+                                          _TORCH_TO_HQ[scales.dtype], rows, n, int(b),
+                                          s.data_ptr(), int(bits), y.data_ptr(),
+                                          _TORCH_TO_HQ[out_dtype], _stream(stream))
+        _raise(st, "hq_dequant_rotate_inv")
+    else:
+        st = load().hq_dequant_rotate_inv_grouped(codes.data_ptr(), scales.data_ptr(),
+                                                  _TORCH_TO_HQ[scales.dtype], rows, n, int(b),
+                                                  s.data_ptr(), int(bits), group, y.data_ptr(),
+                                                  _TORCH_TO_HQ[out_dtype], _stream(stream))
+        _raise(st, "hq_dequant_rotate_inv_grouped")
     return y
 
 

@@ -119,18 +119,29 @@ hq_status dispatch(const hq::Request &r)
     return HQ_OK;
 }
 
-}  // namespace
+// Group size check: n itself (one scale per row) or a power of two >= 2
+// that divides n.  Returns -2 when invalid, else log2(group) (-1 when
+// group == n is not a power of two).
+int group_log2(int32_t n, int32_t group)
+{
+    if (group == n)
+        return is_pow2(n) ? __builtin_ctz((unsigned)n) : -1;
+    if (group < 2 || !is_pow2(group) || n % group != 0)
+        return -2;
+    return __builtin_ctz((unsigned)group);
+}
 
-extern "C" {
-
-hq_status hq_rotate_quant(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
-                          int32_t b, const int8_t *s, int32_t bits, void *codes,
-                          void *scales, hq_dtype scale_dtype, void *stream)
+hq_status rotate_quant_impl(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
+                            int32_t b, const int8_t *s, int32_t bits, int32_t group,
+                            void *codes, void *scales, hq_dtype scale_dtype, void *stream)
 {
     g_hip_error[0] = '\0';
     hq_status st = check_shape(rows, n, b, s);
     if (st == HQ_EINVAL)
         return st;
+    const int logg = group_log2(n, group);
+    if (logg == -2)
+        return HQ_EINVAL;
     if (!valid_in_dtype(x_dtype) || !valid_scale_dtype(scale_dtype))
         return HQ_EINVAL;
     if (bits != 4 && bits != 8)
@@ -157,19 +168,23 @@ hq_status hq_rotate_quant(const void *x, hq_dtype x_dtype, int64_t rows, int32_t
     r.codes = codes;
     r.scales = scales;
     r.scale_dtype = scale_dtype;
+    r.group = group;
+    r.logg = logg;
     r.stream = (hipStream_t)stream;
     return dispatch(r);
 }
 
-hq_status hq_dequant_rotate_inv(const void *codes, const void *scales,
-                                hq_dtype scale_dtype, int64_t rows, int32_t n,
-                                int32_t b, const int8_t *s, int32_t bits, void *y,
-                                hq_dtype y_dtype, void *stream)
+hq_status dequant_inv_impl(const void *codes, const void *scales, hq_dtype scale_dtype,
+                           int64_t rows, int32_t n, int32_t b, const int8_t *s, int32_t bits,
+                           int32_t group, void *y, hq_dtype y_dtype, void *stream)
 {
     g_hip_error[0] = '\0';
     hq_status st = check_shape(rows, n, b, s);
     if (st == HQ_EINVAL)
         return st;
+    const int logg = group_log2(n, group);
+    if (logg == -2)
+        return HQ_EINVAL;
     if (!valid_scale_dtype(scale_dtype) || (y_dtype != HQ_F32 && y_dtype != HQ_BF16))
         return HQ_EINVAL;
     if (bits != 4 && bits != 8)
@@ -196,8 +211,49 @@ hq_status hq_dequant_rotate_inv(const void *codes, const void *scales,
     r.bits = bits;
     r.y = y;
     r.y_dtype = y_dtype;
+    r.group = group;
+    r.logg = logg;
     r.stream = (hipStream_t)stream;
     return dispatch(r);
+}
+
+}  // namespace
+
+extern "C" {
+
+hq_status hq_rotate_quant(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
+                          int32_t b, const int8_t *s, int32_t bits, void *codes,
+                          void *scales, hq_dtype scale_dtype, void *stream)
+{
+    return rotate_quant_impl(x, x_dtype, rows, n, b, s, bits, n, codes, scales, scale_dtype,
+                             stream);
+}
+
+hq_status hq_rotate_quant_grouped(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
+                                  int32_t b, const int8_t *s, int32_t bits, int32_t group,
+                                  void *codes, void *scales, hq_dtype scale_dtype, void *stream)
+{
+    return rotate_quant_impl(x, x_dtype, rows, n, b, s, bits, group, codes, scales,
+                             scale_dtype, stream);
+}
+
+hq_status hq_dequant_rotate_inv(const void *codes, const void *scales,
+                                hq_dtype scale_dtype, int64_t rows, int32_t n,
+                                int32_t b, const int8_t *s, int32_t bits, void *y,
+                                hq_dtype y_dtype, void *stream)
+{
+    return dequant_inv_impl(codes, scales, scale_dtype, rows, n, b, s, bits, n, y, y_dtype,
+                            stream);
+}
+
+hq_status hq_dequant_rotate_inv_grouped(const void *codes, const void *scales,
+                                        hq_dtype scale_dtype, int64_t rows, int32_t n,
+                                        int32_t b, const int8_t *s, int32_t bits,
+                                        int32_t group, void *y, hq_dtype y_dtype,
+                                        void *stream)
+{
+    return dequant_inv_impl(codes, scales, scale_dtype, rows, n, b, s, bits, group, y,
+                            y_dtype, stream);
 }
 
 hq_status hq_rotate(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
@@ -229,6 +285,8 @@ hq_status hq_rotate(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
     r.y_dtype = HQ_F32;
     r.bits = 4;
     r.scale_dtype = HQ_F32;
+    r.group = n;
+    r.logg = group_log2(n, n);
     r.stream = (hipStream_t)stream;
     return dispatch(r);
 }
@@ -254,6 +312,6 @@ int32_t hq_max_n(void)
     return max_n_for(*dev);
 }
 
-int32_t hq_version(void) { return 10000; }
+int32_t hq_version(void) { return 10100; }
 
 }  // extern "C"

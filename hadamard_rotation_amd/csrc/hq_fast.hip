@@ -135,6 +135,9 @@ void fill_args(FastArgs &fa, const Request &r, const Plan &p)
     fa.wpr = p.wpr;
     fa.bits = r.bits;
     fa.scale_f16 = r.scale_dtype == kF16;
+    const bool grouped = r.group != r.n;
+    fa.logg = grouped ? r.logg : 0;
+    fa.ngroups_row = grouped ? r.n / r.group : 1;
     const int lane_bits = p.logb > 3 ? (p.logb - 3 < p.log_lanes ? p.logb - 3 : p.log_lanes) : 0;
     const int n_dpp = lane_bits < 4 ? lane_bits : 4;
     dpp_tables(n_dpp, fa.pi, fa.neg);
@@ -158,23 +161,35 @@ int occupancy_blocks(const void *fn, int threads, size_t lds)
 }
 
 hipError_t launch_rq(const Request &r, const DeviceInfo &dev);
+hipError_t launch_rq_grouped(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rot(const Request &r, const DeviceInfo &dev);
 hipError_t launch_inv(const Request &r, const DeviceInfo &dev);
+hipError_t launch_inv_grouped(const Request &r, const DeviceInfo &dev);
 
 }  // namespace fast
 
 bool fast_available(const Request &r)
 {
     fast::Plan p;
-    return fast::make_plan(r.n, r.b, p);
+    if (!fast::make_plan(r.n, r.b, p))
+        return false;
+    if (r.group == r.n || (r.op != kRotateQuant && r.op != kDequantInv))
+        return true;
+    // group-wise scales: whole 8-element units per group, and (long rows)
+    // no group across two waves' segments
+    if (r.logg < 3)
+        return false;
+    return !p.is_long || (r.group >> 3) <= 64 * p.units;
 }
 
 hipError_t launch_fast(const Request &r, const DeviceInfo &dev)
 {
     switch (r.op) {
-    case kRotateQuant: return fast::launch_rq(r, dev);
+    case kRotateQuant:
+        return r.group == r.n ? fast::launch_rq(r, dev) : fast::launch_rq_grouped(r, dev);
     case kRotate: return fast::launch_rot(r, dev);
-    case kDequantInv: return fast::launch_inv(r, dev);
+    case kDequantInv:
+        return r.group == r.n ? fast::launch_inv(r, dev) : fast::launch_inv_grouped(r, dev);
     }
     return hipErrorInvalidValue;
 }

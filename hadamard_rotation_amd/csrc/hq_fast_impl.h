@@ -74,9 +74,22 @@ struct FastArgs {
     int wpr;              // waves per row (LONG kernels)
     int bits;             // 4 or 8
     int scale_f16;        // scales stored as fp16 (else fp32)
+    int logg;             // log2 group size (group-wise kernels only; >= 3)
+    int ngroups_row;      // n >> logg (group-wise kernels only)
+    int gstride;          // floats of group scratch per wave (grouped forward)
     float kq;             // 1 / (sqrt(b) * qmax)
     float rb;             // 1 / sqrt(b)
 };
+
+// Orders the LDS accesses of one wave around an exchange between its lanes
+// (LDS operations of a wave complete in order; this keeps the compiler
+// from moving them across).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
 
 // ------------------------------------------------------------ primitives
 
@@ -235,10 +248,10 @@ __device__ __forceinline__ uint32_t segment_max(uint32_t v, int log_lanes)
 }
 
 // Raw input of one unit: 16 bytes of bf16/f16, 32 bytes of fp32, or 4/8
-// bytes of codes (inverse path).
-template <int OP, int IN>
+// bytes of codes plus the bits of the unit's group scale (inverse path).
+template <int OP, int IN, bool GR>
 struct RawUnit {
-    uint32_t w[(OP != kDequantInv && IN == kF32) ? 8 : (OP == kDequantInv ? 2 : 4)];
+    uint32_t w[(OP != kDequantInv && IN == kF32) ? 8 : (OP == kDequantInv ? (GR ? 3 : 2) : 4)];
 };
 
 // ----------------------------------------------------------------- kernel
@@ -251,7 +264,8 @@ struct RawUnit {
 // RPL        independent rows per lane per iteration (short rows)
 // LONG       a row spans FastArgs::wpr waves (LOG_LANES == 6, RPL == 1);
 //            units past the row end are loaded clamped and ignored
-template <int OP, int IN, int UNITS, int LOG_LANES, int LOGB, int RPL, bool LONG>
+// GR         group-wise scales (FastArgs::logg) instead of one per row
+template <int OP, int IN, int UNITS, int LOG_LANES, int LOGB, int RPL, bool LONG, bool GR>
 __global__ __launch_bounds__(UNITS < 8 ? 1024 : (LONG ? 256 : 768))
 void fast_kernel(FastArgs a)
 {
@@ -346,7 +360,7 @@ void fast_kernel(FastArgs a)
 
     // ---- loads (addresses clamped to valid memory; results of rows or
     // units past the end are never stored)
-    auto load = [&](int64_t g, RawUnit<OP, IN> (&raw)[RPL][UNITS]) {
+    auto load = [&](int64_t g, RawUnit<OP, IN, GR> (&raw)[RPL][UNITS]) {
         const int64_t r0 = group_row0(g);
         const int64_t left = a.rows - 1 - r0;  // rows after r0 in the tensor
         const int lim = left < rows_per_group ? (int)left : rows_per_group;
@@ -371,6 +385,12 @@ void fast_kernel(FastArgs a)
                         u32x2 t = stream_load((const u32x2 *)(gp + eo));
                         raw[k][u].w[0] = t[0];
                         raw[k][u].w[1] = t[1];
+                    }
+                    if constexpr (GR) {  // the scale of the unit's group
+                        const int64_t gi = (r0 + lr) * a.ngroups_row + ((un * 8) >> a.logg);
+                        raw[k][u].w[2] = a.scale_f16
+                            ? (uint32_t)((const uint16_t *)a.scales_in)[gi]
+                            : ((const uint32_t *)a.scales_in)[gi];
                     }
                 } else if constexpr (IN == kF32) {
                     const float *gp = (const float *)a.x + e0;
@@ -411,7 +431,7 @@ void fast_kernel(FastArgs a)
     // The first row group is loaded unconditionally (a wave without work
     // loads group 0 and ignores it), which keeps the count of loads in
     // flight static, so the sign table below waits only for its own loads.
-    RawUnit<OP, IN> cur[RPL][UNITS];
+    RawUnit<OP, IN, GR> cur[RPL][UNITS];
     load(has_work ? first : 0, cur);
 
 #pragma unroll
@@ -446,7 +466,7 @@ void fast_kernel(FastArgs a)
     // that reads and rewrites the loaded registers fixes where that wait
     // happens: the loop below never waits for the loads at its top (where
     // the previous group's stores were just issued).
-    auto take_delivery = [&](RawUnit<OP, IN> (&raw)[RPL][UNITS]) {
+    auto take_delivery = [&](RawUnit<OP, IN, GR> (&raw)[RPL][UNITS]) {
 #pragma unroll
         for (int k = 0; k < RPL; ++k)
 #pragma unroll
@@ -456,6 +476,103 @@ void fast_kernel(FastArgs a)
                     asm volatile("" : "+v"(raw[k][u].w[t]));
     };
     take_delivery(cur);
+
+    // ---- group-wise scales (forward).  Groups of 2^logg >= 8 elements
+    // never cross a wave's row segment.  Every lane writes the maxima of its
+    // 8-element chunks to this wave's scratch at their natural positions;
+    // one lane per group reduces them, stores the scale and leaves
+    // qmax/max in the group's first slot, which the lanes then read back.
+    auto quant_groups = [&](int64_t g, float (&v)[RPL][UNITS][8]) {
+        float *gm = (float *)((uint8_t *)lds_sign + (size_t)a.n * 2) + wave * a.gstride;
+        const int64_t r0 = group_row0(g);
+        const int64_t left = a.rows - 1 - r0;  // wave-uniform
+        const int lim = left < rows_per_group ? (int)left : rows_per_group;
+        const int lg = a.logg - 3;             // log2 units per group
+        const int gu = 1 << lg;
+#pragma unroll
+        for (int k = 0; k < RPL; ++k)
+#pragma unroll
+            for (int u = 0; u < UNITS; ++u) {
+                float mu = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; j += 2)
+                    mu = fmaxf(fmaxf(mu, fabsf(v[k][u][j])), fabsf(v[k][u][j + 1]));
+                const int ou = out_unit(u);
+                if (!LONG || ou < units_row)
+                    gm[LONG ? ou - seg_base : lane_row(k) * units_row + ou] = mu;
+            }
+        wave_lds_sync();
+        const int used = LONG ? (units_row - seg_base < 64 * UNITS ? units_row - seg_base : 64 * UNITS)
+                              : rows_per_group * units_row;
+        const int ng = used >> lg;
+        const int qmax = a.bits == 4 ? 7 : 127;
+        for (int gi = lane; gi < ng; gi += 64) {
+            float m = 0.0f;
+            const float *p = gm + (gi << lg);
+            if (gu >= 4) {
+                for (int i = 0; i < gu; i += 4) {
+                    const float4 q = *(const float4 *)(p + i);
+                    m = fmaxf(fmaxf(m, q.x), fmaxf(q.y, fmaxf(q.z, q.w)));
+                }
+            } else {
+                for (int i = 0; i < gu; ++i)
+                    m = fmaxf(m, p[i]);
+            }
+            const RowQuant rq = row_quant(m, a.kq, qmax);
+            int64_t sidx;
+            bool ok;
+            if (LONG) {
+                sidx = r0 * a.ngroups_row + ((seg_base >> lg) + gi);
+                ok = true;
+            } else {
+                const int lr = (gi << lg) / units_row;
+                sidx = (r0 + lr) * a.ngroups_row + (gi - lr * a.ngroups_row);
+                ok = lr <= lim;
+            }
+            if (ok) {
+                if (a.scale_f16)
+                    ((uint16_t *)a.scales)[sidx] = f32_to_f16(rq.scale);
+                else
+                    ((float *)a.scales)[sidx] = rq.scale;
+            }
+            gm[gi << lg] = rq.inv;
+        }
+        wave_lds_sync();
+        const int64_t e0 = r0 * (int64_t)a.n;  // wave-uniform
+#pragma unroll
+        for (int k = 0; k < RPL; ++k) {
+            const int lr = lane_row(k);
+            const bool row_ok = lr <= lim;
+            const int ro = lr * a.n;
+#pragma unroll
+            for (int u = 0; u < UNITS; ++u) {
+                const int ou = out_unit(u);
+                if (LONG && ou >= units_row)
+                    continue;
+                const int idx = LONG ? ou - seg_base : lr * units_row + ou;
+                float inv = gm[idx & ~(gu - 1)];
+                inv = lane_neg ? -inv : inv;
+                if (!row_ok)
+                    continue;
+                if (a.bits == 4) {
+                    uint32_t f[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 8
+                        f[j] = __float_as_uint(__builtin_fmaf(v[k][u][j], inv, 12582920.0f));
+                    *(uint32_t *)((uint8_t *)a.codes + (e0 >> 1) + ((ro >> 1) + ou * 4)) =
+                        pack_int4(f);
+                } else {
+                    uint32_t f[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 128
+                        f[j] = __float_as_uint(__builtin_fmaf(v[k][u][j], inv, 12583040.0f));
+                    *(uint2 *)((int8_t *)a.codes + e0 + (ro + ou * 8)) =
+                        make_uint2(pack_int8(f[0], f[1], f[2], f[3]), pack_int8(f[4], f[5], f[6], f[7]));
+                }
+            }
+        }
+        wave_lds_sync();  // the scratch is rewritten by the next row group
+    };
 
     int parity = 0;
     int64_t g = first;
@@ -490,6 +607,14 @@ void fast_kernel(FastArgs a)
                             uint32_t word = cur[k][u].w[j >> 2];
                             v[k][u][j] = (float)((int32_t)(word << (24 - 8 * (j & 3))) >> 24);
                         }
+                    }
+                    if constexpr (GR) {
+                        // group-wise scales: dequantise before the transform
+                        const uint32_t sw = cur[k][u].w[2];
+                        const float sc = a.scale_f16 ? f16_to_f32((uint16_t)sw) : __uint_as_float(sw);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            v[k][u][j] *= sc;
                     }
                     if (logb > 0) {
                         bfly(v[k][u][0], v[k][u][1]);
@@ -645,6 +770,11 @@ void fast_kernel(FastArgs a)
         take_delivery(cur);
 
         // ------------------------------------------------------------ outputs
+        if constexpr (OP == kRotateQuant && GR) {
+            quant_groups(g, v);
+            g = g_next;
+            continue;
+        }
 #pragma unroll
         for (int k = 0; k < RPL; ++k) {
             const int64_t r0 = group_row0(g);
@@ -671,12 +801,14 @@ void fast_kernel(FastArgs a)
                     }
                 }
             } else if constexpr (OP == kDequantInv) {
-                float sc = 0.0f;
+                float sc = 1.0f;  // group-wise scales were applied to the codes
                 const int lc = lr < lim ? lr : lim;  // clamped into the tensor
-                if (a.scale_f16)
-                    sc = f16_to_f32(((const uint16_t *)a.scales_in + r0)[lc]);
-                else
-                    sc = ((const float *)a.scales_in + r0)[lc];
+                if constexpr (!GR) {
+                    if (a.scale_f16)
+                        sc = f16_to_f32(((const uint16_t *)a.scales_in + r0)[lc]);
+                    else
+                        sc = ((const float *)a.scales_in + r0)[lc];
+                }
                 float t = sc * a.rb;
                 t = lane_neg ? -t : t;
                 if (row_ok) {
@@ -804,27 +936,33 @@ void dpp_tables(int n_dpp, uint64_t &pi, uint32_t &neg);
 void fill_args(FastArgs &fa, const Request &r, const Plan &p);
 int occupancy_blocks(const void *fn, int threads, size_t lds);
 
-template <int OP, int IN, int UNITS, int LOG_LANES, int LOGB, int RPL, bool LONG>
+template <int OP, int IN, int UNITS, int LOG_LANES, int LOGB, int RPL, bool LONG, bool GR>
 hipError_t launch_one(FastArgs fa, const Plan &p, const Request &r, const DeviceInfo &dev)
 {
     // groups: rows of one workgroup iteration (LONG) or of one wave
     // iteration (short rows)
     const int rows_per_group = LONG ? 1 : (64 >> p.log_lanes) * RPL;
     fa.groups = (r.rows + rows_per_group - 1) / rows_per_group;
-    const size_t lds = OP == kDequantInv ? (size_t)r.n : (size_t)r.n * 2;
-    auto fn = fast_kernel<OP, IN, UNITS, LOG_LANES, LOGB, RPL, LONG>;
+    const size_t lds_sign = OP == kDequantInv ? (size_t)r.n : (size_t)r.n * 2;
+    // group-wise forward: per-wave scratch of one float per 8-element unit
+    fa.gstride = 0;
+    if (OP == kRotateQuant && GR)
+        fa.gstride = LONG ? 64 * UNITS : rows_per_group * (r.n >> 3);
+    const size_t per_wave = (size_t)fa.gstride * 4;
+    auto fn = fast_kernel<OP, IN, UNITS, LOG_LANES, LOGB, RPL, LONG, GR>;
     int threads, grid_per_cu;
     if (LONG) {
         threads = 64 * p.wpr;
-        grid_per_cu = occupancy_blocks((const void *)fn, threads, lds);
+        grid_per_cu = occupancy_blocks((const void *)fn, threads, lds_sign + per_wave * p.wpr);
     } else {
         // every wave the CU can hold, in as few workgroups as the
         // 1024-thread (768 for the widest rows) limit allows
         const int max_threads = UNITS < 8 ? 1024 : 768;
-        const int waves_cu = 4 * occupancy_blocks((const void *)fn, 256, lds);
+        const int waves_cu = 4 * occupancy_blocks((const void *)fn, 256, lds_sign + per_wave * 4);
         grid_per_cu = (waves_cu * 64 + max_threads - 1) / max_threads;
         threads = 64 * (waves_cu / grid_per_cu);
     }
+    const size_t lds = lds_sign + per_wave * (threads / 64);
     int64_t grid = (int64_t)dev.cu_count * grid_per_cu;
     if (grid > fa.groups)
         grid = fa.groups;
@@ -833,8 +971,10 @@ hipError_t launch_one(FastArgs fa, const Plan &p, const Request &r, const Device
 }
 
 // Specialised instantiations for one (OP, IN); anything else runs the
-// variant with a run-time stage plan.
-template <int OP, int IN>
+// variant with a run-time stage plan.  Group-wise scales (GR) have their own
+// instantiations for the long 128-block rows, 4096-wide rows and 128-wide
+// heads, and the run-time plan elsewhere.
+template <int OP, int IN, bool GR>
 hipError_t dispatch_op(const Request &r, const DeviceInfo &dev)
 {
     Plan p;
@@ -845,50 +985,58 @@ hipError_t dispatch_op(const Request &r, const DeviceInfo &dev)
     if (p.is_long) {
         if (p.logb == 7) {
             switch (p.units) {
-            case 1: return launch_one<OP, IN, 1, 6, 7, 1, true>(fa, p, r, dev);
-            case 2: return launch_one<OP, IN, 2, 6, 7, 1, true>(fa, p, r, dev);
-            case 4: return launch_one<OP, IN, 4, 6, 7, 1, true>(fa, p, r, dev);
+            case 1: return launch_one<OP, IN, 1, 6, 7, 1, true, GR>(fa, p, r, dev);
+            case 2: return launch_one<OP, IN, 2, 6, 7, 1, true, GR>(fa, p, r, dev);
+            case 4: return launch_one<OP, IN, 4, 6, 7, 1, true, GR>(fa, p, r, dev);
             default: break;
             }
         }
         switch (p.units) {
-        case 1: return launch_one<OP, IN, 1, 6, -1, 1, true>(fa, p, r, dev);
-        case 2: return launch_one<OP, IN, 2, 6, -1, 1, true>(fa, p, r, dev);
-        case 4: return launch_one<OP, IN, 4, 6, -1, 1, true>(fa, p, r, dev);
-        default: return launch_one<OP, IN, 8, 6, -1, 1, true>(fa, p, r, dev);
+        case 1: return launch_one<OP, IN, 1, 6, -1, 1, true, GR>(fa, p, r, dev);
+        case 2: return launch_one<OP, IN, 2, 6, -1, 1, true, GR>(fa, p, r, dev);
+        case 4: return launch_one<OP, IN, 4, 6, -1, 1, true, GR>(fa, p, r, dev);
+        default: return launch_one<OP, IN, 8, 6, -1, 1, true, GR>(fa, p, r, dev);
         }
     }
     const int n = r.n;
     if (p.logb == 7 || (1 << p.logb) == n) {
         const bool full = (1 << p.logb) == n;
-        switch (n) {
-        case 16: return launch_one<OP, IN, 1, 1, 4, 4, false>(fa, p, r, dev);
-        case 32: return launch_one<OP, IN, 1, 2, 5, 4, false>(fa, p, r, dev);
-        case 64: return launch_one<OP, IN, 1, 3, 6, 4, false>(fa, p, r, dev);
-        case 128: return launch_one<OP, IN, 1, 4, 7, 4, false>(fa, p, r, dev);
-        case 256:
-            return full ? launch_one<OP, IN, 2, 4, 8, 2, false>(fa, p, r, dev)
-                        : launch_one<OP, IN, 2, 4, 7, 2, false>(fa, p, r, dev);
-        case 512:
-            return full ? launch_one<OP, IN, 4, 4, 9, 1, false>(fa, p, r, dev)
-                        : launch_one<OP, IN, 4, 4, 7, 1, false>(fa, p, r, dev);
-        case 1024:
-            return full ? launch_one<OP, IN, 8, 4, 10, 1, false>(fa, p, r, dev)
-                        : launch_one<OP, IN, 8, 4, 7, 1, false>(fa, p, r, dev);
-        case 2048:
-            return full ? launch_one<OP, IN, 8, 5, 11, 1, false>(fa, p, r, dev)
-                        : launch_one<OP, IN, 8, 5, 7, 1, false>(fa, p, r, dev);
-        case 4096:
-            return full ? launch_one<OP, IN, 8, 6, 12, 1, false>(fa, p, r, dev)
-                        : launch_one<OP, IN, 8, 6, 7, 1, false>(fa, p, r, dev);
-        default: break;
+        if constexpr (GR) {
+            if (n == 128)
+                return launch_one<OP, IN, 1, 4, 7, 4, false, GR>(fa, p, r, dev);
+            if (n == 4096)
+                return full ? launch_one<OP, IN, 8, 6, 12, 1, false, GR>(fa, p, r, dev)
+                            : launch_one<OP, IN, 8, 6, 7, 1, false, GR>(fa, p, r, dev);
+        } else {
+            switch (n) {
+            case 16: return launch_one<OP, IN, 1, 1, 4, 4, false, GR>(fa, p, r, dev);
+            case 32: return launch_one<OP, IN, 1, 2, 5, 4, false, GR>(fa, p, r, dev);
+            case 64: return launch_one<OP, IN, 1, 3, 6, 4, false, GR>(fa, p, r, dev);
+            case 128: return launch_one<OP, IN, 1, 4, 7, 4, false, GR>(fa, p, r, dev);
+            case 256:
+                return full ? launch_one<OP, IN, 2, 4, 8, 2, false, GR>(fa, p, r, dev)
+                            : launch_one<OP, IN, 2, 4, 7, 2, false, GR>(fa, p, r, dev);
+            case 512:
+                return full ? launch_one<OP, IN, 4, 4, 9, 1, false, GR>(fa, p, r, dev)
+                            : launch_one<OP, IN, 4, 4, 7, 1, false, GR>(fa, p, r, dev);
+            case 1024:
+                return full ? launch_one<OP, IN, 8, 4, 10, 1, false, GR>(fa, p, r, dev)
+                            : launch_one<OP, IN, 8, 4, 7, 1, false, GR>(fa, p, r, dev);
+            case 2048:
+                return full ? launch_one<OP, IN, 8, 5, 11, 1, false, GR>(fa, p, r, dev)
+                            : launch_one<OP, IN, 8, 5, 7, 1, false, GR>(fa, p, r, dev);
+            case 4096:
+                return full ? launch_one<OP, IN, 8, 6, 12, 1, false, GR>(fa, p, r, dev)
+                            : launch_one<OP, IN, 8, 6, 7, 1, false, GR>(fa, p, r, dev);
+            default: break;
+            }
         }
     }
     switch (p.units) {
-    case 1: return launch_one<OP, IN, 1, -1, -1, 1, false>(fa, p, r, dev);
-    case 2: return launch_one<OP, IN, 2, -1, -1, 1, false>(fa, p, r, dev);
-    case 4: return launch_one<OP, IN, 4, -1, -1, 1, false>(fa, p, r, dev);
-    default: return launch_one<OP, IN, 8, -1, -1, 1, false>(fa, p, r, dev);
+    case 1: return launch_one<OP, IN, 1, -1, -1, 1, false, GR>(fa, p, r, dev);
+    case 2: return launch_one<OP, IN, 2, -1, -1, 1, false, GR>(fa, p, r, dev);
+    case 4: return launch_one<OP, IN, 4, -1, -1, 1, false, GR>(fa, p, r, dev);
+    default: return launch_one<OP, IN, 8, -1, -1, 1, false, GR>(fa, p, r, dev);
     }
 }
 

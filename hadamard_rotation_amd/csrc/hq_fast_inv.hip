@@ -7,8 +7,8 @@ namespace fast {
 
 hipError_t launch_inv(const Request &r, const DeviceInfo &dev)
 {
-    if (r.y_dtype == kF32) return dispatch_op<kDequantInv, kF32>(r, dev);
-    return dispatch_op<kDequantInv, kBF16>(r, dev);
+    if (r.y_dtype == kF32) return dispatch_op<kDequantInv, kF32, false>(r, dev);
+    return dispatch_op<kDequantInv, kBF16, false>(r, dev);
 }
 
 }  // namespace fast

@@ -7,9 +7,9 @@ namespace fast {
 
 hipError_t launch_rot(const Request &r, const DeviceInfo &dev)
 {
-    if (r.x_dtype == kF32) return dispatch_op<kRotate, kF32>(r, dev);
-    if (r.x_dtype == kBF16) return dispatch_op<kRotate, kBF16>(r, dev);
-    return dispatch_op<kRotate, kF16>(r, dev);
+    if (r.x_dtype == kF32) return dispatch_op<kRotate, kF32, false>(r, dev);
+    if (r.x_dtype == kBF16) return dispatch_op<kRotate, kBF16, false>(r, dev);
+    return dispatch_op<kRotate, kF16, false>(r, dev);
 }
 
 }  // namespace fast

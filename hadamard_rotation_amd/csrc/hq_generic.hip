@@ -32,6 +32,7 @@ struct GenericArgs {
     int64_t rows;
     int n;
     int log_b;
+    int group;  // elements per scale (n: one scale per row)
     float kq;   // 1 / (sqrt(b) * qmax)
     float rb;   // 1 / sqrt(b)
 };
@@ -91,11 +92,17 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(GenericArgs a)
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         const int64_t base = row * (int64_t)n;
         if constexpr (OP == kDequantInv) {
-            float sc;
-            if constexpr (SC == kF32)
-                sc = ((const float *)a.scales_in)[row];
-            else
-                sc = f16_to_f32(((const uint16_t *)a.scales_in)[row]);
+            // one scale per row: applied after the (exact, integer) transform;
+            // group-wise scales: applied to every code before it
+            const bool grouped = a.group != n;
+            const int ngroups = n / a.group;
+            auto scale_at = [&](int64_t idx) -> float {
+                if constexpr (SC == kF32)
+                    return ((const float *)a.scales_in)[idx];
+                else
+                    return f16_to_f32(((const uint16_t *)a.scales_in)[idx]);
+            };
+            const float sc = grouped ? 1.0f : scale_at(row);
             for (int i = threadIdx.x; i < n; i += kThreads) {
                 int q;
                 if constexpr (BITS == 8) {
@@ -105,7 +112,8 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(GenericArgs a)
                     int nib = (i & 1) ? (byte >> 4) : (byte & 15);
                     q = nib >= 8 ? nib - 16 : nib;
                 }
-                L[i] = (float)q;  // exact; the FWHT of integer codes stays exact
+                L[i] = grouped ? (float)q * scale_at(row * ngroups + i / a.group)
+                               : (float)q;  // exact; the FWHT of integer codes stays exact
             }
             fwht_lds(L, n, a.log_b);
             const float t = sc * a.rb;
@@ -128,6 +136,40 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(GenericArgs a)
             if constexpr (OP == kRotate) {
                 for (int i = threadIdx.x; i < n; i += kThreads)
                     ((float *)a.y)[base + i] = L[i] * a.rb;
+                __syncthreads();
+            } else if (a.group != n) {
+                // group-wise scales: each wave takes whole groups; lanes
+                // stride over the group's elements
+                const int g = a.group;
+                const int ngroups = n / g;
+                const int lane = threadIdx.x & 63;
+                for (int k = threadIdx.x >> 6; k < ngroups; k += kThreads / 64) {
+                    const int i0 = k * g;
+                    float m = 0.0f;
+                    for (int i = lane; i < g; i += 64)
+                        m = fmaxf(m, fabsf(L[i0 + i]));
+                    for (int off = 32; off > 0; off >>= 1)
+                        m = fmaxf(m, __shfl_xor(m, off, 64));
+                    RowQuant rq = row_quant(m, a.kq, qmax);
+                    if (lane == 0) {
+                        if constexpr (SC == kF32)
+                            ((float *)a.scales)[row * ngroups + k] = rq.scale;
+                        else
+                            ((uint16_t *)a.scales)[row * ngroups + k] = f32_to_f16(rq.scale);
+                    }
+                    if constexpr (BITS == 8) {
+                        for (int i = lane; i < g; i += 64)
+                            ((int8_t *)a.codes)[base + i0 + i] =
+                                (int8_t)quant_code(L[i0 + i], rq.inv, qmax);
+                    } else {
+                        for (int j = lane; j < (g >> 1); j += 64) {
+                            int q0 = quant_code(L[i0 + 2 * j], rq.inv, qmax);
+                            int q1 = quant_code(L[i0 + 2 * j + 1], rq.inv, qmax);
+                            ((uint8_t *)a.codes)[((base + i0) >> 1) + j] =
+                                (uint8_t)((q0 & 15) | ((q1 & 15) << 4));
+                        }
+                    }
+                }
                 __syncthreads();
             } else {
                 float m = 0.0f;
@@ -203,6 +245,7 @@ hipError_t launch_generic(const Request &r, const DeviceInfo &dev)
     while ((1 << lb) < r.b)
         ++lb;
     ga.log_b = lb;
+    ga.group = r.group;
     int qmax = r.bits == 8 ? 127 : 7;
     ga.kq = (float)(1.0 / (__builtin_sqrt((double)r.b) * qmax));
     ga.rb = (float)(1.0 / __builtin_sqrt((double)r.b));

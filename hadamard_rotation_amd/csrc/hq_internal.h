@@ -33,6 +33,9 @@ struct Request {
     void *codes;            // kRotateQuant outputs
     void *scales;
     int scale_dtype;        // kRotateQuant output / kDequantInv input
+    int group;              // elements per scale: n (one scale per row) or a
+                            // power of two dividing n (scales [rows, n/group])
+    int logg;               // log2(group) when group is a power of two, else -1
     void *y;                // kRotate / kDequantInv output
     int y_dtype;
     hipStream_t stream;

@@ -40,6 +40,9 @@ bool plan_ok(const Request &r)
         return false;
     if (r.n < 32 || r.n > 4096 || (r.n & (r.n - 1)) != 0)
         return false;
+    // group-wise scales (forward quantisation): groups of 32 .. n/2
+    if (r.group != r.n && (r.op != kRotateQuant || r.logg < 5))
+        return false;
     return r.b == r.n || (r.b == 128 && r.n >= 256);
 }
 
@@ -52,6 +55,8 @@ void fill_args(MfmaArgs &ma, const Request &r, int tiles_per_group)
     ma.y = r.y;
     ma.rows = r.rows;
     ma.total = r.rows * (int64_t)r.n;
+    ma.ngroups = r.rows * (int64_t)(r.n / r.group);
+    ma.logg = r.logg;
     const int64_t per_group = (int64_t)tiles_per_group * 512;
     ma.groups = (ma.total + per_group - 1) / per_group;
     const int logb = ilog2(r.b);
@@ -81,6 +86,7 @@ int occupancy_waves(const void *fn, size_t lds)
 }
 
 hipError_t launch_rq(const Request &r, const DeviceInfo &dev);
+hipError_t launch_rq_grouped(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rot(const Request &r, const DeviceInfo &dev);
 
 }  // namespace mfma
@@ -92,7 +98,9 @@ bool mfma_available(const Request &r)
 
 hipError_t launch_mfma(const Request &r, const DeviceInfo &dev)
 {
-    return r.op == kRotate ? mfma::launch_rot(r, dev) : mfma::launch_rq(r, dev);
+    if (r.op == kRotate)
+        return mfma::launch_rot(r, dev);
+    return r.group == r.n ? mfma::launch_rq(r, dev) : mfma::launch_rq_grouped(r, dev);
 }
 
 }  // namespace hq

@@ -63,6 +63,8 @@ struct MfmaArgs {
     int64_t rows;
     int64_t total;    // rows * n elements
     int64_t groups;   // groups of T tiles
+    int64_t ngroups;  // scale groups: rows * n / group (rows when per row)
+    int logg;         // log2 of the scale group (the kernel's run-time LOGG)
     uint64_t pi;      // output chunk of lane l & 15 after the DPP stages
     uint32_t neg;     // bit l set: lane l holds the negated value
     int n;
@@ -101,12 +103,56 @@ __device__ __forceinline__ uint32_t row_lane_max(uint32_t v)
     return r32[0] > r32[1] ? r32[0] : r32[1];
 }
 
+// Maximum over the lanes of one scale group of 2^logg elements, 32 <= 2^logg
+// <= 256, in the transposed layout below (each 16-lane row one tile).  The
+// group is the set of lanes whose output chunk pl agrees above bit logg-6.
+// With D >= 3 DPP stages the chunk is a linear permutation of the lane
+// index, and the lanes of a group of 64 or 128 are {l, l^6} or
+// {l, l^3, l^5, l^6}; otherwise they are the low lane bits.
+template <int D>
+__device__ __forceinline__ uint32_t group_lane_max(uint32_t v, int logg)
+{
+    auto xor6 = [](uint32_t x) {  // l^7^1
+        const uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xf, 0xf, true);
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t, 0xB1, 0xf, 0xf, true);
+    };
+    auto xor5 = [](uint32_t x) {  // l^7^2
+        const uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xf, 0xf, true);
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t, 0x4E, 0xf, 0xf, true);
+    };
+    if (logg == 8) {
+        v = fast::dpp_max<0xB1>(v);
+        v = fast::dpp_max<0x4E>(v);
+        v = fast::dpp_max<0x141>(v);
+    } else if (logg == 7) {
+        if constexpr (D >= 3) {
+            v = fast::dpp_max<0x1B>(v);  // quad_perm [3,2,1,0]: l^3
+            const uint32_t o = xor5(v);
+            v = v > o ? v : o;
+        } else {
+            v = fast::dpp_max<0xB1>(v);
+            v = fast::dpp_max<0x4E>(v);
+        }
+    } else if (logg == 6) {
+        if constexpr (D >= 3) {
+            const uint32_t o = xor6(v);
+            v = v > o ? v : o;
+        } else {
+            v = fast::dpp_max<0xB1>(v);
+        }
+    }
+    return v;
+}
+
 // OP    kRotateQuant or kRotate
 // IN    kBF16 or kF16
 // T     tiles per wave and iteration
 // LOGB  log2 b, 5..12
 // LOGN  log2 n, LOGB..12
-template <int OP, int IN, int T, int LOGB, int LOGN>
+// LOGG  log2 of the scale group: LOGN (one scale per row), 9..LOGN-1 (groups
+//       of whole tiles), or 0: a run-time group of 32..256 elements
+//       (MfmaArgs::logg) reduced in the transposed layout
+template <int OP, int IN, int T, int LOGB, int LOGN, int LOGG>
 __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
 {
     extern __shared__ __align__(16) u32x4 lds_mask[];  // n > 512: [tile of row][lane]
@@ -315,37 +361,135 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
                     dst[1] = make_float4(v[t][4] * mul, v[t][5] * mul, v[t][6] * mul, v[t][7] * mul);
                 }
             }
-        } else {
+        } else if constexpr (LOGG == 0) {
+            // ---- scale groups of 32..256 elements: each lies in one tile.
+            // Transposed reduction: permlane16_swap of the chunk maxima of
+            // tiles (2p, 2p+1) reduces lane bit 4 of both at once and leaves
+            // rows [2p, 2p+1, 2p, 2p+1]; permlane32_swap of two such
+            // registers reduces lane bit 5 and leaves one tile per 16-lane
+            // row.  The in-row DPP steps, the reciprocal and the scale
+            // stores then run once per four tiles, and the same swaps in
+            // reverse hand every lane its group's multiplier.
             const int qmax = a.bits == 4 ? 7 : 127;
+            const int logg = a.logg;
+            uint32_t mt[T];
 #pragma unroll
-            for (int rr = 0; rr < T / TPR; ++rr) {
-                // tiles t0 .. t0+TPR-1 hold RPT rows (TPR == 1) or one row
-                const int t0 = rr * TPR;
+            for (int t = 0; t < T; ++t) {
                 float m = 0.0f;
 #pragma unroll
-                for (int t = t0; t < t0 + TPR; ++t)
+                for (int j = 0; j < 8; j += 2)
+                    m = fmaxf(fmaxf(m, fabsf(v[t][j])), fabsf(v[t][j + 1]));
+                mt[t] = __float_as_uint(m);
+            }
+            constexpr int NX = T / 2;
+            constexpr int NZ = T >= 4 ? T / 4 : 1;
+            uint32_t x[NX], z[NZ];
+#pragma unroll
+            for (int p = 0; p < NX; ++p) {
+                const auto r = __builtin_amdgcn_permlane16_swap(mt[2 * p], mt[2 * p + 1], false, false);
+                x[p] = r[0] > r[1] ? r[0] : r[1];
+            }
+#pragma unroll
+            for (int q = 0; q < NZ; ++q) {
+                const auto r = __builtin_amdgcn_permlane32_swap(x[T >= 4 ? 2 * q : 0],
+                                                                x[T >= 4 ? 2 * q + 1 : 0], false, false);
+                z[q] = r[0] > r[1] ? r[0] : r[1];
+            }
+            // z[q], row rho: tile 4q + rho (T >= 4) or rho & 1 (T == 2)
+            const int rho = lane >> 4;
+            const bool rep_lane = (pl & ((1 << (logg - 5)) - 1)) == 0 && (T >= 4 || rho < 2);
+            float iz[NZ];
+#pragma unroll
+            for (int q = 0; q < NZ; ++q) {
+                const uint32_t mb = group_lane_max<D>(z[q], logg);
+                const RowQuant rq = row_quant(__uint_as_float(mb), a.kq, qmax);
+                const int t = T >= 4 ? 4 * q + rho : (rho & 1);
+                const int64_t gi = (e0 + t * 512 + 32 * pl) >> logg;
+                if (rep_lane && gi < a.ngroups) {
+                    if (a.scale_f16)
+                        ((uint16_t *)a.scales)[gi] = f32_to_f16(rq.scale);
+                    else
+                        ((float *)a.scales)[gi] = rq.scale;
+                }
+                iz[q] = lane_neg ? -rq.inv : rq.inv;
+            }
+            // un-transpose: inv[t] for every tile at every lane of it
+            float inv[T];
+            if constexpr (T >= 4) {
+#pragma unroll
+                for (int q = 0; q < NZ; ++q) {
+                    const uint32_t zi = __float_as_uint(iz[q]);
+                    const auto w = __builtin_amdgcn_permlane32_swap(zi, zi, false, false);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const auto u = __builtin_amdgcn_permlane16_swap(w[h], w[h], false, false);
+                        inv[4 * q + 2 * h] = __uint_as_float(u[0]);
+                        inv[4 * q + 2 * h + 1] = __uint_as_float(u[1]);
+                    }
+                }
+            } else {
+                const uint32_t zi = __float_as_uint(iz[0]);
+                const auto u = __builtin_amdgcn_permlane16_swap(zi, zi, false, false);
+                inv[0] = __uint_as_float(u[0]);
+                inv[1] = __uint_as_float(u[1]);
+            }
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const int eo = t * 512 + out_off;
+                if (e0 + eo >= a.total)
+                    continue;
+                if (a.bits == 4) {
+                    uint32_t f[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 8
+                        f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv[t], 12582920.0f));
+                    *(uint32_t *)((uint8_t *)a.codes + (e0 >> 1) + (eo >> 1)) = fast::pack_int4(f);
+                } else {
+                    uint32_t f[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 128
+                        f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv[t], 12583040.0f));
+                    *(uint2 *)((int8_t *)a.codes + e0 + eo) =
+                        make_uint2(fast::pack_int8(f[0], f[1], f[2], f[3]),
+                                   fast::pack_int8(f[4], f[5], f[6], f[7]));
+                }
+            }
+        } else {
+            // ---- one scale per row (LOGG == LOGN) or per group of whole
+            // tiles (9 <= LOGG < LOGN): TPG tiles of a group are reduced in
+            // registers, then over the group's lanes
+            constexpr int TPG = LOGG > 9 ? 1 << (LOGG - 9) : 1;  // tiles per group
+            static_assert(T % TPG == 0, "a tile group holds whole scale groups");
+            const int qmax = a.bits == 4 ? 7 : 127;
+#pragma unroll
+            for (int rr = 0; rr < T / TPG; ++rr) {
+                // tiles t0 .. t0+TPG-1 hold 512/n rows (TPG == 1) or one group
+                const int t0 = rr * TPG;
+                float m = 0.0f;
+#pragma unroll
+                for (int t = t0; t < t0 + TPG; ++t)
 #pragma unroll
                     for (int j = 0; j < 8; j += 2)
                         m = fmaxf(fmaxf(m, fabsf(v[t][j])), fabsf(v[t][j + 1]));
-                constexpr int NDPP = LOGN - 5 < 4 ? LOGN - 5 : 4;
+                constexpr int NDPP = LOGG - 5 < 4 ? LOGG - 5 : 4;
                 const uint32_t mb = row_lane_max<NDPP>(__float_as_uint(m));
                 const RowQuant rq = row_quant(__uint_as_float(mb), a.kq, qmax);
-                // the lane's row: first element of its outputs / n
-                const int64_t row = (e0 + t0 * 512 + out_off) >> LOGN;
-                const bool row_ok = row < a.rows;
-                // one lane per row writes the scale: lane bits 4, 5 and the
-                // row-internal low lane bits all zero
-                constexpr int row_lanes_mask = (1 << NDPP) - 1;
-                if (row_ok && lane < 16 && (l16 & row_lanes_mask) == 0) {
+                // the lane's group: first element of its outputs >> LOGG
+                const int64_t grp = (e0 + t0 * 512 + out_off) >> LOGG;
+                const bool grp_ok = grp < a.ngroups;
+                // one lane per group writes the scale: lane bits 4, 5 and the
+                // group-internal low lane bits all zero
+                constexpr int grp_lanes_mask = (1 << NDPP) - 1;
+                if (grp_ok && lane < 16 && (l16 & grp_lanes_mask) == 0) {
                     if (a.scale_f16)
-                        ((uint16_t *)a.scales)[row] = f32_to_f16(rq.scale);
+                        ((uint16_t *)a.scales)[grp] = f32_to_f16(rq.scale);
                     else
-                        ((float *)a.scales)[row] = rq.scale;
+                        ((float *)a.scales)[grp] = rq.scale;
                 }
                 const float inv = lane_neg ? -rq.inv : rq.inv;
-                if (row_ok) {
+                if (grp_ok) {
 #pragma unroll
-                    for (int t = t0; t < t0 + TPR; ++t) {
+                    for (int t = t0; t < t0 + TPG; ++t) {
                         const int eo = t * 512 + out_off;
                         if (a.bits == 4) {
                             uint32_t f[8];
@@ -382,14 +526,14 @@ bool plan_ok(const Request &r);
 void fill_args(MfmaArgs &ma, const Request &r, int tiles_per_group);
 int occupancy_waves(const void *fn, size_t lds);
 
-template <int OP, int IN, int T, int LOGB, int LOGN>
+template <int OP, int IN, int T, int LOGB, int LOGN, int LOGG>
 hipError_t launch_one(const Request &r, const DeviceInfo &dev)
 {
     MfmaArgs ma;
     fill_args(ma, r, T);
     constexpr int TPR = LOGN > 9 ? 1 << (LOGN - 9) : 1;
     const size_t lds = TPR > 1 ? (size_t)TPR * 64 * 16 : 0;
-    auto fn = mfma_kernel<OP, IN, T, LOGB, LOGN>;
+    auto fn = mfma_kernel<OP, IN, T, LOGB, LOGN, LOGG>;
     // One workgroup per CU with every wave the CU can hold, at most 16
     // (measured on the 128-wide K/V rows: 16 waves per CU beat 20 by 10 %).
     const int max_threads = T < 8 ? 1024 : 768;
@@ -404,40 +548,68 @@ hipError_t launch_one(const Request &r, const DeviceInfo &dev)
     return hipGetLastError();
 }
 
+// The scale grouping of a (T, LOGB, LOGN) plan: one scale per row, or (GROUPED,
+// forward only) a run-time group of 32..256 elements, or whole-tile groups of
+// 512 .. n/2 elements.
+template <int OP, int IN, bool GROUPED, int T, int LOGB, int LOGN>
+hipError_t launch_g(const Request &r, const DeviceInfo &dev)
+{
+    if constexpr (GROUPED && OP == kRotateQuant) {
+        if (r.logg < 9)
+            return launch_one<OP, IN, T, LOGB, LOGN, 0>(r, dev);
+        if constexpr (LOGN > 9)
+            if (r.logg == 9) return launch_one<OP, IN, T, LOGB, LOGN, 9>(r, dev);
+        if constexpr (LOGN > 10)
+            if (r.logg == 10) return launch_one<OP, IN, T, LOGB, LOGN, 10>(r, dev);
+        if constexpr (LOGN > 11)
+            if (r.logg == 11) return launch_one<OP, IN, T, LOGB, LOGN, 11>(r, dev);
+        return hipErrorInvalidValue;
+    } else {
+        return launch_one<OP, IN, T, LOGB, LOGN, LOGN>(r, dev);
+    }
+}
+
 // Full rotations of n = 32..4096 and 128-blocks of n = 256..4096.
 // Rows of up to 512 elements take groups of 4 tiles, or of 2 tiles when
 // that would leave fewer than 4 groups per wave (the last round of groups
 // then idles less of the machine; measured on 131072 x 128).
-template <int OP, int IN, int T>
+template <int OP, int IN, bool GROUPED, int T>
 hipError_t dispatch_short(const Request &r, const DeviceInfo &dev)
 {
     const bool full = r.b == r.n;
     switch (r.n) {
-    case 32: return launch_one<OP, IN, T, 5, 5>(r, dev);
-    case 64: return launch_one<OP, IN, T, 6, 6>(r, dev);
-    case 128: return launch_one<OP, IN, T, 7, 7>(r, dev);
-    case 256: return full ? launch_one<OP, IN, T, 8, 8>(r, dev) : launch_one<OP, IN, T, 7, 8>(r, dev);
-    default: return full ? launch_one<OP, IN, T, 9, 9>(r, dev) : launch_one<OP, IN, T, 7, 9>(r, dev);
+    case 32: return launch_g<OP, IN, GROUPED, T, 5, 5>(r, dev);
+    case 64: return launch_g<OP, IN, GROUPED, T, 6, 6>(r, dev);
+    case 128: return launch_g<OP, IN, GROUPED, T, 7, 7>(r, dev);
+    case 256:
+        return full ? launch_g<OP, IN, GROUPED, T, 8, 8>(r, dev)
+                    : launch_g<OP, IN, GROUPED, T, 7, 8>(r, dev);
+    default:
+        return full ? launch_g<OP, IN, GROUPED, T, 9, 9>(r, dev)
+                    : launch_g<OP, IN, GROUPED, T, 7, 9>(r, dev);
     }
 }
 
-template <int OP, int IN>
+template <int OP, int IN, bool GROUPED>
 hipError_t dispatch_op(const Request &r, const DeviceInfo &dev)
 {
     const bool full = r.b == r.n;
     if (r.n <= 512) {
         const int64_t groups4 = (r.rows * (int64_t)r.n + 4 * 512 - 1) / (4 * 512);
         if (groups4 < (int64_t)dev.cu_count * 16 * 4)
-            return dispatch_short<OP, IN, 2>(r, dev);
-        return dispatch_short<OP, IN, 4>(r, dev);
+            return dispatch_short<OP, IN, GROUPED, 2>(r, dev);
+        return dispatch_short<OP, IN, GROUPED, 4>(r, dev);
     }
     switch (r.n) {
     case 1024:
-        return full ? launch_one<OP, IN, 8, 10, 10>(r, dev) : launch_one<OP, IN, 8, 7, 10>(r, dev);
+        return full ? launch_g<OP, IN, GROUPED, 8, 10, 10>(r, dev)
+                    : launch_g<OP, IN, GROUPED, 8, 7, 10>(r, dev);
     case 2048:
-        return full ? launch_one<OP, IN, 8, 11, 11>(r, dev) : launch_one<OP, IN, 8, 7, 11>(r, dev);
+        return full ? launch_g<OP, IN, GROUPED, 8, 11, 11>(r, dev)
+                    : launch_g<OP, IN, GROUPED, 8, 7, 11>(r, dev);
     default:
-        return full ? launch_one<OP, IN, 8, 12, 12>(r, dev) : launch_one<OP, IN, 8, 7, 12>(r, dev);
+        return full ? launch_g<OP, IN, GROUPED, 8, 12, 12>(r, dev)
+                    : launch_g<OP, IN, GROUPED, 8, 7, 12>(r, dev);
     }
 }
 

@@ -42,13 +42,14 @@ class Workload:
     tensors: tuple       # names of the tensors (e.g. ("q", "k"))
     unit: int            # rows per "token unit" (heads per token etc.)
 
-    def bytes_per_call(self, rows: int | None = None) -> int:
+    def bytes_per_call(self, rows: int | None = None, group: int | None = None) -> int:
         """Algorithmic HBM bytes of one rotate+quantise call: input + codes +
-        scales (the sign vector, n bytes, is negligible and not counted)."""
+        scales, one per row (group None) or per `group` elements (the sign
+        vector, n bytes, is negligible and not counted)."""
         r = self.rows if rows is None else rows
         in_b = 4 if self.x_dtype == F32 else 2
         code_b = self.n // 2 if self.bits == 4 else self.n
-        sc_b = 4 if self.scale_dtype == F32 else 2
+        sc_b = (4 if self.scale_dtype == F32 else 2) * (1 if group is None else self.n // group)
         return r * (self.n * in_b + code_b + sc_b)
 
 

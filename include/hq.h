@@ -105,6 +105,40 @@ hq_status hq_dequant_rotate_inv(const void *codes, const void *scales,
                                 hq_dtype y_dtype, void *stream);
 
 /*
+ * hq_rotate_quant_grouped -- hq_rotate_quant with one scale per run of
+ * `group` consecutive elements of the rotated row instead of one per row
+ * ([RQ] 6.2: group size 128 for 4-bit, 64 or 128 for 8-bit; [QT] 4.2: the
+ * scales of a tensor are stored together, apart from the codes).  For each
+ * group k of a row (elements k*group .. k*group+group-1 of x'):
+ *
+ *       scale_k = max_{i in k} |x'_i| / qmax
+ *       q_i     = clamp(round_half_even(x'_i / scale_k), -qmax, qmax)
+ *
+ *   group    n (identical to hq_rotate_quant), or a power of two with
+ *            2 <= group < n that divides n; anything else is HQ_EINVAL.
+ *            The group size is independent of the block size b.
+ *   scales   [rows, n/group] (row-major), element type scale_dtype.
+ *   Everything else, including the zero and below-2^-120 rules (applied per
+ *   group), is as for hq_rotate_quant.
+ */
+hq_status hq_rotate_quant_grouped(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
+                                  int32_t b, const int8_t *s, int32_t bits, int32_t group,
+                                  void *codes, void *scales, hq_dtype scale_dtype,
+                                  void *stream);
+
+/*
+ * hq_dequant_rotate_inv_grouped -- inverse of hq_rotate_quant_grouped: every
+ * element is dequantised with the scale of its own group (v_i = q_i *
+ * scale_k, scales [rows, n/group]) before the inverse rotation.  Arguments
+ * and errors as for hq_dequant_rotate_inv plus `group` as above.
+ */
+hq_status hq_dequant_rotate_inv_grouped(const void *codes, const void *scales,
+                                        hq_dtype scale_dtype, int64_t rows, int32_t n,
+                                        int32_t b, const int8_t *s, int32_t bits,
+                                        int32_t group, void *y, hq_dtype y_dtype,
+                                        void *stream);
+
+/*
  * hq_rotate -- rotation only: y = x' as fp32 [rows, n] (no quantisation).
  * Used to check the rotated values themselves and Q.K^T preservation
  * ([HQA] 1: rotating Q and K with the same matrix keeps Q.K^T).

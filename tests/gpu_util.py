@@ -54,3 +54,23 @@ def gpu_dequant_inv(codes: np.ndarray, scales: np.ndarray, s, b, bits, out_bf16=
     if out_bf16:
         return y.view(torch.int16).cpu().numpy().view(np.uint16)
     return y.cpu().numpy()
+
+
+def gpu_rotate_quant_grouped(raw, x_dtype, s, b, group, bits, scale_dtype):
+    x = to_dev(raw, x_dtype)
+    sd = torch.float32 if scale_dtype == F32 else torch.float16
+    codes, scales = hq.hq_rotate_quant_grouped(x, s_dev(s), b, group, bits, sd)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy().view(np.uint8), scales.cpu().numpy()
+
+
+def gpu_dequant_inv_grouped(codes: np.ndarray, scales: np.ndarray, s, b, group, bits,
+                            out_bf16=False):
+    c = torch.from_numpy(np.ascontiguousarray(codes).view(np.uint8 if bits == 4 else np.int8)).cuda()
+    sc = torch.from_numpy(np.ascontiguousarray(scales)).cuda()
+    y = hq.hq_dequant_rotate_inv_grouped(c, sc, s_dev(s), b, group, bits,
+                                         torch.bfloat16 if out_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    if out_bf16:
+        return y.view(torch.int16).cpu().numpy().view(np.uint16)
+    return y.cpu().numpy()

@@ -27,8 +27,9 @@ def declared_symbols():
 def test_library_loads_and_exports_header_symbols():
     lib = hq.load()
     syms = declared_symbols()
-    assert set(syms) == {"hq_rotate_quant", "hq_dequant_rotate_inv", "hq_rotate",
-                         "hq_status_str", "hq_last_hip_error", "hq_max_n", "hq_version"}
+    assert set(syms) == {"hq_rotate_quant", "hq_dequant_rotate_inv", "hq_rotate_quant_grouped",
+                         "hq_dequant_rotate_inv_grouped", "hq_rotate", "hq_status_str",
+                         "hq_last_hip_error", "hq_max_n", "hq_version"}
     for name in syms:
         assert hasattr(lib, name), name
     assert set(B.EXPORTS) == set(syms)
@@ -38,7 +39,7 @@ def test_status_strings():
     for code, frag in ((0, "HQ_OK"), (1, "HQ_EINVAL"), (2, "HQ_EUNSUPPORTED"), (3, "HQ_EHIP"),
                        (99, "unknown")):
         assert frag in hq.status_str(code)
-    assert hq.hq_version() == 10000
+    assert hq.hq_version() == 10100
 
 
 def rq(x=A, xd=1, rows=4, n=128, b=128, s=A, bits=4, codes=A, scales=A, sd=0):
@@ -47,6 +48,16 @@ def rq(x=A, xd=1, rows=4, n=128, b=128, s=A, bits=4, codes=A, scales=A, sd=0):
 
 def inv(codes=A, scales=A, sd=0, rows=4, n=128, b=128, s=A, bits=4, y=A, yd=0):
     return hq.load().hq_dequant_rotate_inv(codes, scales, sd, rows, n, b, s, bits, y, yd, None)
+
+
+def rqg(x=A, xd=1, rows=4, n=256, b=128, s=A, bits=4, group=64, codes=A, scales=A, sd=0):
+    return hq.load().hq_rotate_quant_grouped(x, xd, rows, n, b, s, bits, group, codes, scales,
+                                             sd, None)
+
+
+def invg(codes=A, scales=A, sd=0, rows=4, n=256, b=128, s=A, bits=4, group=64, y=A, yd=0):
+    return hq.load().hq_dequant_rotate_inv_grouped(codes, scales, sd, rows, n, b, s, bits, group,
+                                                   y, yd, None)
 
 
 def rot(x=A, xd=1, rows=4, n=128, b=128, s=A, y=A):
@@ -80,6 +91,42 @@ def test_rotate_einval(kw):
     assert rot(**kw) == hq.HQ_EINVAL
 
 
+@pytest.mark.parametrize("fn", [rqg, invg])
+@pytest.mark.parametrize("group", [0, -64, 1, 3, 48, 96, 512, 1024])
+def test_grouped_bad_group_einval(fn, group):
+    # n = 256: a group must be n itself or a power of two >= 2 dividing n
+    assert fn(group=group) == hq.HQ_EINVAL
+    assert fn(group=group, rows=0) == hq.HQ_EINVAL
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(s=None), dict(codes=None), dict(scales=None), dict(rows=-1),
+    dict(n=120, group=8), dict(b=3), dict(bits=5), dict(xd=7), dict(sd=1), dict(x=MIS),
+    dict(codes=MIS), dict(scales=A2),
+])
+def test_rotate_quant_grouped_einval(kw):
+    assert rqg(**kw) == hq.HQ_EINVAL
+
+
+@pytest.mark.parametrize("kw", [
+    dict(codes=None), dict(scales=None), dict(y=None), dict(s=None), dict(rows=-1),
+    dict(n=100, group=4), dict(b=5), dict(bits=2), dict(sd=1), dict(yd=2), dict(codes=MIS),
+    dict(y=MIS), dict(scales=A2),
+])
+def test_dequant_grouped_einval(kw):
+    assert invg(**kw) == hq.HQ_EINVAL
+
+
+def test_grouped_valid_groups_noop_at_zero_rows():
+    # rows == 0: valid groups pass every check and return without launching
+    for n, group in ((256, 256), (256, 2), (256, 128), (11008, 11008), (11008, 128),
+                     (11008, 256), (48, 48), (48, 16)):
+        assert rqg(rows=0, n=n, b=16, group=group, x=None, codes=None, scales=None,
+                   s=None) == hq.HQ_OK, (n, group)
+        assert invg(rows=0, n=n, b=16, group=group, codes=None, scales=None, y=None,
+                    s=None) == hq.HQ_OK, (n, group)
+
+
 def test_block_above_4096_unsupported():
     assert rq(rows=1, n=8192, b=8192) == hq.HQ_EUNSUPPORTED
     assert rot(rows=1, n=8192, b=8192) == hq.HQ_EUNSUPPORTED
@@ -107,6 +154,11 @@ def test_binding_rejects_host_tensors_and_bad_layouts():
     with pytest.raises(ValueError, match="GPU"):
         hq.hq_dequant_rotate_inv(torch.zeros((4, 64), dtype=torch.uint8),
                                  torch.zeros(4), s, 128)
+    with pytest.raises(ValueError, match="GPU"):
+        hq.hq_rotate_quant_grouped(x, s, 128, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        hq.hq_dequant_rotate_inv_grouped(torch.zeros((4, 64), dtype=torch.uint8),
+                                         torch.zeros((4, 2)), s, 128, 64)
     with pytest.raises(TypeError):
         hq.hq_rotate_quant(x.numpy() if False else [1, 2], s, 128)
 
