@@ -273,7 +273,7 @@ void fast_kernel(FastArgs a)
     __shared__ uint32_t red[2][kMaxWpr];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int log_lanes = LOG_LANES >= 0 ? LOG_LANES : a.log_lanes;
     const int logb = LOGB >= 0 ? LOGB : a.logb;
     const int lanes = 1 << log_lanes;

@@ -54,6 +54,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Buffer resource over `bytes` bytes at the wave-uniform address p (raw
+// buffer, 32-bit elements; dword 3 as every gfx9 target wants it).  The
+// base lives in scalar registers, so the lane's offset is the only vector
+// part of an address.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
+}
+constexpr int kNonTemporal = 2;  // buffer cache-policy bit: nt
+
 struct MfmaArgs {
     const void *x;
     const int8_t *s;
@@ -163,7 +173,7 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
     static_assert(LOGB >= 5 && LOGB <= LOGN && LOGN <= 12, "plan");
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int l16 = lane & 15;
     const int lane_off = 8 * (lane >> 4) + 32 * l16;  // element offset in a tile
 
@@ -180,6 +190,25 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
         pl = (l16 & ~mask) | (c & mask);
     }
     const int out_off = 8 * (lane >> 4) + 32 * pl;  // element offset of the 8 outputs
+    // store of the 8 codes of tile t of the group at element e0: a uniform
+    // tile base plus the lane's fixed byte offset
+    auto store_codes = [&](int64_t e0, int t, int bits, const float (&vt)[8], float inv) {
+        uint32_t f[8];
+        if (bits == 4) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 8
+                f[j] = __float_as_uint(__builtin_fmaf(vt[j], inv, 12582920.0f));
+            const auto rs = rsrc((uint8_t *)a.codes + (e0 >> 1), T * 256);
+            __builtin_amdgcn_raw_buffer_store_b32(fast::pack_int4(f), rs, out_off >> 1, t * 256, 0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 128
+                f[j] = __float_as_uint(__builtin_fmaf(vt[j], inv, 12583040.0f));
+            const auto rs = rsrc((int8_t *)a.codes + e0, T * 512);
+            const u32x2 pk = {fast::pack_int8(f[0], f[1], f[2], f[3]), fast::pack_int8(f[4], f[5], f[6], f[7])};
+            __builtin_amdgcn_raw_buffer_store_b64(pk, rs, out_off, t * 512, 0);
+        }
+    };
 
     // The two +-1 slices of H_32 as A operands: lane l holds row m = l & 15
     // at k = 8*(l >> 4) + j; row m of slice h is output Q(m, h).
@@ -203,6 +232,17 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
             }
         }
     }
+    // Wide groups keep the operand in LDS and read it back for the products
+    // only, so that its 8 registers are free while the butterflies and the
+    // quantiser run (what lets 8-tile groups fit four waves per SIMD).
+    constexpr bool kAmatInLds = T == 8;
+    __shared__ u32x4 lds_amat[kAmatInLds ? 2 : 1][64];
+    if constexpr (kAmatInLds) {
+        if (wave == 0) {
+            lds_amat[0][lane] = amat[0];
+            lds_amat[1][lane] = amat[1];
+        }
+    }
 
     // ---- work split: one persistent workgroup per CU hands out groups of
     // T tiles through an LDS counter (groups strided across workgroups)
@@ -224,16 +264,41 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
         return ((int64_t)blockIdx.x + g * gridDim.x) * (int64_t)(T * 512);
     };
 
+    // Addresses: a wave-uniform tile base (scalar registers) plus the lane's
+    // 32-bit byte offset, which is the same for every tile.
+    const uint32_t lane_byte = 2u * (uint32_t)lane_off;
     auto load = [&](int64_t g, u32x4 (&raw)[T]) {
         const int64_t e0 = group_elem0(g);
-        const int64_t left = a.total - 8 - e0;  // >= 0 for every group
-        const int lim = left < T * 512 ? (int)left : T * 512;
-        const uint16_t *gp = (const uint16_t *)a.x + e0;
+        if constexpr (LOGN >= 9) {
+            // whole tiles: a tile past the end rereads the last one
+            const int64_t last = a.total - 512;  // first element of the last tile
+            const int64_t base = e0 < last ? e0 : last;
+            const auto rs = rsrc((const uint16_t *)a.x + base, T * 1024);
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            int eo = t * 512 + lane_off;
-            eo = eo < lim ? eo : lim;  // the ragged end reads valid memory
-            raw[t] = fast::stream_load((const u32x4 *)(gp + eo));
+            for (int t = 0; t < T; ++t) {
+                int64_t tb = e0 + t * 512;
+                tb = tb < last ? tb : last;
+                const int sofs = (int)(2 * (tb - base));  // wave-uniform
+                raw[t] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lane_byte, sofs, kNonTemporal);
+            }
+        } else {
+            const int64_t left = a.total - 8 - e0;  // >= 0 for every group
+            if (left >= T * 512) {  // wave-uniform: a full group
+                const auto rs = rsrc((const uint16_t *)a.x + e0, T * 1024);
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    raw[t] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lane_byte, t * 1024,
+                                                                   kNonTemporal);
+            } else {
+                const int lim = (int)left;
+                const uint16_t *gp = (const uint16_t *)a.x + e0;
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    int eo = t * 512 + lane_off;
+                    eo = eo < lim ? eo : lim;  // the ragged end reads valid memory
+                    raw[t] = fast::stream_load((const u32x4 *)(gp + eo));
+                }
+            }
         }
     };
 
@@ -290,20 +355,27 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
         const int64_t g_next = grab();
         float v[T][8];
         // ------------------------------------------ signs + 32-point product
+        // One lane index per iteration, passed through an empty asm so that
+        // the (row-independent) LDS reads stay in the loop; every tile's read
+        // is then an immediate offset from it.
+        int lofs = lane;
+        asm volatile("" : "+v"(lofs));
+        u32x4 am0 = amat[0], am1 = amat[1];
+        if constexpr (kAmatInLds) {
+            am0 = lds_amat[0][lofs];
+            am1 = lds_amat[1][lofs];
+        }
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             u32x4 m = smask;
-            if constexpr (TPR > 1) {
-                int mofs = (t % TPR) * 64 + lane;
-                asm volatile("" : "+v"(mofs));  // keep the read in the loop
-                m = lds_mask[mofs];
-            }
+            if constexpr (TPR > 1)
+                m = lds_mask[lofs + (t % TPR) * 64];
             u32x4 b;
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 b[c] = cur[t][c] ^ m[c];
-            const f32x4 d0 = hmma<IN>(amat[0], b);
-            const f32x4 d1 = hmma<IN>(amat[1], b);
+            const f32x4 d0 = hmma<IN>(am0, b);
+            const f32x4 d1 = hmma<IN>(am1, b);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 v[t][i] = d0[i];
@@ -433,26 +505,12 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
                 inv[0] = __uint_as_float(u[0]);
                 inv[1] = __uint_as_float(u[1]);
             }
+            const int bits = a.bits;
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                const int eo = t * 512 + out_off;
-                if (e0 + eo >= a.total)
+                if (e0 + t * 512 + out_off >= a.total)
                     continue;
-                if (a.bits == 4) {
-                    uint32_t f[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 8
-                        f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv[t], 12582920.0f));
-                    *(uint32_t *)((uint8_t *)a.codes + (e0 >> 1) + (eo >> 1)) = fast::pack_int4(f);
-                } else {
-                    uint32_t f[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 128
-                        f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv[t], 12583040.0f));
-                    *(uint2 *)((int8_t *)a.codes + e0 + eo) =
-                        make_uint2(fast::pack_int8(f[0], f[1], f[2], f[3]),
-                                   fast::pack_int8(f[4], f[5], f[6], f[7]));
-                }
+                store_codes(e0, t, bits, v[t], inv[t]);
             }
         } else {
             // ---- one scale per row (LOGG == LOGN) or per group of whole
@@ -488,26 +546,10 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
                 }
                 const float inv = lane_neg ? -rq.inv : rq.inv;
                 if (grp_ok) {
+                    const int bits = a.bits;
 #pragma unroll
-                    for (int t = t0; t < t0 + TPG; ++t) {
-                        const int eo = t * 512 + out_off;
-                        if (a.bits == 4) {
-                            uint32_t f[8];
-#pragma unroll
-                            for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 8
-                                f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv, 12582920.0f));
-                            *(uint32_t *)((uint8_t *)a.codes + (e0 >> 1) + (eo >> 1)) =
-                                fast::pack_int4(f);
-                        } else {
-                            uint32_t f[8];
-#pragma unroll
-                            for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 128
-                                f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv, 12583040.0f));
-                            *(uint2 *)((int8_t *)a.codes + e0 + eo) =
-                                make_uint2(fast::pack_int8(f[0], f[1], f[2], f[3]),
-                                           fast::pack_int8(f[4], f[5], f[6], f[7]));
-                        }
-                    }
+                    for (int t = t0; t < t0 + TPG; ++t)
+                        store_codes(e0, t, bits, v[t], inv);
                 }
             }
         }
