@@ -30,14 +30,18 @@ int g_occ_used = 0;
 
 }  // namespace
 
-// Power-of-two rows of 32..4096 elements in a 16-bit type, rotated whole or
-// in 128-element blocks, forward paths only.
+// Power-of-two rows of 32..4096 elements, rotated whole or in 128-element
+// blocks: the forward paths on a 16-bit type, and the inverse path with one
+// scale per row (its codes are exact in f16; group-wise scales make the
+// dequantised values inexact there and stay on the butterfly kernel).
 bool plan_ok(const Request &r)
 {
-    if (r.op != kRotateQuant && r.op != kRotate)
+    if (r.op == kDequantInv) {
+        if (r.group != r.n)
+            return false;
+    } else if (r.x_dtype != kBF16 && r.x_dtype != kF16) {
         return false;
-    if (r.x_dtype != kBF16 && r.x_dtype != kF16)
-        return false;
+    }
     if (r.n < 32 || r.n > 4096 || (r.n & (r.n - 1)) != 0)
         return false;
     // group-wise scales (forward quantisation): groups of 32 .. n/2
@@ -88,6 +92,7 @@ int occupancy_waves(const void *fn, size_t lds)
 hipError_t launch_rq(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rq_grouped(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rot(const Request &r, const DeviceInfo &dev);
+hipError_t launch_inv(const Request &r, const DeviceInfo &dev);
 
 }  // namespace mfma
 
@@ -100,6 +105,8 @@ hipError_t launch_mfma(const Request &r, const DeviceInfo &dev)
 {
     if (r.op == kRotate)
         return mfma::launch_rot(r, dev);
+    if (r.op == kDequantInv)
+        return mfma::launch_inv(r, dev);
     return r.group == r.n ? mfma::launch_rq(r, dev) : mfma::launch_rq_grouped(r, dev);
 }
 

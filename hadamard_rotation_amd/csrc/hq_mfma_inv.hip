@@ -1,0 +1,427 @@
+// hq_mfma_inv.hip -- matrix-core kernel of the inverse path (dequantise +
+// inverse rotation, one scale per row) for gfx950, and its host side.
+//
+// Pages cited: [MS] "QuaRot：基于旋转的离群值抑制算法说明" principle section
+// (the normalised Hadamard matrix is orthogonal and symmetric, so the same
+// transform undoes the rotation); [RQ] "旋转量化：大模型低比特量化中的离群值克星"
+// section 2.1 (H_2n = H_2 (x) H_n, so five index bits of the transform can be
+// one dense 32-point product) and section 2.2 (dequantisation x = q * scale).
+//
+// With one scale per row the scale commutes with the transform:
+//   x_hat = s * (q . H_b) * (scale / sqrt(b)),
+// and q . H_b of integer codes is an integer of magnitude at most
+// b * 127 < 2^24, exact in fp32 at every stage.  The codes are also exact in
+// fp16, so the first five stages run as one 16x16x32 f16 product against the
+// +-1 slices of H_32, like the forward kernel.  A code becomes an f16 operand
+// in a byte permute and one bit operation: 0x6400 | c is 1024 + c for
+// c < 1024, and c = q + 8 (INT4 nibble ^ 8) or q + 128 (INT8 byte ^ 0x80).
+// The offset o = 1032 or 1152 is the same for all 32 inputs of a product, and
+// the rows of H_32 other than row 0 sum to zero, so only output 0 of every
+// 32-point block is shifted, by exactly 32 * o; one subtraction restores it.
+// The remaining stages, the output permutation and the DPP sign tracking are
+// those of the forward kernel; the per-row scale, 1/sqrt(b) and the lane's
+// DPP sign form one multiplier, and the sign vector s is an XOR of the
+// output sign bits (a table in LDS for rows wider than one tile).
+#include "hq_mfma_impl.h"
+
+namespace hq {
+namespace mfma {
+
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// OUT   output dtype (kF32 or kBF16)
+// BITS  4 or 8
+// T, LOGB, LOGN as in mfma_kernel
+template <int OUT, int BITS, int T, int LOGB, int LOGN>
+__global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_inv_kernel(MfmaArgs a)
+{
+    extern __shared__ __align__(16) u32x4 lds_osg[];   // n > 512: [tile of row][lane][2]
+    constexpr int D = LOGB - 5 < 4 ? LOGB - 5 : 4;      // DPP stages (lane bits 0..D-1)
+    constexpr int R = LOGB > 9 ? LOGB - 9 : 0;          // tile-bit stages
+    constexpr int TPR = LOGN > 9 ? 1 << (LOGN - 9) : 1; // tiles per row
+    constexpr int RPG = T / TPR;                        // rows per group (n >= 512)
+    constexpr int CB = BITS == 4 ? 256 : 512;           // code bytes per tile
+    constexpr int OB = OUT == kF32 ? 4 : 2;             // output bytes per element
+    constexpr float kShift = 32.0f * (BITS == 4 ? 1032.0f : 1152.0f);
+    // Output stores: non-temporal except for fp32 rows of 8-tile groups,
+    // where the hint cost a third of the throughput (measured on MI355X:
+    // 16384 x 4096, 70 us plain vs 106-115 us non-temporal; bf16 out 34 vs
+    // 37 us, 1048576 x 128 fp32 141 vs 165 us).
+    constexpr int kStoreAux = (OUT == kF32 && T == 8) ? 0 : kNonTemporal;
+    static_assert(T % TPR == 0, "a group holds whole rows");
+    static_assert(LOGB >= 5 && LOGB <= LOGN && LOGN <= 12, "plan");
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int l16 = lane & 15;
+    const int lane_off = 8 * (lane >> 4) + 32 * l16;  // element offset in a tile
+    const uint32_t code_byte = (uint32_t)(lane_off * BITS / 8);
+
+    const float sig0 = ((l16 ^ (l16 >> 2)) & 1) ? -1.0f : 1.0f;
+    const float sig1 = (((l16 >> 1) ^ (l16 >> 2)) & 1) ? -1.0f : 1.0f;
+    const float sig2 = ((l16 >> 2) & 1) ? -1.0f : 1.0f;
+    const float sig3 = ((l16 >> 3) & 1) ? -1.0f : 1.0f;
+    const bool lane_neg = (a.neg >> l16) & 1;
+    int pl = l16;
+    if constexpr (D > 0) {
+        const int c = (int)((a.pi >> (4 * l16)) & 15);
+        constexpr int mask = (1 << D) - 1;
+        pl = (l16 & ~mask) | (c & mask);
+    }
+    const int out_off = 8 * (lane >> 4) + 32 * pl;  // element offset of the 8 outputs
+    // lanes 0..15 hold transformed index 0 of their 32-point block in v[t][0]
+    const float shift0 = lane < 16 ? kShift : 0.0f;
+    const float rbs = lane_neg ? -a.rb : a.rb;
+
+    // +-1 slices of H_32 in f16 (see the forward kernel)
+    u32x4 amat[2];
+    {
+        const int m = l16;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int q = (m & 3) | (h << 2) | ((m >> 2) << 3);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int k = 8 * (lane >> 4) + 2 * c + e;
+                    const uint32_t sgn = __builtin_popcount(q & k) & 1;
+                    w |= (0x3C00u | (sgn << 15)) << (16 * e);
+                }
+                amat[h][c] = w;
+            }
+        }
+    }
+
+    // ---- work split (as in the forward kernel)
+    __shared__ int pool_next;
+    const int64_t pool_size = (a.groups - blockIdx.x + gridDim.x - 1) / gridDim.x;
+    const int nwaves = blockDim.x >> 6;
+    const int64_t first = wave;
+    const bool has_work = first < pool_size;
+    if (threadIdx.x == 0)
+        pool_next = nwaves;
+    auto grab = [&]() -> int64_t {
+        int v = 0;
+        if (lane == 0)
+            v = atomicAdd(&pool_next, 1);
+        return __builtin_amdgcn_readfirstlane(v);
+    };
+    auto group_elem0 = [&](int64_t g) {
+        return ((int64_t)blockIdx.x + g * gridDim.x) * (int64_t)(T * 512);
+    };
+
+    // ---- raw input of a group: the lane's code bytes per tile and the
+    // scale of each of its rows (RPG rows per group for n >= 512, else the
+    // row of each tile)
+    constexpr int CW = BITS == 4 ? 1 : 2;     // code words per tile
+    constexpr int NS = LOGN >= 9 ? RPG : T;   // scales per lane and group
+    struct Raw {
+        uint32_t c[T][CW];
+        uint32_t s[NS];
+    };
+    auto load = [&](int64_t g, Raw &raw) {
+        const int64_t e0 = group_elem0(g);
+        const int64_t left = a.total - 8 - e0;  // >= 0 for every group
+        const uint8_t *cb = (const uint8_t *)a.codes + e0 * BITS / 8;
+        if (left >= T * 512) {  // wave-uniform: a full group
+            const auto rs = rsrc(cb, T * CB);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                if constexpr (BITS == 4) {
+                    raw.c[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)code_byte, t * CB,
+                                                                       kNonTemporal);
+                } else {
+                    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)code_byte, t * CB,
+                                                                         kNonTemporal);
+                    raw.c[t][0] = w[0];
+                    raw.c[t][1] = w[1];
+                }
+            }
+        } else {
+            const int lim = (int)left;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                int eo = t * 512 + lane_off;
+                eo = eo < lim ? eo : lim;  // the ragged end reads valid memory
+                if constexpr (BITS == 4) {
+                    raw.c[t][0] = fast::stream_load((const uint32_t *)(cb + eo / 2));
+                } else {
+                    const u32x2 w = fast::stream_load((const u32x2 *)(cb + eo));
+                    raw.c[t][0] = w[0];
+                    raw.c[t][1] = w[1];
+                }
+            }
+        }
+        const int64_t row_last = a.rows - 1;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            int64_t row = LOGN >= 9 ? (e0 >> LOGN) + i : (e0 + i * 512 + lane_off) >> LOGN;
+            row = row < row_last ? row : row_last;
+            raw.s[i] = a.scale_f16 ? (uint32_t)((const uint16_t *)a.scales)[row]
+                                   : ((const uint32_t *)a.scales)[row];
+        }
+    };
+
+    // ---- output signs: bit 31 of word j is the sign of output out_off + j.
+    // Rows of up to 512 elements: the same 8 positions in every tile (8
+    // registers); wider rows: two 16-byte words per (tile of the row, lane)
+    // in LDS.
+    uint32_t osg_r[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    auto sign_words = [&](int p, uint32_t (&w)[8]) {
+        const u32x2 sb = *(const u32x2 *)(a.s + p);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            w[j] = ((sb[j >> 2] >> (8 * (j & 3) + 7)) & 1u) << 31;
+    };
+    if constexpr (TPR == 1)
+        sign_words(out_off & ((1 << LOGN) - 1), osg_r);
+
+    Raw cur;
+    load(has_work ? first : 0, cur);
+
+    if constexpr (TPR > 1) {
+        for (int idx = threadIdx.x; idx < TPR * 64; idx += blockDim.x) {
+            const int ln = idx & 63;
+            const int l = ln & 15;
+            int p16 = l;
+            if constexpr (D > 0) {
+                const int c = (int)((a.pi >> (4 * l)) & 15);
+                constexpr int mask = (1 << D) - 1;
+                p16 = (l & ~mask) | (c & mask);
+            }
+            uint32_t w[8];
+            sign_words((idx >> 6) * 512 + 8 * (ln >> 4) + 32 * p16, w);
+            lds_osg[2 * idx] = u32x4{w[0], w[1], w[2], w[3]};
+            lds_osg[2 * idx + 1] = u32x4{w[4], w[5], w[6], w[7]};
+        }
+    }
+    // LDS-only release: the barrier must not wait for the first loads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+    // loads and stores share one completion counter: wait for the prefetch
+    // right before this group's stores (see the forward kernel)
+    auto take_delivery = [&](Raw &raw) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int c = 0; c < CW; ++c)
+                asm volatile("" : "+v"(raw.c[t][c]));
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            asm volatile("" : "+v"(raw.s[i]));
+    };
+    take_delivery(cur);
+
+    int64_t g = first;
+    while (g < pool_size) {
+        const int64_t g_next = grab();
+        float v[T][8];
+        float sc[NS];
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            sc[i] = a.scale_f16 ? f16_to_f32((uint16_t)cur.s[i]) : __uint_as_float(cur.s[i]);
+        // ---------------------------------- codes -> f16 + 32-point product
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            u32x4 b;
+            if constexpr (BITS == 4) {
+                // byte c of w holds codes 2c (low nibble) and 2c+1 (high)
+                const uint32_t w = cur.c[t][0];
+                const uint32_t w4 = w >> 4;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t sel = (uint32_t)c | (0x0Cu << 8) | ((uint32_t)(4 + c) << 16) | (0x0Cu << 24);
+                    const uint32_t x = __builtin_amdgcn_perm(w4, w, sel);  // [w.b_c, 0, w4.b_c, 0]
+                    b[c] = (x & 0x000F000Fu) ^ 0x64086408u;
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t wd = cur.c[t][c >> 1];
+                    const uint32_t lo = (uint32_t)(2 * (c & 1));
+                    const uint32_t sel = lo | (0x0Cu << 8) | ((lo + 1) << 16) | (0x0Cu << 24);
+                    b[c] = __builtin_amdgcn_perm(0u, wd, sel) ^ 0x64806480u;
+                }
+            }
+            const f32x4 d0 = hmma<kF16>(amat[0], b);
+            const f32x4 d1 = hmma<kF16>(amat[1], b);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[t][i] = d0[i];
+                v[t][4 + i] = d1[i];
+            }
+        }
+        // ------------------------------------ prefetch the next tile group
+        if (g_next < pool_size)  // wave-uniform
+            load(g_next, cur);
+
+        // ------------------------------------------ tile-bit stages (b > 512)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                if ((t >> r) & 1)
+                    continue;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    fast::bfly(v[t][j], v[t + (1 << r)][j]);
+            }
+        // the offset of the f16 operands, on index 0 of every block; placed
+        // after the tile stages, which carry it only into index 0 of tile 0
+        // of each block (sums of blocks' index 0 entries with signs +1)
+#pragma unroll
+        for (int t = 0; t < T; t += (1 << R))
+            v[t][0] -= (float)(1 << R) * shift0;
+
+        // ------------------------------------- DPP stages (lane bits 0..D-1)
+        if constexpr (D > 0) {
+            // product results pass through empty asm, then 20 wait states
+            // cover the matrix unit's write latency before the DPP asm
+            if constexpr (R == 0) {
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        asm volatile("" : "+v"(v[t][j]));
+                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::);
+            }
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                fast::dpp_stages<D>(v[t], sig0, sig1, sig2, sig3);
+        }
+
+        take_delivery(cur);
+
+        // ------------------------------------------------------------ outputs
+        const int64_t e0 = group_elem0(g);
+        const bool full = a.total - e0 >= T * 512;  // wave-uniform
+        const auto ry = rsrc((uint8_t *)a.y + e0 * OB, T * 512 * OB);
+        int lofs = lane;
+        asm volatile("" : "+v"(lofs));  // keep the sign-table reads in the loop
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const float mul = (LOGN >= 9 ? sc[t / TPR] : sc[t]) * rbs;
+            uint32_t osg[8];
+            if constexpr (TPR > 1) {
+                const u32x4 w0 = lds_osg[2 * (lofs + (t % TPR) * 64)];
+                const u32x4 w1 = lds_osg[2 * (lofs + (t % TPR) * 64) + 1];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    osg[j] = w0[j];
+                    osg[4 + j] = w1[j];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    osg[j] = osg_r[j];
+            }
+            float o[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                o[j] = __uint_as_float(__float_as_uint(v[t][j] * mul) ^ osg[j]);
+            const bool ok = full || e0 + t * 512 + out_off < a.total;
+            if (!ok)
+                continue;
+            if constexpr (OUT == kF32) {
+                const u32x4 p0 = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                                  __float_as_uint(o[3])};
+                const u32x4 p1 = {__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]),
+                                  __float_as_uint(o[7])};
+                __builtin_amdgcn_raw_buffer_store_b128(p0, ry, out_off * 4, t * 2048, kStoreAux);
+                __builtin_amdgcn_raw_buffer_store_b128(p1, ry, out_off * 4 + 16, t * 2048, kStoreAux);
+            } else {
+                u32x4 p;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x2 f = {o[2 * q], o[2 * q + 1]};
+                    p[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(p, ry, out_off * 2, t * 1024, kStoreAux);
+            }
+        }
+        g = g_next;
+    }
+}
+
+template <int OUT, int BITS, int T, int LOGB, int LOGN>
+hipError_t launch_inv_one(const Request &r, const DeviceInfo &dev)
+{
+    MfmaArgs ma;
+    fill_args(ma, r, T);
+    ma.codes = const_cast<void *>(r.codes_in);
+    ma.scales = const_cast<void *>(r.scales_in);
+    constexpr int TPR = LOGN > 9 ? 1 << (LOGN - 9) : 1;
+    const size_t lds = TPR > 1 ? (size_t)TPR * 64 * 32 : 0;
+    auto fn = mfma_inv_kernel<OUT, BITS, T, LOGB, LOGN>;
+    // every wave the CU holds, except 8 for fp32 rows of narrow groups
+    // (1048576 x 128 fp32: 141 us at 8 waves, 210 us at 12-16)
+    int waves_cu = occupancy_waves((const void *)fn, lds);
+    const int cap = (OUT == kF32 && T < 8) ? 8 : (T < 8 ? 16 : 12);
+    if (waves_cu > cap)
+        waves_cu = cap;
+    const int threads = 64 * waves_cu;
+    int64_t grid = dev.cu_count;
+    if (grid > ma.groups)
+        grid = ma.groups;
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), lds, r.stream, ma);
+    return hipGetLastError();
+}
+
+template <int OUT, int BITS, int T>
+hipError_t inv_short(const Request &r, const DeviceInfo &dev)
+{
+    const bool full = r.b == r.n;
+    switch (r.n) {
+    case 32: return launch_inv_one<OUT, BITS, T, 5, 5>(r, dev);
+    case 64: return launch_inv_one<OUT, BITS, T, 6, 6>(r, dev);
+    case 128: return launch_inv_one<OUT, BITS, T, 7, 7>(r, dev);
+    case 256:
+        return full ? launch_inv_one<OUT, BITS, T, 8, 8>(r, dev)
+                    : launch_inv_one<OUT, BITS, T, 7, 8>(r, dev);
+    default:
+        return full ? launch_inv_one<OUT, BITS, T, 9, 9>(r, dev)
+                    : launch_inv_one<OUT, BITS, T, 7, 9>(r, dev);
+    }
+}
+
+template <int OUT, int BITS>
+hipError_t inv_dispatch(const Request &r, const DeviceInfo &dev)
+{
+    const bool full = r.b == r.n;
+    if (r.n <= 512) {
+        const int64_t groups4 = (r.rows * (int64_t)r.n + 4 * 512 - 1) / (4 * 512);
+        if (groups4 < (int64_t)dev.cu_count * 8 * 4)
+            return inv_short<OUT, BITS, 2>(r, dev);
+        return inv_short<OUT, BITS, 4>(r, dev);
+    }
+    switch (r.n) {
+    case 1024:
+        return full ? launch_inv_one<OUT, BITS, 8, 10, 10>(r, dev)
+                    : launch_inv_one<OUT, BITS, 8, 7, 10>(r, dev);
+    case 2048:
+        return full ? launch_inv_one<OUT, BITS, 8, 11, 11>(r, dev)
+                    : launch_inv_one<OUT, BITS, 8, 7, 11>(r, dev);
+    default:
+        return full ? launch_inv_one<OUT, BITS, 8, 12, 12>(r, dev)
+                    : launch_inv_one<OUT, BITS, 8, 7, 12>(r, dev);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_inv(const Request &r, const DeviceInfo &dev)
+{
+    if (r.y_dtype == kF32)
+        return r.bits == 4 ? inv_dispatch<kF32, 4>(r, dev) : inv_dispatch<kF32, 8>(r, dev);
+    return r.bits == 4 ? inv_dispatch<kBF16, 4>(r, dev) : inv_dispatch<kBF16, 8>(r, dev);
+}
+
+}  // namespace mfma
+}  // namespace hq

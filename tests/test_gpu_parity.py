@@ -139,20 +139,33 @@ def test_shapes_and_dtypes(n, b, x_dtype):
         codes, scales = G.gpu_rotate_quant(raw, x_dtype, s, b, bits, sd)
         P.check_codes(codes, ref, bits, n, what=tag)
         P.check_scales(scales, ref, sd, what=tag)
+        if x_dtype == W.BF16:
+            # inverse on the oracle's own codes and scales, both output types
+            y_ref = O.dequant_rotate_inv(ref["codes"], ref["scales"], sd, b, s, bits, n)
+            y = G.gpu_dequant_inv(ref["codes"], ref["scales"], s, b, bits)
+            P.check_inverse(y, y_ref, bf16=False, what=f"{tag} inverse f32")
+            yb = G.gpu_dequant_inv(ref["codes"], ref["scales"], s, b, bits, out_bf16=True)
+            P.check_inverse(P.bf16_bits_to_f64(yb), y_ref, bf16=True, what=f"{tag} inverse bf16")
     y = G.gpu_rotate(raw, x_dtype, s, b)
     P.check_rotated(y, ref["xr"], what=f"n={n} b={b} rotate")
 
 
 @pytest.mark.parametrize("rows", [1, 2, 3, 5, 15, 17, 63, 65, 255, 257, 1023, 1025])
 def test_ragged_row_counts(rows):
-    for n, b in ((128, 128), (4096, 4096), (11008, 128)):
-        if (rows > 300 and n > 128) or (rows > 65 and n == 4096):
+    for n, b in ((128, 128), (4096, 4096), (11008, 128), (1024, 1024), (256, 128)):
+        if (rows > 300 and n > 128) or (rows > 65 and n >= 1024):
             continue
         raw, s = W.random_rows(rows * 7 + n, rows, n, W.BF16, outliers=1)
         ref = O.rotate_quant(raw, W.BF16, b, s, 4, W.F16)
         codes, scales = G.gpu_rotate_quant(raw, W.BF16, s, b, 4, W.F16)
         P.check_codes(codes, ref, 4, n, what=f"rows={rows} n={n}")
         P.check_scales(scales, ref, W.F16, what=f"rows={rows} n={n}")
+        y_ref = O.dequant_rotate_inv(ref["codes"], ref["scales"], W.F16, b, s, 4, n)
+        for out_bf16 in (False, True):
+            y = G.gpu_dequant_inv(ref["codes"], ref["scales"], s, b, 4, out_bf16=out_bf16)
+            if out_bf16:
+                y = P.bf16_bits_to_f64(y)
+            P.check_inverse(y, y_ref, bf16=out_bf16, what=f"rows={rows} n={n} inverse")
 
 
 def test_zero_rows_and_spikes():
