@@ -145,6 +145,43 @@ def cpu_baseline(workload, target_s: float = 12.0) -> dict:
                       f"H_{w.b} product per block, scalar quantisation"}
 
 
+def time_append(dev, stream, ev0, ev1, seqs: int = 32, heads: int = 8, n: int = 128,
+                cache_tokens: int = 131072, calls: int = 200) -> dict:
+    """One decode step of a K cache: `seqs` sequences append one token of
+    `heads` 128-wide heads (bf16) each, rotated and quantised to INT4 with
+    fp16 scales, into a [cache_tokens * heads, 64] code cache at their own
+    positions.  Launch-latency bound: a few kB move per call."""
+    import numpy as np
+    import torch
+
+    import hadamard_rotation_amd as hq
+    from hadamard_rotation_amd import workloads as W
+
+    rows = seqs * heads
+    raw, s_np = W.random_rows(7, rows, n, W.BF16, outliers=1)
+    x = torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16)
+    s = torch.from_numpy(s_np).to(dev)
+    rng = np.random.default_rng(8)
+    pos = rng.choice(cache_tokens, size=seqs, replace=False)
+    dst = torch.from_numpy((pos[:, None] * heads + np.arange(heads)[None, :])
+                           .reshape(-1).astype(np.int64)).to(dev)
+    codes = torch.zeros((cache_tokens * heads, n // 2), dtype=torch.uint8, device=dev)
+    scales = torch.zeros((cache_tokens * heads,), dtype=torch.float16, device=dev)
+    for _ in range(10):
+        hq.hq_rotate_quant_append(x, s, n, dst, codes, scales, 4, stream=stream)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(calls):
+        hq.hq_rotate_quant_append(x, s, n, dst, codes, scales, 4, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / calls
+    nbytes = rows * (2 * n + n // 2 + 2) + rows * 8
+    return {"rows": rows, "n": n, "cache_rows": cache_tokens * heads,
+            "us_per_call": round(us, 3), "GB/s": round(nbytes / us / 1e3, 3),
+            "bytes_per_call": nbytes}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,6 +354,7 @@ def main(argv=None):
         cs = ev0.elapsed_time(ev1) / 1e3 / 50
         out["copy_reference"] = {"bytes_moved": 2 * nb, "GB/s": round(2 * nb / cs / 1e9, 3)}
         del src, dst
+        out["append"] = time_append(dev, stream, ev0, ev1)
 
     if not args.no_cpu_baseline and g is None:
         out["cpu_baseline"] = cpu_baseline(args.workload)

@@ -27,7 +27,7 @@ _TORCH_TO_HQ = {torch.float32: HQ_F32, torch.bfloat16: HQ_BF16, torch.float16: H
 _HQ_TO_TORCH = {v: k for k, v in _TORCH_TO_HQ.items()}
 
 EXPORTS = ("hq_rotate_quant", "hq_dequant_rotate_inv", "hq_rotate_quant_grouped",
-           "hq_dequant_rotate_inv_grouped", "hq_rotate", "hq_status_str",
+           "hq_dequant_rotate_inv_grouped", "hq_rotate_quant_append", "hq_rotate", "hq_status_str",
            "hq_last_hip_error", "hq_max_n", "hq_version")
 
 _lock = threading.Lock()
@@ -67,6 +67,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.hq_dequant_rotate_inv_grouped.argtypes = [P, P, I32, I64, I32, I32, P, I32, I32, P,
                                                       I32, P]
         lib.hq_dequant_rotate_inv_grouped.restype = I32
+        lib.hq_rotate_quant_append.argtypes = [P, I32, I64, I32, I32, P, I32, P, P, P, I32, I64, P]
+        lib.hq_rotate_quant_append.restype = I32
         lib.hq_rotate.argtypes = [P, I32, I64, I32, I32, P, P, P]
         lib.hq_rotate.restype = I32
         lib.hq_status_str.argtypes = [I32]
@@ -180,6 +182,40 @@ def _rotate_quant(x, s, b, bits, group, scale_dtype, codes, scales, stream):
                                             codes.data_ptr(), scales.data_ptr(),
                                             _TORCH_TO_HQ[scale_dtype], _stream(stream))
         _raise(st, "hq_rotate_quant_grouped")
+    return codes, scales
+
+
+def hq_rotate_quant_append(x: torch.Tensor, s: torch.Tensor, b: int, dst_rows: torch.Tensor,
+                           codes: torch.Tensor, scales: torch.Tensor, bits: int = 4,
+                           stream=None):
+    """Rotate + quantise the rows of x into an existing cache: row r's codes
+    and scale go to cache row dst_rows[r] (int64, on the GPU).  codes is the
+    cache's [cache_rows, n/2] uint8 (bits 4) or [cache_rows, n] int8, scales
+    its [cache_rows] float32 or float16.  Rows whose index is outside the
+    cache are skipped.  Returns (codes, scales)."""
+    _check_dev(x, "x")
+    if x.dtype not in _TORCH_TO_HQ:
+        raise ValueError(f"x dtype {x.dtype} unsupported")
+    rows, n = _rows_n(x, "x")
+    _check_dev(s, "s", torch.int8, (n,))
+    _check_dev(dst_rows, "dst_rows", torch.int64, (rows,))
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    _check_dev(codes, "codes")
+    if codes.dim() != 2:
+        raise ValueError("codes must be 2-D [cache_rows, n/2] or [cache_rows, n]")
+    cache_rows = codes.shape[0]
+    cshape = (cache_rows, n // 2) if bits == 4 else (cache_rows, n)
+    cdtype = torch.uint8 if bits == 4 else torch.int8
+    _check_dev(codes, "codes", cdtype, cshape)
+    _check_dev(scales, "scales", None, (cache_rows,))
+    if scales.dtype not in (torch.float32, torch.float16):
+        raise ValueError("scales must be float32 or float16")
+    st = load().hq_rotate_quant_append(x.data_ptr(), _TORCH_TO_HQ[x.dtype], rows, n, int(b),
+                                       s.data_ptr(), int(bits), dst_rows.data_ptr(),
+                                       codes.data_ptr(), scales.data_ptr(),
+                                       _TORCH_TO_HQ[scales.dtype], cache_rows, _stream(stream))
+    _raise(st, "hq_rotate_quant_append")
     return codes, scales
 
 

@@ -133,7 +133,8 @@ int group_log2(int32_t n, int32_t group)
 
 hq_status rotate_quant_impl(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
                             int32_t b, const int8_t *s, int32_t bits, int32_t group,
-                            void *codes, void *scales, hq_dtype scale_dtype, void *stream)
+                            void *codes, void *scales, hq_dtype scale_dtype, void *stream,
+                            const int64_t *dst_rows = nullptr, int64_t cache_rows = 0)
 {
     g_hip_error[0] = '\0';
     hq_status st = check_shape(rows, n, b, s);
@@ -170,6 +171,8 @@ hq_status rotate_quant_impl(const void *x, hq_dtype x_dtype, int64_t rows, int32
     r.scale_dtype = scale_dtype;
     r.group = group;
     r.logg = logg;
+    r.dst_rows = dst_rows;
+    r.cache_rows = cache_rows;
     r.stream = (hipStream_t)stream;
     return dispatch(r);
 }
@@ -235,6 +238,19 @@ hq_status hq_rotate_quant_grouped(const void *x, hq_dtype x_dtype, int64_t rows,
 {
     return rotate_quant_impl(x, x_dtype, rows, n, b, s, bits, group, codes, scales,
                              scale_dtype, stream);
+}
+
+hq_status hq_rotate_quant_append(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
+                                 int32_t b, const int8_t *s, int32_t bits,
+                                 const int64_t *dst_rows, void *codes, void *scales,
+                                 hq_dtype scale_dtype, int64_t cache_rows, void *stream)
+{
+    if (cache_rows < 0 || (rows > 0 && !dst_rows))
+        return HQ_EINVAL;
+    if (dst_rows && !aligned(dst_rows, 8))
+        return HQ_EINVAL;
+    return rotate_quant_impl(x, x_dtype, rows, n, b, s, bits, n, codes, scales, scale_dtype,
+                             stream, dst_rows, cache_rows);
 }
 
 hq_status hq_dequant_rotate_inv(const void *codes, const void *scales,
@@ -312,6 +328,6 @@ int32_t hq_max_n(void)
     return max_n_for(*dev);
 }
 
-int32_t hq_version(void) { return 10100; }
+int32_t hq_version(void) { return 10200; }
 
 }  // extern "C"

@@ -171,7 +171,7 @@ hipError_t launch_inv_grouped(const Request &r, const DeviceInfo &dev);
 bool fast_available(const Request &r)
 {
     fast::Plan p;
-    if (!fast::make_plan(r.n, r.b, p))
+    if (r.dst_rows || !fast::make_plan(r.n, r.b, p))
         return false;
     if (r.group == r.n || (r.op != kRotateQuant && r.op != kDequantInv))
         return true;

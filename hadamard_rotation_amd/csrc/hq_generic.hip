@@ -33,6 +33,8 @@ struct GenericArgs {
     int n;
     int log_b;
     int group;  // elements per scale (n: one scale per row)
+    const int64_t *dst_rows;  // output row of each input row, or null
+    int64_t cache_rows;
     float kq;   // 1 / (sqrt(b) * qmax)
     float rb;   // 1 / sqrt(b)
 };
@@ -177,20 +179,25 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(GenericArgs a)
                     m = fmaxf(m, fabsf(L[i]));
                 m = block_max(m, red);
                 RowQuant rq = row_quant(m, a.kq, qmax);
-                if (threadIdx.x == 0) {
+                // output row: the row itself, or its cache row (append);
+                // a cache row outside the cache writes nothing
+                const int64_t orow = a.dst_rows ? a.dst_rows[row] : row;
+                const bool live = !a.dst_rows || (orow >= 0 && orow < a.cache_rows);
+                const int64_t obase = orow * (int64_t)n;
+                if (live && threadIdx.x == 0) {
                     if constexpr (SC == kF32)
-                        ((float *)a.scales)[row] = rq.scale;
+                        ((float *)a.scales)[orow] = rq.scale;
                     else
-                        ((uint16_t *)a.scales)[row] = f32_to_f16(rq.scale);
+                        ((uint16_t *)a.scales)[orow] = f32_to_f16(rq.scale);
                 }
                 if constexpr (BITS == 8) {
-                    for (int i = threadIdx.x; i < n; i += kThreads)
-                        ((int8_t *)a.codes)[base + i] = (int8_t)quant_code(L[i], rq.inv, qmax);
+                    for (int i = threadIdx.x; live && i < n; i += kThreads)
+                        ((int8_t *)a.codes)[obase + i] = (int8_t)quant_code(L[i], rq.inv, qmax);
                 } else {
-                    for (int j = threadIdx.x; j < (n >> 1); j += kThreads) {
+                    for (int j = threadIdx.x; live && j < (n >> 1); j += kThreads) {
                         int q0 = quant_code(L[2 * j], rq.inv, qmax);
                         int q1 = quant_code(L[2 * j + 1], rq.inv, qmax);
-                        ((uint8_t *)a.codes)[(base >> 1) + j] =
+                        ((uint8_t *)a.codes)[(obase >> 1) + j] =
                             (uint8_t)((q0 & 15) | ((q1 & 15) << 4));
                     }
                 }
@@ -246,6 +253,8 @@ hipError_t launch_generic(const Request &r, const DeviceInfo &dev)
         ++lb;
     ga.log_b = lb;
     ga.group = r.group;
+    ga.dst_rows = r.dst_rows;
+    ga.cache_rows = r.cache_rows;
     int qmax = r.bits == 8 ? 127 : 7;
     ga.kq = (float)(1.0 / (__builtin_sqrt((double)r.b) * qmax));
     ga.rb = (float)(1.0 / __builtin_sqrt((double)r.b));

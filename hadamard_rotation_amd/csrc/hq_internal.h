@@ -36,6 +36,9 @@ struct Request {
     int group;              // elements per scale: n (one scale per row) or a
                             // power of two dividing n (scales [rows, n/group])
     int logg;               // log2(group) when group is a power of two, else -1
+    const int64_t *dst_rows;  // kRotateQuant append: output row of each input
+                              // row (device), or null: row r writes row r
+    int64_t cache_rows;       // rows of codes / scales when dst_rows is set
     void *y;                // kRotate / kDequantInv output
     int y_dtype;
     hipStream_t stream;

@@ -61,6 +61,8 @@ void fill_args(MfmaArgs &ma, const Request &r, int tiles_per_group)
     ma.total = r.rows * (int64_t)r.n;
     ma.ngroups = r.rows * (int64_t)(r.n / r.group);
     ma.logg = r.logg;
+    ma.dst_rows = r.dst_rows;
+    ma.cache_rows = r.cache_rows;
     const int64_t per_group = (int64_t)tiles_per_group * 512;
     ma.groups = (ma.total + per_group - 1) / per_group;
     const int logb = ilog2(r.b);
@@ -91,6 +93,7 @@ int occupancy_waves(const void *fn, size_t lds)
 
 hipError_t launch_rq(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rq_grouped(const Request &r, const DeviceInfo &dev);
+hipError_t launch_rq_append(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rot(const Request &r, const DeviceInfo &dev);
 hipError_t launch_inv(const Request &r, const DeviceInfo &dev);
 
@@ -107,6 +110,8 @@ hipError_t launch_mfma(const Request &r, const DeviceInfo &dev)
         return mfma::launch_rot(r, dev);
     if (r.op == kDequantInv)
         return mfma::launch_inv(r, dev);
+    if (r.dst_rows)
+        return mfma::launch_rq_append(r, dev);
     return r.group == r.n ? mfma::launch_rq(r, dev) : mfma::launch_rq_grouped(r, dev);
 }
 

@@ -75,6 +75,8 @@ struct MfmaArgs {
     int64_t groups;   // groups of T tiles
     int64_t ngroups;  // scale groups: rows * n / group (rows when per row)
     int logg;         // log2 of the scale group (the kernel's run-time LOGG)
+    const int64_t *dst_rows;  // append: cache row of each input row
+    int64_t cache_rows;       // append: rows of the cache
     uint64_t pi;      // output chunk of lane l & 15 after the DPP stages
     uint32_t neg;     // bit l set: lane l holds the negated value
     int n;
@@ -162,7 +164,9 @@ __device__ __forceinline__ uint32_t group_lane_max(uint32_t v, int logg)
 // LOGG  log2 of the scale group: LOGN (one scale per row), 9..LOGN-1 (groups
 //       of whole tiles), or 0: a run-time group of 32..256 elements
 //       (MfmaArgs::logg) reduced in the transposed layout
-template <int OP, int IN, int T, int LOGB, int LOGN, int LOGG>
+// APPEND  one scale per row, and row r's codes and scale go to cache row
+//       MfmaArgs::dst_rows[r] (skipped outside [0, cache_rows))
+template <int OP, int IN, int T, int LOGB, int LOGN, int LOGG, bool APPEND = false>
 __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
 {
     extern __shared__ __align__(16) u32x4 lds_mask[];  // n > 512: [tile of row][lane]
@@ -534,22 +538,49 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
                 const RowQuant rq = row_quant(__uint_as_float(mb), a.kq, qmax);
                 // the lane's group: first element of its outputs >> LOGG
                 const int64_t grp = (e0 + t0 * 512 + out_off) >> LOGG;
-                const bool grp_ok = grp < a.ngroups;
+                bool grp_ok = grp < a.ngroups;
+                int64_t orow = grp;  // where the group's scale goes
+                if constexpr (APPEND) {
+                    orow = grp_ok ? a.dst_rows[grp] : -1;
+                    grp_ok = grp_ok && orow >= 0 && orow < a.cache_rows;
+                }
                 // one lane per group writes the scale: lane bits 4, 5 and the
                 // group-internal low lane bits all zero
                 constexpr int grp_lanes_mask = (1 << NDPP) - 1;
                 if (grp_ok && lane < 16 && (l16 & grp_lanes_mask) == 0) {
                     if (a.scale_f16)
-                        ((uint16_t *)a.scales)[grp] = f32_to_f16(rq.scale);
+                        ((uint16_t *)a.scales)[orow] = f32_to_f16(rq.scale);
                     else
-                        ((float *)a.scales)[grp] = rq.scale;
+                        ((float *)a.scales)[orow] = rq.scale;
                 }
                 const float inv = lane_neg ? -rq.inv : rq.inv;
                 if (grp_ok) {
                     const int bits = a.bits;
 #pragma unroll
-                    for (int t = t0; t < t0 + TPG; ++t)
-                        store_codes(e0, t, bits, v[t], inv);
+                    for (int t = t0; t < t0 + TPG; ++t) {
+                        if constexpr (APPEND) {
+                            // the lane's 8 codes at their place in cache row orow
+                            const int in_row = (int)((e0 + t * 512 + out_off) & ((1 << LOGN) - 1));
+                            uint32_t f[8];
+                            if (bits == 4) {
+#pragma unroll
+                                for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 8
+                                    f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv, 12582920.0f));
+                                uint8_t *dst = (uint8_t *)a.codes + orow * (int64_t)(a.n >> 1);
+                                *(uint32_t *)(dst + (in_row >> 1)) = fast::pack_int4(f);
+                            } else {
+#pragma unroll
+                                for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 128
+                                    f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv, 12583040.0f));
+                                int8_t *dst = (int8_t *)a.codes + orow * (int64_t)a.n;
+                                *(uint2 *)(dst + in_row) =
+                                    make_uint2(fast::pack_int8(f[0], f[1], f[2], f[3]),
+                                               fast::pack_int8(f[4], f[5], f[6], f[7]));
+                            }
+                        } else {
+                            store_codes(e0, t, bits, v[t], inv);
+                        }
+                    }
                 }
             }
         }
@@ -568,35 +599,47 @@ bool plan_ok(const Request &r);
 void fill_args(MfmaArgs &ma, const Request &r, int tiles_per_group);
 int occupancy_waves(const void *fn, size_t lds);
 
-template <int OP, int IN, int T, int LOGB, int LOGN, int LOGG>
+template <int OP, int IN, int T, int LOGB, int LOGN, int LOGG, bool APPEND = false>
 hipError_t launch_one(const Request &r, const DeviceInfo &dev)
 {
     MfmaArgs ma;
     fill_args(ma, r, T);
     constexpr int TPR = LOGN > 9 ? 1 << (LOGN - 9) : 1;
     const size_t lds = TPR > 1 ? (size_t)TPR * 64 * 16 : 0;
-    auto fn = mfma_kernel<OP, IN, T, LOGB, LOGN, LOGG>;
+    auto fn = mfma_kernel<OP, IN, T, LOGB, LOGN, LOGG, APPEND>;
     // One workgroup per CU with every wave the CU can hold, at most 16
     // (measured on the 128-wide K/V rows: 16 waves per CU beat 20 by 10 %).
     const int max_threads = T < 8 ? 1024 : 768;
     int waves_cu = occupancy_waves((const void *)fn, lds);
     if (waves_cu > max_threads / 64)
         waves_cu = max_threads / 64;
-    const int threads = 64 * waves_cu;
     int64_t grid = dev.cu_count;
     if (grid > ma.groups)
         grid = ma.groups;
+    // small launches (a decode step's few rows): no more waves per
+    // workgroup than it has groups of tiles
+    const int64_t per_wg = (ma.groups + grid - 1) / grid;
+    if (waves_cu > per_wg)
+        waves_cu = (int)per_wg;
+    const int threads = 64 * waves_cu;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), lds, r.stream, ma);
     return hipGetLastError();
 }
 
-// The scale grouping of a (T, LOGB, LOGN) plan: one scale per row, or (GROUPED,
-// forward only) a run-time group of 32..256 elements, or whole-tile groups of
-// 512 .. n/2 elements.
-template <int OP, int IN, bool GROUPED, int T, int LOGB, int LOGN>
+// Launch modes of the forward kernels: one scale per row, group-wise scales,
+// or rows appended into a cache.
+enum Mode : int { kPerRow = 0, kGrouped = 1, kAppend = 2 };
+
+// The scale grouping of a (T, LOGB, LOGN) plan: one scale per row, or
+// (kGrouped, forward only) a run-time group of 32..256 elements, or whole-tile
+// groups of 512 .. n/2 elements; kAppend: one scale per row, written to the
+// cache rows the caller names.
+template <int OP, int IN, int MODE, int T, int LOGB, int LOGN>
 hipError_t launch_g(const Request &r, const DeviceInfo &dev)
 {
-    if constexpr (GROUPED && OP == kRotateQuant) {
+    if constexpr (MODE == kAppend && OP == kRotateQuant) {
+        return launch_one<OP, IN, T, LOGB, LOGN, LOGN, true>(r, dev);
+    } else if constexpr (MODE == kGrouped && OP == kRotateQuant) {
         if (r.logg < 9)
             return launch_one<OP, IN, T, LOGB, LOGN, 0>(r, dev);
         if constexpr (LOGN > 9)
@@ -615,43 +658,43 @@ hipError_t launch_g(const Request &r, const DeviceInfo &dev)
 // Rows of up to 512 elements take groups of 4 tiles, or of 2 tiles when
 // that would leave fewer than 4 groups per wave (the last round of groups
 // then idles less of the machine; measured on 131072 x 128).
-template <int OP, int IN, bool GROUPED, int T>
+template <int OP, int IN, int MODE, int T>
 hipError_t dispatch_short(const Request &r, const DeviceInfo &dev)
 {
     const bool full = r.b == r.n;
     switch (r.n) {
-    case 32: return launch_g<OP, IN, GROUPED, T, 5, 5>(r, dev);
-    case 64: return launch_g<OP, IN, GROUPED, T, 6, 6>(r, dev);
-    case 128: return launch_g<OP, IN, GROUPED, T, 7, 7>(r, dev);
+    case 32: return launch_g<OP, IN, MODE, T, 5, 5>(r, dev);
+    case 64: return launch_g<OP, IN, MODE, T, 6, 6>(r, dev);
+    case 128: return launch_g<OP, IN, MODE, T, 7, 7>(r, dev);
     case 256:
-        return full ? launch_g<OP, IN, GROUPED, T, 8, 8>(r, dev)
-                    : launch_g<OP, IN, GROUPED, T, 7, 8>(r, dev);
+        return full ? launch_g<OP, IN, MODE, T, 8, 8>(r, dev)
+                    : launch_g<OP, IN, MODE, T, 7, 8>(r, dev);
     default:
-        return full ? launch_g<OP, IN, GROUPED, T, 9, 9>(r, dev)
-                    : launch_g<OP, IN, GROUPED, T, 7, 9>(r, dev);
+        return full ? launch_g<OP, IN, MODE, T, 9, 9>(r, dev)
+                    : launch_g<OP, IN, MODE, T, 7, 9>(r, dev);
     }
 }
 
-template <int OP, int IN, bool GROUPED>
+template <int OP, int IN, int MODE>
 hipError_t dispatch_op(const Request &r, const DeviceInfo &dev)
 {
     const bool full = r.b == r.n;
     if (r.n <= 512) {
         const int64_t groups4 = (r.rows * (int64_t)r.n + 4 * 512 - 1) / (4 * 512);
         if (groups4 < (int64_t)dev.cu_count * 16 * 4)
-            return dispatch_short<OP, IN, GROUPED, 2>(r, dev);
-        return dispatch_short<OP, IN, GROUPED, 4>(r, dev);
+            return dispatch_short<OP, IN, MODE, 2>(r, dev);
+        return dispatch_short<OP, IN, MODE, 4>(r, dev);
     }
     switch (r.n) {
     case 1024:
-        return full ? launch_g<OP, IN, GROUPED, 8, 10, 10>(r, dev)
-                    : launch_g<OP, IN, GROUPED, 8, 7, 10>(r, dev);
+        return full ? launch_g<OP, IN, MODE, 8, 10, 10>(r, dev)
+                    : launch_g<OP, IN, MODE, 8, 7, 10>(r, dev);
     case 2048:
-        return full ? launch_g<OP, IN, GROUPED, 8, 11, 11>(r, dev)
-                    : launch_g<OP, IN, GROUPED, 8, 7, 11>(r, dev);
+        return full ? launch_g<OP, IN, MODE, 8, 11, 11>(r, dev)
+                    : launch_g<OP, IN, MODE, 8, 7, 11>(r, dev);
     default:
-        return full ? launch_g<OP, IN, GROUPED, 8, 12, 12>(r, dev)
-                    : launch_g<OP, IN, GROUPED, 8, 7, 12>(r, dev);
+        return full ? launch_g<OP, IN, MODE, 8, 12, 12>(r, dev)
+                    : launch_g<OP, IN, MODE, 8, 7, 12>(r, dev);
     }
 }
 

@@ -366,10 +366,13 @@ hipError_t launch_inv_one(const Request &r, const DeviceInfo &dev)
     const int cap = (OUT == kF32 && T < 8) ? 8 : (T < 8 ? 16 : 12);
     if (waves_cu > cap)
         waves_cu = cap;
-    const int threads = 64 * waves_cu;
     int64_t grid = dev.cu_count;
     if (grid > ma.groups)
         grid = ma.groups;
+    const int64_t per_wg = (ma.groups + grid - 1) / grid;
+    if (waves_cu > per_wg)
+        waves_cu = (int)per_wg;
+    const int threads = 64 * waves_cu;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), lds, r.stream, ma);
     return hipGetLastError();
 }

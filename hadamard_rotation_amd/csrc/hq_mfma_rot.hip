@@ -7,8 +7,8 @@ namespace mfma {
 
 hipError_t launch_rot(const Request &r, const DeviceInfo &dev)
 {
-    if (r.x_dtype == kBF16) return dispatch_op<kRotate, kBF16, false>(r, dev);
-    return dispatch_op<kRotate, kF16, false>(r, dev);
+    if (r.x_dtype == kBF16) return dispatch_op<kRotate, kBF16, kPerRow>(r, dev);
+    return dispatch_op<kRotate, kF16, kPerRow>(r, dev);
 }
 
 }  // namespace mfma

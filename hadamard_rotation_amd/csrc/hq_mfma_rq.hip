@@ -7,8 +7,8 @@ namespace mfma {
 
 hipError_t launch_rq(const Request &r, const DeviceInfo &dev)
 {
-    if (r.x_dtype == kBF16) return dispatch_op<kRotateQuant, kBF16, false>(r, dev);
-    return dispatch_op<kRotateQuant, kF16, false>(r, dev);
+    if (r.x_dtype == kBF16) return dispatch_op<kRotateQuant, kBF16, kPerRow>(r, dev);
+    return dispatch_op<kRotateQuant, kF16, kPerRow>(r, dev);
 }
 
 }  // namespace mfma

@@ -7,8 +7,8 @@ namespace mfma {
 
 hipError_t launch_rq_grouped(const Request &r, const DeviceInfo &dev)
 {
-    if (r.x_dtype == kBF16) return dispatch_op<kRotateQuant, kBF16, true>(r, dev);
-    return dispatch_op<kRotateQuant, kF16, true>(r, dev);
+    if (r.x_dtype == kBF16) return dispatch_op<kRotateQuant, kBF16, kGrouped>(r, dev);
+    return dispatch_op<kRotateQuant, kF16, kGrouped>(r, dev);
 }
 
 }  // namespace mfma

@@ -139,6 +139,27 @@ hq_status hq_dequant_rotate_inv_grouped(const void *codes, const void *scales,
                                         void *stream);
 
 /*
+ * hq_rotate_quant_append -- hq_rotate_quant of a few new rows written into a
+ * preallocated per-row-scale cache at given rows: the online K/V rotation
+ * into a 4-bit cache, one decode step at a time ([QT] 2.2: K and V are
+ * rotated online and kept as 4-bit codes).
+ *   x, x_dtype, rows, n, b, s, bits, scale_dtype: as for hq_rotate_quant
+ *   dst_rows  [rows] int64, device, 8-byte aligned: input row r is written to
+ *             cache row dst_rows[r].  Rows whose index lies outside
+ *             [0, cache_rows) are skipped (nothing is written for them; the
+ *             host cannot see device indices without synchronising).  Two
+ *             input rows with the same index race: the cache row then holds
+ *             one of them.
+ *   codes     the cache's codes: [cache_rows, n/2] (bits 4) or [cache_rows, n]
+ *   scales    the cache's scales: [cache_rows]
+ * Cache rows that no input row names are not touched.
+ */
+hq_status hq_rotate_quant_append(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
+                                 int32_t b, const int8_t *s, int32_t bits,
+                                 const int64_t *dst_rows, void *codes, void *scales,
+                                 hq_dtype scale_dtype, int64_t cache_rows, void *stream);
+
+/*
  * hq_rotate -- rotation only: y = x' as fp32 [rows, n] (no quantisation).
  * Used to check the rotated values themselves and Q.K^T preservation
  * ([HQA] 1: rotating Q and K with the same matrix keeps Q.K^T).

@@ -28,7 +28,8 @@ def test_library_loads_and_exports_header_symbols():
     lib = hq.load()
     syms = declared_symbols()
     assert set(syms) == {"hq_rotate_quant", "hq_dequant_rotate_inv", "hq_rotate_quant_grouped",
-                         "hq_dequant_rotate_inv_grouped", "hq_rotate", "hq_status_str",
+                         "hq_dequant_rotate_inv_grouped", "hq_rotate_quant_append", "hq_rotate",
+                         "hq_status_str",
                          "hq_last_hip_error", "hq_max_n", "hq_version"}
     for name in syms:
         assert hasattr(lib, name), name
@@ -39,7 +40,7 @@ def test_status_strings():
     for code, frag in ((0, "HQ_OK"), (1, "HQ_EINVAL"), (2, "HQ_EUNSUPPORTED"), (3, "HQ_EHIP"),
                        (99, "unknown")):
         assert frag in hq.status_str(code)
-    assert hq.hq_version() == 10100
+    assert hq.hq_version() == 10200
 
 
 def rq(x=A, xd=1, rows=4, n=128, b=128, s=A, bits=4, codes=A, scales=A, sd=0):
@@ -58,6 +59,12 @@ def rqg(x=A, xd=1, rows=4, n=256, b=128, s=A, bits=4, group=64, codes=A, scales=
 def invg(codes=A, scales=A, sd=0, rows=4, n=256, b=128, s=A, bits=4, group=64, y=A, yd=0):
     return hq.load().hq_dequant_rotate_inv_grouped(codes, scales, sd, rows, n, b, s, bits, group,
                                                    y, yd, None)
+
+
+def rqa(x=A, xd=1, rows=4, n=128, b=128, s=A, bits=4, dst=A, codes=A, scales=A, sd=0,
+        cache_rows=1024):
+    return hq.load().hq_rotate_quant_append(x, xd, rows, n, b, s, bits, dst, codes, scales, sd,
+                                            cache_rows, None)
 
 
 def rot(x=A, xd=1, rows=4, n=128, b=128, s=A, y=A):
@@ -127,6 +134,20 @@ def test_grouped_valid_groups_noop_at_zero_rows():
                     s=None) == hq.HQ_OK, (n, group)
 
 
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(s=None), dict(dst=None), dict(codes=None), dict(scales=None),
+    dict(rows=-1), dict(n=120), dict(b=3), dict(bits=5), dict(xd=7), dict(sd=1),
+    dict(cache_rows=-1), dict(dst=A2), dict(x=MIS), dict(codes=MIS), dict(scales=A2),
+])
+def test_rotate_quant_append_einval(kw):
+    assert rqa(**kw) == hq.HQ_EINVAL
+
+
+def test_rotate_quant_append_zero_rows_noop():
+    assert rqa(rows=0, x=None, dst=None, codes=None, scales=None, s=None) == hq.HQ_OK
+    assert rqa(rows=0, cache_rows=0) == hq.HQ_OK
+
+
 def test_block_above_4096_unsupported():
     assert rq(rows=1, n=8192, b=8192) == hq.HQ_EUNSUPPORTED
     assert rot(rows=1, n=8192, b=8192) == hq.HQ_EUNSUPPORTED
@@ -159,6 +180,9 @@ def test_binding_rejects_host_tensors_and_bad_layouts():
     with pytest.raises(ValueError, match="GPU"):
         hq.hq_dequant_rotate_inv_grouped(torch.zeros((4, 64), dtype=torch.uint8),
                                          torch.zeros((4, 2)), s, 128, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        hq.hq_rotate_quant_append(x, s, 128, torch.zeros(4, dtype=torch.int64),
+                                  torch.zeros((16, 64), dtype=torch.uint8), torch.zeros(16))
     with pytest.raises(TypeError):
         hq.hq_rotate_quant(x.numpy() if False else [1, 2], s, 128)
 
