@@ -493,5 +493,95 @@ int hqo_dequant_rotate_inv(const uint8_t *codes, const void *scales,
                                     threads);
 }
 
+/* Decode attention over a rotated, quantised K/V cache: the consumer of the
+ * codes written above.  [QT] 2.2: K and V are rotated online, stored as 4-bit
+ * codes and dequantised when attention reads them; [HQA] 1: rotating Q and K
+ * with the same orthogonal matrix leaves Q.K^T unchanged, so the query is
+ * rotated with the cache's rotation.  One query token per head:
+ *   q        [q_heads, n] (q_dtype), not rotated
+ *   k_codes, v_codes   [tokens, kv_heads, n/2] (bits 4) or [.., n] (bits 8)
+ *   k_scales, v_scales [tokens, kv_heads] (scale_dtype), one per row
+ *   query head h reads kv head h / (q_heads / kv_heads)
+ *   q'   = (q * s) . H_b / sqrt(b)              the cache's rotation
+ *   k_t  = code_k[t] * scale_k[t], v_t likewise  (rotated, dequantised)
+ *   a_t  = exp(c_t - max c) / sum_u exp(c_u - max c),  c_t = q'.k_t / sqrt(n)
+ *   o'   = sum_t a_t v_t                          (rotated space)
+ *   o    = (o' . H_b / sqrt(b)) * s               back to the query's space
+ * out [q_heads, n], double.  Returns 0, or -1 on invalid arguments. */
+int hqo_decode_attention(const void *q, int q_dtype, int q_heads, int kv_heads, int n, int b,
+                         const int8_t *s, int64_t tokens, int bits, const uint8_t *k_codes,
+                         const void *k_scales, const uint8_t *v_codes, const void *v_scales,
+                         int scale_dtype, double *out)
+{
+    if (check_shape(1, n, b, s) || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads != 0)
+        return -1;
+    if (tokens <= 0 || (bits != 4 && bits != 8) || (bits == 4 && n % 2 != 0))
+        return -1;
+    if (scale_dtype != HQO_F32 && scale_dtype != HQO_F16)
+        return -1;
+    if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !out)
+        return -1;
+    int8_t *Ht = make_ht(b);
+    double *qin = (double *)malloc(sizeof(double) * n);
+    double *qr = (double *)malloc(sizeof(double) * n);
+    double *u = (double *)malloc(sizeof(double) * n);
+    double *o = (double *)malloc(sizeof(double) * n);
+    double *c = (double *)malloc(sizeof(double) * (size_t)tokens);
+    int8_t *ones = (int8_t *)malloc((size_t)n);
+    int err = 0;
+    if (!Ht || !qin || !qr || !u || !o || !c || !ones) {
+        err = -2;
+        goto done;
+    }
+    memset(ones, 1, (size_t)n);
+    size_t qsz = q_dtype == HQO_F32 ? 4 : 2;
+    int group = q_heads / kv_heads;
+    for (int h = 0; h < q_heads; ++h) {
+        int kh = h / group;
+        if (hqo_decode((const char *)q + (size_t)h * n * qsz, q_dtype, n, qin)) {
+            err = -1;
+            goto done;
+        }
+        rotate_row(qin, s, n, b, Ht, u, qr);
+        double cmax = -INFINITY;
+        for (int64_t t = 0; t < tokens; ++t) {
+            int64_t row = t * kv_heads + kh; /* the row of (token t, kv head kh) */
+            double sc = stored_scale(k_scales, scale_dtype, row);
+            double dot = 0.0;
+            for (int i = 0; i < n; ++i)
+                dot += qr[i] * ((double)unpack_code(k_codes, row, n, bits, i) * sc);
+            c[t] = dot / sqrt((double)n);
+            if (c[t] > cmax)
+                cmax = c[t];
+        }
+        double denom = 0.0;
+        for (int64_t t = 0; t < tokens; ++t) {
+            c[t] = exp(c[t] - cmax);
+            denom += c[t];
+        }
+        for (int i = 0; i < n; ++i)
+            o[i] = 0.0;
+        for (int64_t t = 0; t < tokens; ++t) {
+            int64_t row = t * kv_heads + kh;
+            double w = c[t] / denom * stored_scale(v_scales, scale_dtype, row);
+            for (int i = 0; i < n; ++i)
+                o[i] += w * (double)unpack_code(v_codes, row, n, bits, i);
+        }
+        /* back to the query's space: o . H_b / sqrt(b), then * s */
+        rotate_row(o, ones, n, b, Ht, u, qin);
+        for (int i = 0; i < n; ++i)
+            out[(int64_t)h * n + i] = s[i] < 0 ? -qin[i] : qin[i];
+    }
+done:
+    free(Ht);
+    free(qin);
+    free(qr);
+    free(u);
+    free(o);
+    free(c);
+    free(ones);
+    return err;
+}
+
 /* Number of worker threads a call with threads<=0 would use. */
 int hqo_default_threads(void) { return (int)sysconf(_SC_NPROCESSORS_ONLN); }

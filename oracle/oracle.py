@@ -58,6 +58,7 @@ def _load():
         lib.hqo_rotate_quant_g.argtypes = [P, I, L, I, I, P, I, I, P, P, I, P, P, P, I]
         lib.hqo_dequant_rotate_inv.argtypes = [P, P, I, L, I, I, P, I, P, I]
         lib.hqo_dequant_rotate_inv_g.argtypes = [P, P, I, L, I, I, P, I, I, P, I]
+        lib.hqo_decode_attention.argtypes = [P, I, I, I, I, I, P, L, I, P, P, P, P, I, P]
         lib.hqo_f64_to_f16.argtypes = [ctypes.c_double]
         lib.hqo_f64_to_f16.restype = ctypes.c_uint16
         lib.hqo_f16_to_f64.argtypes = [ctypes.c_uint16]
@@ -65,7 +66,8 @@ def _load():
         lib.hqo_default_threads.restype = ctypes.c_int
         for f in (lib.hqo_hadamard, lib.hqo_decode, lib.hqo_rotate,
                   lib.hqo_rotate_quant, lib.hqo_rotate_quant_g,
-                  lib.hqo_dequant_rotate_inv, lib.hqo_dequant_rotate_inv_g):
+                  lib.hqo_dequant_rotate_inv, lib.hqo_dequant_rotate_inv_g,
+                  lib.hqo_decode_attention):
             f.restype = ctypes.c_int
         _lib = lib
         return lib
@@ -176,6 +178,34 @@ def dequant_rotate_inv(codes: np.ndarray, scales: np.ndarray, scale_dtype: int,
                                           _ptr(y), threads)
     _check(rc, "dequant_rotate_inv")
     return y
+
+
+def decode_attention(q_raw: np.ndarray, q_dtype: int, kv_heads: int, b: int, s: np.ndarray,
+                     k_codes: np.ndarray, k_scales: np.ndarray, v_codes: np.ndarray,
+                     v_scales: np.ndarray, scale_dtype: int, bits: int) -> np.ndarray:
+    """Decode attention of one query token per head over a rotated,
+    quantised K/V cache (hqo_decode_attention): q_raw [q_heads, n] raw values,
+    codes [tokens * kv_heads, n/2 or n] (row = token * kv_heads + head),
+    scales [tokens * kv_heads].  Returns float64 [q_heads, n] in the query's
+    (unrotated) space."""
+    q_raw = np.ascontiguousarray(q_raw)
+    q_heads, n = q_raw.shape
+    s = np.ascontiguousarray(s, dtype=np.int8)
+    k_codes = np.ascontiguousarray(k_codes, dtype=np.uint8)
+    v_codes = np.ascontiguousarray(v_codes, dtype=np.uint8)
+    k_scales = np.ascontiguousarray(k_scales)
+    v_scales = np.ascontiguousarray(v_scales)
+    if scale_dtype == F16:
+        k_scales = k_scales.view(np.uint16)
+        v_scales = v_scales.view(np.uint16)
+    tokens = k_codes.shape[0] // kv_heads
+    out = np.empty((q_heads, n), dtype=np.float64)
+    rc = _load().hqo_decode_attention(_ptr(q_raw), int(q_dtype), q_heads, int(kv_heads), n,
+                                      int(b), _ptr(s), tokens, int(bits), _ptr(k_codes),
+                                      _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+                                      int(scale_dtype), _ptr(out))
+    _check(rc, "decode_attention")
+    return out
 
 
 def f64_to_f16_bits(v: float) -> int:
