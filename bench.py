@@ -182,6 +182,53 @@ def time_append(dev, stream, ev0, ev1, seqs: int = 32, heads: int = 8, n: int = 
             "bytes_per_call": nbytes}
 
 
+def time_attention(dev, stream, ev0, ev1, tokens: int = 131072, kv_heads: int = 8,
+                   q_heads: int = 32, calls: int = 50) -> dict:
+    """Decode attention of 32 query heads over the 131072-token x 8-head INT4
+    K/V cache (fp16 scales): the consumer of the codes.  Two cache copies
+    alternate so that the 138 MB read per call exceeds the last-level cache
+    over two calls.  Algorithmic bytes: the K and V codes and scales, q and
+    the output; the workspace traffic (4 MB) is not counted."""
+    import numpy as np
+    import torch
+
+    import hadamard_rotation_amd as hq
+
+    n = 128
+    g = torch.Generator(device="cpu").manual_seed(5)
+    caches = []
+    for _ in range(2):
+        kc = torch.randint(0, 256, (tokens, kv_heads, n // 2), dtype=torch.uint8, generator=g)
+        vc = torch.randint(0, 256, (tokens, kv_heads, n // 2), dtype=torch.uint8, generator=g)
+        ks = (torch.rand((tokens, kv_heads), generator=g) * 0.5 + 0.1).to(torch.float16)
+        vs = (torch.rand((tokens, kv_heads), generator=g) * 0.5 + 0.1).to(torch.float16)
+        caches.append([t.to(dev) for t in (kc, ks, vc, vs)])
+    q = torch.randn((q_heads, n), generator=g).to(torch.bfloat16).to(dev)
+    s = torch.from_numpy(np.where(np.arange(n) % 3 == 0, -1, 1).astype(np.int8)).to(dev)
+    out = torch.empty((q_heads, n), dtype=torch.float32, device=dev)
+    ws = torch.empty(hq.hq_decode_attention_workspace(q_heads, kv_heads, tokens),
+                     dtype=torch.uint8, device=dev)
+
+    def call(i):
+        kc, ks, vc, vs = caches[i % 2]
+        hq.hq_decode_attention(q, s, n, kc, ks, vc, vs, 4, out=out, workspace=ws, stream=stream)
+
+    for i in range(5):
+        call(i)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(calls):
+        call(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / calls
+    nbytes = 2 * tokens * kv_heads * (n // 2 + 2) + q_heads * n * (2 + 4)
+    return {"tokens": tokens, "kv_heads": kv_heads, "q_heads": q_heads, "head_dim": n,
+            "us_per_call": round(us, 3), "GB/s": round(nbytes / us / 1e3, 3),
+            "frac_of_8TBs": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+            "bytes_per_call": nbytes}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,6 +402,7 @@ def main(argv=None):
         out["copy_reference"] = {"bytes_moved": 2 * nb, "GB/s": round(2 * nb / cs / 1e9, 3)}
         del src, dst
         out["append"] = time_append(dev, stream, ev0, ev1)
+        out["decode_attention"] = time_attention(dev, stream, ev0, ev1)
 
     if not args.no_cpu_baseline and g is None:
         out["cpu_baseline"] = cpu_baseline(args.workload)

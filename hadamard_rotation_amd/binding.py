@@ -27,7 +27,8 @@ _TORCH_TO_HQ = {torch.float32: HQ_F32, torch.bfloat16: HQ_BF16, torch.float16: H
 _HQ_TO_TORCH = {v: k for k, v in _TORCH_TO_HQ.items()}
 
 EXPORTS = ("hq_rotate_quant", "hq_dequant_rotate_inv", "hq_rotate_quant_grouped",
-           "hq_dequant_rotate_inv_grouped", "hq_rotate_quant_append", "hq_rotate", "hq_status_str",
+           "hq_dequant_rotate_inv_grouped", "hq_rotate_quant_append", "hq_decode_attention",
+           "hq_decode_attention_workspace", "hq_rotate", "hq_status_str",
            "hq_last_hip_error", "hq_max_n", "hq_version")
 
 _lock = threading.Lock()
@@ -69,6 +70,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.hq_dequant_rotate_inv_grouped.restype = I32
         lib.hq_rotate_quant_append.argtypes = [P, I32, I64, I32, I32, P, I32, P, P, P, I32, I64, P]
         lib.hq_rotate_quant_append.restype = I32
+        lib.hq_decode_attention_workspace.argtypes = [I32, I32, I64]
+        lib.hq_decode_attention_workspace.restype = I64
+        lib.hq_decode_attention.argtypes = [P, I32, I32, I32, I32, I32, P, I64, I32, P, P, P, P,
+                                            I32, P, P, I64, P]
+        lib.hq_decode_attention.restype = I32
         lib.hq_rotate.argtypes = [P, I32, I64, I32, I32, P, P, P]
         lib.hq_rotate.restype = I32
         lib.hq_status_str.argtypes = [I32]
@@ -217,6 +223,52 @@ def hq_rotate_quant_append(x: torch.Tensor, s: torch.Tensor, b: int, dst_rows: t
                                        _TORCH_TO_HQ[scales.dtype], cache_rows, _stream(stream))
     _raise(st, "hq_rotate_quant_append")
     return codes, scales
+
+
+def hq_decode_attention_workspace(q_heads: int, kv_heads: int, tokens: int) -> int:
+    """Bytes of workspace hq_decode_attention needs."""
+    return int(load().hq_decode_attention_workspace(int(q_heads), int(kv_heads), int(tokens)))
+
+
+def hq_decode_attention(q: torch.Tensor, s: torch.Tensor, b: int, k_codes: torch.Tensor,
+                        k_scales: torch.Tensor, v_codes: torch.Tensor, v_scales: torch.Tensor,
+                        bits: int = 4, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Attention of one query token per head (q [q_heads, n], not rotated)
+    over a rotated, quantised K/V cache: codes [tokens, kv_heads, n/2] uint8,
+    scales [tokens, kv_heads].  Returns out [q_heads, n] float32 in the
+    query's space.  The workspace is allocated with torch when not given."""
+    _check_dev(q, "q")
+    if q.dtype not in _TORCH_TO_HQ:
+        raise ValueError(f"q dtype {q.dtype} unsupported")
+    q_heads, n = _rows_n(q, "q")
+    _check_dev(s, "s", torch.int8, (n,))
+    for name, t in (("k_codes", k_codes), ("v_codes", v_codes)):
+        _check_dev(t, name, torch.uint8)
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be [tokens, kv_heads, n/2]")
+    tokens, kv_heads, w = k_codes.shape
+    if tuple(v_codes.shape) != (tokens, kv_heads, w):
+        raise ValueError("k_codes and v_codes must have the same shape")
+    if k_scales.dtype not in (torch.float32, torch.float16):
+        raise ValueError("scales must be float32 or float16")
+    _check_dev(k_scales, "k_scales", None, (tokens, kv_heads))
+    _check_dev(v_scales, "v_scales", k_scales.dtype, (tokens, kv_heads))
+    if out is None:
+        out = torch.empty((q_heads, n), dtype=torch.float32, device=q.device)
+    _check_dev(out, "out", torch.float32, (q_heads, n))
+    need = hq_decode_attention_workspace(q_heads, kv_heads, tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_dev(workspace, "workspace")
+    st = load().hq_decode_attention(q.data_ptr(), _TORCH_TO_HQ[q.dtype], q_heads, kv_heads, n,
+                                    int(b), s.data_ptr(), tokens, int(bits), k_codes.data_ptr(),
+                                    k_scales.data_ptr(), v_codes.data_ptr(), v_scales.data_ptr(),
+                                    _TORCH_TO_HQ[k_scales.dtype], out.data_ptr(),
+                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                    _stream(stream))
+    _raise(st, "hq_decode_attention")
+    return out
 
 
 def hq_dequant_rotate_inv(codes: torch.Tensor, scales: torch.Tensor, s: torch.Tensor,

@@ -272,6 +272,68 @@ hq_status hq_dequant_rotate_inv_grouped(const void *codes, const void *scales,
                             y_dtype, stream);
 }
 
+int64_t hq_decode_attention_workspace(int32_t q_heads, int32_t kv_heads, int64_t tokens)
+{
+    if (q_heads <= 0 || kv_heads <= 0 || tokens < 1)
+        return 0;
+    return (int64_t)hq::attention_workspace(q_heads, kv_heads, tokens);
+}
+
+hq_status hq_decode_attention(const void *q, hq_dtype q_dtype, int32_t q_heads,
+                              int32_t kv_heads, int32_t n, int32_t b, const int8_t *s,
+                              int64_t tokens, int32_t bits, const void *k_codes,
+                              const void *k_scales, const void *v_codes, const void *v_scales,
+                              hq_dtype scale_dtype, float *out, void *workspace,
+                              int64_t workspace_bytes, void *stream)
+{
+    g_hip_error[0] = '\0';
+    if (q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads != 0 || tokens < 1)
+        return HQ_EINVAL;
+    if (n < 16 || n % 16 != 0 || !is_pow2(b) || n % b != 0)
+        return HQ_EINVAL;
+    if (bits != 4 && bits != 8)
+        return HQ_EINVAL;
+    if (!valid_in_dtype(q_dtype) || !valid_scale_dtype(scale_dtype))
+        return HQ_EINVAL;
+    if (!q || !s || !k_codes || !k_scales || !v_codes || !v_scales || !out || !workspace)
+        return HQ_EINVAL;
+    if (!aligned(q, q_dtype == HQ_F32 ? 4 : 2) || !aligned(s, 16) || !aligned(k_codes, 16) ||
+        !aligned(v_codes, 16) || !aligned(out, 16) || !aligned(workspace, 16))
+        return HQ_EINVAL;
+    const uintptr_t sa = scale_dtype == HQ_F32 ? 4 : 2;
+    if (!aligned(k_scales, sa) || !aligned(v_scales, sa))
+        return HQ_EINVAL;
+    const int g = q_heads / kv_heads;
+    if (n != 128 || bits != 4 || (g != 1 && g != 2 && g != 4 && g != 8))
+        return HQ_EUNSUPPORTED;
+    if (workspace_bytes < (int64_t)hq::attention_workspace(q_heads, kv_heads, tokens))
+        return HQ_EINVAL;
+    const hq::DeviceInfo *dev = nullptr;
+    hq_status st = current_device(&dev);
+    if (st != HQ_OK)
+        return st;
+    hq::AttnRequest r{};
+    r.q = q;
+    r.q_dtype = q_dtype;
+    r.q_heads = q_heads;
+    r.kv_heads = kv_heads;
+    r.b = b;
+    r.s = s;
+    r.tokens = tokens;
+    r.k_codes = k_codes;
+    r.k_scales = k_scales;
+    r.v_codes = v_codes;
+    r.v_scales = v_scales;
+    r.scale_dtype = scale_dtype;
+    r.out = out;
+    r.workspace = workspace;
+    r.stream = (hipStream_t)stream;
+    hipError_t e = hq::launch_attention(r);
+    if (e != hipSuccess)
+        return hip_fail(e, "kernel launch");
+    return HQ_OK;
+}
+
 hq_status hq_rotate(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
                     int32_t b, const int8_t *s, float *y, void *stream)
 {
@@ -328,6 +390,6 @@ int32_t hq_max_n(void)
     return max_n_for(*dev);
 }
 
-int32_t hq_version(void) { return 10200; }
+int32_t hq_version(void) { return 10300; }
 
 }  // extern "C"

@@ -50,6 +50,29 @@ struct DeviceInfo {
     int lds_per_block;   // bytes of LDS one workgroup may allocate
 };
 
+// Decode attention over a rotated, quantised K/V cache (head dim 128, 4-bit
+// codes, one scale per row); validated by the host dispatcher beforehand.
+struct AttnRequest {
+    const void *q;          // [q_heads, 128], q_dtype
+    int q_dtype;
+    int q_heads;
+    int kv_heads;           // q_heads % kv_heads == 0, q_heads / kv_heads <= 8
+    int b;                  // block size of the cache's rotation
+    const int8_t *s;        // [128]
+    int64_t tokens;         // >= 1
+    const void *k_codes;    // [tokens, kv_heads, 64]
+    const void *k_scales;   // [tokens, kv_heads]
+    const void *v_codes;
+    const void *v_scales;
+    int scale_dtype;
+    float *out;             // [q_heads, 128]
+    void *workspace;        // attention_workspace() bytes
+    hipStream_t stream;
+};
+
+size_t attention_workspace(int q_heads, int kv_heads, int64_t tokens);
+hipError_t launch_attention(const AttnRequest &r);
+
 // Generic path: any supported (n, b); one workgroup per row with the row
 // staged in LDS as fp32.  Requires 4*n <= dev.lds_per_block.
 hipError_t launch_generic(const Request &r, const DeviceInfo &dev);

@@ -160,6 +160,40 @@ hq_status hq_rotate_quant_append(const void *x, hq_dtype x_dtype, int64_t rows, 
                                  hq_dtype scale_dtype, int64_t cache_rows, void *stream);
 
 /*
+ * hq_decode_attention -- the consumer of the codes: attention of one query
+ * token per head over a K/V cache written by hq_rotate_quant /
+ * hq_rotate_quant_append with one scale per row ([QT] 2.2: K and V rotated
+ * online, stored as 4-bit codes and dequantised when attention reads them;
+ * [HQA] 1: rotating Q with the same matrix keeps Q.K^T).  For query head h
+ * and its kv head kh = h / (q_heads / kv_heads):
+ *
+ *       q'  = (q_h * s) . H_b / sqrt(b)                 (the cache's rotation)
+ *       c_t = q' . (code_k[t, kh] * scale_k[t, kh]) / sqrt(n)
+ *       o'  = sum_t softmax_t(c) * code_v[t, kh] * scale_v[t, kh]
+ *       out_h = (o' . H_b / sqrt(b)) * s                (the query's space)
+ *
+ *   q         [q_heads, n], q_dtype (HQ_F32, HQ_BF16, HQ_F16), not rotated
+ *   s, b      the sign vector [n] and block size the cache was written with
+ *   k_codes, v_codes    [tokens, kv_heads, n/2] uint8, 16-byte aligned
+ *   k_scales, v_scales  [tokens, kv_heads], scale_dtype (one per row)
+ *   out       [q_heads, n] fp32, 16-byte aligned
+ *   workspace device memory of at least hq_decode_attention_workspace(...)
+ *             bytes, 16-byte aligned; its contents on entry do not matter and
+ *             two calls in flight on one workspace race.
+ * Errors: HQ_EINVAL for invalid arguments (tokens < 1, q_heads not a
+ * multiple of kv_heads, a short workspace, ...); HQ_EUNSUPPORTED for valid
+ * requests outside this build's kernel: n != 128, bits != 4, or
+ * q_heads / kv_heads not 1, 2, 4 or 8.
+ */
+int64_t hq_decode_attention_workspace(int32_t q_heads, int32_t kv_heads, int64_t tokens);
+hq_status hq_decode_attention(const void *q, hq_dtype q_dtype, int32_t q_heads,
+                              int32_t kv_heads, int32_t n, int32_t b, const int8_t *s,
+                              int64_t tokens, int32_t bits, const void *k_codes,
+                              const void *k_scales, const void *v_codes, const void *v_scales,
+                              hq_dtype scale_dtype, float *out, void *workspace,
+                              int64_t workspace_bytes, void *stream);
+
+/*
  * hq_rotate -- rotation only: y = x' as fp32 [rows, n] (no quantisation).
  * Used to check the rotated values themselves and Q.K^T preservation
  * ([HQA] 1: rotating Q and K with the same matrix keeps Q.K^T).

@@ -29,7 +29,7 @@ def test_library_loads_and_exports_header_symbols():
     syms = declared_symbols()
     assert set(syms) == {"hq_rotate_quant", "hq_dequant_rotate_inv", "hq_rotate_quant_grouped",
                          "hq_dequant_rotate_inv_grouped", "hq_rotate_quant_append", "hq_rotate",
-                         "hq_status_str",
+                         "hq_decode_attention", "hq_decode_attention_workspace", "hq_status_str",
                          "hq_last_hip_error", "hq_max_n", "hq_version"}
     for name in syms:
         assert hasattr(lib, name), name
@@ -40,7 +40,7 @@ def test_status_strings():
     for code, frag in ((0, "HQ_OK"), (1, "HQ_EINVAL"), (2, "HQ_EUNSUPPORTED"), (3, "HQ_EHIP"),
                        (99, "unknown")):
         assert frag in hq.status_str(code)
-    assert hq.hq_version() == 10200
+    assert hq.hq_version() == 10300
 
 
 def rq(x=A, xd=1, rows=4, n=128, b=128, s=A, bits=4, codes=A, scales=A, sd=0):
@@ -65,6 +65,12 @@ def rqa(x=A, xd=1, rows=4, n=128, b=128, s=A, bits=4, dst=A, codes=A, scales=A, 
         cache_rows=1024):
     return hq.load().hq_rotate_quant_append(x, xd, rows, n, b, s, bits, dst, codes, scales, sd,
                                             cache_rows, None)
+
+
+def att(q=A, qd=1, qh=32, kvh=8, n=128, b=128, s=A, tokens=100, bits=4, kc=A, ks=A, vc=A, vs=A,
+        sd=2, out=A, ws=A, wsb=1 << 40):
+    return hq.load().hq_decode_attention(q, qd, qh, kvh, n, b, s, tokens, bits, kc, ks, vc, vs, sd,
+                                         out, ws, wsb, None)
 
 
 def rot(x=A, xd=1, rows=4, n=128, b=128, s=A, y=A):
@@ -146,6 +152,30 @@ def test_rotate_quant_append_einval(kw):
 def test_rotate_quant_append_zero_rows_noop():
     assert rqa(rows=0, x=None, dst=None, codes=None, scales=None, s=None) == hq.HQ_OK
     assert rqa(rows=0, cache_rows=0) == hq.HQ_OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(s=None), dict(kc=None), dict(ks=None), dict(vc=None), dict(vs=None),
+    dict(out=None), dict(ws=None), dict(qh=0), dict(kvh=0), dict(qh=30), dict(tokens=0),
+    dict(n=100), dict(b=96), dict(bits=3), dict(qd=5), dict(sd=1), dict(kc=MIS), dict(out=MIS),
+    dict(ws=MIS), dict(ks=MIS), dict(wsb=16),
+])
+def test_decode_attention_einval(kw):
+    assert att(**kw) == hq.HQ_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(n=64, b=64), dict(bits=8), dict(qh=24, kvh=8),
+                                dict(qh=32, kvh=2)])
+def test_decode_attention_unsupported(kw):
+    assert att(**kw) == hq.HQ_EUNSUPPORTED
+
+
+def test_decode_attention_workspace_size():
+    w = hq.hq_decode_attention_workspace(32, 8, 131072)
+    assert w > 0 and w % 16 == 0
+    assert hq.hq_decode_attention_workspace(32, 8, 0) == 0
+    # one partial at least per query head, 130 floats each
+    assert hq.hq_decode_attention_workspace(1, 1, 1) >= 130 * 4
 
 
 def test_block_above_4096_unsupported():
