@@ -335,52 +335,72 @@ __global__ __launch_bounds__(64 * kWaves) void attn_part_kernel(AttnArgs a)
     }
 }
 
-// One wave per query head: merge the partials, rotate back, store.
-__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a)
+// One workgroup of 256 threads per query head: merge the partials (the
+// largest maximum, the rescaled sums, the rescaled accumulators), rotate the
+// result back, store.  exp(m_p - M) of every partial is kept in LDS.
+constexpr int kMergeThreads = 256;
+
+__device__ float block_reduce(float v, float *red, bool is_max)
 {
+    for (int off = 32; off > 0; off >>= 1) {
+        const float o = __shfl_xor(v, off, 64);
+        v = is_max ? fmaxf(v, o) : v + o;
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int w = 1; w < kMergeThreads / 64; ++w)
+        r = is_max ? fmaxf(r, red[w]) : r + red[w];
+    return r;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a)
+{
+    extern __shared__ float e_part[];  // [nparts]
+    __shared__ float red[kMergeThreads / 64];
+    __shared__ float osum[2][kHeadDim];
     __shared__ float o[kHeadDim];
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
     const int h = blockIdx.x;
     const float *base = a.ws + (int64_t)h * a.nparts * kPartStride;
     float m = -INFINITY;
-    for (int p = lane; p < a.nparts; p += 64)
+    for (int p = tid; p < a.nparts; p += kMergeThreads)
         m = fmaxf(m, base[(int64_t)p * kPartStride + kHeadDim]);
-    for (int off = 32; off > 0; off >>= 1)
-        m = fmaxf(m, __shfl_xor(m, off, 64));
+    const float M = block_reduce(m, red, true);
     float l = 0.0f;
-    for (int p = lane; p < a.nparts; p += 64) {
+    for (int p = tid; p < a.nparts; p += kMergeThreads) {
         const float *pp = base + (int64_t)p * kPartStride;
         const float pl = pp[kHeadDim + 1];
-        l += pl > 0.0f ? __expf(pp[kHeadDim] - m) * pl : 0.0f;
+        // partials of empty token ranges (sum 0) carry nothing
+        const float e = pl > 0.0f ? __expf(pp[kHeadDim] - M) : 0.0f;
+        e_part[p] = e;
+        l += e * pl;
     }
-    for (int off = 32; off > 0; off >>= 1)
-        l += __shfl_xor(l, off, 64);
-    float o0 = 0.0f, o1 = 0.0f;
-    for (int p = 0; p < a.nparts; ++p) {
-        const float *pp = base + (int64_t)p * kPartStride;
-        const float pl = pp[kHeadDim + 1];
-        if (pl > 0.0f) {  // partials of empty token ranges carry nothing
-            const float e = __expf(pp[kHeadDim] - m);
-            o0 = __builtin_fmaf(e, pp[lane], o0);
-            o1 = __builtin_fmaf(e, pp[lane + 64], o1);
-        }
-    }
-    const float inv = 1.0f / l;
-    o[lane] = o0 * inv;
-    o[lane + 64] = o1 * inv;
+    const float L = block_reduce(l, red, false);  // also orders the e_part writes
+    const int d = tid & (kHeadDim - 1), half = tid >> 7;
+    float acc = 0.0f;
+#pragma unroll 4
+    for (int p = half; p < a.nparts; p += 2)
+        acc = __builtin_fmaf(e_part[p], base[(int64_t)p * kPartStride + d], acc);
+    osum[half][d] = acc;
+    __syncthreads();
+    if (tid < kHeadDim)
+        o[tid] = (osum[0][tid] + osum[1][tid]) / L;
     fwht_rows(o, 1, a.log_b);
-    for (int d = lane; d < kHeadDim; d += 64) {
-        const float v = o[d] * a.rb;
-        a.out[(int64_t)h * kHeadDim + d] = a.s[d] < 0 ? -v : v;
+    if (tid < kHeadDim) {
+        const float v = o[tid] * a.rb;
+        a.out[(int64_t)h * kHeadDim + tid] = a.s[tid] < 0 ? -v : v;
     }
 }
 
 int parts_for(int kv_heads, int64_t tokens)
 {
-    // about 2048 waves in kernel 1 (8 per CU), whole workgroups, at most one
+    // about 3072 waves in kernel 1 (12 per CU), whole workgroups, at most one
     // part per 16-token block
     const int64_t blocks = (tokens + 15) / 16;
-    int64_t p = (2048 + kv_heads - 1) / kv_heads;
+    int64_t p = (3072 + kv_heads - 1) / kv_heads;
     p = (p + kWaves - 1) / kWaves * kWaves;
     const int64_t pmax = (blocks + kWaves - 1) / kWaves * kWaves;
     if (p > pmax)
@@ -396,7 +416,8 @@ hipError_t launch_g(const AttnArgs &aa, hipStream_t st)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(aa.q_heads), dim3(64), 0, st, aa);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(aa.q_heads), dim3(kMergeThreads),
+                       (size_t)aa.nparts * sizeof(float), st, aa);
     return hipGetLastError();
 }
 
