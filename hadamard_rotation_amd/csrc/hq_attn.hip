@@ -14,17 +14,19 @@
 //   o'  = sum_t softmax(c)_t * code_v[t] * scale_v[t]
 //   o   = (o' . H_b / sqrt(b)) * s
 //
-// Kernel 1 (attn_part_kernel): one wave per (kv head, token range).  The
-// wave's G query rows (rotated and scaled by 1/sqrt(n) once per workgroup in
-// LDS) are the B operand of 16x16x32 f16 products: each row is scaled by a
-// power of two that puts its largest entry in [512, 1024) and split into hi
-// and lo f16 halves, and the two products accumulate into the same column, so
-// the scores keep fp32 accuracy; the 4-bit key
-// codes of 16 tokens are the A operand, exact in f16.  Scores, an online
-// softmax (running maximum and sum per head) and the weighted sum of the
-// value codes follow; the value codes are summed on the VALU with lanes
-// owning 8 dimensions, the weights passing through LDS.  Each wave writes its
-// partial (maximum, sum, 128 accumulators per head) to the workspace.
+// Kernel 1 (attn_part_kernel): one wave per (kv head, token range), two
+// 16-token blocks per step.  The wave's G query rows (rotated and scaled by
+// 1/sqrt(n) once per workgroup in LDS) are the B operand of 16x16x32 f16
+// products: each row is scaled by a power of two that puts its largest entry
+// in [512, 1024) and split into hi and lo f16 halves, and the two products
+// accumulate into the same column, so the scores keep fp32 accuracy; the
+// 4-bit key codes of 16 tokens are the A operand, exact in f16.  An online
+// softmax (running maximum and sum per head) turns the scores into weights,
+// which become the A operand of the value products: rows 0..G-1 hold their hi
+// f16 halves, rows G..2G-1 the lo halves, the contraction runs over the 32
+// tokens of the step, and the value codes (exact in f16) are the B operand,
+// product ng covering dimensions 8*j + ng.  Each wave writes its partial
+// (maximum, sum, 128 accumulators per head) to the workspace.
 // Kernel 2 (attn_merge_kernel): per query head, merges the partials with the
 // usual rescaling and rotates the result back.
 #include "hq_device.h"
@@ -39,7 +41,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kHeadDim = 128;
-constexpr int kPartStride = kHeadDim + 2;  // floats per (head, part): o[128], max, sum
+constexpr int kPartStride = kHeadDim + 4;  // floats per (head, partial): o[128], max, sum, 2 unused
 constexpr int kWaves = 4;                  // waves per workgroup of kernel 1
 
 struct AttnArgs {
@@ -57,16 +59,12 @@ struct AttnArgs {
     int scale_f16;
     int q_heads;
     int kv_heads;
-    int nparts;         // partials per query head (= waves per kv head)
+    int nparts;         // token ranges per kv head (= waves of kernel 1 per kv head)
+    int nws;            // partials per query head in the workspace (= workgroups per kv head)
     int log_b;
     float rb;           // 1 / sqrt(b)
-    float qscale;       // 1 / (sqrt(b) * sqrt(n)): rotation and softmax scale
+    float qscale;       // log2(e) / (sqrt(b) * sqrt(n)): rotation, softmax scale, base 2
 };
-
-__device__ __forceinline__ float load_scale(const void *p, int f16, int64_t i)
-{
-    return f16 ? f16_to_f32(((const uint16_t *)p)[i]) : ((const float *)p)[i];
-}
 
 __device__ __forceinline__ float load_q(const void *p, int dtype, int64_t i)
 {
@@ -112,14 +110,56 @@ __device__ __forceinline__ float xsum16_32(float v)
     return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
+// x = hi + lo as f16 pairs, to about 2^-21 of |x| for |x| >= 2^-14 (and to
+// 2^-25 absolute below): hi is x truncated to f16 by one conversion whose
+// result both goes into the operand and forms the remainder, so the
+// remainder x - hi is exact in fp32 and only its own rounding to f16 is lost.
+// (Rounding hi to nearest instead lets the compiler round the same product
+// twice, once through a mixed-precision multiply, and the two can differ by
+// one f16 unit at a midpoint.)
+__device__ __forceinline__ void split_f16x2(float x0, float x1, uint32_t &hi, uint32_t &lo)
+{
+    const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+    const f16x2 l = {(_Float16)(x0 - (float)h[0]), (_Float16)(x1 - (float)h[1])};
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
+}
+
+// v(lane) + v(lane ^ 16)
+__device__ __forceinline__ float xsum16(float v)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// v(lane) + v(lane ^ 32)
+__device__ __forceinline__ float xsum32(float v)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ks[j] = v of lane j, vs[j] = v of lane 8 + j, within each row of 16 lanes
+template <int J>
+__device__ __forceinline__ void bcast_row(float v, float (&ks)[8], float (&vs)[8])
+{
+    if constexpr (J < 8) {
+        ks[J] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + J, 0xf, 0xf, false));
+        vs[J] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x158 + J, 0xf, 0xf, false));
+        bcast_row<J + 1>(v, ks, vs);
+    }
+}
+
+constexpr float kGrowLog2 = 5.0f;  // scores are in base 2: a factor of 32
+
 // G: query heads per kv head (1, 2, 4 or 8)
 template <int G>
-__global__ __launch_bounds__(64 * kWaves) void attn_part_kernel(AttnArgs a)
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))) void attn_part_kernel(AttnArgs a)
 {
     __shared__ float qrot[G * kHeadDim];
     __shared__ float qpow[G];              // power of two applied to each query row
-    __shared__ float wbuf[kWaves][16][G];  // per wave: weight of (token, head) for one block
-    __shared__ float abuf[kWaves][G];      // per wave: rescale factor of each head
+    __shared__ float po[kWaves][G][kHeadDim];  // each wave's partial accumulators
+    __shared__ float pm[kWaves][G], pl[kWaves][G];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -128,7 +168,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_part_kernel(AttnArgs a)
     const int kh = blockIdx.y;
     const int part = blockIdx.x * kWaves + wave;
 
-    // ---- the G query rows of this kv head, rotated and scaled, in LDS
+    // ---- the G query rows of this kv head, rotated and scaled, in LDS; the
+    // scale includes log2(e), so scores come out in base 2 and exp2 serves
     for (int i = threadIdx.x; i < G * kHeadDim; i += blockDim.x) {
         const int g = i / kHeadDim, d = i % kHeadDim;
         const float v = load_q(a.q, a.q_dtype, (int64_t)(kh * G + g) * kHeadDim + d);
@@ -154,19 +195,14 @@ __global__ __launch_bounds__(64 * kWaves) void attn_part_kernel(AttnArgs a)
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            uint32_t wh = 0, wl = 0;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int d = 32 * rg + 8 * c + 2 * p + e;
-                _Float16 hi = (_Float16)0.0f, lo = (_Float16)0.0f;
-                if (l16 < G) {
-                    const float x = qrot[l16 * kHeadDim + d] * a.qscale * qpow[l16];
-                    hi = (_Float16)x;
-                    lo = (_Float16)(x - (float)hi);
-                }
-                wh |= (uint32_t)__builtin_bit_cast(uint16_t, hi) << (16 * e);
-                wl |= (uint32_t)__builtin_bit_cast(uint16_t, lo) << (16 * e);
+            const int d = 32 * rg + 8 * c + 2 * p;
+            float x0 = 0.0f, x1 = 0.0f;
+            if (l16 < G) {
+                x0 = qrot[l16 * kHeadDim + d] * a.qscale * qpow[l16];
+                x1 = qrot[l16 * kHeadDim + d + 1] * a.qscale * qpow[l16];
             }
+            uint32_t wh, wl;
+            split_f16x2(x0, x1, wh, wl);
             bqh[c][p] = wh;
             bql[c][p] = wl;
         }
@@ -176,169 +212,300 @@ __global__ __launch_bounds__(64 * kWaves) void attn_part_kernel(AttnArgs a)
     // ---- token range of this wave
     const int64_t b0 = a.blocks * part / a.nparts;
     const int64_t b1 = a.blocks * (part + 1) / a.nparts;
-    const int64_t last_row = (a.tokens - 1) * a.kv_heads + kh;
+    const int64_t lim = a.tokens < b1 * 16 ? a.tokens : b1 * 16;  // first token not ours
 
-    float m_run = -INFINITY, l_run = 0.0f;  // score lanes (l16 < G): head l16
-    float acc[G][8];                        // value lanes: dims 8*l16 .. +7
-    float wsum[G];
+    // Running softmax state per head (score lanes l16 < G, the same in every
+    // row group).  The maximum only moves when a block beats it by more than
+    // ln 32, so the weights exp(s - m_run) stay below 32 and the accumulators
+    // are rescaled rarely.  The weights also carry the power of two `wscale`
+    // that puts the largest value scale seen so far in [512, 1024): with the
+    // bound on exp that keeps every weight below 32768, inside f16.
+    float m_run = -INFINITY, l_run = 0.0f;
+    float wscale = 0.0f;  // 0 until a nonzero value scale is seen
+    int wexp = 0;         // log2(wscale) once it is set
+    // Weighted value sums: product ng covers dimensions 8*j + ng (column j);
+    // row m < G holds the hi halves of head m's weights, row G + m the lo
+    // halves.  Lane (l16, rg) holds rows 4*rg .. 4*rg+3 of column l16.
+    f32x4 acc[8];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        wsum[g] = 0.0f;
+    for (int ng = 0; ng < 8; ++ng)
+        acc[ng] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Raw data of two 16-token blocks.  Value element j is token
+    // 4*rg + (j & 3) of block j >> 2: the tokens whose scores the lane holds,
+    // and the tokens of contraction index 8*rg + j of the value products.
+    // Each lane loads one scale: lane l16 = j < 8 the key scale of that token,
+    // lane l16 = 8 + j its value scale; DPP broadcasts hand them out per row.
+    struct Pair {
+        u32x4 k[2];      // key codes: token l16 of each block, dimensions 32*rg .. +31
+        uint32_t v[8];   // value codes: dimensions 8*l16 .. +7
+        float s;         // one scale
+    };
+    // Loads go through buffer descriptors rebased to the step's first row
+    // and cut off at the first row of a token >= lim: rows past the wave's
+    // range read as 0 without touching memory.  Lane offsets (bytes from the
+    // step's first row) are the same for every step.
+    const int kv = a.kv_heads;
+    const int ssz = a.scale_f16 ? 2 : 4;
+    const int64_t lim_rows = lim * kv;
+    auto span = [&](int64_t row0, int bytes_per_row) -> int {
+        int64_t r = (lim_rows - row0) * bytes_per_row;
+        r = r < 0 ? 0 : r;
+        return (int)(r < 0x7FFFFFFF ? r : 0x7FFFFFFF);
+    };
+    int ok_[2], ov_[8];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        ok_[b] = ((16 * b + l16) * kv + kh) * (kHeadDim / 2) + 16 * rg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ov_[4 * b + i] = ((16 * b + 4 * rg + i) * kv + kh) * (kHeadDim / 2) + 4 * l16;
+    }
+    const int sj = l16 & 7;
+    const int srow = (16 * (sj >> 2) + 4 * rg + (sj & 3)) * kv + kh;
+    // the other half of each row asks past every span: it reads 0
+    const int oks = l16 < 8 ? srow * ssz : 0x7FFFFFFF;
+    const int ovs = l16 < 8 ? 0x7FFFFFFF : srow * ssz;
+    auto load_pair = [&](int64_t blk, Pair &r) {
+        const int64_t row0 = blk * 16 * kv;
+        const int cb = span(row0, kHeadDim / 2);
+        const auto rk = rsrc(a.k_codes + row0 * (kHeadDim / 2), cb);
+        const auto rv = rsrc(a.v_codes + row0 * (kHeadDim / 2), cb);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            r.k[b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ok_[b], 0, kNonTemporal));
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            acc[g][j] = 0.0f;
-    }
-
-    // raw data of one 16-token block
-    struct Blk {
-        u32x4 k;         // key codes: token l16, dimensions 32*rg .. +31
-        uint32_t v[4];   // value codes: token 4*step + rg, dimensions 8*l16 .. +7
-        float ks[4];     // key scales of tokens 4*rg + i
-        float vs[4];     // value scales of the same tokens
-    };
-    auto load_blk = [&](int64_t blk, Blk &r) {
-        const int64_t t0 = blk * 16;
-        int64_t row = (t0 + l16) * a.kv_heads + kh;
-        row = row < last_row ? row : last_row;  // rows past the end: read a valid one
-        r.k = __builtin_nontemporal_load((const u32x4 *)(a.k_codes + row * (kHeadDim / 2)) + rg);
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            int64_t vr = (t0 + 4 * st + rg) * a.kv_heads + kh;
-            vr = vr < last_row ? vr : last_row;
-            r.v[st] = __builtin_nontemporal_load((const uint32_t *)(a.v_codes + vr * (kHeadDim / 2)) + l16);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int64_t sr = (t0 + 4 * rg + i) * a.kv_heads + kh;
-            sr = sr < last_row ? sr : last_row;
-            r.ks[i] = load_scale(a.k_scales, a.scale_f16, sr);
-            r.vs[i] = load_scale(a.v_scales, a.scale_f16, sr);
+            r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(rv, ov_[j], 0, kNonTemporal);
+        const int sb = span(row0, ssz);
+        const auto rks = rsrc((const uint8_t *)a.k_scales + row0 * ssz, sb);
+        const auto rvs = rsrc((const uint8_t *)a.v_scales + row0 * ssz, sb);
+        if (a.scale_f16) {
+            const uint32_t h = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rks, oks, 0, 0) |
+                               (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rvs, ovs, 0, 0);
+            r.s = f16_to_f32((uint16_t)h);
+        } else {
+            r.s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, oks, 0, 0) |
+                                  __builtin_amdgcn_raw_buffer_load_b32(rvs, ovs, 0, 0));
         }
     };
+    // lane's token offsets within a step (element j)
+    int tj[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        tj[j] = 16 * (j >> 2) + 4 * rg + (j & 3);
 
-    Blk cur;
-    if (b0 < b1)
-        load_blk(b0, cur);
-    for (int64_t blk = b0; blk < b1; ++blk) {
-        Blk nxt = cur;
-        if (blk + 1 < b1)
-            load_blk(blk + 1, nxt);
+    auto step = [&](const Pair &cur, int64_t blk) {
         // -------------------------------------------------------- scores
-        f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 d[2];
+        d[0] = d[1] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            // 8 key codes (dimension 32*rg + 8c + j) -> exact f16: 0x6400 |
-            // (nib ^ 8) is 1032 + q, and 1032 is subtracted in f16
-            const uint32_t w = cur.k[c];
-            const uint32_t w4 = w >> 4;
-            u32x4 ak;
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const uint32_t sel = (uint32_t)p | (0x0Cu << 8) | ((uint32_t)(4 + p) << 16) | (0x0Cu << 24);
-                const uint32_t x = (__builtin_amdgcn_perm(w4, w, sel) & 0x000F000Fu) ^ 0x64086408u;
-                const f16x2 h = __builtin_bit_cast(f16x2, x) + (f16x2){(_Float16)-1032.0f, (_Float16)-1032.0f};
-                ak[p] = __builtin_bit_cast(uint32_t, h);
+            for (int b = 0; b < 2; ++b) {
+                // 8 key codes (dimension 32*rg + 8c + j) -> exact f16: 0x6400 |
+                // (nib ^ 8) is 1032 + q, and 1032 is subtracted in f16
+                const uint32_t w = cur.k[b][c];
+                const uint32_t w4 = w >> 4;
+                u32x4 ak;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t sel = (uint32_t)p | (0x0Cu << 8) | ((uint32_t)(4 + p) << 16) | (0x0Cu << 24);
+                    const uint32_t x = (__builtin_amdgcn_perm(w4, w, sel) & 0x000F000Fu) ^ 0x64086408u;
+                    const f16x2 h = __builtin_bit_cast(f16x2, x) + (f16x2){(_Float16)-1032.0f, (_Float16)-1032.0f};
+                    ak[p] = __builtin_bit_cast(uint32_t, h);
+                }
+                d[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ak),
+                                                              __builtin_bit_cast(f16x8, bqh[c]), d[b], 0, 0, 0);
+                d[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ak),
+                                                              __builtin_bit_cast(f16x8, bql[c]), d[b], 0, 0, 0);
             }
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ak),
-                                                       __builtin_bit_cast(f16x8, bqh[c]), d, 0, 0, 0);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ak),
-                                                       __builtin_bit_cast(f16x8, bql[c]), d, 0, 0, 0);
         }
-        // lane l16 < G: scores of head l16 for tokens 4*rg + i
-        float sc[4];
-        const int64_t t0 = blk * 16;
+        float ks[8], vs[8];
+        bcast_row<0>(cur.s, ks, vs);
+        // lane l16 < G: scores of head l16 for the lane's 8 tokens
+        float sc[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t t = t0 + 4 * rg + i;
-            sc[i] = t < a.tokens ? d[i] * unscale * cur.ks[i] : -INFINITY;
-        }
-        // ------------------------------------------------- online softmax
-        float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        mb = xmax16_32(mb);
-        const float m_new = fmaxf(m_run, mb);
-        const float alpha = __expf(m_run - m_new);
-        float p[4], ps = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p[i] = __expf(sc[i] - m_new);
-            ps += p[i];
-        }
-        ps = xsum16_32(ps);
-        l_run = l_run * alpha + ps;
-        m_run = m_new;
-        if (l16 < G) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                wbuf[wave][4 * rg + i][l16] = p[i] * cur.vs[i];
-            if (rg == 0)
-                abuf[wave][l16] = alpha;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-        // ------------------------------------------- weighted value codes
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float al = abuf[wave][g];
-            wsum[g] *= al;
+        for (int j = 0; j < 8; ++j)
+            sc[j] = d[j >> 2][j & 3] * unscale * ks[j];
+        if (blk * 16 + 32 > lim) {  // the last step: tokens past the range
+            const int left = (int)(lim - blk * 16);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                acc[g][j] *= al;
+                sc[j] = tj[j] < left ? sc[j] : -INFINITY;
         }
+        // ------------------------------------------------- online softmax
+        float mb = sc[0], vm = vs[0];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            // codes + 8 as bytes, converted by v_cvt_f32_ubyte*
-            const uint32_t xw = cur.v[st] ^ 0x88888888u;
-            const uint32_t lo = xw & 0x0F0F0F0Fu, hi = (xw >> 4) & 0x0F0F0F0Fu;
-            float cv[8];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                cv[2 * k] = (float)((lo >> (8 * k)) & 0xFFu);
-                cv[2 * k + 1] = (float)((hi >> (8 * k)) & 0xFFu);
+        for (int j = 1; j < 8; ++j) {
+            mb = fmaxf(mb, sc[j]);
+            vm = fmaxf(vm, vs[j]);
+        }
+        mb = xmax16_32(mb);
+        vm = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, xmax16_32(vm))));
+        const bool grow = l16 < G && mb > m_run + kGrowLog2;
+        const bool need_e = vm * wscale >= 1024.0f || (wscale == 0.0f && vm > 0.0f);
+        if (__builtin_amdgcn_ballot_w64(grow) != 0 || need_e) {
+            const float m_new = grow ? mb : m_run;
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // 0 on the first block
+            m_run = m_new;
+            l_run *= alpha;
+            float ratio = 1.0f;
+            if (need_e) {
+                int e = 0;
+                (void)frexpf(vm, &e);  // vm = f * 2^e, f in [0.5, 1)
+                const int enew = 10 - e < 127 ? 10 - e : 127;
+                ratio = wscale > 0.0f ? ldexpf(1.0f, enew - wexp) : 0.0f;  // accumulators are 0 while wscale is
+                wexp = enew;
+                wscale = ldexpf(1.0f, enew);
             }
+            float al[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float wt = wbuf[wave][4 * st + rg][g];
-                wsum[g] += wt;
+            for (int g = 0; g < G; ++g)
+                al[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), g)) * ratio;
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    acc[g][j] = __builtin_fmaf(wt, cv[j], acc[g][j]);
+            for (int i = 0; i < 4; ++i) {
+                // row 4*rg + i belongs to head (4*rg + i) mod G
+                float f;
+                if constexpr (G == 8)
+                    f = (rg & 1) ? al[4 + i] : al[i];
+                else
+                    f = al[i % G];
+#pragma unroll
+                for (int ng = 0; ng < 8; ++ng)
+                    acc[ng][i] *= f;
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-        cur = nxt;
-    }
-
-    // ---- partial of this wave: codes were summed as q + 8
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
+        float pw[8], ps = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float v = __builtin_fmaf(-8.0f, wsum[g], acc[g][j]);
-            v = xsum16_32(v);  // the four row groups hold different tokens
-            acc[g][j] = v;
+            pw[j] = __builtin_amdgcn_exp2f(sc[j] - m_run);
+            ps += pw[j];
+        }
+        ps = xsum16_32(ps);
+        l_run += ps;
+        // ------------------------------ A operand: weights as hi/lo f16 rows
+        u32x4 aw;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const float w0 = vs[2 * p] * wscale * pw[2 * p];
+            const float w1 = vs[2 * p + 1] * wscale * pw[2 * p + 1];
+            uint32_t hw, lw;
+            split_f16x2(w0, w1, hw, lw);
+            // lanes G .. 2G-1 of each row take the lo halves of lanes 0 .. G-1
+            const uint32_t lsh = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lw, 0x110 + G, 0xf, 0xf, false);
+            aw[p] = l16 < G ? hw : (l16 < 2 * G ? lsh : 0u);
+        }
+        // ------------------------------------------- weighted value codes
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            // byte k of the codes of tokens (2p, 2p+1) -> 16-bit halves
+            uint32_t x[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t sel = (uint32_t)k | (0x0Cu << 8) | ((uint32_t)(4 + k) << 16) | (0x0Cu << 24);
+                x[p] = __builtin_amdgcn_perm(cur.v[2 * p + 1], cur.v[2 * p], sel);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                // dimension 8*l16 + 2k + h: the low (h = 0) or high nibble
+                u32x4 bv;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t y = ((h ? x[p] >> 4 : x[p]) & 0x000F000Fu) ^ 0x64086408u;
+                    const f16x2 c = __builtin_bit_cast(f16x2, y) + (f16x2){(_Float16)-1032.0f, (_Float16)-1032.0f};
+                    bv[p] = __builtin_bit_cast(uint32_t, c);
+                }
+                acc[2 * k + h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aw),
+                                                                        __builtin_bit_cast(f16x8, bv),
+                                                                        acc[2 * k + h], 0, 0, 0);
+            }
+        }
+    };
+
+    // two register sets, alternating, so no step copies its data
+    Pair pa, pb;
+    if (b0 < b1) {
+        load_pair(b0, pa);
+        for (int64_t blk = b0;;) {
+            load_pair(blk + 2, pb);  // past the range: reads 0
+            step(pa, blk);
+            blk += 2;
+            if (blk >= b1)
+                break;
+            load_pair(blk + 2, pa);
+            step(pb, blk);
+            blk += 2;
+            if (blk >= b1)
+                break;
         }
     }
+
+    // ---- partial of this wave: add the lo rows to the hi rows, undo wscale
+    const float inv = wscale > 0.0f ? 1.0f / wscale : 0.0f;  // exact: a power of two
+    float o[4][8];  // [row i][product ng]
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        float *dst = a.ws + ((int64_t)(kh * G + g) * a.nparts + part) * kPartStride;
-        if (rg == 0) {
-            *(float4 *)(dst + 8 * l16) = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
-            *(float4 *)(dst + 8 * l16 + 4) = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int ng = 0; ng < 8; ++ng) {
+            float v;
+            if constexpr (G == 1)
+                v = acc[ng][0] + acc[ng][1];
+            else if constexpr (G == 2)
+                v = acc[ng][i & 1] + acc[ng][(i & 1) + 2];
+            else if constexpr (G == 4)
+                v = xsum16(acc[ng][i]);
+            else
+                v = xsum32(acc[ng][i]);
+            o[i][ng] = v * inv;
         }
-        if (lane == g) {
-            dst[kHeadDim] = m_run;
-            dst[kHeadDim + 1] = l_run;
+    }
+    // row 4*rg + i < G now holds head 4*rg + i: the wave's partials go to
+    // LDS, and the workgroup merges its waves' partials (the largest maximum,
+    // rescaled sums and accumulators) into one per head
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = 4 * rg + i;
+        if (i < G && g < G) {
+            *(float4 *)&po[wave][g][8 * l16] = make_float4(o[i][0], o[i][1], o[i][2], o[i][3]);
+            *(float4 *)&po[wave][g][8 * l16 + 4] = make_float4(o[i][4], o[i][5], o[i][6], o[i][7]);
+        }
+    }
+    if (lane < G) {
+        pm[wave][lane] = m_run;
+        pl[wave][lane] = l_run;
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < G * kHeadDim; t += 64 * kWaves) {
+        const int g = t / kHeadDim, dd = t % kHeadDim;
+        float M = pm[0][g];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            M = fmaxf(M, pm[w][g]);
+        float L = 0.0f, O = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            // waves with no tokens (sum 0) carry nothing
+            const float e = pl[w][g] > 0.0f ? __builtin_amdgcn_exp2f(pm[w][g] - M) : 0.0f;
+            L = __builtin_fmaf(e, pl[w][g], L);
+            O = __builtin_fmaf(e, po[w][g][dd], O);
+        }
+        float *dst = a.ws + ((int64_t)(kh * G + g) * a.nws + blockIdx.x) * kPartStride;
+        dst[dd] = O;
+        if (dd == 0) {
+            dst[kHeadDim] = M;
+            dst[kHeadDim + 1] = L;
         }
     }
 }
 
-// One workgroup of 256 threads per query head: merge the partials (the
+// One workgroup of 1024 threads per query head: merge the partials (the
 // largest maximum, the rescaled sums, the rescaled accumulators), rotate the
-// result back, store.  exp(m_p - M) of every partial is kept in LDS.
-constexpr int kMergeThreads = 256;
+// result back, store.  exp2(m_p - M) of every partial is kept in LDS; eight
+// groups of 128 threads take every eighth partial, so each thread has a
+// dozen or so independent loads in flight.
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeGroups = kMergeThreads / kHeadDim;
 
 __device__ float block_reduce(float v, float *red, bool is_max)
 {
@@ -358,36 +525,41 @@ __device__ float block_reduce(float v, float *red, bool is_max)
 
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a)
 {
-    extern __shared__ float e_part[];  // [nparts]
+    extern __shared__ float e_part[];  // [nws]
     __shared__ float red[kMergeThreads / 64];
-    __shared__ float osum[2][kHeadDim];
+    __shared__ float osum[kMergeGroups][kHeadDim];
     __shared__ float o[kHeadDim];
     const int tid = threadIdx.x;
     const int h = blockIdx.x;
-    const float *base = a.ws + (int64_t)h * a.nparts * kPartStride;
+    const float *base = a.ws + (int64_t)h * a.nws * kPartStride;
     float m = -INFINITY;
-    for (int p = tid; p < a.nparts; p += kMergeThreads)
+    for (int p = tid; p < a.nws; p += kMergeThreads)
         m = fmaxf(m, base[(int64_t)p * kPartStride + kHeadDim]);
     const float M = block_reduce(m, red, true);
     float l = 0.0f;
-    for (int p = tid; p < a.nparts; p += kMergeThreads) {
+    for (int p = tid; p < a.nws; p += kMergeThreads) {
         const float *pp = base + (int64_t)p * kPartStride;
         const float pl = pp[kHeadDim + 1];
         // partials of empty token ranges (sum 0) carry nothing
-        const float e = pl > 0.0f ? __expf(pp[kHeadDim] - M) : 0.0f;
+        const float e = pl > 0.0f ? __builtin_amdgcn_exp2f(pp[kHeadDim] - M) : 0.0f;
         e_part[p] = e;
         l += e * pl;
     }
     const float L = block_reduce(l, red, false);  // also orders the e_part writes
-    const int d = tid & (kHeadDim - 1), half = tid >> 7;
+    const int d = tid & (kHeadDim - 1), grp = tid / kHeadDim;
     float acc = 0.0f;
-#pragma unroll 4
-    for (int p = half; p < a.nparts; p += 2)
+#pragma unroll 8
+    for (int p = grp; p < a.nws; p += kMergeGroups)
         acc = __builtin_fmaf(e_part[p], base[(int64_t)p * kPartStride + d], acc);
-    osum[half][d] = acc;
+    osum[grp][d] = acc;
     __syncthreads();
-    if (tid < kHeadDim)
-        o[tid] = (osum[0][tid] + osum[1][tid]) / L;
+    if (tid < kHeadDim) {
+        float t = 0.0f;
+#pragma unroll
+        for (int g = 0; g < kMergeGroups; ++g)
+            t += osum[g][tid];
+        o[tid] = t / L;
+    }
     fwht_rows(o, 1, a.log_b);
     if (tid < kHeadDim) {
         const float v = o[tid] * a.rb;
@@ -417,7 +589,7 @@ hipError_t launch_g(const AttnArgs &aa, hipStream_t st)
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(attn_merge_kernel, dim3(aa.q_heads), dim3(kMergeThreads),
-                       (size_t)aa.nparts * sizeof(float), st, aa);
+                       (size_t)aa.nws * sizeof(float), st, aa);
     return hipGetLastError();
 }
 
@@ -425,7 +597,7 @@ hipError_t launch_g(const AttnArgs &aa, hipStream_t st)
 
 size_t attention_workspace(int q_heads, int kv_heads, int64_t tokens)
 {
-    return (size_t)q_heads * parts_for(kv_heads, tokens) * kPartStride * sizeof(float);
+    return (size_t)q_heads * (parts_for(kv_heads, tokens) / kWaves) * kPartStride * sizeof(float);
 }
 
 hipError_t launch_attention(const AttnRequest &r)
@@ -446,12 +618,13 @@ hipError_t launch_attention(const AttnRequest &r)
     aa.q_heads = r.q_heads;
     aa.kv_heads = r.kv_heads;
     aa.nparts = parts_for(r.kv_heads, r.tokens);
+    aa.nws = aa.nparts / kWaves;
     int lb = 0;
     while ((1 << lb) < r.b)
         ++lb;
     aa.log_b = lb;
     aa.rb = (float)(1.0 / __builtin_sqrt((double)r.b));
-    aa.qscale = (float)(1.0 / (__builtin_sqrt((double)r.b) * __builtin_sqrt((double)kHeadDim)));
+    aa.qscale = (float)(1.4426950408889634 / (__builtin_sqrt((double)r.b) * __builtin_sqrt((double)kHeadDim)));
     switch (r.q_heads / r.kv_heads) {
     case 1: return launch_g<1>(aa, r.stream);
     case 2: return launch_g<2>(aa, r.stream);

@@ -15,6 +15,17 @@
 
 namespace hq {
 
+// Buffer resource over `bytes` bytes at the wave-uniform address p (raw
+// buffer, 32-bit elements; dword 3 as every gfx9 target wants it).  The
+// base lives in scalar registers, so the lane's offset is the only vector
+// part of an address; a load whose lane offset is at or past `bytes` returns
+// 0 without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
+}
+constexpr int kNonTemporal = 2;  // buffer cache-policy bit: nt
+
 // 1.5 * 2^23: adding it to a value v with |v| < 2^22 leaves round_half_even(v)
 // in the low mantissa bits, because the sum's unit in the last place is 1.
 constexpr float kRoundMagic = 12582912.0f;

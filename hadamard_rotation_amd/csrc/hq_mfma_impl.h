@@ -54,15 +54,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Buffer resource over `bytes` bytes at the wave-uniform address p (raw
-// buffer, 32-bit elements; dword 3 as every gfx9 target wants it).  The
-// base lives in scalar registers, so the lane's offset is the only vector
-// part of an address.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
-}
-constexpr int kNonTemporal = 2;  // buffer cache-policy bit: nt
 
 struct MfmaArgs {
     const void *x;
