@@ -66,13 +66,24 @@ struct AttnArgs {
     float qscale;       // log2(e) / (sqrt(b) * sqrt(n)): rotation, softmax scale, base 2
 };
 
-__device__ __forceinline__ float load_q(const void *p, int dtype, int64_t i)
+// The query entries and sign bits this thread rotates: element
+// threadIdx.x + 256 r of the kv head's G rows, loads issued back to back.
+template <int DT, int G, int R>
+__device__ __forceinline__ void load_q_rows(const AttnArgs &a, int kh, float (&qv)[R], int (&sv)[R])
 {
-    if (dtype == kF32)
-        return ((const float *)p)[i];
-    if (dtype == kBF16)
-        return bf16_to_f32(((const uint16_t *)p)[i]);
-    return f16_to_f32(((const uint16_t *)p)[i]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = threadIdx.x + 64 * kWaves * r;
+        const int ic = i < G * kHeadDim ? i : G * kHeadDim - 1;
+        const int64_t e = (int64_t)kh * G * kHeadDim + ic;
+        if constexpr (DT == kF32)
+            qv[r] = ((const float *)a.q)[e];
+        else if constexpr (DT == kBF16)
+            qv[r] = bf16_to_f32(((const uint16_t *)a.q)[e]);
+        else
+            qv[r] = f16_to_f32(((const uint16_t *)a.q)[e]);
+        sv[r] = a.s[ic & (kHeadDim - 1)];
+    }
 }
 
 // Fast Walsh-Hadamard transform of `rows` rows of 128 floats in LDS, in
@@ -152,14 +163,34 @@ __device__ __forceinline__ void bcast_row(float v, float (&ks)[8], float (&vs)[8
 
 constexpr float kGrowLog2 = 5.0f;  // scores are in base 2: a factor of 32
 
+// 4-bit codes -> exact f16 pairs.  Of the 8 nibbles of a code word,
+// (i, i + 4) share a 16-bit-lane pair: nibbles 0/4 and 2/6 (after >> 8) sit
+// in bits 0-3 of each half, where 0x6400 | (nib ^ 8) is 1032 + q; nibbles 1/5
+// and 3/7 sit in bits 4-7, where 0x6400 | ((nib ^ 8) << 4) is 1152 + 16 q.
+// The offsets are subtracted in f16, exactly; the factor 16 of the odd
+// nibbles is undone on the other operand or on the result.
+__device__ __forceinline__ uint32_t codes_lo(uint32_t x)  // bits 0-3 of each half -> q
+{
+    const f16x2 h = __builtin_bit_cast(f16x2, (x & 0x000F000Fu) ^ 0x64086408u) +
+                    (f16x2){(_Float16)-1032.0f, (_Float16)-1032.0f};
+    return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ uint32_t codes_hi(uint32_t x)  // bits 4-7 of each half -> 16 q
+{
+    const f16x2 h = __builtin_bit_cast(f16x2, (x & 0x00F000F0u) ^ 0x64806480u) +
+                    (f16x2){(_Float16)-1152.0f, (_Float16)-1152.0f};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
 // G: query heads per kv head (1, 2, 4 or 8)
 template <int G>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))) void attn_part_kernel(AttnArgs a)
 {
     __shared__ float qrot[G * kHeadDim];
-    __shared__ float qpow[G];              // power of two applied to each query row
+    __shared__ float qpow[G];                  // power of two applied to each query row
     __shared__ float po[kWaves][G][kHeadDim];  // each wave's partial accumulators
     __shared__ float pm[kWaves][G], pl[kWaves][G];
+    __shared__ u32x4 bq_lds[2][kWaves][64];    // query operands: [hi/lo][chunk][lane]
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -168,68 +199,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     const int kh = blockIdx.y;
     const int part = blockIdx.x * kWaves + wave;
 
-    // ---- the G query rows of this kv head, rotated and scaled, in LDS; the
-    // scale includes log2(e), so scores come out in base 2 and exp2 serves
-    for (int i = threadIdx.x; i < G * kHeadDim; i += blockDim.x) {
-        const int g = i / kHeadDim, d = i % kHeadDim;
-        const float v = load_q(a.q, a.q_dtype, (int64_t)(kh * G + g) * kHeadDim + d);
-        qrot[i] = a.s[d] < 0 ? -v : v;
-    }
-    fwht_rows(qrot, G, a.log_b);
-    if (threadIdx.x < G) {
-        float mx = 0.0f;
-        for (int d = 0; d < kHeadDim; ++d)
-            mx = fmaxf(mx, fabsf(qrot[threadIdx.x * kHeadDim + d] * a.qscale));
-        int e = 0;
-        (void)frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
-        qpow[threadIdx.x] = mx > 0.0f ? ldexpf(1.0f, 10 - e) : 1.0f;
-    }
-    __syncthreads();
-
-    // ---- B operands: column n < G holds query row n (hi halves in bqh, lo
-    // halves in bql), other columns zero.  For chunk c lane l holds
-    // k = 8*(l >> 4) + j, dimension 32*(l >> 4) + 8c + j (the same
-    // permutation the key codes use).
-    u32x4 bqh[4], bql[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int d = 32 * rg + 8 * c + 2 * p;
-            float x0 = 0.0f, x1 = 0.0f;
-            if (l16 < G) {
-                x0 = qrot[l16 * kHeadDim + d] * a.qscale * qpow[l16];
-                x1 = qrot[l16 * kHeadDim + d + 1] * a.qscale * qpow[l16];
-            }
-            uint32_t wh, wl;
-            split_f16x2(x0, x1, wh, wl);
-            bqh[c][p] = wh;
-            bql[c][p] = wl;
-        }
-    }
-    const float unscale = l16 < G ? 1.0f / qpow[l16] : 1.0f;  // exact: a power of two
-
     // ---- token range of this wave
     const int64_t b0 = a.blocks * part / a.nparts;
     const int64_t b1 = a.blocks * (part + 1) / a.nparts;
     const int64_t lim = a.tokens < b1 * 16 ? a.tokens : b1 * 16;  // first token not ours
-
-    // Running softmax state per head (score lanes l16 < G, the same in every
-    // row group).  The maximum only moves when a block beats it by more than
-    // ln 32, so the weights exp(s - m_run) stay below 32 and the accumulators
-    // are rescaled rarely.  The weights also carry the power of two `wscale`
-    // that puts the largest value scale seen so far in [512, 1024): with the
-    // bound on exp that keeps every weight below 32768, inside f16.
-    float m_run = -INFINITY, l_run = 0.0f;
-    float wscale = 0.0f;  // 0 until a nonzero value scale is seen
-    int wexp = 0;         // log2(wscale) once it is set
-    // Weighted value sums: product ng covers dimensions 8*j + ng (column j);
-    // row m < G holds the hi halves of head m's weights, row G + m the lo
-    // halves.  Lane (l16, rg) holds rows 4*rg .. 4*rg+3 of column l16.
-    f32x4 acc[8];
-#pragma unroll
-    for (int ng = 0; ng < 8; ++ng)
-        acc[ng] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
     // Raw data of two 16-token blocks.  Value element j is token
     // 4*rg + (j & 3) of block j >> 2: the tokens whose scores the lane holds,
@@ -238,8 +211,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     // lane l16 = 8 + j its value scale; DPP broadcasts hand them out per row.
     struct Pair {
         u32x4 k[2];      // key codes: token l16 of each block, dimensions 32*rg .. +31
+        uint32_t s;      // one scale, raw bits (f16 or f32)
         uint32_t v[8];   // value codes: dimensions 8*l16 .. +7
-        float s;         // one scale
     };
     // Loads go through buffer descriptors rebased to the step's first row
     // and cut off at the first row of a token >= lim: rows past the wave's
@@ -253,47 +226,147 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         r = r < 0 ? 0 : r;
         return (int)(r < 0x7FFFFFFF ? r : 0x7FFFFFFF);
     };
-    int ok_[2], ov_[8];
+    // (the two blocks of a step have descriptors of their own, so they share
+    // these offsets)
+    const int ok_ = (l16 * kv + kh) * (kHeadDim / 2) + 16 * rg;
+    int ov_[4];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        ok_[b] = ((16 * b + l16) * kv + kh) * (kHeadDim / 2) + 16 * rg;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            ov_[4 * b + i] = ((16 * b + 4 * rg + i) * kv + kh) * (kHeadDim / 2) + 4 * l16;
-    }
+    for (int i = 0; i < 4; ++i)
+        ov_[i] = ((4 * rg + i) * kv + kh) * (kHeadDim / 2) + 4 * l16;
     const int sj = l16 & 7;
     const int srow = (16 * (sj >> 2) + 4 * rg + (sj & 3)) * kv + kh;
-    // the other half of each row asks past every span: it reads 0
-    const int oks = l16 < 8 ? srow * ssz : 0x7FFFFFFF;
-    const int ovs = l16 < 8 ? 0x7FFFFFFF : srow * ssz;
+    const int os_ = srow * ssz;
+    // Loads are issued in the order a step uses them (key codes, scales,
+    // value codes), and nothing combines their results here, so waits on the
+    // in-order load counter cover only what a step is about to use.
     auto load_pair = [&](int64_t blk, Pair &r) {
         const int64_t row0 = blk * 16 * kv;
-        const int cb = span(row0, kHeadDim / 2);
-        const auto rk = rsrc(a.k_codes + row0 * (kHeadDim / 2), cb);
-        const auto rv = rsrc(a.v_codes + row0 * (kHeadDim / 2), cb);
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-            r.k[b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ok_[b], 0, kNonTemporal));
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(rv, ov_[j], 0, kNonTemporal);
+        const int64_t row1 = row0 + 16 * kv;
+        const int cb0 = span(row0, kHeadDim / 2), cb1 = span(row1, kHeadDim / 2);
+        const auto rk0 = rsrc(a.k_codes + row0 * (kHeadDim / 2), cb0);
+        const auto rk1 = rsrc(a.k_codes + row1 * (kHeadDim / 2), cb1);
+        const auto rv0 = rsrc(a.v_codes + row0 * (kHeadDim / 2), cb0);
+        const auto rv1 = rsrc(a.v_codes + row1 * (kHeadDim / 2), cb1);
+        r.k[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk0, ok_, 0, kNonTemporal));
+        r.k[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk1, ok_, 0, kNonTemporal));
         const int sb = span(row0, ssz);
         const auto rks = rsrc((const uint8_t *)a.k_scales + row0 * ssz, sb);
         const auto rvs = rsrc((const uint8_t *)a.v_scales + row0 * ssz, sb);
-        if (a.scale_f16) {
-            const uint32_t h = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rks, oks, 0, 0) |
-                               (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rvs, ovs, 0, 0);
-            r.s = f16_to_f32((uint16_t)h);
-        } else {
-            r.s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, oks, 0, 0) |
-                                  __builtin_amdgcn_raw_buffer_load_b32(rvs, ovs, 0, 0));
-        }
-    };
-    // lane's token offsets within a step (element j)
-    int tj[8];
+        // lanes 0-7 of a row load key scales, lanes 8-15 value scales, into
+        // the same register
+        if (l16 < 8)
+            r.s = a.scale_f16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rks, os_, 0, 0)
+                              : __builtin_amdgcn_raw_buffer_load_b32(rks, os_, 0, 0);
+        else
+            r.s = a.scale_f16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rvs, os_, 0, 0)
+                              : __builtin_amdgcn_raw_buffer_load_b32(rvs, os_, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        tj[j] = 16 * (j >> 2) + 4 * rg + (j & 3);
+        for (int i = 0; i < 4; ++i)
+            r.v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv0, ov_[i], 0, kNonTemporal);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r.v[4 + i] = __builtin_amdgcn_raw_buffer_load_b32(rv1, ov_[i], 0, kNonTemporal);
+    };
+
+    // ---- the G query rows of this kv head, rotated and scaled, in LDS; the
+    // scale includes log2(e), so scores come out in base 2 and exp2 serves.
+    // Their loads are issued first and all at once; the first two steps'
+    // codes follow and stay in flight while the rows are prepared.
+    constexpr int kQPer = (G * kHeadDim + 64 * kWaves - 1) / (64 * kWaves);
+    float qv[kQPer];
+    int sv[kQPer];
+    if (a.q_dtype == kF32)
+        load_q_rows<kF32, G, kQPer>(a, kh, qv, sv);
+    else if (a.q_dtype == kBF16)
+        load_q_rows<kBF16, G, kQPer>(a, kh, qv, sv);
+    else
+        load_q_rows<kF16, G, kQPer>(a, kh, qv, sv);
+    Pair pa, pb;
+    if (b0 < b1) {  // the first two steps' data, in flight during the set-up
+        load_pair(b0, pa);
+        load_pair(b0 + 2, pb);  // past the range: reads 0
+    }
+#pragma unroll
+    for (int r = 0; r < kQPer; ++r) {
+        const int i = threadIdx.x + 64 * kWaves * r;
+        if (i < G * kHeadDim)
+            qrot[i] = sv[r] < 0 ? -qv[r] : qv[r];
+    }
+    fwht_rows(qrot, G, a.log_b);
+    for (int g = wave; g < G; g += kWaves) {  // row maxima, one wave per row
+        float mx = fmaxf(fabsf(qrot[g * kHeadDim + lane]), fabsf(qrot[g * kHeadDim + 64 + lane]));
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        mx *= a.qscale;
+        if (lane == 0) {
+            int e = 0;
+            (void)frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
+            qpow[g] = mx > 0.0f ? ldexpf(1.0f, 10 - e) : 1.0f;
+        }
+    }
+    __syncthreads();
+
+    // ---- B operands of the scores: column n < 2G holds query row n mod G
+    // (hi halves in bqh, lo halves in bql; the copies in columns G..2G-1 give
+    // the lanes that form the lo halves of the weights their own scores),
+    // other columns zero.  For chunk c, lane l holds k = 8*(l >> 4) + 2p + e,
+    // dimension 32*(l >> 4) + 8c + p + 4e: the order the key codes unpack in.
+    // Odd p pairs with key codes carrying a factor 16, so those entries are
+    // divided by 16 here.
+    // Every wave of the workgroup needs the same operands: wave c builds
+    // chunk c into LDS and all of them read the four chunks back.
+    static_assert(kWaves == 4, "one chunk of the query operands per wave");
+    const int gq = l16 & (G - 1);
+    const bool qcol = l16 < 2 * G;
+    {
+        u32x4 h, l;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int d = 32 * rg + 8 * wave + p;
+            float x0 = 0.0f, x1 = 0.0f;
+            if (qcol) {
+                const float sc = a.qscale * qpow[gq] * ((p & 1) ? 0.0625f : 1.0f);
+                x0 = qrot[gq * kHeadDim + d] * sc;
+                x1 = qrot[gq * kHeadDim + d + 4] * sc;
+            }
+            uint32_t wh, wl;
+            split_f16x2(x0, x1, wh, wl);
+            h[p] = wh;
+            l[p] = wl;
+        }
+        bq_lds[0][wave][lane] = h;
+        bq_lds[1][wave][lane] = l;
+    }
+    __syncthreads();
+    u32x4 bqh[4], bql[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        bqh[c] = bq_lds[0][c][lane];
+        bql[c] = bq_lds[1][c][lane];
+    }
+    const float unscale = qcol ? 1.0f / qpow[gq] : 1.0f;  // exact: a power of two
+
+    // Running softmax state per head (score lanes l16 < 2G, the same in every
+    // row group and in the two copies of a head).  The maximum only moves
+    // when a step beats it by more than 5 (base 2), so exp2(s - m_run) stays
+    // below 32 and the accumulators are rescaled rarely.  The weights also
+    // carry the power of two 2^wexp that puts the largest value scale seen so
+    // far in [512, 1024): with the bound on exp2 every weight stays below
+    // 32768, inside f16.  l_run and the accumulators are kept in the same
+    // units (times 2^wexp); the partial's maximum is stored as m_run - wexp,
+    // which makes partials with different wexp merge correctly.
+    float m_run = -INFINITY, l_run = 0.0f;
+    int wexp = 0;
+    bool wset = false;  // wave-uniform: a nonzero value scale has been seen
+    // Weighted value sums: product ng covers dimensions 8*j + ng (column j),
+    // odd ng times 16; row m < G holds the hi halves of head m's weights, row
+    // G + m the lo halves.  Lane (l16, rg) holds rows 4*rg .. 4*rg+3 of
+    // column l16.
+    f32x4 acc[8];
+#pragma unroll
+    for (int ng = 0; ng < 8; ++ng)
+        acc[ng] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
     auto step = [&](const Pair &cur, int64_t blk) {
         // -------------------------------------------------------- scores
@@ -301,38 +374,31 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         d[0] = d[1] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
+            const u32x4 bh = bqh[c], bl = bql[c];
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
-                // 8 key codes (dimension 32*rg + 8c + j) -> exact f16: 0x6400 |
-                // (nib ^ 8) is 1032 + q, and 1032 is subtracted in f16
                 const uint32_t w = cur.k[b][c];
-                const uint32_t w4 = w >> 4;
-                u32x4 ak;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const uint32_t sel = (uint32_t)p | (0x0Cu << 8) | ((uint32_t)(4 + p) << 16) | (0x0Cu << 24);
-                    const uint32_t x = (__builtin_amdgcn_perm(w4, w, sel) & 0x000F000Fu) ^ 0x64086408u;
-                    const f16x2 h = __builtin_bit_cast(f16x2, x) + (f16x2){(_Float16)-1032.0f, (_Float16)-1032.0f};
-                    ak[p] = __builtin_bit_cast(uint32_t, h);
-                }
+                const uint32_t w8 = w >> 8;
+                const u32x4 ak = {codes_lo(w), codes_hi(w), codes_lo(w8), codes_hi(w8)};
                 d[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ak),
-                                                              __builtin_bit_cast(f16x8, bqh[c]), d[b], 0, 0, 0);
+                                                              __builtin_bit_cast(f16x8, bh), d[b], 0, 0, 0);
                 d[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ak),
-                                                              __builtin_bit_cast(f16x8, bql[c]), d[b], 0, 0, 0);
+                                                              __builtin_bit_cast(f16x8, bl), d[b], 0, 0, 0);
             }
         }
+        const float sl = a.scale_f16 ? f16_to_f32((uint16_t)cur.s) : __uint_as_float(cur.s);
         float ks[8], vs[8];
-        bcast_row<0>(cur.s, ks, vs);
-        // lane l16 < G: scores of head l16 for the lane's 8 tokens
+        bcast_row<0>(sl, ks, vs);
+        // lane l16 < 2G: scores of head l16 mod G for the lane's 8 tokens
         float sc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             sc[j] = d[j >> 2][j & 3] * unscale * ks[j];
         if (blk * 16 + 32 > lim) {  // the last step: tokens past the range
-            const int left = (int)(lim - blk * 16);
+            const int left = (int)(lim - blk * 16) - 4 * rg;  // against the lane's token offsets
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                sc[j] = tj[j] < left ? sc[j] : -INFINITY;
+                sc[j] = 16 * (j >> 2) + (j & 3) < left ? sc[j] : -INFINITY;
         }
         // ------------------------------------------------- online softmax
         float mb = sc[0], vm = vs[0];
@@ -343,58 +409,56 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         }
         mb = xmax16_32(mb);
         vm = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, xmax16_32(vm))));
-        const bool grow = l16 < G && mb > m_run + kGrowLog2;
-        const bool need_e = vm * wscale >= 1024.0f || (wscale == 0.0f && vm > 0.0f);
+        const bool grow = qcol && mb > m_run + kGrowLog2;
+        const bool need_e = wset ? vm * ldexpf(1.0f, wexp) >= 1024.0f : vm > 0.0f;
         if (__builtin_amdgcn_ballot_w64(grow) != 0 || need_e) {
             const float m_new = grow ? mb : m_run;
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // 0 on the first block
+            float f = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // 0 on the first step
             m_run = m_new;
-            l_run *= alpha;
-            float ratio = 1.0f;
             if (need_e) {
                 int e = 0;
                 (void)frexpf(vm, &e);  // vm = f * 2^e, f in [0.5, 1)
-                const int enew = 10 - e < 127 ? 10 - e : 127;
-                ratio = wscale > 0.0f ? ldexpf(1.0f, enew - wexp) : 0.0f;  // accumulators are 0 while wscale is
+                int enew = 10 - e;
+                enew = enew < 90 ? enew : 90;  // keeps l_run * 2^wexp finite
+                f *= ldexpf(1.0f, enew - wexp);
                 wexp = enew;
-                wscale = ldexpf(1.0f, enew);
+                wset = true;
             }
+            l_run *= f;
             float al[G];
 #pragma unroll
             for (int g = 0; g < G; ++g)
-                al[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), g)) * ratio;
+                al[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), g));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 // row 4*rg + i belongs to head (4*rg + i) mod G
-                float f;
+                float fr;
                 if constexpr (G == 8)
-                    f = (rg & 1) ? al[4 + i] : al[i];
+                    fr = (rg & 1) ? al[4 + i] : al[i];
                 else
-                    f = al[i % G];
+                    fr = al[i % G];
 #pragma unroll
                 for (int ng = 0; ng < 8; ++ng)
-                    acc[ng][i] *= f;
+                    acc[ng][i] *= fr;
             }
         }
+        const float mw = m_run - (float)wexp;  // exp2(s - mw) = exp2(s - m_run) * 2^wexp
         float pw[8], ps = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            pw[j] = __builtin_amdgcn_exp2f(sc[j] - m_run);
+            pw[j] = __builtin_amdgcn_exp2f(sc[j] - mw);
             ps += pw[j];
         }
         ps = xsum16_32(ps);
         l_run += ps;
         // ------------------------------ A operand: weights as hi/lo f16 rows
+        // (lanes l16 >= 2G feed rows that are never read)
         u32x4 aw;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const float w0 = vs[2 * p] * wscale * pw[2 * p];
-            const float w1 = vs[2 * p + 1] * wscale * pw[2 * p + 1];
             uint32_t hw, lw;
-            split_f16x2(w0, w1, hw, lw);
-            // lanes G .. 2G-1 of each row take the lo halves of lanes 0 .. G-1
-            const uint32_t lsh = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lw, 0x110 + G, 0xf, 0xf, false);
-            aw[p] = l16 < G ? hw : (l16 < 2 * G ? lsh : 0u);
+            split_f16x2(pw[2 * p] * vs[2 * p], pw[2 * p + 1] * vs[2 * p + 1], hw, lw);
+            aw[p] = l16 < G ? hw : lw;
         }
         // ------------------------------------------- weighted value codes
 #pragma unroll
@@ -406,43 +470,36 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
                 const uint32_t sel = (uint32_t)k | (0x0Cu << 8) | ((uint32_t)(4 + k) << 16) | (0x0Cu << 24);
                 x[p] = __builtin_amdgcn_perm(cur.v[2 * p + 1], cur.v[2 * p], sel);
             }
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                // dimension 8*l16 + 2k + h: the low (h = 0) or high nibble
-                u32x4 bv;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const uint32_t y = ((h ? x[p] >> 4 : x[p]) & 0x000F000Fu) ^ 0x64086408u;
-                    const f16x2 c = __builtin_bit_cast(f16x2, y) + (f16x2){(_Float16)-1032.0f, (_Float16)-1032.0f};
-                    bv[p] = __builtin_bit_cast(uint32_t, c);
-                }
-                acc[2 * k + h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aw),
-                                                                        __builtin_bit_cast(f16x8, bv),
-                                                                        acc[2 * k + h], 0, 0, 0);
-            }
+            // dimension 8*l16 + 2k (low nibbles) and 8*l16 + 2k + 1 (high, times 16)
+            const u32x4 bv0 = {codes_lo(x[0]), codes_lo(x[1]), codes_lo(x[2]), codes_lo(x[3])};
+            const u32x4 bv1 = {codes_hi(x[0]), codes_hi(x[1]), codes_hi(x[2]), codes_hi(x[3])};
+            acc[2 * k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aw),
+                                                                __builtin_bit_cast(f16x8, bv0),
+                                                                acc[2 * k], 0, 0, 0);
+            acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aw),
+                                                                    __builtin_bit_cast(f16x8, bv1),
+                                                                    acc[2 * k + 1], 0, 0, 0);
         }
     };
 
-    // two register sets, alternating, so no step copies its data
-    Pair pa, pb;
+    // two register sets, alternating, so no step copies its data: a set is
+    // refilled with the step after next as soon as its step is done
     if (b0 < b1) {
-        load_pair(b0, pa);
         for (int64_t blk = b0;;) {
-            load_pair(blk + 2, pb);  // past the range: reads 0
             step(pa, blk);
             blk += 2;
             if (blk >= b1)
                 break;
-            load_pair(blk + 2, pa);
+            load_pair(blk + 2, pa);  // past the range: reads 0
             step(pb, blk);
             blk += 2;
             if (blk >= b1)
                 break;
+            load_pair(blk + 2, pb);
         }
     }
 
-    // ---- partial of this wave: add the lo rows to the hi rows, undo wscale
-    const float inv = wscale > 0.0f ? 1.0f / wscale : 0.0f;  // exact: a power of two
+    // ---- partial of this wave: add the lo rows to the hi rows
     float o[4][8];  // [row i][product ng]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -457,7 +514,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
                 v = xsum16(acc[ng][i]);
             else
                 v = xsum32(acc[ng][i]);
-            o[i][ng] = v * inv;
+            o[i][ng] = v;
         }
     }
     // row 4*rg + i < G now holds head 4*rg + i: the wave's partials go to
@@ -472,7 +529,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         }
     }
     if (lane < G) {
-        pm[wave][lane] = m_run;
+        pm[wave][lane] = m_run - (float)wexp;
         pl[wave][lane] = l_run;
     }
     __syncthreads();
@@ -491,7 +548,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
             O = __builtin_fmaf(e, po[w][g][dd], O);
         }
         float *dst = a.ws + ((int64_t)(kh * G + g) * a.nws + blockIdx.x) * kPartStride;
-        dst[dd] = O;
+        dst[dd] = (dd & 1) ? O * 0.0625f : O;  // odd dimensions were summed times 16
         if (dd == 0) {
             dst[kHeadDim] = M;
             dst[kHeadDim + 1] = L;
