@@ -559,10 +559,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
 // One workgroup of 1024 threads per query head: merge the partials (the
 // largest maximum, the rescaled sums, the rescaled accumulators), rotate the
 // result back, store.  exp2(m_p - M) of every partial is kept in LDS; eight
-// groups of 128 threads take every eighth partial, so each thread has a
-// dozen or so independent loads in flight.
+// groups of 128 threads take every eighth partial.
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeGroups = kMergeThreads / kHeadDim;
+constexpr int kMergeChunk = 16;  // partials per thread whose loads go out at once
 
 __device__ float block_reduce(float v, float *red, bool is_max)
 {
@@ -589,24 +589,42 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a)
     const int tid = threadIdx.x;
     const int h = blockIdx.x;
     const float *base = a.ws + (int64_t)h * a.nws * kPartStride;
-    float m = -INFINITY;
-    for (int p = tid; p < a.nws; p += kMergeThreads)
+    const int d = tid & (kHeadDim - 1), grp = tid / kHeadDim;
+    // Every load of the first kMergeChunk partials per thread group is issued
+    // before anything waits: one round trip for up to 8 * kMergeChunk
+    // partials per head.
+    float ov[kMergeChunk];
+#pragma unroll
+    for (int r = 0; r < kMergeChunk; ++r) {
+        const int p = grp + kMergeGroups * r;
+        ov[r] = p < a.nws ? base[(int64_t)p * kPartStride + d] : 0.0f;
+    }
+    float m = -INFINITY, pl = 0.0f;
+    if (tid < a.nws) {
+        m = base[(int64_t)tid * kPartStride + kHeadDim];
+        pl = base[(int64_t)tid * kPartStride + kHeadDim + 1];
+    }
+    for (int p = tid + kMergeThreads; p < a.nws; p += kMergeThreads)
         m = fmaxf(m, base[(int64_t)p * kPartStride + kHeadDim]);
     const float M = block_reduce(m, red, true);
     float l = 0.0f;
     for (int p = tid; p < a.nws; p += kMergeThreads) {
-        const float *pp = base + (int64_t)p * kPartStride;
-        const float pl = pp[kHeadDim + 1];
+        const float pm = p == tid ? m : base[(int64_t)p * kPartStride + kHeadDim];
+        const float pp = p == tid ? pl : base[(int64_t)p * kPartStride + kHeadDim + 1];
         // partials of empty token ranges (sum 0) carry nothing
-        const float e = pl > 0.0f ? __builtin_amdgcn_exp2f(pp[kHeadDim] - M) : 0.0f;
+        const float e = pp > 0.0f ? __builtin_amdgcn_exp2f(pm - M) : 0.0f;
         e_part[p] = e;
-        l += e * pl;
+        l = __builtin_fmaf(e, pp, l);
     }
     const float L = block_reduce(l, red, false);  // also orders the e_part writes
-    const int d = tid & (kHeadDim - 1), grp = tid / kHeadDim;
     float acc = 0.0f;
-#pragma unroll 8
-    for (int p = grp; p < a.nws; p += kMergeGroups)
+#pragma unroll
+    for (int r = 0; r < kMergeChunk; ++r) {
+        const int p = grp + kMergeGroups * r;
+        if (p < a.nws)
+            acc = __builtin_fmaf(e_part[p], ov[r], acc);
+    }
+    for (int p = grp + kMergeGroups * kMergeChunk; p < a.nws; p += kMergeGroups)
         acc = __builtin_fmaf(e_part[p], base[(int64_t)p * kPartStride + d], acc);
     osum[grp][d] = acc;
     __syncthreads();
