@@ -37,9 +37,11 @@
  *   two's complement ([QT] 2.2 gives the 4x size reduction; the nibble
  *   order is this library's convention).
  *   Inverse: v = q * scale_stored (the scale of the element's group);
- *        x_hat_blk = (v_blk . H_b / sqrt(b)) * s
- *        (the normalised H is orthogonal and symmetric, so it is its own
- *         inverse: [MS] principle, [HQA] 1).
+ *        x_hat_blk = (v_blk . H_b^T / sqrt(b)) * s
+ *        (the normalised H is orthogonal, so its transpose undoes it: [MS]
+ *         principle, [HQA] 1; the Sylvester matrix is also symmetric).
+ *   Orders that are not a power of two: H_b = H_k (x) H_(b/k) with H_k from
+ *   Paley's first construction (see hqo_hadamard_split / hqo_paley).
  *
  * Parity pins for every function are in tests/test_oracle_pins.py.
  */
@@ -136,7 +138,7 @@ int hqo_decode(const void *src, int dtype, int64_t count, double *dst)
  * entries +1/-1, by repeated doubling H_2m = [[H_m, H_m], [H_m, -H_m]]
  * ([RQ] 2.1 prints H_2 and H_4 = H_2 (x) H_2; [HQA] 1 builds the same
  * recursion).  Returns 0, or -1 if b is not a power of two. */
-int hqo_hadamard(int b, int8_t *H)
+static int sylvester(int b, int8_t *H)
 {
     if (!is_pow2(b) || !H)
         return -1;
@@ -154,26 +156,227 @@ int hqo_hadamard(int b, int8_t *H)
     return 0;
 }
 
-/* Builds Ht[i][j] = H[j][i] so that the matrix-vector product below walks
- * memory contiguously.  (The Sylvester matrix is symmetric, but the oracle
- * does not rely on that: it transposes explicitly.) */
-static int8_t *make_ht(int b)
+/* ------------------------------------- Paley matrices (non-power-of-two) */
+
+/* Widths that are not a power of two ([MS] YAML table: the block size is a
+ * power of two or the full width; [RQ] 2.1: H_4 = H_2 (x) H_2, larger orders
+ * by Kronecker products).  Reading: H_n = H_k (x) H_(n/k), where n/k is a
+ * power of two and H_k is Paley's first construction of order k = q + 1,
+ * q = p^e a prime power with q = 3 (mod 4), k the smallest such order of the
+ * form (odd part of n) * 2^a.  Element (i, j) of the Kronecker product has
+ * index i * (n/k) + j.
+ *
+ * Paley's first construction: with GF(q) and its quadratic character chi
+ * (chi(0) = 0, chi(a) = 1 if a is a nonzero square, -1 otherwise), the
+ * Jacobsthal matrix Q[a][b] = chi(a - b) is skew-symmetric for q = 3 (mod 4)
+ * and H = I + [[0, 1^T], [-1, Q]] has H H^T = (q + 1) I.  Conventions this
+ * library fixes: GF(p^e) is GF(p)[x] modulo the monic irreducible polynomial
+ * x^e + c_(e-1) x^(e-1) + ... + c_0 with the smallest index
+ * c_0 + p c_1 + ... (e <= 3, where irreducible means "has no root"); an
+ * element c_0 + c_1 x + c_2 x^2 has index c_0 + p c_1 + p^2 c_2; row and
+ * column 0 of H belong to the extra point, row and column a + 1 to element a. */
+
+/* q = p^e with p prime; returns 0, or -1 if q is not a prime power. */
+static int prime_power(int q, int *p, int *e)
+{
+    if (q < 2)
+        return -1;
+    int f = 2;
+    while (q % f != 0)
+        ++f;
+    int r = q, k = 0;
+    while (r % f == 0) {
+        r /= f;
+        ++k;
+    }
+    if (r != 1)
+        return -1;
+    *p = f;
+    *e = k;
+    return 0;
+}
+
+static int ipow(int b, int e)
+{
+    int r = 1;
+    while (e-- > 0)
+        r *= b;
+    return r;
+}
+
+/* the e coefficients of an element / of the modulus, lowest first */
+static void digits(int a, int p, int e, int *c)
+{
+    for (int i = 0; i < e; ++i) {
+        c[i] = a % p;
+        a /= p;
+    }
+}
+
+static int undigits(const int *c, int p, int e)
+{
+    int a = 0;
+    for (int i = e - 1; i >= 0; --i)
+        a = a * p + c[i];
+    return a;
+}
+
+/* a * b in GF(p^e) = GF(p)[x] / (x^e + mod[e-1] x^(e-1) + ... + mod[0]) */
+static int gf_mul(int a, int b, int p, int e, const int *mod)
+{
+    int ca[3], cb[3], prod[5] = {0, 0, 0, 0, 0};
+    digits(a, p, e, ca);
+    digits(b, p, e, cb);
+    for (int i = 0; i < e; ++i)
+        for (int j = 0; j < e; ++j)
+            prod[i + j] = (prod[i + j] + ca[i] * cb[j]) % p;
+    /* x^d = x^(d-e) * x^e and x^e = -(mod[e-1] x^(e-1) + ... + mod[0]) */
+    for (int d = 2 * e - 2; d >= e; --d) {
+        int c = prod[d];
+        prod[d] = 0;
+        for (int i = 0; i < e; ++i)
+            prod[d - e + i] = ((prod[d - e + i] - c * mod[i]) % p + p) % p;
+    }
+    return undigits(prod, p, e);
+}
+
+static int gf_sub(int a, int b, int p, int e)
+{
+    int ca[3], cb[3], c[3];
+    digits(a, p, e, ca);
+    digits(b, p, e, cb);
+    for (int i = 0; i < e; ++i)
+        c[i] = ((ca[i] - cb[i]) % p + p) % p;
+    return undigits(c, p, e);
+}
+
+/* the modulus of GF(p^e): the first monic polynomial of degree e (e <= 3)
+ * without a root in GF(p), by the index of its lower coefficients */
+static int gf_modulus(int p, int e, int *mod)
+{
+    if (e == 1) {
+        mod[0] = 0; /* GF(p): arithmetic mod p; x^1 = 0 never used */
+        return 0;
+    }
+    for (int c = 0; c < ipow(p, e); ++c) {
+        digits(c, p, e, mod);
+        int has_root = 0;
+        for (int r = 0; r < p && !has_root; ++r) {
+            int v = ipow(r, e) % p;
+            for (int i = 0; i < e; ++i)
+                v = (v + mod[i] * ipow(r, i)) % p;
+            has_root = v == 0;
+        }
+        if (!has_root)
+            return 0;
+    }
+    return -1;
+}
+
+/* Paley's first construction of order k (k - 1 = p^e = 3 mod 4, e <= 3):
+ * H (k*k, row-major, +1/-1).  Returns 0, or -1 if k is not such an order. */
+int hqo_paley(int k, int8_t *H)
+{
+    int q = k - 1, p = 0, e = 0, mod[3] = {0, 0, 0};
+    if (!H || prime_power(q, &p, &e) != 0 || q % 4 != 3 || e > 3 || gf_modulus(p, e, mod) != 0)
+        return -1;
+    int8_t *square = (int8_t *)calloc((size_t)q, 1);
+    if (!square)
+        return -1;
+    for (int a = 1; a < q; ++a)
+        square[e == 1 ? (int)((int64_t)a * a % q) : gf_mul(a, a, p, e, mod)] = 1;
+    for (int j = 0; j < k; ++j)
+        H[j] = 1; /* row of the extra point: 1 on the diagonal, 1 elsewhere */
+    for (int a = 0; a < q; ++a) {
+        int8_t *row = H + (int64_t)(a + 1) * k;
+        row[0] = -1;
+        for (int b = 0; b < q; ++b) {
+            int d = e == 1 ? ((a - b) % q + q) % q : gf_sub(a, b, p, e);
+            int chi = d == 0 ? 0 : (square[d] ? 1 : -1);
+            row[b + 1] = (int8_t)(chi + (a == b ? 1 : 0));
+        }
+    }
+    free(square);
+    return 0;
+}
+
+/* n = k * m2 as above (m2 a power of two, k a Paley order or k = 1 when n
+ * itself is a power of two).  Returns 0, or -1 when n has no such split. */
+int hqo_hadamard_split(int n, int *k, int *m2)
+{
+    if (n <= 0)
+        return -1;
+    if (is_pow2(n)) {
+        *k = 1;
+        *m2 = n;
+        return 0;
+    }
+    int odd = n, twos = 1;
+    while (odd % 2 == 0) {
+        odd /= 2;
+        twos *= 2;
+    }
+    for (int a = 1; a <= twos; a *= 2) {
+        int kk = odd * a, q = kk - 1, p = 0, e = 0, mod[3];
+        if (prime_power(q, &p, &e) == 0 && q % 4 == 3 && e <= 3 && gf_modulus(p, e, mod) == 0) {
+            *k = kk;
+            *m2 = twos / a;
+            return 0;
+        }
+    }
+    return -1;
+}
+
+/* The Hadamard matrix of order b this library rotates with: Sylvester for a
+ * power of two, H_k (x) H_(b/k) otherwise (see above).  H is b*b, row-major,
+ * +1/-1.  Returns 0, or -1 when b has no such matrix. */
+int hqo_hadamard(int b, int8_t *H)
+{
+    int k = 0, m2 = 0;
+    if (!H || hqo_hadamard_split(b, &k, &m2) != 0)
+        return -1;
+    if (k == 1)
+        return sylvester(b, H);
+    int8_t *P = (int8_t *)malloc((size_t)k * k);
+    int8_t *S = (int8_t *)malloc((size_t)m2 * m2);
+    int rc = -1;
+    if (P && S && hqo_paley(k, P) == 0 && sylvester(m2, S) == 0) {
+        for (int i = 0; i < k; ++i)
+            for (int j = 0; j < m2; ++j)
+                for (int i2 = 0; i2 < k; ++i2)
+                    for (int j2 = 0; j2 < m2; ++j2)
+                        H[((int64_t)i * m2 + j) * b + (int64_t)i2 * m2 + j2] =
+                            (int8_t)(P[(int64_t)i * k + i2] * S[(int64_t)j * m2 + j2]);
+        rc = 0;
+    }
+    free(P);
+    free(S);
+    return rc;
+}
+
+/* Builds H and Ht[i][j] = H[j][i].  The forward rotation u.H walks Ht
+ * contiguously; the inverse v.H^T walks H.  (The Sylvester matrix is
+ * symmetric and Paley matrices are not; the oracle transposes explicitly in
+ * both cases.) */
+static int make_mats(int b, int8_t **Hp, int8_t **Htp)
 {
     int8_t *H = (int8_t *)malloc((size_t)b * b);
     int8_t *Ht = (int8_t *)malloc((size_t)b * b);
     if (!H || !Ht || hqo_hadamard(b, H) != 0) {
         free(H);
         free(Ht);
-        return NULL;
+        return -1;
     }
     for (int i = 0; i < b; ++i)
         for (int j = 0; j < b; ++j)
             Ht[(int64_t)i * b + j] = H[(int64_t)j * b + i];
-    free(H);
-    return Ht;
+    *Hp = H;
+    *Htp = Ht;
+    return 0;
 }
 
-/* One row: out[kb+i] = sum_j (x[kb+j]*s[kb+j]) * H[j][i] / sqrt(b). */
+/* One row: out[kb+i] = sum_j (x[kb+j]*s[kb+j]) * M[i][j] / sqrt(b), with M
+ * = Ht for the forward rotation u.H and M = H for the inverse v.H^T. */
 static void rotate_row(const double *x, const int8_t *s, int n, int b,
                        const int8_t *Ht, double *u, double *out)
 {
@@ -269,7 +472,7 @@ typedef struct {
     int64_t rows;
     int n, b, group, bits, scale_dtype;
     const int8_t *s;
-    const int8_t *Ht;
+    const int8_t *H, *Ht;
     double *xr;
     uint8_t *codes;
     void *scales;
@@ -314,7 +517,7 @@ static void *worker(void *arg)
                                          r * ngroups + i / j->group);
                 xin[i] = (double)unpack_code(j->codes_in, r, n, j->bits, i) * sc;
             }
-            rotate_row(xin, ones, n, j->b, j->Ht, u, out);
+            rotate_row(xin, ones, n, j->b, j->H, u, out);
             for (int i = 0; i < n; ++i)
                 j->y[r * n + i] = j->s[i] < 0 ? -out[i] : out[i];
         }
@@ -337,9 +540,11 @@ static int run_jobs(job_t *tmpl, int threads)
         threads = 1;
     if ((int64_t)threads > tmpl->rows)
         threads = (int)tmpl->rows;
-    tmpl->Ht = make_ht(tmpl->b);
-    if (!tmpl->Ht)
+    int8_t *H = NULL, *Ht = NULL;
+    if (make_mats(tmpl->b, &H, &Ht) != 0)
         return -2;
+    tmpl->H = H;
+    tmpl->Ht = Ht;
     job_t *jobs = (job_t *)calloc((size_t)threads, sizeof(job_t));
     pthread_t *tids = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
     int rc = 0;
@@ -365,13 +570,15 @@ static int run_jobs(job_t *tmpl, int threads)
 out:
     free(jobs);
     free(tids);
-    free((void *)tmpl->Ht);
+    free(H);
+    free(Ht);
     return rc;
 }
 
 static int check_shape(int64_t rows, int n, int b, const int8_t *s)
 {
-    if (rows < 0 || n <= 0 || !is_pow2(b) || n % b != 0 || !s)
+    int k = 0, m2 = 0;
+    if (rows < 0 || n <= 0 || b <= 0 || n % b != 0 || !s || hqo_hadamard_split(b, &k, &m2) != 0)
         return -1;
     return 0;
 }
@@ -521,7 +728,9 @@ int hqo_decode_attention(const void *q, int q_dtype, int q_heads, int kv_heads, 
         return -1;
     if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !out)
         return -1;
-    int8_t *Ht = make_ht(b);
+    int8_t *H = NULL, *Ht = NULL;
+    if (make_mats(b, &H, &Ht) != 0)
+        return -2;
     double *qin = (double *)malloc(sizeof(double) * n);
     double *qr = (double *)malloc(sizeof(double) * n);
     double *u = (double *)malloc(sizeof(double) * n);
@@ -567,12 +776,13 @@ int hqo_decode_attention(const void *q, int q_dtype, int q_heads, int kv_heads, 
             for (int i = 0; i < n; ++i)
                 o[i] += w * (double)unpack_code(v_codes, row, n, bits, i);
         }
-        /* back to the query's space: o . H_b / sqrt(b), then * s */
-        rotate_row(o, ones, n, b, Ht, u, qin);
+        /* back to the query's space: o . H_b^T / sqrt(b), then * s */
+        rotate_row(o, ones, n, b, H, u, qin);
         for (int i = 0; i < n; ++i)
             out[(int64_t)h * n + i] = s[i] < 0 ? -qin[i] : qin[i];
     }
 done:
+    free(H);
     free(Ht);
     free(qin);
     free(qr);

@@ -52,6 +52,8 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
         lib.hqo_hadamard.argtypes = [I, P]
+        lib.hqo_paley.argtypes = [I, P]
+        lib.hqo_hadamard_split.argtypes = [I, P, P]
         lib.hqo_decode.argtypes = [P, I, L, P]
         lib.hqo_rotate.argtypes = [P, L, I, I, P, P, I]
         lib.hqo_rotate_quant.argtypes = [P, I, L, I, I, P, I, P, P, I, P, P, P, I]
@@ -64,7 +66,7 @@ def _load():
         lib.hqo_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.hqo_f16_to_f64.restype = ctypes.c_double
         lib.hqo_default_threads.restype = ctypes.c_int
-        for f in (lib.hqo_hadamard, lib.hqo_decode, lib.hqo_rotate,
+        for f in (lib.hqo_hadamard, lib.hqo_paley, lib.hqo_hadamard_split, lib.hqo_decode, lib.hqo_rotate,
                   lib.hqo_rotate_quant, lib.hqo_rotate_quant_g,
                   lib.hqo_dequant_rotate_inv, lib.hqo_dequant_rotate_inv_g,
                   lib.hqo_decode_attention):
@@ -99,10 +101,28 @@ def dtype_code(raw: np.ndarray, name: str | None = None) -> int:
 
 
 def hadamard(b: int) -> np.ndarray:
-    """Sylvester Hadamard matrix of order b, entries +1/-1 ([RQ] 2.1)."""
+    """The Hadamard matrix of order b the library rotates with, entries
+    +1/-1: Sylvester for a power of two ([RQ] 2.1), else the Kronecker
+    product of a Paley matrix and a Sylvester matrix (hadamard_split)."""
     H = np.empty((b, b), dtype=np.int8)
     _check(_load().hqo_hadamard(int(b), _ptr(H)), "hadamard")
     return H
+
+
+def paley(k: int) -> np.ndarray:
+    """Paley's first construction of order k (k - 1 a prime power = 3 mod 4,
+    at most a cube), entries +1/-1."""
+    H = np.empty((k, k), dtype=np.int8)
+    _check(_load().hqo_paley(int(k), _ptr(H)), "paley")
+    return H
+
+
+def hadamard_split(n: int) -> tuple[int, int] | None:
+    """(k, m2) with n = k * m2, m2 a power of two and k the Paley order the
+    library uses (k = 1 when n is a power of two), or None."""
+    k, m2 = ctypes.c_int(0), ctypes.c_int(0)
+    rc = _load().hqo_hadamard_split(int(n), ctypes.byref(k), ctypes.byref(m2))
+    return None if rc != 0 else (k.value, m2.value)
 
 
 def decode(raw: np.ndarray, dtype: int) -> np.ndarray:
