@@ -84,13 +84,21 @@ hq_status check_shape(int64_t rows, int32_t n, int32_t b, const int8_t *s)
         return HQ_EINVAL;
     if (n < 16 || n % 16 != 0)
         return HQ_EINVAL;
-    if (!is_pow2(b) || n % b != 0)
-        return HQ_EINVAL;
+    if (is_pow2(b)) {
+        if (n % b != 0)
+            return HQ_EINVAL;
+    } else {
+        // a width that is not a power of two: the full rotation by
+        // H_k (x) H_(n/k), when n has such a factorisation
+        hq::PaleySpec ps;
+        if (b != n || !hq::hadamard_split(n, ps))
+            return HQ_EINVAL;
+    }
     if (rows > 0 && !s)
         return HQ_EINVAL;
     if (s && !aligned(s, 16))
         return HQ_EINVAL;
-    if (b > kMaxB)
+    if (is_pow2(b) && b > kMaxB)
         return HQ_EUNSUPPORTED;
     return HQ_OK;
 }
@@ -108,7 +116,15 @@ hq_status dispatch(const hq::Request &r)
     if (r.n > max_n_for(*dev))
         return HQ_EUNSUPPORTED;
     hipError_t e;
-    if (hq::mfma_available(r))
+    if (!is_pow2(r.b)) {
+        // H_k (x) H_m2: the generic kernel
+        hq::Request rp = r;
+        if (!hq::hadamard_split(r.b, rp.paley))
+            return HQ_EINVAL;
+        if (!hq::generic_paley_fits(rp, *dev))
+            return HQ_EUNSUPPORTED;
+        e = hq::launch_generic(rp, *dev);
+    } else if (hq::mfma_available(r))
         e = hq::launch_mfma(r, *dev);
     else if (hq::fast_available(r))
         e = hq::launch_fast(r, *dev);

@@ -12,6 +12,14 @@
 // Butterfly order: pairs (i, i+h) for h = 1, 2, 4, ..., b/2 with
 // (a, c) -> (a+c, a-c).  This is the Sylvester factorisation
 // H_b = H_2 (x) H_2 (x) ... (x) H_2, so the result comes out in natural order.
+//
+// Widths that are not a power of two rotate by H_n = H_k (x) H_m2 ([RQ] 2.1:
+// larger Hadamard matrices as Kronecker products), H_k from Paley's first
+// construction over GF(k - 1): the butterflies run on each run of m2
+// elements, then a dense k-point stage mixes the runs (element i * m2 + j of
+// the row is entry (i, j)).  The workgroup builds H_k as a +-1 bit matrix in
+// LDS once: Q[a][b] = chi(a - b), chi the quadratic character of GF(q), from
+// a table of the squares of GF(q) it computes itself.
 #include "hq_device.h"
 #include "hq_internal.h"
 
@@ -37,7 +45,126 @@ struct GenericArgs {
     int64_t cache_rows;
     float kq;   // 1 / (sqrt(b) * qmax)
     float rb;   // 1 / sqrt(b)
+    // b == n not a power of two: H_pk (x) H_(n/pk) over GF(pp^pe) (see
+    // PaleySpec); pk == 1 otherwise
+    int pk, pm2, pp, pe, pmod0, pmod1, pmod2;
+    int pwords;  // 32-bit words per row of the bit matrix: ceil(pk / 32)
+    int pjb;     // columns of the dense stage per pass
 };
+
+// GF(p^e) arithmetic on element indices c0 + p c1 + p^2 c2 (e <= 3)
+__device__ int gf_sub_dev(int a, int b, int p, int e)
+{
+    int r = 0, w = 1;
+    for (int i = 0; i < e; ++i) {
+        int d = a % p - b % p;
+        d += d < 0 ? p : 0;
+        r += d * w;
+        w *= p;
+        a /= p;
+        b /= p;
+    }
+    return r;
+}
+
+__device__ int gf_mul_dev(int a, int b, const GenericArgs &g)
+{
+    const int p = g.pp, e = g.pe;
+    if (e == 1)
+        return (int)((int64_t)a * b % p);
+    int ca[3] = {0, 0, 0}, cb[3] = {0, 0, 0}, pr[5] = {0, 0, 0, 0, 0};
+    const int md[3] = {g.pmod0, g.pmod1, g.pmod2};
+    for (int i = 0; i < e; ++i) {
+        ca[i] = a % p;
+        cb[i] = b % p;
+        a /= p;
+        b /= p;
+    }
+    for (int i = 0; i < e; ++i)
+        for (int j = 0; j < e; ++j)
+            pr[i + j] += ca[i] * cb[j];
+    // x^e = -(md[e-1] x^(e-1) + ... + md[0]), highest power first
+    for (int d = 2 * e - 2; d >= e; --d) {
+        const int c = pr[d] % p;
+        pr[d] = 0;
+        for (int i = 0; i < e; ++i)
+            pr[d - e + i] -= c * md[i];
+    }
+    int r = 0;
+    for (int i = e - 1; i >= 0; --i)
+        r = r * p + ((pr[i] % p) + p) % p;
+    return r;
+}
+
+// Entry (r, c) of Paley's H_k: row/column 0 is the extra point
+__device__ int paley_entry(int r, int c, const unsigned char *sq, const GenericArgs &g)
+{
+    if (r == 0)
+        return 1;
+    if (c == 0)
+        return -1;
+    if (r == c)
+        return 1;  // chi(0) + 1
+    return sq[gf_sub_dev(r - 1, c - 1, g.pp, g.pe)] ? 1 : -1;
+}
+
+// Builds, for every output index c of the k-point stage, the bits of the k
+// coefficients it sums (bit set: -1): column c of H_k for the forward
+// rotation u.H, row c for the inverse v.H^T.
+__device__ void paley_setup(uint32_t *Pb, unsigned char *sq, const GenericArgs &g, bool transpose)
+{
+    const int k = g.pk, q = k - 1;
+    for (int i = threadIdx.x; i < q; i += kThreads)
+        sq[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x + 1; i < q; i += kThreads)
+        sq[gf_mul_dev(i, i, g)] = 1;  // concurrent writes store the same 1
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < k * g.pwords; idx += kThreads) {
+        const int c = idx / g.pwords, w = idx % g.pwords;
+        uint32_t bits = 0;
+        for (int t = 0; t < 32 && 32 * w + t < k; ++t) {
+            const int i = 32 * w + t;
+            const int v = transpose ? paley_entry(c, i, sq, g) : paley_entry(i, c, sq, g);
+            bits |= (v < 0 ? 1u : 0u) << t;
+        }
+        Pb[idx] = bits;
+    }
+    __syncthreads();
+}
+
+// L[c * m2 + j] = sum_i (+-1) L[i * m2 + j] with the signs of output c's
+// bit row; pjb columns j at a time through the scratch C.
+__device__ void paley_stage(float *L, float *C, const uint32_t *Pb, const GenericArgs &g)
+{
+    const int k = g.pk, m2 = g.pm2, jb = g.pjb;
+    for (int j0 = 0; j0 < m2; j0 += jb) {
+        __syncthreads();
+        for (int t = threadIdx.x; t < jb * k; t += kThreads) {
+            const int jj = t / k, i = t % k;
+            C[t] = L[i * m2 + j0 + jj];
+        }
+        __syncthreads();
+        for (int t = threadIdx.x; t < jb * k; t += kThreads) {
+            const int jj = t / k, c = t % k;
+            const float *col = C + jj * k;
+            const uint32_t *bits = Pb + c * g.pwords;
+            float acc = 0.0f;
+            for (int w = 0; w < g.pwords; ++w) {  // one partial sum per word
+                const uint32_t bw = bits[w];
+                const int i0 = 32 * w, lim = k - i0 < 32 ? k - i0 : 32;
+                float part = 0.0f;
+                for (int t2 = 0; t2 < lim; ++t2) {
+                    const float v = col[i0 + t2];
+                    part += ((bw >> t2) & 1u) ? -v : v;
+                }
+                acc += part;
+            }
+            L[c * m2 + j0 + jj] = acc;
+        }
+    }
+    __syncthreads();
+}
 
 template <int IN>
 __device__ __forceinline__ float load_in(const void *x, int64_t idx)
@@ -90,6 +217,13 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(GenericArgs a)
     __shared__ float red[kThreads / 64];
     const int n = a.n;
     constexpr int qmax = (1 << (BITS - 1)) - 1;
+    // dynamic LDS: the row, then (k > 1) the dense stage's scratch, the bit
+    // matrix and the table of squares
+    float *C = L + n;
+    uint32_t *Pb = (uint32_t *)(C + a.pjb * a.pk);
+    unsigned char *sq = (unsigned char *)(Pb + a.pk * a.pwords);
+    if (a.pk > 1)
+        paley_setup(Pb, sq, a, OP == kDequantInv);
 
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         const int64_t base = row * (int64_t)n;
@@ -118,6 +252,8 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(GenericArgs a)
                                : (float)q;  // exact; the FWHT of integer codes stays exact
             }
             fwht_lds(L, n, a.log_b);
+            if (a.pk > 1)
+                paley_stage(L, C, Pb, a);
             const float t = sc * a.rb;
             for (int i = threadIdx.x; i < n; i += kThreads) {
                 float v = L[i] * t;
@@ -135,6 +271,8 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(GenericArgs a)
                 L[i] = a.s[i] < 0 ? -v : v;
             }
             fwht_lds(L, n, a.log_b);
+            if (a.pk > 1)
+                paley_stage(L, C, Pb, a);
             if constexpr (OP == kRotate) {
                 for (int i = threadIdx.x; i < n; i += kThreads)
                     ((float *)a.y)[base + i] = L[i] * a.rb;
@@ -207,12 +345,23 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(GenericArgs a)
     }
 }
 
+// dynamic LDS of a launch (see the kernel's layout)
+size_t generic_lds(const GenericArgs &ga)
+{
+    size_t lds = (size_t)ga.n * sizeof(float);
+    if (ga.pk > 1)
+        lds += (size_t)ga.pjb * ga.pk * sizeof(float) + (size_t)ga.pk * ga.pwords * sizeof(uint32_t) +
+               (size_t)((ga.pk + 3) & ~3);
+    return lds;
+}
+
 template <int OP, int IN, int BITS, int SC>
 hipError_t go(const GenericArgs &ga, const Request &r, const DeviceInfo &dev)
 {
-    (void)dev;
-    int64_t grid = r.rows < (1 << 20) ? r.rows : (1 << 20);
-    size_t lds = (size_t)r.n * sizeof(float);
+    // persistent workgroups when each builds a Paley matrix first
+    const int64_t cap = ga.pk > 1 ? (int64_t)dev.cu_count * 2 : (1 << 20);
+    int64_t grid = r.rows < cap ? r.rows : cap;
+    size_t lds = generic_lds(ga);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void *)generic_kernel<OP, IN, BITS, SC>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -236,6 +385,14 @@ hipError_t pick_bits(const GenericArgs &ga, const Request &r, const DeviceInfo &
 
 }  // namespace
 
+bool generic_paley_fits(const Request &r, const DeviceInfo &dev)
+{
+    const int k = r.paley.k, m2 = r.paley.m2;
+    const size_t lds = (size_t)r.n * sizeof(float) + (size_t)(m2 < 8 ? m2 : 8) * k * sizeof(float) +
+                       (size_t)k * ((k + 31) / 32) * sizeof(uint32_t) + (size_t)((k + 3) & ~3);
+    return (int64_t)(lds + kStaticLds) <= dev.lds_per_block;
+}
+
 hipError_t launch_generic(const Request &r, const DeviceInfo &dev)
 {
     GenericArgs ga{};
@@ -248,10 +405,21 @@ hipError_t launch_generic(const Request &r, const DeviceInfo &dev)
     ga.y = r.y;
     ga.rows = r.rows;
     ga.n = r.n;
+    // butterflies over runs of b elements, or of m2 for H_k (x) H_m2
+    const int fw = r.paley.k > 1 ? r.paley.m2 : r.b;
     int lb = 0;
-    while ((1 << lb) < r.b)
+    while ((1 << lb) < fw)
         ++lb;
     ga.log_b = lb;
+    ga.pk = r.paley.k;
+    ga.pm2 = r.paley.m2;
+    ga.pp = r.paley.p;
+    ga.pe = r.paley.e;
+    ga.pmod0 = r.paley.mod[0];
+    ga.pmod1 = r.paley.mod[1];
+    ga.pmod2 = r.paley.mod[2];
+    ga.pwords = (r.paley.k + 31) / 32;
+    ga.pjb = r.paley.m2 < 8 ? r.paley.m2 : 8;
     ga.group = r.group;
     ga.dst_rows = r.dst_rows;
     ga.cache_rows = r.cache_rows;
@@ -259,8 +427,7 @@ hipError_t launch_generic(const Request &r, const DeviceInfo &dev)
     ga.kq = (float)(1.0 / (__builtin_sqrt((double)r.b) * qmax));
     ga.rb = (float)(1.0 / __builtin_sqrt((double)r.b));
 
-    size_t lds = (size_t)r.n * sizeof(float) + kStaticLds;
-    if ((int64_t)lds > dev.lds_per_block)
+    if ((int64_t)(generic_lds(ga) + kStaticLds) > dev.lds_per_block)
         return hipErrorInvalidValue;
 
     switch (r.op) {

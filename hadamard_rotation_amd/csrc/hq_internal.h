@@ -18,6 +18,22 @@ enum Op : int {
     kDequantInv = 2    // codes + scales -> rows (inverse rotation)
 };
 
+// The Hadamard matrix of a width n that is not a power of two:
+// H_n = H_k (x) H_m2, m2 = n / k a power of two, H_k Paley's first
+// construction over GF(q), q = k - 1 = p^e = 3 (mod 4), e <= 3.  GF(p^e) is
+// GF(p)[x] modulo x^e + mod[e-1] x^(e-1) + ... + mod[0], the first monic
+// polynomial of degree e without a root in GF(p) by the index
+// mod[0] + p mod[1] + p^2 mod[2]; an element c0 + c1 x + c2 x^2 has index
+// c0 + p c1 + p^2 c2.  k is the smallest order of the form
+// (odd part of n) * 2^a.  k = 1 (and m2 = n) for a power of two.
+struct PaleySpec {
+    int k = 1, m2 = 0, p = 0, e = 0;
+    int mod[3] = {0, 0, 0};
+};
+
+// Fills ps for a width n; false when n has no such matrix.
+bool hadamard_split(int n, PaleySpec &ps);
+
 // Everything a launcher needs; validated by the host dispatcher beforehand.
 struct Request {
     Op op;
@@ -42,6 +58,7 @@ struct Request {
     void *y;                // kRotate / kDequantInv output
     int y_dtype;
     hipStream_t stream;
+    PaleySpec paley;        // b == n not a power of two: its factors
 };
 
 // Per-device facts the dispatcher uses to choose and size launches.
@@ -76,6 +93,8 @@ hipError_t launch_attention(const AttnRequest &r);
 // Generic path: any supported (n, b); one workgroup per row with the row
 // staged in LDS as fp32.  Requires 4*n <= dev.lds_per_block.
 hipError_t launch_generic(const Request &r, const DeviceInfo &dev);
+// Whether the generic kernel's LDS holds a request with r.paley.k > 1.
+bool generic_paley_fits(const Request &r, const DeviceInfo &dev);
 
 // Tuned register-resident paths.  fast_plan() says whether one exists for
 // the request; launch_fast() enqueues it.

@@ -225,3 +225,16 @@ def test_product_package_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), f
                 assert "hq_oracle" not in text and "liboracle" not in text, f
+
+
+def test_full_width_rotation_that_is_not_a_power_of_two():
+    # b == n with n = k * 2^m, k a Paley order: accepted (a no-op at rows 0)
+    for n in (96, 688, 11008):
+        assert rq(rows=0, n=n, b=n) == hq.HQ_OK
+        assert inv(rows=0, n=n, b=n) == hq.HQ_OK
+        assert rot(rows=0, n=n, b=n) == hq.HQ_OK
+    # 496 = 31 * 16: no order 31 * 2^a - 1 is a prime power = 3 (mod 4)
+    assert rq(rows=0, n=496, b=496) == hq.HQ_EINVAL
+    # a block size that is neither a power of two nor the whole width
+    assert rq(rows=0, n=11008, b=344) == hq.HQ_EINVAL
+    assert rq(rows=0, n=11008, b=5504) == hq.HQ_EINVAL

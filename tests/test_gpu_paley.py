@@ -1,0 +1,112 @@
+"""GPU parity of full-width rotations whose width is not a power of two:
+H_n = H_k (x) H_(n/k), H_k from Paley's first construction (the Kronecker
+route of [RQ] "旋转量化：大模型低比特量化中的离群值克星" section 2.1, for the full-width
+block size of the [MS] "QuaRot：基于旋转的离群值抑制算法说明" YAML table).
+
+Widths: 48 = 12 x 4, 96 = 12 x 8, 160 = 20 x 8, 688 = 344 x 2 and the FFN
+width 11008 = 344 x 32 (Paley over GF(7^3)).  Inputs are seeded Gaussians
+with outlier channels; expected values come from the oracle only, with the
+tolerances of oracle/parity.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import hadamard_rotation_amd as hq
+from hadamard_rotation_amd import workloads as W
+from oracle import oracle as O
+from oracle import parity as P
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    G.require_gpu()
+
+
+def _input(seed, rows, n, x_dtype, outliers=3):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, n), dtype=np.float32)
+    cols = rng.choice(n, size=outliers, replace=False)
+    x[:, cols] *= np.float32(50.0)
+    s = np.where(rng.integers(0, 2, n) == 1, 1, -1).astype(np.int8)
+    if x_dtype == W.F32:
+        return x, s
+    if x_dtype == W.BF16:
+        return W.to_bf16_bits(x), s
+    return x.astype(np.float16).view(np.uint16), s
+
+
+CASES = [
+    (48, 37, W.BF16, 4, W.F16),
+    (96, 64, W.F32, 8, W.F32),
+    (96, 130, W.F16, 4, W.F32),
+    (160, 33, W.BF16, 8, W.F16),
+    (688, 19, W.BF16, 4, W.F32),
+    (11008, 6, W.BF16, 4, W.F32),
+    (11008, 3, W.F32, 8, W.F16),
+]
+
+
+@pytest.mark.parametrize("n,rows,x_dtype,bits,sd", CASES)
+def test_rotate_quant_and_inverse(n, rows, x_dtype, bits, sd):
+    print(f"[paley] n={n} rows={rows} x={x_dtype} bits={bits} sd={sd}", flush=True)
+    raw, s = _input(n + rows, rows, n, x_dtype)
+    ref = O.rotate_quant(raw, x_dtype, n, s, bits, sd)
+    codes, scales = G.gpu_rotate_quant(raw, x_dtype, s, n, bits, sd)
+    P.check_codes(codes, ref, bits, n, what=f"n={n} codes")
+    P.check_scales(scales, ref, sd, what=f"n={n} scales")
+    y_ref = O.dequant_rotate_inv(ref["codes"], ref["scales"], sd, n, s, bits, n)
+    y = G.gpu_dequant_inv(ref["codes"], ref["scales"], s, n, bits)
+    P.check_inverse(y, y_ref, bf16=False, what=f"n={n} inverse f32")
+    yb = G.gpu_dequant_inv(ref["codes"], ref["scales"], s, n, bits, out_bf16=True)
+    P.check_inverse(P.bf16_bits_to_f64(yb), y_ref, bf16=True, what=f"n={n} inverse bf16")
+
+
+@pytest.mark.parametrize("n,rows,x_dtype", [(96, 33, W.BF16), (688, 9, W.F32), (11008, 4, W.BF16)])
+def test_rotate_only(n, rows, x_dtype):
+    print(f"[paley] rotate n={n} rows={rows}", flush=True)
+    raw, s = _input(7 * n + rows, rows, n, x_dtype)
+    xr = O.rotate(O.decode(raw, x_dtype), s, n)
+    P.check_rotated(G.gpu_rotate(raw, x_dtype, s, n), xr, what=f"n={n} rotated")
+
+
+@pytest.mark.parametrize("n,rows,group,bits", [(96, 20, 32, 4), (688, 7, 16, 8), (11008, 3, 128, 4)])
+def test_grouped(n, rows, group, bits):
+    print(f"[paley] grouped n={n} group={group}", flush=True)
+    raw, s = _input(3 * n + group, rows, n, W.BF16)
+    ref = O.rotate_quant(raw, W.BF16, n, s, bits, W.F32, group=group)
+    codes, scales = G.gpu_rotate_quant_grouped(raw, W.BF16, s, n, group, bits, W.F32)
+    P.check_codes(codes, ref, bits, n, what=f"n={n} g={group} codes")
+    P.check_scales(scales, ref, W.F32, what=f"n={n} g={group} scales")
+    y_ref = O.dequant_rotate_inv(ref["codes"], ref["scales"], W.F32, n, s, bits, n, group=group)
+    y = G.gpu_dequant_inv_grouped(ref["codes"], ref["scales"], s, n, group, bits)
+    P.check_inverse(y, y_ref, bf16=False, what=f"n={n} g={group} inverse")
+
+
+def test_append_into_cache():
+    n, rows, cache_rows = 688, 5, 40
+    print(f"[paley] append n={n}", flush=True)
+    raw, s = _input(99, rows, n, W.BF16)
+    ref = O.rotate_quant(raw, W.BF16, n, s, 4, W.F16)
+    dst = np.array([3, 39, 0, 17, 40], dtype=np.int64)  # the last one lies outside
+    codes = torch.zeros((cache_rows, n // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((cache_rows,), dtype=torch.float16, device="cuda")
+    hq.hq_rotate_quant_append(G.to_dev(raw, W.BF16), G.s_dev(s), n, torch.from_numpy(dst).cuda(),
+                              codes, scales, 4)
+    torch.cuda.synchronize()
+    c = codes.cpu().numpy()
+    sc = scales.cpu().numpy()
+    for r, d in enumerate(dst):
+        if d >= cache_rows:
+            continue
+        one = {k: (v[r:r + 1] if isinstance(v, np.ndarray) and v.ndim >= 1 and len(v) == rows else v)
+               for k, v in ref.items()}
+        P.check_codes(c[d:d + 1], one, 4, n, what=f"append row {r}")
+        P.check_scales(sc[d:d + 1], one, W.F16, what=f"append row {r}")
+    untouched = np.setdiff1d(np.arange(cache_rows), dst)
+    assert not c[untouched].any() and not sc[untouched].view(np.uint16).any()
