@@ -117,13 +117,17 @@ hq_status dispatch(const hq::Request &r)
         return HQ_EUNSUPPORTED;
     hipError_t e;
     if (!is_pow2(r.b)) {
-        // H_k (x) H_m2: the generic kernel
+        // H_k (x) H_m2: the matrix-core kernel where it has a plan, else the
+        // generic kernel
         hq::Request rp = r;
         if (!hq::hadamard_split(r.b, rp.paley))
             return HQ_EINVAL;
-        if (!hq::generic_paley_fits(rp, *dev))
+        if (hq::paley_mfma_available(rp))
+            e = hq::launch_paley_mfma(rp, *dev);
+        else if (!hq::generic_paley_fits(rp, *dev))
             return HQ_EUNSUPPORTED;
-        e = hq::launch_generic(rp, *dev);
+        else
+            e = hq::launch_generic(rp, *dev);
     } else if (hq::mfma_available(r))
         e = hq::launch_mfma(r, *dev);
     else if (hq::fast_available(r))

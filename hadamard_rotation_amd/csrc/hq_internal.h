@@ -93,6 +93,10 @@ hipError_t launch_attention(const AttnRequest &r);
 // Generic path: any supported (n, b); one workgroup per row with the row
 // staged in LDS as fp32.  Requires 4*n <= dev.lds_per_block.
 hipError_t launch_generic(const Request &r, const DeviceInfo &dev);
+// Matrix-core path for H_k (x) H_32 rotations (k in (320, 352], 16-bit
+// input, per-row fp32 scales).
+bool paley_mfma_available(const Request &r);
+hipError_t launch_paley_mfma(const Request &r, const DeviceInfo &dev);
 // Whether the generic kernel's LDS holds a request with r.paley.k > 1.
 bool generic_paley_fits(const Request &r, const DeviceInfo &dev);
 

@@ -1,0 +1,389 @@
+// hq_paley_mfma.hip -- matrix-core kernel for the full-width rotation of rows
+// whose width is not a power of two: n = k * 32, H_n = H_k (x) H_32 with H_k
+// from Paley's first construction (e.g. the FFN width 11008 = 344 x 32 over
+// GF(7^3)), fused with the per-row quantiser.
+//
+// Pages cited: [RQ] "旋转量化：大模型低比特量化中的离群值克星" section 2.1 (larger
+// Hadamard matrices as Kronecker products; the transform is additions and
+// subtractions) and section 2.2 (absmax quantisation); [QT]
+// "手把手教你用QuaRot实现LLM的4位量化：从原理到代码实践" section 2.1 (sign flip, then the
+// Hadamard matrix); [MS] "QuaRot：基于旋转的离群值抑制算法说明" YAML table (full-width
+// block size).
+//
+// Element i * 32 + j of a row is entry (i, j).  y = (x * s) . H_n splits into
+//   Z[i'][j] = sum_i H_k[i][i'] u[i][j]      a dense k-point product
+//   y[i'][j'] = sum_j H_32[j][j'] Z[i'][j]   32-point butterflies
+// The dense product runs on the matrix core: u is bf16 or f16 and H_k is
+// +-1, so every product is exact and the sums are fp32.  As a 16x16x32
+// product D[m][n] = sum_k A[m][k] B[k][n] it has m = j (two tiles of 16),
+// k = i (chunks of 32) and n = i' (tiles of 16): A is the row, staged in LDS
+// transposed to [j][i]; B is H_k, which each wave builds once for its share
+// of the i' tiles and keeps in registers.  The butterflies then run on the
+// result in registers: j = 16 mt + 4 rg + r is the tile, the lane's row
+// group and the register, so two of the five stages cross lanes.
+#include "hq_device.h"
+#include "hq_internal.h"
+
+namespace hq {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWaves = 8;               // waves per workgroup (two per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kM2 = 32;                 // the power-of-two factor this kernel takes
+
+struct PaleyArgs {
+    const void *x;
+    const int8_t *s;
+    void *codes;
+    void *scales;
+    int64_t rows;
+    int n;          // k * 32
+    int k;          // Paley order
+    int p, e, mod0, mod1, mod2;  // GF(k - 1) = GF(p^e) (see PaleySpec)
+    float kq;       // 1 / (sqrt(n) * qmax)
+};
+
+// GF(p^e) on element indices c0 + p c1 + p^2 c2 (e <= 3)
+__device__ int gfp_sub(int a, int b, int p, int e)
+{
+    int r = 0, w = 1;
+    for (int i = 0; i < e; ++i) {
+        int d = a % p - b % p;
+        d += d < 0 ? p : 0;
+        r += d * w;
+        w *= p;
+        a /= p;
+        b /= p;
+    }
+    return r;
+}
+
+__device__ int gfp_square(int a, const PaleyArgs &g)
+{
+    const int p = g.p, e = g.e;
+    if (e == 1)
+        return (int)((int64_t)a * a % p);
+    int c[3] = {0, 0, 0}, pr[5] = {0, 0, 0, 0, 0};
+    const int md[3] = {g.mod0, g.mod1, g.mod2};
+    for (int i = 0; i < e; ++i) {
+        c[i] = a % p;
+        a /= p;
+    }
+    for (int i = 0; i < e; ++i)
+        for (int j = 0; j < e; ++j)
+            pr[i + j] += c[i] * c[j];
+    for (int d = 2 * e - 2; d >= e; --d) {  // x^e = -(md[e-1] x^(e-1) + ... + md[0])
+        const int t = pr[d] % p;
+        pr[d] = 0;
+        for (int i = 0; i < e; ++i)
+            pr[d - e + i] -= t * md[i];
+    }
+    int r = 0;
+    for (int i = e - 1; i >= 0; --i)
+        r = r * p + ((pr[i] % p) + p) % p;
+    return r;
+}
+
+// H_k[r][c] as the 16-bit pattern of +-1 (0 outside the k x k matrix)
+template <int IN>
+__device__ uint32_t paley_bits16(int r, int c, const unsigned char *sq, const PaleyArgs &g)
+{
+    constexpr uint32_t kOne = IN == kBF16 ? 0x3F80u : 0x3C00u;
+    if (r >= g.k || c >= g.k)
+        return 0u;
+    int v;
+    if (r == 0)
+        v = 1;
+    else if (c == 0)
+        v = -1;
+    else if (r == c)
+        v = 1;  // chi(0) + 1
+    else
+        v = sq[gfp_sub(r - 1, c - 1, g.p, g.e)] ? 1 : -1;
+    return v > 0 ? kOne : (kOne | 0x8000u);
+}
+
+// One B operand: H_k[i][i'] for i = 32c + 8rg + e (e = 0..7), i' = 16t + l16
+// (kept out of line: the caller's unrolled loop then stays small enough to
+// keep every operand in registers)
+template <int IN>
+__device__ __noinline__ u32x4 paley_operand(int t, int c, int l16, int rg, const unsigned char *sq,
+                                            const PaleyArgs &g)
+{
+    u32x4 r;
+    for (int p = 0; p < 4; ++p) {
+        const int i = 32 * c + 8 * rg + 2 * p, ip = 16 * t + l16;
+        r[p] = paley_bits16<IN>(i, ip, sq, g) | (paley_bits16<IN>(i + 1, ip, sq, g) << 16);
+    }
+    return r;
+}
+
+template <int IN>
+__device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c)
+{
+    if constexpr (IN == kBF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// butterfly across lanes l and l ^ 16 (X = 16) or l ^ 32 (X = 32): the lower
+// lane gets own + partner, the upper partner - own
+template <int X>
+__device__ __forceinline__ float xbutterfly(float v, float sgn)
+{
+    const uint32_t u = __float_as_uint(v);
+    auto r = X == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                     : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    // lower lane: r[0] own, r[1] partner; upper lane: r[0] partner, r[1] own
+    return __builtin_fmaf(sgn, __uint_as_float(r[1]), __uint_as_float(r[0]));
+}
+
+// KC: chunks of 32 of the contraction index i (k <= 32 KC); the i' tiles
+// number 2 KC, and wave w takes tiles w, w + 8, ...
+template <int KC, int IN, int BITS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void paley_mfma_kernel(PaleyArgs a)
+{
+    constexpr int kRS = KC * 32 + 8;            // LDS row stride of the staged row (elements)
+    constexpr int kNT = 2 * KC;                 // i' tiles of 16
+    constexpr int kTPW = (kNT + kWaves - 1) / kWaves;
+    constexpr int kChunks = KC * 32 * kM2 / 8;  // 16-byte chunks of a padded row
+    constexpr int kCPT = (kChunks + kThreads - 1) / kThreads;
+    constexpr int qmax = (1 << (BITS - 1)) - 1;
+    __shared__ __align__(16) uint16_t xt[kM2 * kRS];  // the row, [j][i]
+    __shared__ __align__(16) uint32_t cst[KC * 32 * kM2 * BITS / 32];  // its codes
+    __shared__ unsigned char sq[KC * 32];
+    __shared__ float red[kWaves];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, rg = lane >> 4;
+    const int n = a.n, k = a.k;
+    const int nchunks = n / 8;  // 16-byte chunks of a row
+
+    // ---- once: the table of squares, the zero padding of the staged row
+    for (int i = tid; i < KC * 32; i += kThreads)
+        sq[i] = 0;
+    for (int t = tid; t < kM2 * kRS; t += kThreads)
+        xt[t] = 0;
+    __syncthreads();
+    for (int i = tid + 1; i < k - 1; i += kThreads)
+        sq[gfp_square(i, a)] = 1;  // concurrent writes store the same 1
+    __syncthreads();
+
+    // ---- once: this wave's B operands, H_k[i][i'] for i = 32c + 8rg + e
+    // (e = 0..7) and i' = 16t + l16
+    u32x4 hb[kTPW][KC];
+#pragma unroll
+    for (int tt = 0; tt < kTPW; ++tt) {
+        const int t = wave + kWaves * tt;
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            hb[tt][c] = t < kNT ? paley_operand<IN>(t, c, l16, rg, sq, a) : (u32x4){0u, 0u, 0u, 0u};
+    }
+
+    // ---- the chunks this thread stages: chunk q holds elements 8q .. 8q+7,
+    // i.e. i = q / 4, j = 8 (q % 4) .. +7; their signs are the same every row
+    uint32_t neg[kCPT];
+#pragma unroll
+    for (int cc = 0; cc < kCPT; ++cc) {
+        const int q = tid + kThreads * cc;
+        uint32_t m = 0;
+        if (q < nchunks)
+            for (int e = 0; e < 8; ++e)
+                m |= (a.s[8 * q + e] < 0 ? 1u : 0u) << e;
+        neg[cc] = m;
+    }
+    auto load_row = [&](int64_t row, u32x4 (&r)[kCPT]) {
+        const auto rs = rsrc((const uint16_t *)a.x + row * n, 2 * n);
+#pragma unroll
+        for (int cc = 0; cc < kCPT; ++cc) {
+            const int q = tid + kThreads * cc;
+            r[cc] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rs, q < nchunks ? 16 * q : 0x7FFFFFF0, 0, kNonTemporal));
+        }
+    };
+
+    const float sgn16 = (lane & 16) ? -1.0f : 1.0f;
+    const float sgn32 = (lane & 32) ? -1.0f : 1.0f;
+
+    u32x4 cur[kCPT];
+    int64_t row = blockIdx.x;
+    if (row < a.rows)
+        load_row(row, cur);
+    for (; row < a.rows; row += gridDim.x) {
+        // ---- stage the row in LDS, transposed, signs applied
+#pragma unroll
+        for (int cc = 0; cc < kCPT; ++cc) {
+            const int q = tid + kThreads * cc;
+            if (q < nchunks) {
+                const int i = q >> 2, j0 = 8 * (q & 3);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t wv = cur[cc][e >> 1];
+                    uint32_t h = (e & 1) ? (wv >> 16) : (wv & 0xFFFFu);
+                    h ^= ((neg[cc] >> e) & 1u) << 15;
+                    xt[(j0 + e) * kRS + i] = (uint16_t)h;
+                }
+            }
+        }
+        if (row + gridDim.x < a.rows)
+            load_row(row + gridDim.x, cur);  // the next row, in flight meanwhile
+        __syncthreads();
+
+        // ---- Z[i'][j] on the matrix core
+        f32x4 acc[kTPW][2];
+#pragma unroll
+        for (int tt = 0; tt < kTPW; ++tt)
+            acc[tt][0] = acc[tt][1] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const u32x4 av = *(const u32x4 *)&xt[(16 * mt + l16) * kRS + 32 * c + 8 * rg];
+#pragma unroll
+                for (int tt = 0; tt < kTPW; ++tt)
+                    if (wave + kWaves * tt < kNT)
+                        acc[tt][mt] = mma<IN>(av, hb[tt][c], acc[tt][mt]);
+            }
+        }
+
+        // ---- 32-point butterflies over j = 16 mt + 4 rg + r, natural order
+        float mx = 0.0f;
+#pragma unroll
+        for (int tt = 0; tt < kTPW; ++tt) {
+            if (wave + kWaves * tt >= kNT)
+                continue;
+            float v[2][4];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[mt][r] = acc[tt][mt][r];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                // j bit 0, then bit 1
+                float a0 = v[mt][0] + v[mt][1], a1 = v[mt][0] - v[mt][1];
+                float a2 = v[mt][2] + v[mt][3], a3 = v[mt][2] - v[mt][3];
+                v[mt][0] = a0 + a2;
+                v[mt][2] = a0 - a2;
+                v[mt][1] = a1 + a3;
+                v[mt][3] = a1 - a3;
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[mt][r] = xbutterfly<32>(xbutterfly<16>(v[mt][r], sgn16), sgn32);  // bits 2, 3
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {  // bit 4
+                const float lo = v[0][r], hi = v[1][r];
+                v[0][r] = lo + hi;
+                v[1][r] = lo - hi;
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    acc[tt][mt][r] = v[mt][r];
+                    mx = fmaxf(mx, fabsf(v[mt][r]));
+                }
+        }
+        // ---- row maximum (columns i' >= k are 0)
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        if (lane == 0)
+            red[wave] = mx;
+        __syncthreads();
+        float m = red[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            m = fmaxf(m, red[w]);
+        const RowQuant rq = row_quant(m, a.kq, qmax);
+
+        // ---- codes of y[i'][16 mt + 4 rg .. +3] into LDS
+#pragma unroll
+        for (int tt = 0; tt < kTPW; ++tt) {
+            const int ip = 16 * (wave + kWaves * tt) + l16;
+            if (wave + kWaves * tt >= kNT || ip >= k)
+                continue;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const int e0 = ip * kM2 + 16 * mt + 4 * rg;  // first element
+                uint32_t w = 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int qc = quant_code(acc[tt][mt][r], rq.inv, qmax);
+                    w |= BITS == 4 ? ((uint32_t)qc & 15u) << (4 * r) : ((uint32_t)qc & 255u) << (8 * r);
+                }
+                if constexpr (BITS == 4)
+                    ((uint16_t *)cst)[e0 >> 2] = (uint16_t)w;
+                else
+                    cst[e0 >> 2] = w;
+            }
+        }
+        __syncthreads();
+        // ---- coalesced stores
+        const int cbytes = n * BITS / 8;
+        uint8_t *crow = (uint8_t *)a.codes + row * (int64_t)cbytes;
+        for (int t = tid; t < cbytes / 16; t += kThreads)
+            ((u32x4 *)crow)[t] = ((const u32x4 *)cst)[t];
+        if (tid == 0)
+            ((float *)a.scales)[row] = rq.scale;
+    }
+}
+
+}  // namespace
+
+bool paley_mfma_available(const Request &r)
+{
+    return r.op == kRotateQuant && !r.dst_rows && r.group == r.n &&
+           (r.x_dtype == kBF16 || r.x_dtype == kF16) && r.paley.k > 1 && r.paley.m2 == kM2 &&
+           r.paley.k > 320 && r.paley.k <= 352 && r.scale_dtype == kF32;
+}
+
+hipError_t launch_paley_mfma(const Request &r, const DeviceInfo &dev)
+{
+    PaleyArgs pa{};
+    pa.x = r.x;
+    pa.s = r.s;
+    pa.codes = r.codes;
+    pa.scales = r.scales;
+    pa.rows = r.rows;
+    pa.n = r.n;
+    pa.k = r.paley.k;
+    pa.p = r.paley.p;
+    pa.e = r.paley.e;
+    pa.mod0 = r.paley.mod[0];
+    pa.mod1 = r.paley.mod[1];
+    pa.mod2 = r.paley.mod[2];
+    const int qmax = r.bits == 8 ? 127 : 7;
+    pa.kq = (float)(1.0 / (__builtin_sqrt((double)r.n) * qmax));
+    const int64_t grid = r.rows < dev.cu_count ? r.rows : dev.cu_count;
+    if (r.x_dtype == kBF16) {
+        if (r.bits == 4)
+            hipLaunchKernelGGL((paley_mfma_kernel<11, kBF16, 4>), dim3((unsigned)grid), dim3(kThreads), 0,
+                               r.stream, pa);
+        else
+            hipLaunchKernelGGL((paley_mfma_kernel<11, kBF16, 8>), dim3((unsigned)grid), dim3(kThreads), 0,
+                               r.stream, pa);
+    } else {
+        if (r.bits == 4)
+            hipLaunchKernelGGL((paley_mfma_kernel<11, kF16, 4>), dim3((unsigned)grid), dim3(kThreads), 0,
+                               r.stream, pa);
+        else
+            hipLaunchKernelGGL((paley_mfma_kernel<11, kF16, 8>), dim3((unsigned)grid), dim3(kThreads), 0,
+                               r.stream, pa);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hq

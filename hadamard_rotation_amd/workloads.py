@@ -90,6 +90,12 @@ WORKLOADS = {
         "86 blocks of 128 with one shared 128-sign vector; per-token INT4, "
         "fp32 scales",
         16384, 11008, 128, BF16, 4, F32, ("x",), 1),
+    "ffn_11008_full": Workload(
+        "ffn_11008_full",
+        "16384 tokens x 11008 bf16, N(0,1) with 11 fixed channels x100; "
+        "full 11008-point rotation H_344 (x) H_32 (Paley over GF(7^3)) with an "
+        "11008-sign vector; per-token INT4, fp32 scales",
+        16384, 11008, 11008, BF16, 4, F32, ("x",), 1),
     "kv_cache": Workload(
         "kv_cache",
         "K and V of 131072 tokens x 8 KV heads x head_dim 128, bf16, N(0,1); "
@@ -116,6 +122,7 @@ def generate(name: str, seed: int = 42, tokens: int | None = None) -> dict:
       qk_heads    : s(128); outlier channel per head (32); Q N(0,1) f32; K N(0,1)
       hidden_4096 : s(4096); 4 distinct outlier channels; x Student-t(4) f64
       ffn_11008   : s(128) tiled x86; 11 distinct outlier channels; x N(0,1)
+      ffn_11008_full: s(11008); 11 distinct outlier channels; x N(0,1)
       kv_cache    : s(128); outlier channel per KV head (8); K N(0,1); V N(0,1)
     """
     w = WORKLOADS[name]
@@ -151,6 +158,14 @@ def generate(name: str, seed: int = 42, tokens: int | None = None) -> dict:
     elif name == "ffn_11008":
         rows = w.rows if tokens is None else tokens
         out["s"] = sign_vector(rng, 128, 11008)
+        ch = rng.choice(11008, size=11, replace=False)
+        x = rng.standard_normal((rows, 11008), dtype=np.float32)
+        x[:, ch] *= 100.0
+        out["x"] = to_bf16_bits(x)
+        out["channels"] = ch
+    elif name == "ffn_11008_full":
+        rows = w.rows if tokens is None else tokens
+        out["s"] = sign_vector(rng, 11008, 11008)
         ch = rng.choice(11008, size=11, replace=False)
         x = rng.standard_normal((rows, 11008), dtype=np.float32)
         x[:, ch] *= 100.0

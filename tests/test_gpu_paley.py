@@ -110,3 +110,17 @@ def test_append_into_cache():
         P.check_scales(sc[d:d + 1], one, W.F16, what=f"append row {r}")
     untouched = np.setdiff1d(np.arange(cache_rows), dst)
     assert not c[untouched].any() and not sc[untouched].view(np.uint16).any()
+
+
+@pytest.mark.parametrize("x_dtype,bits", [(W.BF16, 4), (W.F16, 8), (W.BF16, 8)])
+def test_11008_many_rows_sampled(x_dtype, bits):
+    # more rows than workgroups: every workgroup walks several rows; the
+    # oracle checks a sample of them (rows are independent)
+    n, rows = 11008, 600
+    print(f"[paley] 11008 x {rows} x={x_dtype} bits={bits}", flush=True)
+    raw, s = _input(1234 + bits, rows, n, x_dtype, outliers=11)
+    codes, scales = G.gpu_rotate_quant(raw, x_dtype, s, n, bits, W.F32)
+    pick = np.array([0, 1, 127, 255, 256, 257, 300, 511, 512, 513, 599])
+    ref = O.rotate_quant(raw[pick], x_dtype, n, s, bits, W.F32)
+    P.check_codes(codes[pick], ref, bits, n, what=f"11008 sampled codes")
+    P.check_scales(scales[pick], ref, W.F32, what=f"11008 sampled scales")
