@@ -89,37 +89,86 @@ __device__ int gfp_square(int a, const PaleyArgs &g)
     return r;
 }
 
-// H_k[r][c] as the 16-bit pattern of +-1 (0 outside the k x k matrix)
-template <int IN>
-__device__ uint32_t paley_bits16(int r, int c, const unsigned char *sq, const PaleyArgs &g)
+// Field elements as packed digits, one byte each (a prime order keeps its
+// index): a - b digit by digit mod p without any division, then back to an
+// element index.  Every byte of t stays in [1, 2p - 1] and of t + 128 - p
+// below 256, so no carry crosses a byte.
+__device__ __forceinline__ int diff_index(int pa, int pb, int p, int e)
 {
-    constexpr uint32_t kOne = IN == kBF16 ? 0x3F80u : 0x3C00u;
-    if (r >= g.k || c >= g.k)
-        return 0u;
-    int v;
-    if (r == 0)
-        v = 1;
-    else if (c == 0)
-        v = -1;
-    else if (r == c)
-        v = 1;  // chi(0) + 1
-    else
-        v = sq[gfp_sub(r - 1, c - 1, g.p, g.e)] ? 1 : -1;
-    return v > 0 ? kOne : (kOne | 0x8000u);
+    if (e == 1) {
+        const int d = pa - pb;
+        return d < 0 ? d + p : d;
+    }
+    constexpr int kOnes = 0x10101;
+    int t = pa + p * kOnes - pb;
+    t -= (((t + (128 - p) * kOnes) >> 7) & kOnes) * p;  // digits >= p
+    return (t & 0xFF) + p * ((t >> 8) & 0xFF) + p * p * ((t >> 16) & 0xFF);
 }
 
-// One B operand: H_k[i][i'] for i = 32c + 8rg + e (e = 0..7), i' = 16t + l16
-// (kept out of line: the caller's unrolled loop then stays small enough to
-// keep every operand in registers)
-template <int IN>
-__device__ __noinline__ u32x4 paley_operand(int t, int c, int l16, int rg, const unsigned char *sq,
-                                            const PaleyArgs &g)
+// LDS tables of the set-up: the packed digits of every element, the squares
+// by packed code, and H_k as bits (bit i of word [i'][i / 32] set: -1)
+struct PaleyLds {
+    int digits[352];
+    unsigned char square[352];
+    uint32_t hbits[352 * 11];
+};
+
+// Builds the LDS tables (all threads of the workgroup; ends with a barrier)
+__device__ void paley_build(PaleyLds &L, const PaleyArgs &g, int words)
 {
-    u32x4 r;
-    for (int p = 0; p < 4; ++p) {
-        const int i = 32 * c + 8 * rg + 2 * p, ip = 16 * t + l16;
-        r[p] = paley_bits16<IN>(i, ip, sq, g) | (paley_bits16<IN>(i + 1, ip, sq, g) << 16);
+    const int q = g.k - 1, p = g.p, e = g.e;
+    for (int a = threadIdx.x; a < q; a += kThreads) {
+        L.square[a] = 0;
+        int code = a;
+        if (e > 1) {
+            int r = a;
+            code = 0;
+            for (int i = 0; i < e; ++i) {
+                code |= (r % p) << (8 * i);
+                r /= p;
+            }
+        }
+        L.digits[a] = code;
     }
+    __syncthreads();
+    for (int a = threadIdx.x + 1; a < q; a += kThreads)
+        L.square[gfp_square(a, g)] = 1;  // concurrent writes store the same 1
+    __syncthreads();
+    // H_k[i][i']: row 0 all +1; column 0 -1 below row 0; 1 on the diagonal;
+    // chi(a - b) for a = i - 1, b = i' - 1 elsewhere
+    for (int idx = threadIdx.x; idx < g.k * words; idx += kThreads) {
+        const int ip = idx / words, w = idx % words;
+        uint32_t bits = 0;
+        const int pb = ip > 0 ? L.digits[ip - 1] : 0;
+        for (int t = 0; t < 32; ++t) {
+            const int i = 32 * w + t;
+            bool neg = false;
+            if (i > 0 && i < g.k) {
+                if (ip == 0)
+                    neg = true;
+                else if (i != ip)
+                    neg = !L.square[diff_index(L.digits[i - 1], pb, p, e)];
+            }
+            bits |= (neg ? 1u : 0u) << t;
+        }
+        L.hbits[idx] = bits;
+    }
+    __syncthreads();
+}
+
+// One B operand from the bit matrix: H_k[i][i'] for i = 32c + 8rg + e
+// (e = 0..7) and i' = 16t + l16, as +-1 in the 16-bit type
+template <int IN>
+__device__ __forceinline__ u32x4 paley_operand(const PaleyLds &L, int t, int c, int l16, int rg, int words,
+                                               int k)
+{
+    constexpr uint32_t kOnes = IN == kBF16 ? 0x3F803F80u : 0x3C003C00u;
+    const int ip = 16 * t + l16;
+    const uint32_t b = ip < k ? (L.hbits[ip * words + c] >> (8 * rg)) & 0xFFu : 0u;
+    u32x4 r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        r[p] = kOnes | (((b >> (2 * p)) & 1u) << 15) | (((b >> (2 * p + 1)) & 1u) << 31);
     return r;
 }
 
@@ -150,16 +199,20 @@ __device__ __forceinline__ float xbutterfly(float v, float sgn)
 template <int KC, int IN, int BITS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void paley_mfma_kernel(PaleyArgs a)
 {
-    constexpr int kRS = KC * 32 + 8;            // LDS row stride of the staged row (elements)
     constexpr int kNT = 2 * KC;                 // i' tiles of 16
     constexpr int kTPW = (kNT + kWaves - 1) / kWaves;
     constexpr int kChunks = KC * 32 * kM2 / 8;  // 16-byte chunks of a padded row
     constexpr int kCPT = (kChunks + kThreads - 1) / kThreads;
+    // LDS row stride of the staged row (elements): every chunk index a thread
+    // takes lands inside a row (those past the data write zeros into the
+    // padding), and 16 rows apart by a multiple of 4 banks plus 4
+    constexpr int kRS = ((kCPT * kThreads / 4 + 31) / 32) * 32 + 8;
     constexpr int qmax = (1 << (BITS - 1)) - 1;
-    __shared__ __align__(16) uint16_t xt[kM2 * kRS];  // the row, [j][i]
+    __shared__ __align__(16) uint16_t xt[2][kM2 * kRS];  // two rows, [j][i]
     __shared__ __align__(16) uint32_t cst[KC * 32 * kM2 * BITS / 32];  // its codes
-    __shared__ unsigned char sq[KC * 32];
+    __shared__ PaleyLds pl;
     __shared__ float red[kWaves];
+    static_assert(KC <= 11, "the set-up tables hold k <= 352");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -168,33 +221,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int n = a.n, k = a.k;
     const int nchunks = n / 8;  // 16-byte chunks of a row
 
-    // ---- once: the table of squares, the zero padding of the staged row
-    for (int i = tid; i < KC * 32; i += kThreads)
-        sq[i] = 0;
-    for (int t = tid; t < kM2 * kRS; t += kThreads)
-        xt[t] = 0;
-    __syncthreads();
-    for (int i = tid + 1; i < k - 1; i += kThreads)
-        sq[gfp_square(i, a)] = 1;  // concurrent writes store the same 1
-    __syncthreads();
-
-    // ---- once: this wave's B operands, H_k[i][i'] for i = 32c + 8rg + e
-    // (e = 0..7) and i' = 16t + l16
+    // ---- once: H_k as bits in LDS, the zero padding of the staged row, and
+    // this wave's B operands in registers
+    for (int t = tid; t < 2 * kM2 * kRS; t += kThreads)
+        (&xt[0][0])[t] = 0;
+    paley_build(pl, a, KC);
     u32x4 hb[kTPW][KC];
+    // (a wave without a tile in the last slot computes a copy of the last
+    // tile there and drops it: no branch around any product)
 #pragma unroll
     for (int tt = 0; tt < kTPW; ++tt) {
         const int t = wave + kWaves * tt;
 #pragma unroll
         for (int c = 0; c < KC; ++c)
-            hb[tt][c] = t < kNT ? paley_operand<IN>(t, c, l16, rg, sq, a) : (u32x4){0u, 0u, 0u, 0u};
+            hb[tt][c] = paley_operand<IN>(pl, t < kNT ? t : kNT - 1, c, l16, rg, KC, k);
     }
 
     // ---- the chunks this thread stages: chunk q holds elements 8q .. 8q+7,
-    // i.e. i = q / 4, j = 8 (q % 4) .. +7; their signs are the same every row
+    // i.e. i = q / 4, j = 8 (q % 4) .. +7.  The 64 lanes of a wave take 64
+    // consecutive i of one j block, so their LDS writes fall in consecutive
+    // words.  Their signs are the same every row.
+    auto chunk_of = [&](int cc) {
+        const int c = tid + kThreads * cc;
+        const int i = (c >> 8) * 64 + (c & 63), jq = (c >> 6) & 3;
+        return 4 * i + jq;
+    };
     uint32_t neg[kCPT];
 #pragma unroll
     for (int cc = 0; cc < kCPT; ++cc) {
-        const int q = tid + kThreads * cc;
+        const int q = chunk_of(cc);
         uint32_t m = 0;
         if (q < nchunks)
             for (int e = 0; e < 8; ++e)
@@ -205,7 +260,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const auto rs = rsrc((const uint16_t *)a.x + row * n, 2 * n);
 #pragma unroll
         for (int cc = 0; cc < kCPT; ++cc) {
-            const int q = tid + kThreads * cc;
+            const int q = chunk_of(cc);
             r[cc] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                   rs, q < nchunks ? 16 * q : 0x7FFFFFF0, 0, kNonTemporal));
         }
@@ -215,28 +270,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const float sgn32 = (lane & 32) ? -1.0f : 1.0f;
 
     u32x4 cur[kCPT];
-    int64_t row = blockIdx.x;
-    if (row < a.rows)
-        load_row(row, cur);
-    for (; row < a.rows; row += gridDim.x) {
-        // ---- stage the row in LDS, transposed, signs applied
+    // stages the row held in cur into LDS buffer `buf`, transposed, signs
+    // applied (chunks past the row were read as 0 and write 0 into the
+    // padding)
+    auto stage = [&](int buf) {
 #pragma unroll
         for (int cc = 0; cc < kCPT; ++cc) {
-            const int q = tid + kThreads * cc;
-            if (q < nchunks) {
-                const int i = q >> 2, j0 = 8 * (q & 3);
+            const int q = chunk_of(cc);
+            const int i = q >> 2, j0 = 8 * (q & 3);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t wv = cur[cc][e >> 1];
-                    uint32_t h = (e & 1) ? (wv >> 16) : (wv & 0xFFFFu);
-                    h ^= ((neg[cc] >> e) & 1u) << 15;
-                    xt[(j0 + e) * kRS + i] = (uint16_t)h;
-                }
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t wv = cur[cc][e >> 1];
+                uint32_t h = (e & 1) ? (wv >> 16) : (wv & 0xFFFFu);
+                h ^= ((neg[cc] >> e) & 1u) << 15;
+                xt[buf][(j0 + e) * kRS + i] = (uint16_t)h;
             }
         }
+    };
+    // Rows go through two LDS buffers: while one row is multiplied, the next
+    // is staged and the one after it is loaded.
+    int64_t row = blockIdx.x;
+    if (row < a.rows) {
+        load_row(row, cur);
+        stage(0);
         if (row + gridDim.x < a.rows)
-            load_row(row + gridDim.x, cur);  // the next row, in flight meanwhile
-        __syncthreads();
+            load_row(row + gridDim.x, cur);
+    }
+    __syncthreads();
+    int buf = 0;
+    for (; row < a.rows; row += gridDim.x, buf ^= 1) {
+        if (row + gridDim.x < a.rows) {
+            stage(buf ^ 1);
+            if (row + 2 * gridDim.x < a.rows)
+                load_row(row + 2 * gridDim.x, cur);
+        }
 
         // ---- Z[i'][j] on the matrix core
         f32x4 acc[kTPW][2];
@@ -247,20 +314,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int c = 0; c < KC; ++c) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                const u32x4 av = *(const u32x4 *)&xt[(16 * mt + l16) * kRS + 32 * c + 8 * rg];
+                const u32x4 av = *(const u32x4 *)&xt[buf][(16 * mt + l16) * kRS + 32 * c + 8 * rg];
 #pragma unroll
                 for (int tt = 0; tt < kTPW; ++tt)
-                    if (wave + kWaves * tt < kNT)
-                        acc[tt][mt] = mma<IN>(av, hb[tt][c], acc[tt][mt]);
+                    acc[tt][mt] = mma<IN>(av, hb[tt][c], acc[tt][mt]);
             }
         }
 
         // ---- 32-point butterflies over j = 16 mt + 4 rg + r, natural order
         float mx = 0.0f;
+        // (a duplicated last tile repeats values of the row: harmless to the
+        // maximum)
 #pragma unroll
         for (int tt = 0; tt < kTPW; ++tt) {
-            if (wave + kWaves * tt >= kNT)
-                continue;
             float v[2][4];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
