@@ -61,16 +61,19 @@ def source_hash() -> str:
 
 def _csv_means(path: str, counter: str) -> dict:
     """Mean per dispatch of `counter` for every (kernel name, grid size) in a
-    rocprofv3 counter_collection CSV, with the dispatch count."""
+    rocprofv3 counter_collection CSV, with the dispatch count and the first
+    dispatch id."""
     import csv
     acc: dict = {}
+    first: dict = {}
     with open(path) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] != counter:
                 continue
             key = (r["Kernel_Name"], int(r["Grid_Size"]))
             acc.setdefault(key, []).append(float(r["Counter_Value"]))
-    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+            first[key] = min(first.get(key, 1 << 62), int(r["Dispatch_Id"]))
+    return {k: (sum(v) / len(v), len(v), first[k]) for k, v in acc.items()}
 
 
 def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_bytes: int) -> dict:
@@ -83,7 +86,9 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_bytes: int
     fetch = _csv_means(fetch_csv, "FETCH_SIZE")
     write = _csv_means(write_csv, "WRITE_SIZE")
     copy_key = max((k for k in fetch if "copyBuffer" in k[0]), key=lambda k: fetch[k][1])
-    kern_key = max((k for k in fetch if "hq::" in k[0]), key=lambda k: fetch[k][0] * fetch[k][1])
+    # the timed launch: the first library kernel the script dispatches (the
+    # extras, inverse, append and attention, come after it)
+    kern_key = min((k for k in fetch if "hq::" in k[0]), key=lambda k: fetch[k][2])
     f_scale = copy_bytes / (fetch[copy_key][0] * 1024.0)
     w_scale = copy_bytes / (write[copy_key][0] * 1024.0)
     fb = fetch[kern_key][0] * 1024.0 * f_scale
