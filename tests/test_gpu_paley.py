@@ -124,3 +124,18 @@ def test_11008_many_rows_sampled(x_dtype, bits):
     ref = O.rotate_quant(raw[pick], x_dtype, n, s, bits, W.F32)
     P.check_codes(codes[pick], ref, bits, n, what=f"11008 sampled codes")
     P.check_scales(scales[pick], ref, W.F32, what=f"11008 sampled scales")
+
+
+def test_ffn_11008_full_at_full_size_sampled():
+    # the benchmarked call: 16384 x 11008 from the workload's own generator,
+    # in the launch configuration bench.py times; the oracle checks a sample
+    # of rows spread over every workgroup's range
+    w = W.WORKLOADS["ffn_11008_full"]
+    data = W.generate("ffn_11008_full", seed=42)
+    raw, s = data["x"], data["s"]
+    print(f"[paley] ffn_11008_full {raw.shape}", flush=True)
+    codes, scales = G.gpu_rotate_quant(raw, w.x_dtype, s, w.b, w.bits, w.scale_dtype)
+    pick = np.array([0, 1, 255, 256, 4095, 8191, 12000, 16128, 16383])
+    ref = O.rotate_quant(raw[pick], w.x_dtype, w.b, s, w.bits, w.scale_dtype)
+    P.check_codes(codes[pick], ref, w.bits, w.n, what="ffn_11008_full sampled codes")
+    P.check_scales(scales[pick], ref, w.scale_dtype, what="ffn_11008_full sampled scales")
