@@ -23,11 +23,13 @@
 // group and the register, so two of the five stages cross lanes.
 #include "hq_device.h"
 #include "hq_internal.h"
+#include "hq_fast_impl.h"  // the INT4 / INT8 code packers
 
 namespace hq {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -407,6 +409,322 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
+// ---------------------------------------------------------------------------
+// k = 344 (q = 343 = 7^3): H_k from its block structure.
+//
+// The additive group of GF(7^3) is Z_7^3 (digits c0, c1, c2 of a = c0 + 7 c1
+// + 49 c2), so chi(a - b) depends on the top digits only through
+// d = (a2 - b2) mod 7: the 343 x 343 core of H_k is 7 x 7 blocks of 49 x 49,
+// and block (a2, b2) is the same matrix K_d for every pair with the same d.
+// Each block is padded to 64 x 64 and the border of H_k goes into the
+// padding: input slot 49 of block 0 holds u[0] (the extra point), and
+//   K_d[sa][sb]  = chi(49 d + (sa - sb digit-wise)), sa, sb < 49,
+//                  with 1 on the diagonal of K_0 (the identity of H_k)
+//   K_d[49][sb]  = +1        (H_k[0][i'] = +1 for every i')
+//   K_d[sa][49]  = -1        (H_k[i][0] = -1 for i >= 1)
+//   K_d[49][49]  = +1        (H_k[0][0])
+// so that output (b2, sb < 49) is Z[1 + 49 b2 + sb] and output (b2, 49) is
+// Z[0] for every b2 (the copies with b2 > 0 are dropped; columns 50..63
+// are zero).  The product is 7 x 7 x 2 x 2 matrix-core steps per 16-column
+// tile and 32 rows j, 1.62 times the dense count, but a wave's share of H
+// (its 16 columns of every K_d) is 56 registers instead of 132, which
+// leaves room for a row of prefetch and for two workgroups per compute unit
+// that overlap their rows' phases.
+constexpr int kBW = 4;                   // waves per workgroup: one 16-column tile each
+constexpr int kBThreads = 64 * kBW;
+constexpr int kBTop = 7;                 // values of the top digit
+constexpr int kBBlk = 49;                // block size 7^2
+constexpr int kBPad = 64;                // padded block
+constexpr int kBK = 344;                 // Paley order
+constexpr int kBRS = kBTop * kBPad + 8;  // LDS row stride of the staged row (elements)
+constexpr int kBCPT = 6;                 // 16-byte chunks per thread: i = 64 cc + lane
+constexpr int kBOcc = 2;                 // workgroups per compute unit
+
+// entry (sa, sb) of the padded block K_d (see above); sq: the squares of
+// GF(343) by element index
+__device__ int block_entry(const unsigned char *sq, int d, int sa, int sb)
+{
+    if (sa < kBBlk && sb < kBBlk) {
+        if (d == 0 && sa == sb)
+            return 1;
+        const int d0 = (sa % 7 - sb % 7 + 7) % 7;
+        const int d1 = (sa / 7 - sb / 7 + 7) % 7;
+        return sq[d0 + 7 * d1 + 49 * d] ? 1 : -1;
+    }
+    if (sa < kBBlk && sb == kBBlk)
+        return -1;
+    if (sa == kBBlk && sb <= kBBlk)
+        return 1;
+    return 0;
+}
+
+template <int IN, int BITS>
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc))) void paley343_kernel(PaleyArgs a)
+{
+    constexpr int qmax = (1 << (BITS - 1)) - 1;
+    constexpr int n = kBK * kM2;
+    __shared__ __align__(16) uint16_t xt[kM2 * kBRS];             // [j][a2][slot]
+    __shared__ __align__(16) uint32_t cst[n * BITS / 32];         // the row's codes
+    __shared__ unsigned char sq[kBK];
+    __shared__ float red[kBW];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, rg = lane >> 4;
+
+    // ---- once: zero padding, the squares, this wave's 16 columns of every K_d
+    for (int t = tid; t < kM2 * kBRS / 8; t += kBThreads)
+        ((u32x4 *)xt)[t] = (u32x4){0u, 0u, 0u, 0u};
+    for (int t = tid; t < kBK; t += kBThreads)
+        sq[t] = 0;
+    __syncthreads();
+    for (int t = tid + 1; t < kBK - 1; t += kBThreads)
+        sq[gfp_square(t, a)] = 1;  // concurrent writes store the same 1
+    __syncthreads();
+    constexpr uint32_t kOne = IN == kBF16 ? 0x3F80u : 0x3C00u;
+    u32x4 bd[kBTop][2];
+#pragma unroll
+    for (int d = 0; d < kBTop; ++d)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int v = block_entry(sq, d, 32 * c + 8 * rg + 2 * p + h, 16 * wave + l16);
+                    const uint32_t bits = v == 0 ? 0u : (v > 0 ? kOne : (kOne | 0x8000u));
+                    w |= bits << (16 * h);
+                }
+                bd[d][c][p] = w;
+            }
+
+    // ---- the chunks this thread stages: chunk (i, wave) holds elements
+    // i * 32 + 8 * wave .. +7 (j = 8 wave .. +7), i = 64 cc + lane; its
+    // slot in the staged row and its signs are the same every row
+    // Signs of a chunk as one word: element 2p's at bit 15 - 4p and element
+    // 2p + 1's at bit 31 - 4p, so (w << 4p) & 0x80008000 is the sign mask of
+    // dword p.
+    uint32_t neg[kBCPT];
+#pragma unroll
+    for (int cc = 0; cc < kBCPT; ++cc) {
+        const int i = 64 * cc + lane;
+        uint32_t m = 0;
+        if (i < kBK)
+            for (int e = 0; e < 8; ++e)
+                m |= (a.s[i * kM2 + 8 * wave + e] < 0 ? 1u : 0u) << ((e & 1) ? 31 - 2 * (e - 1) : 15 - 2 * e);
+        neg[cc] = m;
+    }
+    u32x4 cur[kBCPT];
+    auto load_row = [&](int64_t row) {
+        const auto rs = rsrc((const uint16_t *)a.x + row * n, 2 * n);
+#pragma unroll
+        for (int cc = 0; cc < kBCPT; ++cc) {
+            const int i = 64 * cc + lane;
+            cur[cc] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rs, i < kBK ? 64 * i + 16 * wave : 0x7FFFFFF0, 0, kNonTemporal));
+        }
+    };
+    // the row held in cur into the staged layout, signs applied
+    auto stage = [&]() {
+#pragma unroll
+        for (int cc = 0; cc < kBCPT; ++cc) {
+            const int i = 64 * cc + lane;
+            if (i >= kBK)
+                continue;
+            const int slot = i == 0 ? kBBlk : kBPad * ((i - 1) / kBBlk) + (i - 1) % kBBlk;
+            uint16_t *dst = xt + 8 * wave * kBRS + slot;
+            // (opaque to the compiler: otherwise it keeps all 48 masks of
+            // the loop in registers)
+            uint32_t ng = neg[cc];
+            asm volatile("" : "+v"(ng));
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                // ((ng << 4p) & 0x80008000) ^ data in one v_bitop3_b32 (the
+                // data in the middle operand: the truth table is then the
+                // same whichever outer operand indexes its high bit)
+                const uint32_t wv = __builtin_amdgcn_bitop3_b32(ng << (4 * p), cur[cc][p], 0x80008000u, 0x6C);
+                dst[2 * p * kBRS] = (uint16_t)wv;
+                dst[(2 * p + 1) * kBRS] = (uint16_t)(wv >> 16);
+            }
+        }
+    };
+
+    const float sgn16 = (lane & 16) ? -1.0f : 1.0f;
+    const float sgn32 = (lane & 32) ? -1.0f : 1.0f;
+    const int sb = 16 * wave + l16;  // this lane's column in every block
+    // One row at a time per workgroup, the next one in flight: its loads go
+    // out as soon as the row before it is staged and are staged once this
+    // row's codes are in LDS.  Two workgroups per compute unit cover each
+    // other's barriers.
+    int64_t row = blockIdx.x;
+    if (row < a.rows) {
+        load_row(row);
+        stage();
+        if (row + gridDim.x < a.rows)
+            load_row(row + gridDim.x);
+    }
+    __syncthreads();
+    for (; row < a.rows; row += gridDim.x) {
+        // ---- Z on the matrix core: acc[b2][mt] = block row b2, j tile mt
+        f32x4 acc[kBTop][2];
+#pragma unroll
+        for (int b2 = 0; b2 < kBTop; ++b2)
+            acc[b2][0] = acc[b2][1] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int a2 = 0; a2 < kBTop; ++a2) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const u32x4 av = *(const u32x4 *)&xt[(16 * mt + l16) * kBRS + kBPad * a2 + 32 * c + 8 * rg];
+#pragma unroll
+                    for (int b2 = 0; b2 < kBTop; ++b2)
+                        acc[b2][mt] = mma<IN>(av, bd[(a2 - b2 + kBTop) % kBTop][c], acc[b2][mt]);
+                }
+            // (keeps the scheduler from hoisting every block's operand
+            // reads to the top, which would need 112 registers at once)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // ---- 32-point butterflies over j = 16 mt + 4 rg + r.  Bits 0, 1
+        // (r) and 4 (mt) are in registers.  Bits 2 and 3 cross lanes; each
+        // swap exchanges two registers at once, which hands the register
+        // index to the lanes and takes the j bit into the registers:
+        //  - bit 2 pairs mt = 0, 1: afterwards lane bit 4 is output bit 4 and
+        //    register slot s is output bit 2;
+        //  - bit 3 pairs b2 = 2k, 2k + 1: afterwards lane bit 5 is the low bit
+        //    of b2 and register 2k + t is output bit 3.  Block 6 has no
+        //    partner and keeps bit 3 on lane bit 5.
+        // So for k < 3 a lane ends with the 16 outputs j = 16 (lane bit 4) +
+        // r + 4 s + 8 t of row 1 + 49 (2k + lane bit 5) + sb, and with the 8
+        // outputs j = 16 (lane bit 4) + 8 (lane bit 5) + r + 4 s of block 6.
+        float mx = 0.0f;
+#pragma unroll
+        for (int b2 = 0; b2 < kBTop; ++b2)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const float a0 = acc[b2][mt][0] + acc[b2][mt][1], a1 = acc[b2][mt][0] - acc[b2][mt][1];
+                const float a2_ = acc[b2][mt][2] + acc[b2][mt][3], a3 = acc[b2][mt][2] - acc[b2][mt][3];
+                acc[b2][mt][0] = a0 + a2_;
+                acc[b2][mt][2] = a0 - a2_;
+                acc[b2][mt][1] = a1 + a3;
+                acc[b2][mt][3] = a1 - a3;
+            }
+#pragma unroll
+        for (int b2 = 0; b2 < kBTop; ++b2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float lo = acc[b2][0][r], hi = acc[b2][1][r];  // bit 4
+                const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo + hi), __float_as_uint(lo - hi),
+                                                                false, false);  // bit 2
+                const float x0 = __uint_as_float(w[0]), x1 = __uint_as_float(w[1]);
+                acc[b2][0][r] = x0 + x1;
+                acc[b2][1][r] = x0 - x1;
+            }
+#pragma unroll
+        for (int k = 0; k < kBTop / 2; ++k)
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[2 * k][sl][r]),
+                                                                    __float_as_uint(acc[2 * k + 1][sl][r]), false,
+                                                                    false);  // bit 3
+                    const float x0 = __uint_as_float(w[0]), x1 = __uint_as_float(w[1]);
+                    acc[2 * k][sl][r] = x0 + x1;
+                    acc[2 * k + 1][sl][r] = x0 - x1;
+                }
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[kBTop - 1][sl][r] = xbutterfly<32>(acc[kBTop - 1][sl][r], sgn32);
+        // padding columns are 0 and the copies of Z[0] repeat it: neither
+        // changes the maximum
+#pragma unroll
+        for (int b2 = 0; b2 < kBTop; ++b2)
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+                mx = fmaxf(fmaxf(mx, fmaxf(fabsf(acc[b2][sl][0]), fabsf(acc[b2][sl][1]))),
+                           fmaxf(fabsf(acc[b2][sl][2]), fabsf(acc[b2][sl][3])));
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        if (lane == 0)
+            red[wave] = mx;
+        __syncthreads();  // every wave is done with the staged row and its maximum is in
+        float m = red[0];
+#pragma unroll
+        for (int w = 1; w < kBW; ++w)
+            m = fmaxf(m, red[w]);
+        const RowQuant rq = row_quant(m, a.kq, qmax);
+
+        // ---- codes into LDS.  |y| <= m and inv is qmax / m to within an ulp,
+        // so |y * inv| < qmax + 1/2 and the codes need no clamp; the fma's
+        // constant is 1.5 * 2^23 plus the offset the packers expect.
+        constexpr float kMagic = BITS == 4 ? 12582920.0f : 12583040.0f;
+        auto fcode = [&](float v) { return __float_as_uint(__builtin_fmaf(v, rq.inv, kMagic)); };
+        const int lb4 = (lane >> 4) & 1, lb5 = lane >> 5;
+#pragma unroll
+        for (int k = 0; k < kBTop / 2; ++k) {
+            const int b2 = 2 * k + lb5;
+            if (sb > kBBlk || (sb == kBBlk && b2 > 0))
+                continue;
+            const int ip = sb == kBBlk ? 0 : 1 + kBBlk * b2 + sb;
+            const int e0 = ip * kM2 + 16 * lb4;  // the first of 16 consecutive outputs
+            uint32_t f[2][8];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        f[t][4 * sl + r] = fcode(acc[2 * k + t][sl][r]);
+            if constexpr (BITS == 4) {
+                *(u32x2 *)((uint8_t *)cst + (e0 >> 1)) = (u32x2){fast::pack_int4(f[0]), fast::pack_int4(f[1])};
+            } else {
+                *(u32x4 *)((uint8_t *)cst + e0) =
+                    (u32x4){fast::pack_int8(f[0][0], f[0][1], f[0][2], f[0][3]),
+                            fast::pack_int8(f[0][4], f[0][5], f[0][6], f[0][7]),
+                            fast::pack_int8(f[1][0], f[1][1], f[1][2], f[1][3]),
+                            fast::pack_int8(f[1][4], f[1][5], f[1][6], f[1][7])};
+            }
+        }
+        if (sb < kBBlk) {  // block 6
+            const int ip = 1 + kBBlk * (kBTop - 1) + sb;
+            const int e0 = ip * kM2 + 16 * lb4 + 8 * lb5;  // the first of 8 consecutive outputs
+            uint32_t f[8];
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    f[4 * sl + r] = fcode(acc[kBTop - 1][sl][r]);
+            if constexpr (BITS == 4)
+                *(uint32_t *)((uint8_t *)cst + (e0 >> 1)) = fast::pack_int4(f);
+            else
+                *(u32x2 *)((uint8_t *)cst + e0) =
+                    (u32x2){fast::pack_int8(f[0], f[1], f[2], f[3]), fast::pack_int8(f[4], f[5], f[6], f[7])};
+        }
+        if (row + gridDim.x < a.rows) {  // the next row (loaded one row ago) into the staged layout
+            stage();
+            if (row + 2 * gridDim.x < a.rows)
+                load_row(row + 2 * gridDim.x);
+        }
+        __syncthreads();  // the codes are in and the next row is staged
+        // ---- coalesced stores
+        constexpr int kVec = n * BITS / 8 / 16;
+        uint8_t *crow = (uint8_t *)a.codes + row * (int64_t)(n * BITS / 8);
+#pragma unroll
+        for (int t0 = 0; t0 < kVec; t0 += kBThreads)
+            if (t0 + tid < kVec)
+                ((u32x4 *)crow)[t0 + tid] = ((const u32x4 *)cst)[t0 + tid];
+        if (tid == 0)
+            ((float *)a.scales)[row] = rq.scale;
+    }
+}
+
 }  // namespace
 
 bool paley_mfma_available(const Request &r)
@@ -433,6 +751,22 @@ hipError_t launch_paley_mfma(const Request &r, const DeviceInfo &dev)
     pa.mod2 = r.paley.mod[2];
     const int qmax = r.bits == 8 ? 127 : 7;
     pa.kq = (float)(1.0 / (__builtin_sqrt((double)r.n) * qmax));
+    if (r.paley.k == kBK && r.paley.p == 7 && r.paley.e == 3) {
+        const int64_t g3 = kBOcc * (int64_t)dev.cu_count;
+        const int64_t grid3 = r.rows < g3 ? r.rows : g3;
+        if (r.x_dtype == kBF16) {
+            if (r.bits == 4)
+                hipLaunchKernelGGL((paley343_kernel<kBF16, 4>), dim3((unsigned)grid3), dim3(kBThreads), 0, r.stream, pa);
+            else
+                hipLaunchKernelGGL((paley343_kernel<kBF16, 8>), dim3((unsigned)grid3), dim3(kBThreads), 0, r.stream, pa);
+        } else {
+            if (r.bits == 4)
+                hipLaunchKernelGGL((paley343_kernel<kF16, 4>), dim3((unsigned)grid3), dim3(kBThreads), 0, r.stream, pa);
+            else
+                hipLaunchKernelGGL((paley343_kernel<kF16, 8>), dim3((unsigned)grid3), dim3(kBThreads), 0, r.stream, pa);
+        }
+        return hipGetLastError();
+    }
     const int64_t grid = r.rows < dev.cu_count ? r.rows : dev.cu_count;
     if (r.x_dtype == kBF16) {
         if (r.bits == 4)
