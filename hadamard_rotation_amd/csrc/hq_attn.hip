@@ -66,24 +66,47 @@ struct AttnArgs {
     float qscale;       // log2(e) / (sqrt(b) * sqrt(n)): rotation, softmax scale, base 2
 };
 
-// The query entries and sign bits this thread rotates: element
-// threadIdx.x + 256 r of the kv head's G rows, loads issued back to back.
-template <int DT, int G, int R>
-__device__ __forceinline__ void load_q_rows(const AttnArgs &a, int kh, float (&qv)[R], int (&sv)[R])
+// Barrier for LDS traffic only.  (__syncthreads() also orders global
+// memory, which makes every wave wait for all of its loads in flight first:
+// here those are the prefetched key and value codes.)
+__device__ __forceinline__ void lds_barrier()
 {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// The query entries and sign bytes this thread rotates (element
+// threadIdx.x + 256 r of the kv head's G rows) as raw dwords: one load each,
+// whatever the query type, so that nothing waits for them before the key
+// and value loads are issued; q_value() converts them afterwards.
+template <int G, int R>
+__device__ __forceinline__ void load_q_raw(const AttnArgs &a, int kh, uint32_t (&qw)[R], uint32_t (&sw)[R])
+{
+    const int esz = a.q_dtype == kF32 ? 4 : 2;
+    const auto rq = rsrc(a.q, a.q_heads * kHeadDim * esz);
+    const auto rs = rsrc(a.s, kHeadDim);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int i = threadIdx.x + 64 * kWaves * r;
         const int ic = i < G * kHeadDim ? i : G * kHeadDim - 1;
-        const int64_t e = (int64_t)kh * G * kHeadDim + ic;
-        if constexpr (DT == kF32)
-            qv[r] = ((const float *)a.q)[e];
-        else if constexpr (DT == kBF16)
-            qv[r] = bf16_to_f32(((const uint16_t *)a.q)[e]);
-        else
-            qv[r] = f16_to_f32(((const uint16_t *)a.q)[e]);
-        sv[r] = a.s[ic & (kHeadDim - 1)];
+        const int e = kh * G * kHeadDim + ic;
+        qw[r] = __builtin_amdgcn_raw_buffer_load_b32(rq, esz == 4 ? 4 * e : (2 * e) & ~3, 0, 0);
+        sw[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, (ic & (kHeadDim - 1)) & ~3, 0, 0);
     }
+}
+
+// entry r of load_q_raw as fp32, its sign applied
+template <int G>
+__device__ __forceinline__ float q_value(const AttnArgs &a, int kh, int r, uint32_t qw, uint32_t sw)
+{
+    const int i = threadIdx.x + 64 * kWaves * r;
+    const int ic = i < G * kHeadDim ? i : G * kHeadDim - 1;
+    const int e = kh * G * kHeadDim + ic;
+    const uint16_t h = (uint16_t)((e & 1) ? qw >> 16 : qw);
+    const float v = a.q_dtype == kF32 ? __uint_as_float(qw) : (a.q_dtype == kBF16 ? bf16_to_f32(h) : f16_to_f32(h));
+    const int8_t sg = (int8_t)(sw >> (8 * (ic & 3)));
+    return sg < 0 ? -v : v;
 }
 
 // Fast Walsh-Hadamard transform of `rows` rows of 128 floats in LDS, in
@@ -91,7 +114,7 @@ __device__ __forceinline__ void load_q_rows(const AttnArgs &a, int kh, float (&q
 __device__ void fwht_rows(float *L, int rows, int log_b)
 {
     for (int lh = 0; lh < log_b; ++lh) {
-        __syncthreads();
+        lds_barrier();
         const int h = 1 << lh;
         for (int p = threadIdx.x; p < rows * (kHeadDim / 2); p += blockDim.x) {
             const int r = p / (kHeadDim / 2), pp = p % (kHeadDim / 2);
@@ -102,7 +125,7 @@ __device__ void fwht_rows(float *L, int rows, int log_b)
             row[i + h] = x - y;
         }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 __device__ __forceinline__ float xmax16_32(float v)
@@ -214,6 +237,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         uint32_t s;      // one scale, raw bits (f16 or f32)
         uint32_t v[8];   // value codes: dimensions 8*l16 .. +7
     };
+    // The key and value loads are ordinary (cached) loads: a 128-byte line
+    // holds the rows of two kv heads, and the workgroup of the other head
+    // reads its second half at about the same time (same blockIdx.x; with
+    // a grid row length that is a multiple of 8, as at long caches, the
+    // round-robin placement puts it on the same XCD and its L2).
     // Loads go through buffer descriptors rebased to the step's first row
     // and cut off at the first row of a token >= lim: rows past the wave's
     // range read as 0 without touching memory.  Lane offsets (bytes from the
@@ -247,25 +275,25 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         const auto rk1 = rsrc(a.k_codes + row1 * (kHeadDim / 2), cb1);
         const auto rv0 = rsrc(a.v_codes + row0 * (kHeadDim / 2), cb0);
         const auto rv1 = rsrc(a.v_codes + row1 * (kHeadDim / 2), cb1);
-        r.k[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk0, ok_, 0, kNonTemporal));
-        r.k[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk1, ok_, 0, kNonTemporal));
+        r.k[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk0, ok_, 0, 0));
+        r.k[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk1, ok_, 0, 0));
         const int sb = span(row0, ssz);
         const auto rks = rsrc((const uint8_t *)a.k_scales + row0 * ssz, sb);
         const auto rvs = rsrc((const uint8_t *)a.v_scales + row0 * ssz, sb);
-        // lanes 0-7 of a row load key scales, lanes 8-15 value scales, into
-        // the same register
-        if (l16 < 8)
-            r.s = a.scale_f16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rks, os_, 0, 0)
-                              : __builtin_amdgcn_raw_buffer_load_b32(rks, os_, 0, 0);
-        else
-            r.s = a.scale_f16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rvs, os_, 0, 0)
-                              : __builtin_amdgcn_raw_buffer_load_b32(rvs, os_, 0, 0);
+        // lanes 0-7 of a row keep key scales, lanes 8-15 value scales, in
+        // the same register (both are loaded: no branch around a load, which
+        // would make the compiler's load-count waits wait for everything)
+        const uint32_t sk = a.scale_f16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rks, os_, 0, 0)
+                                        : __builtin_amdgcn_raw_buffer_load_b32(rks, os_, 0, 0);
+        const uint32_t sv = a.scale_f16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rvs, os_, 0, 0)
+                                        : __builtin_amdgcn_raw_buffer_load_b32(rvs, os_, 0, 0);
+        r.s = l16 < 8 ? sk : sv;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            r.v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv0, ov_[i], 0, kNonTemporal);
+            r.v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv0, ov_[i], 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            r.v[4 + i] = __builtin_amdgcn_raw_buffer_load_b32(rv1, ov_[i], 0, kNonTemporal);
+            r.v[4 + i] = __builtin_amdgcn_raw_buffer_load_b32(rv1, ov_[i], 0, 0);
     };
 
     // ---- the G query rows of this kv head, rotated and scaled, in LDS; the
@@ -273,24 +301,18 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     // Their loads are issued first and all at once; the first two steps'
     // codes follow and stay in flight while the rows are prepared.
     constexpr int kQPer = (G * kHeadDim + 64 * kWaves - 1) / (64 * kWaves);
-    float qv[kQPer];
-    int sv[kQPer];
-    if (a.q_dtype == kF32)
-        load_q_rows<kF32, G, kQPer>(a, kh, qv, sv);
-    else if (a.q_dtype == kBF16)
-        load_q_rows<kBF16, G, kQPer>(a, kh, qv, sv);
-    else
-        load_q_rows<kF16, G, kQPer>(a, kh, qv, sv);
+    uint32_t qw[kQPer], sw[kQPer];
+    load_q_raw<G, kQPer>(a, kh, qw, sw);
+    // the first two steps' data, in flight during the set-up (an empty or
+    // short range reads 0 without touching memory; no branch, see above)
     Pair pa, pb;
-    if (b0 < b1) {  // the first two steps' data, in flight during the set-up
-        load_pair(b0, pa);
-        load_pair(b0 + 2, pb);  // past the range: reads 0
-    }
+    load_pair(b0, pa);
+    load_pair(b0 + 2, pb);
 #pragma unroll
     for (int r = 0; r < kQPer; ++r) {
         const int i = threadIdx.x + 64 * kWaves * r;
         if (i < G * kHeadDim)
-            qrot[i] = sv[r] < 0 ? -qv[r] : qv[r];
+            qrot[i] = q_value<G>(a, kh, r, qw[r], sw[r]);
     }
     fwht_rows(qrot, G, a.log_b);
     for (int g = wave; g < G; g += kWaves) {  // row maxima, one wave per row
@@ -305,7 +327,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
             qpow[g] = mx > 0.0f ? ldexpf(1.0f, 10 - e) : 1.0f;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- B operands of the scores: column n < 2G holds query row n mod G
     // (hi halves in bqh, lo halves in bql; the copies in columns G..2G-1 give
@@ -338,7 +360,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         bq_lds[0][wave][lane] = h;
         bq_lds[1][wave][lane] = l;
     }
-    __syncthreads();
+    lds_barrier();
     u32x4 bqh[4], bql[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -532,7 +554,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
         pm[wave][lane] = m_run - (float)wexp;
         pl[wave][lane] = l_run;
     }
-    __syncthreads();
+    lds_barrier();
     for (int t = threadIdx.x; t < G * kHeadDim; t += 64 * kWaves) {
         const int g = t / kHeadDim, dd = t % kHeadDim;
         float M = pm[0][g];
@@ -570,10 +592,10 @@ __device__ float block_reduce(float v, float *red, bool is_max)
         const float o = __shfl_xor(v, off, 64);
         v = is_max ? fmaxf(v, o) : v + o;
     }
-    __syncthreads();
+    lds_barrier();
     if ((threadIdx.x & 63) == 0)
         red[threadIdx.x >> 6] = v;
-    __syncthreads();
+    lds_barrier();
     float r = red[0];
     for (int w = 1; w < kMergeThreads / 64; ++w)
         r = is_max ? fmaxf(r, red[w]) : r + red[w];
@@ -627,7 +649,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a)
     for (int p = grp + kMergeGroups * kMergeChunk; p < a.nws; p += kMergeGroups)
         acc = __builtin_fmaf(e_part[p], base[(int64_t)p * kPartStride + d], acc);
     osum[grp][d] = acc;
-    __syncthreads();
+    lds_barrier();
     if (tid < kHeadDim) {
         float t = 0.0f;
 #pragma unroll
