@@ -66,16 +66,6 @@ struct AttnArgs {
     float qscale;       // log2(e) / (sqrt(b) * sqrt(n)): rotation, softmax scale, base 2
 };
 
-// Barrier for LDS traffic only.  (__syncthreads() also orders global
-// memory, which makes every wave wait for all of its loads in flight first:
-// here those are the prefetched key and value codes.)
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // The query entries and sign bytes this thread rotates (element
 // threadIdx.x + 256 r of the kv head's G rows) as raw dwords: one load each,
 // whatever the query type, so that nothing waits for them before the key

@@ -26,6 +26,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes)
 }
 constexpr int kNonTemporal = 2;  // buffer cache-policy bit: nt
 
+// Workgroup barrier for LDS traffic only.  __syncthreads() also orders
+// global memory, which makes every wave wait for all of its loads and
+// stores in flight first (prefetched rows, earlier rows' stores).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // 1.5 * 2^23: adding it to a value v with |v| < 2^22 leaves round_half_even(v)
 // in the low mantissa bits, because the sum's unit in the last place is 1.
 constexpr float kRoundMagic = 12582912.0f;

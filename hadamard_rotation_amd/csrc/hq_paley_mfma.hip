@@ -132,10 +132,10 @@ __device__ void paley_build(PaleyLds &L, const PaleyArgs &g, int words)
         }
         L.digits[a] = code;
     }
-    __syncthreads();
+    lds_barrier();
     for (int a = threadIdx.x + 1; a < q; a += kThreads)
         L.square[gfp_square(a, g)] = 1;  // concurrent writes store the same 1
-    __syncthreads();
+    lds_barrier();
     // H_k[i][i']: row 0 all +1; column 0 -1 below row 0; 1 on the diagonal;
     // chi(a - b) for a = i - 1, b = i' - 1 elsewhere
     for (int idx = threadIdx.x; idx < g.k * words; idx += kThreads) {
@@ -155,7 +155,7 @@ __device__ void paley_build(PaleyLds &L, const PaleyArgs &g, int words)
         }
         L.hbits[idx] = bits;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // One B operand from the bit matrix: H_k[i][i'] for i = 32c + 8rg + e
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (row + gridDim.x < a.rows)
             load_row(row + gridDim.x, cur);
     }
-    __syncthreads();
+    lds_barrier();
     int buf = 0;
     for (; row < a.rows; row += gridDim.x, buf ^= 1) {
         if (row + gridDim.x < a.rows) {
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             mx = fmaxf(mx, __shfl_xor(mx, off, 64));
         if (lane == 0)
             red[wave] = mx;
-        __syncthreads();
+        lds_barrier();
         float m = red[0];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w)
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     cst[e0 >> 2] = w;
             }
         }
-        __syncthreads();
+        lds_barrier();
         // ---- coalesced stores
         const int cbytes = n * BITS / 8;
         uint8_t *crow = (uint8_t *)a.codes + row * (int64_t)cbytes;
@@ -478,10 +478,10 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
         ((u32x4 *)xt)[t] = (u32x4){0u, 0u, 0u, 0u};
     for (int t = tid; t < kBK; t += kBThreads)
         sq[t] = 0;
-    __syncthreads();
+    lds_barrier();
     for (int t = tid + 1; t < kBK - 1; t += kBThreads)
         sq[gfp_square(t, a)] = 1;  // concurrent writes store the same 1
-    __syncthreads();
+    lds_barrier();
     constexpr uint32_t kOne = IN == kBF16 ? 0x3F80u : 0x3C00u;
     u32x4 bd[kBTop][2];
 #pragma unroll
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
         if (row + gridDim.x < a.rows)
             load_row(row + gridDim.x);
     }
-    __syncthreads();
+    lds_barrier();
     for (; row < a.rows; row += gridDim.x) {
         // ---- Z on the matrix core: acc[b2][mt] = block row b2, j tile mt
         f32x4 acc[kBTop][2];
@@ -654,7 +654,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
             mx = fmaxf(mx, __shfl_xor(mx, off, 64));
         if (lane == 0)
             red[wave] = mx;
-        __syncthreads();  // every wave is done with the staged row and its maximum is in
+        lds_barrier();  // every wave is done with the staged row and its maximum is in
         float m = red[0];
 #pragma unroll
         for (int w = 1; w < kBW; ++w)
@@ -712,7 +712,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
             if (row + 2 * gridDim.x < a.rows)
                 load_row(row + 2 * gridDim.x);
         }
-        __syncthreads();  // the codes are in and the next row is staged
+        lds_barrier();  // the codes are in and the next row is staged
         // ---- coalesced stores
         constexpr int kVec = n * BITS / 8 / 16;
         uint8_t *crow = (uint8_t *)a.codes + row * (int64_t)(n * BITS / 8);
