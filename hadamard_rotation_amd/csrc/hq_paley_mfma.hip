@@ -437,7 +437,7 @@ constexpr int kBBlk = 49;                // block size 7^2
 constexpr int kBPad = 64;                // padded block
 constexpr int kBK = 344;                 // Paley order
 constexpr int kBRS = kBTop * kBPad + 8;  // LDS row stride of the staged row (elements)
-constexpr int kBCPT = 6;                 // 16-byte chunks per thread: i = 64 cc + lane
+constexpr int kBCPT = 6;                 // 16-byte chunks per thread (6 x 256 >= 1376)
 constexpr int kBOcc = 2;                 // workgroups per compute unit
 
 // entry (sa, sb) of the padded block K_d (see above); sq: the squares of
@@ -500,20 +500,21 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
                 bd[d][c][p] = w;
             }
 
-    // ---- the chunks this thread stages: chunk (i, wave) holds elements
-    // i * 32 + 8 * wave .. +7 (j = 8 wave .. +7), i = 64 cc + lane; its
-    // slot in the staged row and its signs are the same every row
+    // ---- the chunks this thread stages: chunk q = 256 cc + tid holds the
+    // elements 8q .. 8q + 7 of a row, i.e. i = q / 4 and j = 8 (q % 4) .. +7,
+    // so a wave's load is 1 KB of contiguous memory; the chunk's slot in the
+    // staged row and its signs are the same every row
     // Signs of a chunk as one word: element 2p's at bit 15 - 4p and element
     // 2p + 1's at bit 31 - 4p, so (w << 4p) & 0x80008000 is the sign mask of
     // dword p.
     uint32_t neg[kBCPT];
 #pragma unroll
     for (int cc = 0; cc < kBCPT; ++cc) {
-        const int i = 64 * cc + lane;
+        const int q = kBThreads * cc + tid;
         uint32_t m = 0;
-        if (i < kBK)
+        if (q < kBK * kM2 / 8)
             for (int e = 0; e < 8; ++e)
-                m |= (a.s[i * kM2 + 8 * wave + e] < 0 ? 1u : 0u) << ((e & 1) ? 31 - 2 * (e - 1) : 15 - 2 * e);
+                m |= (a.s[8 * q + e] < 0 ? 1u : 0u) << ((e & 1) ? 31 - 2 * (e - 1) : 15 - 2 * e);
         neg[cc] = m;
     }
     u32x4 cur[kBCPT];
@@ -521,20 +522,21 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
         const auto rs = rsrc((const uint16_t *)a.x + row * n, 2 * n);
 #pragma unroll
         for (int cc = 0; cc < kBCPT; ++cc) {
-            const int i = 64 * cc + lane;
+            const int q = kBThreads * cc + tid;
             cur[cc] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    rs, i < kBK ? 64 * i + 16 * wave : 0x7FFFFFF0, 0, kNonTemporal));
+                                                    rs, q < kBK * kM2 / 8 ? 16 * q : 0x7FFFFFF0, 0, 0));
         }
     };
     // the row held in cur into the staged layout, signs applied
     auto stage = [&]() {
 #pragma unroll
         for (int cc = 0; cc < kBCPT; ++cc) {
-            const int i = 64 * cc + lane;
+            const int q = kBThreads * cc + tid;
+            const int i = q >> 2;
             if (i >= kBK)
                 continue;
             const int slot = i == 0 ? kBBlk : kBPad * ((i - 1) / kBBlk) + (i - 1) % kBBlk;
-            uint16_t *dst = xt + 8 * wave * kBRS + slot;
+            uint16_t *dst = xt + 8 * (q & 3) * kBRS + slot;
             // (opaque to the compiler: otherwise it keeps all 48 masks of
             // the loop in registers)
             uint32_t ng = neg[cc];

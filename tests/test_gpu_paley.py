@@ -3,8 +3,10 @@ H_n = H_k (x) H_(n/k), H_k from Paley's first construction (the Kronecker
 route of [RQ] "旋转量化：大模型低比特量化中的离群值克星" section 2.1, for the full-width
 block size of the [MS] "QuaRot：基于旋转的离群值抑制算法说明" YAML table).
 
-Widths: 48 = 12 x 4, 96 = 12 x 8, 160 = 20 x 8, 688 = 344 x 2 and the FFN
-width 11008 = 344 x 32 (Paley over GF(7^3)).  Inputs are seeded Gaussians
+Widths: 48 = 12 x 4, 96 = 12 x 8, 160 = 20 x 8, 688 = 344 x 2, the FFN
+width 11008 = 344 x 32 (Paley over GF(7^3): the block-circulant matrix-core
+kernel) and 10624 = 332 x 32, 11136 = 348 x 32 (prime fields: the dense
+matrix-core kernel).  Inputs are seeded Gaussians
 with outlier channels; expected values come from the oracle only, with the
 tolerances of oracle/parity.py.
 """
@@ -49,6 +51,8 @@ CASES = [
     (688, 19, W.BF16, 4, W.F32),
     (11008, 6, W.BF16, 4, W.F32),
     (11008, 3, W.F32, 8, W.F16),
+    (10624, 5, W.BF16, 4, W.F32),
+    (11136, 4, W.F16, 8, W.F32),
 ]
 
 
