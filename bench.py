@@ -9,7 +9,11 @@ per-token INT4, fp32 scales; --group G times hq_rotate_quant_grouped with one
 scale per G rotated elements instead).  The inputs are resident in HBM before timing
 starts; steps cycle through several independent buffer sets whose total
 size is well above the 256 MB last-level cache, so every step streams from
-HBM.  Rank 0 prints one JSON line.
+HBM.  Before the W warm-up steps the same call runs untimed for at least
+SETTLE_S seconds: on this GPU the first tens of milliseconds of a burst of
+calls run up to 60 % slower while clocks and translation caches settle, and
+the timed steps are meant to measure the steady state.  Rank 0 prints one
+JSON line.
 
 `value` is GB/s of algorithmic traffic (input + codes + scales) per second of
 kernel time; `roofline` relates it to the 8 TB/s HBM peak; `cpu_baseline` is
@@ -34,6 +38,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 LLC_BYTES = 256 * 2 ** 20
 METRIC = "fused rotate+INT4-quant GB/s and % of HBM peak at 16384x4096 bf16"
+SETTLE_S = 0.05  # untimed calls before the warm-up steps (see the docstring)
 
 
 def copy_bytes_for(bytes_call: int) -> int:
@@ -237,7 +242,7 @@ def time_attention(dev, stream, ev0, ev1, tokens: int = 131072, kv_heads: int = 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="hidden_4096")
     ap.add_argument("--group", type=int, default=None,
@@ -316,6 +321,14 @@ def main(argv=None):
             hq.hq_dequant_rotate_inv_grouped(codes[k], scales[k], s, w.b, g, w.bits, y=y,
                                              stream=stream)
 
+    # untimed settle phase (at least SETTLE_S seconds of the same calls)
+    t_settle = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for _ in range(20):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
