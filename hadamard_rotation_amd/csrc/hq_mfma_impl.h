@@ -598,9 +598,12 @@ hipError_t launch_one(const Request &r, const DeviceInfo &dev)
     constexpr int TPR = LOGN > 9 ? 1 << (LOGN - 9) : 1;
     const size_t lds = TPR > 1 ? (size_t)TPR * 64 * 16 : 0;
     auto fn = mfma_kernel<OP, IN, T, LOGB, LOGN, LOGG, APPEND>;
-    // One workgroup per CU with every wave the CU can hold, at most 16
-    // (measured on the 128-wide K/V rows: 16 waves per CU beat 20 by 10 %).
-    const int max_threads = T < 8 ? 1024 : 768;
+    // One workgroup per CU with every wave the CU can hold, at most 16 for
+    // groups of 2 tiles and 12 otherwise (steady-state timings: 131072 x 128
+    // rows 9.8 us with 16 waves, 10.4 with 12; 1048576 x 128 rows, groups of
+    // 4 tiles, 54.6 us with 12, 55.1 with 16; 16384 x 4096, 8 tiles, 31.3 us
+    // with 12, 31.7 with 16, 31.8 with 8).
+    const int max_threads = T == 2 ? 1024 : 768;
     int waves_cu = occupancy_waves((const void *)fn, lds);
     if (waves_cu > max_threads / 64)
         waves_cu = max_threads / 64;
