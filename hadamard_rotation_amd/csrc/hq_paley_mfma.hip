@@ -1,7 +1,9 @@
-// hq_paley_mfma.hip -- matrix-core kernel for the full-width rotation of rows
-// whose width is not a power of two: n = k * 32, H_n = H_k (x) H_32 with H_k
-// from Paley's first construction (e.g. the FFN width 11008 = 344 x 32 over
-// GF(7^3)), fused with the per-row quantiser.
+// hq_paley_mfma.hip -- matrix-core kernels for the full-width rotation of
+// rows whose width is not a power of two: n = k * 32, H_n = H_k (x) H_32 with
+// H_k from Paley's first construction, fused with the per-row quantiser.
+// paley343_kernel takes k = 344 (the FFN width 11008, GF(7^3)) from the
+// block structure of H_344 (see its own comment); paley_mfma_kernel takes
+// the other orders in (320, 352] as one dense product.
 //
 // Pages cited: [RQ] "旋转量化：大模型低比特量化中的离群值克星" section 2.1 (larger
 // Hadamard matrices as Kronecker products; the transform is additions and
