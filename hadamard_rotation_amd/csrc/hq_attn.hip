@@ -568,90 +568,97 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     }
 }
 
-// One workgroup of 1024 threads per query head: merge the partials (the
-// largest maximum, the rescaled sums, the rescaled accumulators), rotate the
-// result back, store.  exp2(m_p - M) of every partial is kept in LDS; eight
-// groups of 128 threads take every eighth partial.
-constexpr int kMergeThreads = 1024;
-constexpr int kMergeGroups = kMergeThreads / kHeadDim;
-constexpr int kMergeChunk = 16;  // partials per thread whose loads go out at once
+// One workgroup of 4 waves per query head.  Each wave merges every 4th
+// partial online (the largest maximum so far, the rescaled sums and
+// accumulators), lane l holding dimensions 2l and 2l + 1; the partials'
+// loads go out 24 at a time.  The four waves meet once in LDS, and wave
+// 0 divides by the sum, rotates back with butterflies between lanes and
+// applies the signs.
+constexpr int kMergeWaves = 4;
+constexpr int kMergeBatch = 24;  // partials per wave whose loads go out together (96 per head: one round)
 
-__device__ float block_reduce(float v, float *red, bool is_max)
+__global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(AttnArgs a)
 {
-    for (int off = 32; off > 0; off >>= 1) {
-        const float o = __shfl_xor(v, off, 64);
-        v = is_max ? fmaxf(v, o) : v + o;
-    }
-    lds_barrier();
-    if ((threadIdx.x & 63) == 0)
-        red[threadIdx.x >> 6] = v;
-    lds_barrier();
-    float r = red[0];
-    for (int w = 1; w < kMergeThreads / 64; ++w)
-        r = is_max ? fmaxf(r, red[w]) : r + red[w];
-    return r;
-}
-
-__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a)
-{
-    extern __shared__ float e_part[];  // [nws]
-    __shared__ float red[kMergeThreads / 64];
-    __shared__ float osum[kMergeGroups][kHeadDim];
-    __shared__ float o[kHeadDim];
-    const int tid = threadIdx.x;
+    __shared__ float wm[kMergeWaves], wl[kMergeWaves];
+    __shared__ float2 wo[kMergeWaves][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int h = blockIdx.x;
     const float *base = a.ws + (int64_t)h * a.nws * kPartStride;
-    const int d = tid & (kHeadDim - 1), grp = tid / kHeadDim;
-    // Every load of the first kMergeChunk partials per thread group is issued
-    // before anything waits: one round trip for up to 8 * kMergeChunk
-    // partials per head.
-    float ov[kMergeChunk];
+    float M = -INFINITY, L = 0.0f;
+    float2 O = make_float2(0.0f, 0.0f);
+    for (int p0 = wave; p0 < a.nws; p0 += kMergeBatch * kMergeWaves) {
+        float mp[kMergeBatch], lp[kMergeBatch];
+        float2 op[kMergeBatch];
 #pragma unroll
-    for (int r = 0; r < kMergeChunk; ++r) {
-        const int p = grp + kMergeGroups * r;
-        ov[r] = p < a.nws ? base[(int64_t)p * kPartStride + d] : 0.0f;
-    }
-    float m = -INFINITY, pl = 0.0f;
-    if (tid < a.nws) {
-        m = base[(int64_t)tid * kPartStride + kHeadDim];
-        pl = base[(int64_t)tid * kPartStride + kHeadDim + 1];
-    }
-    for (int p = tid + kMergeThreads; p < a.nws; p += kMergeThreads)
-        m = fmaxf(m, base[(int64_t)p * kPartStride + kHeadDim]);
-    const float M = block_reduce(m, red, true);
-    float l = 0.0f;
-    for (int p = tid; p < a.nws; p += kMergeThreads) {
-        const float pm = p == tid ? m : base[(int64_t)p * kPartStride + kHeadDim];
-        const float pp = p == tid ? pl : base[(int64_t)p * kPartStride + kHeadDim + 1];
-        // partials of empty token ranges (sum 0) carry nothing
-        const float e = pp > 0.0f ? __builtin_amdgcn_exp2f(pm - M) : 0.0f;
-        e_part[p] = e;
-        l = __builtin_fmaf(e, pp, l);
-    }
-    const float L = block_reduce(l, red, false);  // also orders the e_part writes
-    float acc = 0.0f;
+        for (int k = 0; k < kMergeBatch; ++k) {
+            // (past the end: partial 0 is read and given no weight; no
+            // branch around the loads)
+            const int p = p0 + k * kMergeWaves;
+            const bool ok = p < a.nws;
+            const float *b = base + (int64_t)(ok ? p : 0) * kPartStride;
+            const float m = b[kHeadDim], l = b[kHeadDim + 1];
+            const float2 o = *(const float2 *)(b + 2 * lane);
+            mp[k] = m;
+            lp[k] = ok ? l : 0.0f;  // partials of empty token ranges (sum 0) carry nothing
+            op[k] = o;
+        }
+        float cm = M;
 #pragma unroll
-    for (int r = 0; r < kMergeChunk; ++r) {
-        const int p = grp + kMergeGroups * r;
-        if (p < a.nws)
-            acc = __builtin_fmaf(e_part[p], ov[r], acc);
+        for (int k = 0; k < kMergeBatch; ++k)
+            cm = lp[k] > 0.0f ? fmaxf(cm, mp[k]) : cm;
+        const float f = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - cm);  // cm >= M
+        L *= f;
+        O.x *= f;
+        O.y *= f;
+        M = cm;
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+            const float e = lp[k] > 0.0f ? __builtin_amdgcn_exp2f(mp[k] - M) : 0.0f;
+            L = __builtin_fmaf(e, lp[k], L);
+            O.x = __builtin_fmaf(e, op[k].x, O.x);
+            O.y = __builtin_fmaf(e, op[k].y, O.y);
+        }
     }
-    for (int p = grp + kMergeGroups * kMergeChunk; p < a.nws; p += kMergeGroups)
-        acc = __builtin_fmaf(e_part[p], base[(int64_t)p * kPartStride + d], acc);
-    osum[grp][d] = acc;
+    if (lane == 0) {
+        wm[wave] = M;
+        wl[wave] = L;
+    }
+    wo[wave][lane] = O;
     lds_barrier();
-    if (tid < kHeadDim) {
-        float t = 0.0f;
+    if (wave != 0)
+        return;
+    float Mt = -INFINITY;
 #pragma unroll
-        for (int g = 0; g < kMergeGroups; ++g)
-            t += osum[g][tid];
-        o[tid] = t / L;
+    for (int w = 0; w < kMergeWaves; ++w)
+        Mt = wl[w] > 0.0f ? fmaxf(Mt, wm[w]) : Mt;
+    float Lt = 0.0f, x0 = 0.0f, x1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) {
+        const float e = wl[w] > 0.0f ? __builtin_amdgcn_exp2f(wm[w] - Mt) : 0.0f;
+        Lt = __builtin_fmaf(e, wl[w], Lt);
+        x0 = __builtin_fmaf(e, wo[w][lane].x, x0);
+        x1 = __builtin_fmaf(e, wo[w][lane].y, x1);
     }
-    fwht_rows(o, 1, a.log_b);
-    if (tid < kHeadDim) {
-        const float v = o[tid] * a.rb;
-        a.out[(int64_t)h * kHeadDim + tid] = a.s[tid] < 0 ? -v : v;
+    x0 /= Lt;
+    x1 /= Lt;
+    // inverse rotation in blocks of 2^log_b: dimension bit 0 in the lane,
+    // bits 1..log_b-1 across lanes (lane bits 0..)
+    if (a.log_b > 0) {
+        const float t0 = x0 + x1, t1 = x0 - x1;
+        x0 = t0;
+        x1 = t1;
     }
+    for (int k = 1; k < a.log_b; ++k) {
+        const int m = 1 << (k - 1);
+        const float p0 = __shfl_xor(x0, m, 64), p1 = __shfl_xor(x1, m, 64);
+        const bool up = (lane & m) != 0;
+        x0 = up ? p0 - x0 : x0 + p0;
+        x1 = up ? p1 - x1 : x1 + p1;
+    }
+    const int8_t s0 = a.s[2 * lane], s1 = a.s[2 * lane + 1];
+    const float v0 = x0 * a.rb, v1 = x1 * a.rb;
+    *(float2 *)&a.out[(int64_t)h * kHeadDim + 2 * lane] = make_float2(s0 < 0 ? -v0 : v0, s1 < 0 ? -v1 : v1);
 }
 
 int parts_for(int kv_heads, int64_t tokens)
@@ -675,8 +682,7 @@ hipError_t launch_g(const AttnArgs &aa, hipStream_t st)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(aa.q_heads), dim3(kMergeThreads),
-                       (size_t)aa.nws * sizeof(float), st, aa);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(aa.q_heads), dim3(64 * kMergeWaves), 0, st, aa);
     return hipGetLastError();
 }
 
