@@ -36,7 +36,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // BITS  4 or 8
 // T, LOGB, LOGN as in mfma_kernel
 template <int OUT, int BITS, int T, int LOGB, int LOGN>
-__global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_inv_kernel(MfmaArgs a)
+__global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_kernel(MfmaArgs a)
 {
     extern __shared__ __align__(16) u32x4 lds_osg[];   // n > 512: [tile of row][lane][2]
     constexpr int D = LOGB - 5 < 4 ? LOGB - 5 : 4;      // DPP stages (lane bits 0..D-1)
@@ -360,10 +360,13 @@ hipError_t launch_inv_one(const Request &r, const DeviceInfo &dev)
     constexpr int TPR = LOGN > 9 ? 1 << (LOGN - 9) : 1;
     const size_t lds = TPR > 1 ? (size_t)TPR * 64 * 32 : 0;
     auto fn = mfma_inv_kernel<OUT, BITS, T, LOGB, LOGN>;
-    // every wave the CU holds, except 8 for fp32 rows of narrow groups
-    // (1048576 x 128 fp32: 141 us at 8 waves, 210 us at 12-16)
+    // every wave the CU holds, up to a cap per case (steady-state timings):
+    // fp32 out, narrow groups 8 (1048576 x 128: 142 us at 8 waves, 210 at
+    // 12, 215 at 16); fp32 out, 8-tile groups 16 (16384 x 4096: 65.5 us at
+    // 16, 68.1 at 12, 74.5 at 8); bf16 out 16 for narrow groups and 12 for
+    // 8-tile groups (33.0 us at 12, 33.2 at 16)
     int waves_cu = occupancy_waves((const void *)fn, lds);
-    const int cap = (OUT == kF32 && T < 8) ? 8 : (T < 8 ? 16 : 12);
+    const int cap = OUT == kF32 ? (T < 8 ? 8 : 16) : (T < 8 ? 16 : 12);
     if (waves_cu > cap)
         waves_cu = cap;
     int64_t grid = dev.cu_count;
