@@ -34,9 +34,24 @@ int g_occ_used = 0;
 // blocks: the forward paths on a 16-bit type, and the inverse path with one
 // scale per row (its codes are exact in f16; group-wise scales make the
 // dequantised values inexact there and stay on the butterfly kernel).
+bool wide_inv_ok(const Request &r)
+{
+    // the inverse of 128-blocks as rows of one block: rows wider than the
+    // per-row plans take (or not a power of two), or one scale per block
+    if (r.op != kDequantInv || r.b != 128 || r.n <= 128 || r.n % 128 != 0)
+        return false;
+    const bool pow2 = (r.n & (r.n - 1)) == 0;
+    const bool per_row_planned = pow2 && r.n <= 4096;
+    if (!(r.group == 128 || (r.group == r.n && !per_row_planned)))
+        return false;
+    return r.rows * (int64_t)(r.n / 128) < ((int64_t)1 << 31);
+}
+
 bool plan_ok(const Request &r)
 {
     if (r.op == kDequantInv) {
+        if (wide_inv_ok(r))
+            return true;
         if (r.group != r.n)
             return false;
     } else if (r.x_dtype != kBF16 && r.x_dtype != kF16) {

@@ -75,6 +75,12 @@ struct MfmaArgs {
     int scale_f16;
     float kq;         // 1 / (sqrt(b) * qmax)
     float rb;         // 1 / sqrt(b)
+    // inverse of rows wider than one block, run as rows of one 128-block
+    // (rows and n above count blocks): blocks per real row, its inverse,
+    // and whether a scale belongs to a real row (else to each block)
+    int wide_div;
+    double wide_rdiv;
+    int wide_row_scale;
 };
 
 // 16x16x32 product of the +-1 slice a with the 16-bit tile b (fp32 sums).
@@ -587,6 +593,7 @@ namespace mfma {
 
 // Host side (hq_mfma.hip): plan check, argument setup and the launch.
 bool plan_ok(const Request &r);
+bool wide_inv_ok(const Request &r);
 void fill_args(MfmaArgs &ma, const Request &r, int tiles_per_group);
 int occupancy_waves(const void *fn, size_t lds);
 

@@ -35,9 +35,13 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // OUT   output dtype (kF32 or kBF16)
 // BITS  4 or 8
 // T, LOGB, LOGN as in mfma_kernel
-template <int OUT, int BITS, int T, int LOGB, int LOGN>
+// WIDE  rows wider than one block, run as rows of one 128-block (LOGB =
+//       LOGN = 7): each block row takes the scale of its real row (or its
+//       own, one scale per block) and the signs of its place in the real row
+template <int OUT, int BITS, int T, int LOGB, int LOGN, bool WIDE = false>
 __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_kernel(MfmaArgs a)
 {
+    static_assert(!WIDE || (LOGB == 7 && LOGN == 7), "wide rows run as 128-blocks");
     extern __shared__ __align__(16) u32x4 lds_osg[];   // n > 512: [tile of row][lane][2]
     constexpr int D = LOGB - 5 < 4 ? LOGB - 5 : 4;      // DPP stages (lane bits 0..D-1)
     constexpr int R = LOGB > 9 ? LOGB - 9 : 0;          // tile-bit stages
@@ -123,6 +127,15 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
     struct Raw {
         uint32_t c[T][CW];
         uint32_t s[NS];
+        u32x2 sg[WIDE ? T : 1];  // WIDE: sign bytes of the lane's 8 outputs per tile
+    };
+    // WIDE: the real row of block row vr (vr < 2^31; the double product is
+    // within one of the quotient, and one step corrects it)
+    auto wide_row = [&](int64_t vr) -> int64_t {
+        int64_t q = (int64_t)((double)vr * a.wide_rdiv);
+        const int64_t rem = vr - q * a.wide_div;
+        q += rem < 0 ? -1 : (rem >= a.wide_div ? 1 : 0);
+        return q;
     };
     auto load = [&](int64_t g, Raw &raw) {
         const int64_t e0 = group_elem0(g);
@@ -162,8 +175,17 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
         for (int i = 0; i < NS; ++i) {
             int64_t row = LOGN >= 9 ? (e0 >> LOGN) + i : (e0 + i * 512 + lane_off) >> LOGN;
             row = row < row_last ? row : row_last;
-            raw.s[i] = a.scale_f16 ? (uint32_t)((const uint16_t *)a.scales)[row]
-                                   : ((const uint32_t *)a.scales)[row];
+            int64_t srow = row;
+            if constexpr (WIDE) {
+                // (input and output positions of a lane share the block row)
+                const int64_t rr = wide_row(row);
+                if (a.wide_row_scale)
+                    srow = rr;
+                const int64_t p = ((row - rr * a.wide_div) << 7) + (out_off & 127);
+                raw.sg[i] = *(const u32x2 *)(a.s + p);
+            }
+            raw.s[i] = a.scale_f16 ? (uint32_t)((const uint16_t *)a.scales)[srow]
+                                   : ((const uint32_t *)a.scales)[srow];
         }
     };
 
@@ -178,7 +200,7 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
         for (int j = 0; j < 8; ++j)
             w[j] = ((sb[j >> 2] >> (8 * (j & 3) + 7)) & 1u) << 31;
     };
-    if constexpr (TPR == 1)
+    if constexpr (TPR == 1 && !WIDE)
         sign_words(out_off & ((1 << LOGN) - 1), osg_r);
 
     Raw cur;
@@ -216,6 +238,11 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
 #pragma unroll
         for (int i = 0; i < NS; ++i)
             asm volatile("" : "+v"(raw.s[i]));
+        if constexpr (WIDE) {
+#pragma unroll
+            for (int i = 0; i < T; ++i)
+                asm volatile("" : "+v"(raw.sg[i][0]), "+v"(raw.sg[i][1]));
+        }
     };
     take_delivery(cur);
 
@@ -257,6 +284,12 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
                 v[t][i] = d0[i];
                 v[t][4 + i] = d1[i];
             }
+        }
+        u32x2 sgt[WIDE ? T : 1];
+        if constexpr (WIDE) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                sgt[t] = cur.sg[t];
         }
         // ------------------------------------ prefetch the next tile group
         if (g_next < pool_size)  // wave-uniform
@@ -309,7 +342,13 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
         for (int t = 0; t < T; ++t) {
             const float mul = (LOGN >= 9 ? sc[t / TPR] : sc[t]) * rbs;
             uint32_t osg[8];
-            if constexpr (TPR > 1) {
+            if constexpr (WIDE) {
+                // (the signs of this tile's block row, loaded with the codes;
+                // cur was refilled by the prefetch, so they were kept aside)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    osg[j] = ((sgt[t][j >> 2] >> (8 * (j & 3) + 7)) & 1u) << 31;
+            } else if constexpr (TPR > 1) {
                 const u32x4 w0 = lds_osg[2 * (lofs + (t % TPR) * 64)];
                 const u32x4 w1 = lds_osg[2 * (lofs + (t % TPR) * 64) + 1];
 #pragma unroll
@@ -350,16 +389,19 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
     }
 }
 
-template <int OUT, int BITS, int T, int LOGB, int LOGN>
-hipError_t launch_inv_one(const Request &r, const DeviceInfo &dev)
+template <int OUT, int BITS, int T, int LOGB, int LOGN, bool WIDE = false>
+hipError_t launch_inv_one(const Request &r, const DeviceInfo &dev, int wide_div = 1, int wide_row_scale = 0)
 {
     MfmaArgs ma;
     fill_args(ma, r, T);
     ma.codes = const_cast<void *>(r.codes_in);
     ma.scales = const_cast<void *>(r.scales_in);
+    ma.wide_div = wide_div;
+    ma.wide_rdiv = 1.0 / (double)wide_div;
+    ma.wide_row_scale = wide_row_scale;
     constexpr int TPR = LOGN > 9 ? 1 << (LOGN - 9) : 1;
     const size_t lds = TPR > 1 ? (size_t)TPR * 64 * 32 : 0;
-    auto fn = mfma_inv_kernel<OUT, BITS, T, LOGB, LOGN>;
+    auto fn = mfma_inv_kernel<OUT, BITS, T, LOGB, LOGN, WIDE>;
     // every wave the CU holds, up to a cap per case (steady-state timings):
     // fp32 out, narrow groups 8 (1048576 x 128: 142 us at 8 waves, 210 at
     // 12, 215 at 16); fp32 out, 8-tile groups 16 (16384 x 4096: 65.5 us at
@@ -420,10 +462,32 @@ hipError_t inv_dispatch(const Request &r, const DeviceInfo &dev)
     }
 }
 
+// Rows of several 128-blocks (see wide_inv_ok) as rows of one block.
+template <int OUT, int BITS>
+hipError_t inv_wide(const Request &r, const DeviceInfo &dev)
+{
+    const int blocks = r.n / 128;
+    Request w = r;
+    w.rows = r.rows * blocks;
+    w.n = 128;
+    w.group = 128;
+    w.logg = 7;
+    const int row_scale = r.group == r.n ? 1 : 0;
+    const int64_t groups4 = (w.rows * 128 + 4 * 512 - 1) / (4 * 512);
+    if (groups4 < (int64_t)dev.cu_count * 8 * 4)
+        return launch_inv_one<OUT, BITS, 2, 7, 7, true>(w, dev, blocks, row_scale);
+    return launch_inv_one<OUT, BITS, 4, 7, 7, true>(w, dev, blocks, row_scale);
+}
+
 }  // namespace
 
 hipError_t launch_inv(const Request &r, const DeviceInfo &dev)
 {
+    if (wide_inv_ok(r)) {
+        if (r.y_dtype == kF32)
+            return r.bits == 4 ? inv_wide<kF32, 4>(r, dev) : inv_wide<kF32, 8>(r, dev);
+        return r.bits == 4 ? inv_wide<kBF16, 4>(r, dev) : inv_wide<kBF16, 8>(r, dev);
+    }
     if (r.y_dtype == kF32)
         return r.bits == 4 ? inv_dispatch<kF32, 4>(r, dev) : inv_dispatch<kF32, 8>(r, dev);
     return r.bits == 4 ? inv_dispatch<kBF16, 4>(r, dev) : inv_dispatch<kBF16, 8>(r, dev);
