@@ -47,8 +47,25 @@ bool wide_inv_ok(const Request &r)
     return r.rows * (int64_t)(r.n / 128) < ((int64_t)1 << 31);
 }
 
+bool wide_fwd_ok(const Request &r)
+{
+    // rotation + quantisation of 128-blocks with one scale per block, as rows
+    // of one block, where the per-row plans do not take the row width
+    if (r.op != kRotateQuant || r.dst_rows || r.b != 128 || r.group != 128 || r.n <= 128 ||
+        r.n % 128 != 0)
+        return false;
+    if (r.x_dtype != kBF16 && r.x_dtype != kF16)
+        return false;
+    const bool pow2 = (r.n & (r.n - 1)) == 0;
+    if (pow2 && r.n <= 4096)
+        return false;
+    return r.rows * (int64_t)(r.n / 128) < ((int64_t)1 << 31);
+}
+
 bool plan_ok(const Request &r)
 {
+    if (wide_fwd_ok(r))
+        return true;
     if (r.op == kDequantInv) {
         if (wide_inv_ok(r))
             return true;
@@ -108,6 +125,7 @@ int occupancy_waves(const void *fn, size_t lds)
 
 hipError_t launch_rq(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rq_grouped(const Request &r, const DeviceInfo &dev);
+hipError_t launch_rq_wide(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rq_append(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rot(const Request &r, const DeviceInfo &dev);
 hipError_t launch_inv(const Request &r, const DeviceInfo &dev);
@@ -127,6 +145,8 @@ hipError_t launch_mfma(const Request &r, const DeviceInfo &dev)
         return mfma::launch_inv(r, dev);
     if (r.dst_rows)
         return mfma::launch_rq_append(r, dev);
+    if (mfma::wide_fwd_ok(r))
+        return mfma::launch_rq_wide(r, dev);
     return r.group == r.n ? mfma::launch_rq(r, dev) : mfma::launch_rq_grouped(r, dev);
 }
 

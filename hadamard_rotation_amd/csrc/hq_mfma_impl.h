@@ -163,9 +163,13 @@ __device__ __forceinline__ uint32_t group_lane_max(uint32_t v, int logg)
 //       (MfmaArgs::logg) reduced in the transposed layout
 // APPEND  one scale per row, and row r's codes and scale go to cache row
 //       MfmaArgs::dst_rows[r] (skipped outside [0, cache_rows))
-template <int OP, int IN, int T, int LOGB, int LOGN, int LOGG, bool APPEND = false>
+// WIDE  rows of several 128-blocks with one scale per block, run as rows of
+//       one block (LOGB = LOGN = LOGG = 7): each block row takes the signs of
+//       its place in the real row (MfmaArgs::wide_div blocks per real row)
+template <int OP, int IN, int T, int LOGB, int LOGN, int LOGG, bool APPEND = false, bool WIDE = false>
 __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
 {
+    static_assert(!WIDE || (LOGB == 7 && LOGN == 7 && LOGG == 7 && !APPEND), "wide rows run as 128-blocks");
     extern __shared__ __align__(16) u32x4 lds_mask[];  // n > 512: [tile of row][lane]
     constexpr int D = LOGB - 5 < 4 ? LOGB - 5 : 4;      // DPP stages (lane bits 0..D-1)
     constexpr int R = LOGB > 9 ? LOGB - 9 : 0;          // tile-bit stages
@@ -320,6 +324,26 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
 
     u32x4 cur[T];
     load(has_work ? first : 0, cur);
+    // WIDE: the sign bytes of the lane's 8 inputs of each tile, loaded with
+    // the tile (block row v is block v mod wide_div of its real row; the
+    // double product is within one of the quotient, one step corrects it)
+    u32x2 csg[WIDE ? T : 1];
+    auto load_signs = [&](int64_t g) {
+        if constexpr (WIDE) {
+            const int64_t e0 = group_elem0(g);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                int64_t vr = (e0 + t * 512 + lane_off) >> 7;
+                vr = vr < a.rows - 1 ? vr : a.rows - 1;
+                int64_t q = (int64_t)((double)vr * a.wide_rdiv);
+                const int64_t rem = vr - q * a.wide_div;
+                q += rem < 0 ? -1 : (rem >= a.wide_div ? 1 : 0);
+                const int64_t p = ((vr - q * a.wide_div) << 7) + (lane_off & 127);
+                csg[t] = *(const u32x2 *)(a.s + p);
+            }
+        }
+    };
+    load_signs(has_work ? first : 0);
 
     if constexpr (TPR > 1) {
         for (int idx = threadIdx.x; idx < TPR * 64; idx += blockDim.x) {
@@ -348,6 +372,11 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 asm volatile("" : "+v"(raw[t][c]));
+        if constexpr (WIDE) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                asm volatile("" : "+v"(csg[t][0]), "+v"(csg[t][1]));
+        }
     };
     take_delivery(cur);
 
@@ -371,6 +400,13 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
             u32x4 m = smask;
             if constexpr (TPR > 1)
                 m = lds_mask[lofs + (t % TPR) * 64];
+            if constexpr (WIDE) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t w = csg[t][c >> 1] >> (16 * (c & 1));
+                    m[c] = ((w >> 7) & 1) << 15 | ((w >> 15) & 1) << 31;
+                }
+            }
             u32x4 b;
 #pragma unroll
             for (int c = 0; c < 4; ++c)
@@ -384,8 +420,10 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
             }
         }
         // ------------------------------------ prefetch the next tile group
-        if (g_next < pool_size)  // wave-uniform
+        if (g_next < pool_size) {  // wave-uniform
             load(g_next, cur);
+            load_signs(g_next);
+        }
 
         // ------------------------------------------ tile-bit stages (b > 512)
 #pragma unroll
@@ -594,17 +632,21 @@ namespace mfma {
 // Host side (hq_mfma.hip): plan check, argument setup and the launch.
 bool plan_ok(const Request &r);
 bool wide_inv_ok(const Request &r);
+bool wide_fwd_ok(const Request &r);
 void fill_args(MfmaArgs &ma, const Request &r, int tiles_per_group);
 int occupancy_waves(const void *fn, size_t lds);
 
-template <int OP, int IN, int T, int LOGB, int LOGN, int LOGG, bool APPEND = false>
-hipError_t launch_one(const Request &r, const DeviceInfo &dev)
+template <int OP, int IN, int T, int LOGB, int LOGN, int LOGG, bool APPEND = false, bool WIDE = false>
+hipError_t launch_one(const Request &r, const DeviceInfo &dev, int wide_div = 1)
 {
     MfmaArgs ma;
     fill_args(ma, r, T);
+    ma.wide_div = wide_div;
+    ma.wide_rdiv = 1.0 / (double)wide_div;
+    ma.wide_row_scale = 0;
     constexpr int TPR = LOGN > 9 ? 1 << (LOGN - 9) : 1;
     const size_t lds = TPR > 1 ? (size_t)TPR * 64 * 16 : 0;
-    auto fn = mfma_kernel<OP, IN, T, LOGB, LOGN, LOGG, APPEND>;
+    auto fn = mfma_kernel<OP, IN, T, LOGB, LOGN, LOGG, APPEND, WIDE>;
     // One workgroup per CU with every wave the CU can hold, at most 16 for
     // groups of 2 tiles and 12 otherwise (steady-state timings: 131072 x 128
     // rows 9.8 us with 16 waves, 10.4 with 12; 1048576 x 128 rows, groups of
