@@ -35,6 +35,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;               // waves per workgroup (two per SIMD)
 constexpr int kThreads = 64 * kWaves;
@@ -50,6 +53,11 @@ struct PaleyArgs {
     int k;          // Paley order
     int p, e, mod0, mod1, mod2;  // GF(k - 1) = GF(p^e) (see PaleySpec)
     float kq;       // 1 / (sqrt(n) * qmax)
+    // inverse: codes and scales above are its inputs
+    void *y;
+    int y_bf16;
+    int scale_f16;
+    float rb;       // 1 / sqrt(n)
 };
 
 // GF(p^e) on element indices c0 + p c1 + p^2 c2 (e <= 3)
@@ -443,7 +451,12 @@ constexpr int kBCPT = 6;                 // 16-byte chunks per thread (6 x 256 >
 constexpr int kBOcc = 2;                 // workgroups per compute unit
 
 // entry (sa, sb) of the padded block K_d (see above); sq: the squares of
-// GF(343) by element index
+// GF(343) by element index.  TR: the blocks of H_k^T instead, for the
+// inverse: chi(-x) = -chi(x) (q = 3 mod 4), so the core changes sign and the
+// border rows and columns trade theirs:
+//   K_d[sa][sb] = -chi(49 d + (sa - sb)), 1 on the diagonal of K_0;
+//   K_d[49][sb] = -1; K_d[sa][49] = +1; K_d[49][49] = +1.
+template <bool TR = false>
 __device__ int block_entry(const unsigned char *sq, int d, int sa, int sb)
 {
     if (sa < kBBlk && sb < kBBlk) {
@@ -451,11 +464,14 @@ __device__ int block_entry(const unsigned char *sq, int d, int sa, int sb)
             return 1;
         const int d0 = (sa % 7 - sb % 7 + 7) % 7;
         const int d1 = (sa / 7 - sb / 7 + 7) % 7;
-        return sq[d0 + 7 * d1 + 49 * d] ? 1 : -1;
+        const bool sqr = sq[d0 + 7 * d1 + 49 * d];
+        return (sqr != TR) ? 1 : -1;
     }
     if (sa < kBBlk && sb == kBBlk)
-        return -1;
-    if (sa == kBBlk && sb <= kBBlk)
+        return TR ? 1 : -1;
+    if (sa == kBBlk && sb < kBBlk)
+        return TR ? -1 : 1;
+    if (sa == kBBlk && sb == kBBlk)
         return 1;
     return 0;
 }
@@ -729,10 +745,278 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
     }
 }
 
+// Inverse for k = 344: y = scale * (q . H_n^T) / sqrt(n), then the signs.
+// The codes are integers, exact in f16, and one scale per row commutes with
+// the transform, so the codes go onto the matrix core as they are, with the
+// blocks of H_k^T (block_entry<true>); the butterflies are those of the
+// forward kernel (H_32 is symmetric).  No row maximum: one barrier per row,
+// two staging buffers, and each lane stores its 16 (block 6: 8) consecutive
+// outputs directly.
+template <int BITS, int OUT>
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc))) void paley343_inv_kernel(PaleyArgs a)
+{
+    constexpr int n = kBK * kM2;
+    constexpr int kChunks = n * BITS / 8 / 16;  // 16-byte chunks of a row's codes
+    constexpr int kCPTi = (kChunks + kBThreads - 1) / kBThreads;
+    constexpr int OB = OUT == kF32 ? 4 : 2;      // output bytes per element
+    __shared__ __align__(16) uint16_t xt[2][kM2 * kBRS];  // [buffer][j][a2][slot]
+    __shared__ unsigned char sq[kBK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, rg = lane >> 4;
+    const int lb4 = (lane >> 4) & 1, lb5 = lane >> 5;
+    const int sb = 16 * wave + l16;  // this lane's column in every block
+
+    // ---- once: zero padding, the squares, this wave's columns of H_k^T
+    for (int t = tid; t < 2 * kM2 * kBRS / 8; t += kBThreads)
+        ((u32x4 *)&xt[0][0])[t] = (u32x4){0u, 0u, 0u, 0u};
+    for (int t = tid; t < kBK; t += kBThreads)
+        sq[t] = 0;
+    lds_barrier();
+    for (int t = tid + 1; t < kBK - 1; t += kBThreads)
+        sq[gfp_square(t, a)] = 1;  // concurrent writes store the same 1
+    lds_barrier();
+    u32x4 bd[kBTop][2];
+#pragma unroll
+    for (int d = 0; d < kBTop; ++d)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int v = block_entry<true>(sq, d, 32 * c + 8 * rg + 2 * p + h, sb);
+                    const uint32_t bits = v == 0 ? 0u : (v > 0 ? 0x3C00u : 0xBC00u);
+                    w |= bits << (16 * h);
+                }
+                bd[d][c][p] = w;
+            }
+    // the output signs of this lane, one bit per value: bits 16k .. 16k+15
+    // for rows 1 + 49 (2k + lane bit 5) + sb (k < 3), bits 48 .. 55 for block
+    // 6 (see the butterflies for which outputs a lane holds)
+    uint32_t sgw[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < kBTop / 2; ++k) {
+        const int b2 = 2 * k + lb5;
+        if (sb < kBBlk || (sb == kBBlk && b2 == 0)) {
+            const int ip = sb == kBBlk ? 0 : 1 + kBBlk * b2 + sb;
+            for (int jj = 0; jj < 16; ++jj)
+                if (a.s[ip * kM2 + 16 * lb4 + jj] < 0)
+                    sgw[k >> 1] |= 1u << ((16 * k + jj) & 31);
+        }
+    }
+    if (sb < kBBlk) {
+        const int ip = 1 + kBBlk * (kBTop - 1) + sb;
+        for (int jj = 0; jj < 8; ++jj)
+            if (a.s[ip * kM2 + 16 * lb4 + 8 * lb5 + jj] < 0)
+                sgw[1] |= 1u << (16 + jj);
+    }
+
+    // ---- codes -> f16 in the staged layout [j][block][slot] (no signs: they
+    // apply to the outputs).  INT4: chunk c is row i = c (32 codes); INT8:
+    // chunk c holds i = c / 2, j = 16 (c % 2) .. +15.
+    u32x4 cur[kCPTi];
+    auto load_row = [&](int64_t row) {
+        const auto rs = rsrc((const uint8_t *)a.codes + row * (int64_t)(n * BITS / 8), n * BITS / 8);
+#pragma unroll
+        for (int cc = 0; cc < kCPTi; ++cc) {
+            const int c = kBThreads * cc + tid;
+            cur[cc] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rs, c < kChunks ? 16 * c : 0x7FFFFFF0, 0, kNonTemporal));
+        }
+    };
+    auto put2 = [&](uint16_t *dst, int ja, int jb, uint32_t h2) {
+        dst[ja * kBRS] = (uint16_t)h2;
+        dst[jb * kBRS] = (uint16_t)(h2 >> 16);
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int cc = 0; cc < kCPTi; ++cc) {
+            const int c = kBThreads * cc + tid;
+            const int i = BITS == 4 ? c : c >> 1;
+            const int j0 = BITS == 4 ? 0 : 16 * (c & 1);
+            // (rows past the codes go to slot 448 + , which no product reads)
+            const int slot = c >= kChunks ? kBTop * kBPad : (i == 0 ? kBBlk : kBPad * ((i - 1) / kBBlk) + (i - 1) % kBBlk);
+            uint16_t *dst = &xt[buf][j0 * kBRS + slot];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t w = cur[cc][p];
+                if constexpr (BITS == 4) {
+                    // element 8p + e sits in nibble e: even e in the low
+                    // nibbles of the bytes, odd e in the high ones
+                    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+                    const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+                    auto cv = [&](uint32_t x) {
+                        return __builtin_bit_cast(uint32_t,
+                                                  __builtin_bit_cast(f16x2, (x & 0x000F000Fu) ^ 0x64086408u) + bias);
+                    };
+                    put2(dst, 8 * p + 0, 8 * p + 4, cv(lo));
+                    put2(dst, 8 * p + 2, 8 * p + 6, cv(lo >> 8));
+                    put2(dst, 8 * p + 1, 8 * p + 5, cv(hi));
+                    put2(dst, 8 * p + 3, 8 * p + 7, cv(hi >> 8));
+                } else {
+                    const f16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+                    auto cv = [&](uint32_t x) {
+                        return __builtin_bit_cast(uint32_t,
+                                                  __builtin_bit_cast(f16x2, (x & 0x00FF00FFu) ^ 0x64806480u) + bias);
+                    };
+                    put2(dst, 4 * p + 0, 4 * p + 2, cv(w));
+                    put2(dst, 4 * p + 1, 4 * p + 3, cv(w >> 8));
+                }
+            }
+        }
+    };
+
+    const float sgn32 = (lane & 32) ? -1.0f : 1.0f;
+    int64_t row = blockIdx.x;
+    const int64_t G = gridDim.x;
+    if (row < a.rows) {
+        load_row(row);
+        stage(0);
+        if (row + G < a.rows)
+            load_row(row + G);
+    }
+    lds_barrier();
+    int buf = 0;
+    for (; row < a.rows; row += G, buf ^= 1) {
+        const float sc = a.scale_f16 ? f16_to_f32(((const uint16_t *)a.scales)[row]) : ((const float *)a.scales)[row];
+        // ---- Z on the matrix core
+        f32x4 acc[kBTop][2];
+#pragma unroll
+        for (int b2 = 0; b2 < kBTop; ++b2)
+            acc[b2][0] = acc[b2][1] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int a2 = 0; a2 < kBTop; ++a2) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const u32x4 av = *(const u32x4 *)&xt[buf][(16 * mt + l16) * kBRS + kBPad * a2 + 32 * c + 8 * rg];
+#pragma unroll
+                    for (int b2 = 0; b2 < kBTop; ++b2)
+                        acc[b2][mt] = mma<kF16>(av, bd[(a2 - b2 + kBTop) % kBTop][c], acc[b2][mt]);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- the next row into the other buffer, the one after it in flight
+        if (row + G < a.rows) {
+            stage(buf ^ 1);
+            if (row + 2 * G < a.rows)
+                load_row(row + 2 * G);
+        }
+
+        // ---- 32-point butterflies (as in the forward kernel)
+#pragma unroll
+        for (int b2 = 0; b2 < kBTop; ++b2)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const float a0 = acc[b2][mt][0] + acc[b2][mt][1], a1 = acc[b2][mt][0] - acc[b2][mt][1];
+                const float a2_ = acc[b2][mt][2] + acc[b2][mt][3], a3 = acc[b2][mt][2] - acc[b2][mt][3];
+                acc[b2][mt][0] = a0 + a2_;
+                acc[b2][mt][2] = a0 - a2_;
+                acc[b2][mt][1] = a1 + a3;
+                acc[b2][mt][3] = a1 - a3;
+            }
+#pragma unroll
+        for (int b2 = 0; b2 < kBTop; ++b2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float lo = acc[b2][0][r], hi = acc[b2][1][r];  // bit 4
+                const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo + hi), __float_as_uint(lo - hi),
+                                                                false, false);  // bit 2
+                const float x0 = __uint_as_float(w[0]), x1 = __uint_as_float(w[1]);
+                acc[b2][0][r] = x0 + x1;
+                acc[b2][1][r] = x0 - x1;
+            }
+#pragma unroll
+        for (int k = 0; k < kBTop / 2; ++k)
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[2 * k][sl][r]),
+                                                                    __float_as_uint(acc[2 * k + 1][sl][r]), false,
+                                                                    false);  // bit 3
+                    const float x0 = __uint_as_float(w[0]), x1 = __uint_as_float(w[1]);
+                    acc[2 * k][sl][r] = x0 + x1;
+                    acc[2 * k + 1][sl][r] = x0 - x1;
+                }
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[kBTop - 1][sl][r] = xbutterfly<32>(acc[kBTop - 1][sl][r], sgn32);
+
+        // ---- outputs: times scale / sqrt(n), signs, stores
+        const float mul = sc * a.rb;
+        const auto ry = rsrc((uint8_t *)a.y + row * (int64_t)(n * OB), n * OB);
+        // value of output bit `bit` of the lane's sign words
+        auto outv = [&](float v, int bit) {
+            const uint32_t sw = sgw[bit >> 5];
+            // ((sw << (31 - bit)) & 0x80000000) ^ v (the value in the middle
+            // operand keeps the truth table independent of operand order)
+            return __uint_as_float(__builtin_amdgcn_bitop3_b32(sw << (31 - (bit & 31)), __float_as_uint(v * mul),
+                                                               0x80000000u, 0x6C));
+        };
+        auto store8 = [&](int e0, const float (&o)[8]) {  // 8 consecutive outputs from element e0
+            if constexpr (OUT == kF32) {
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    (u32x4){__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])},
+                    ry, 4 * e0, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    (u32x4){__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])},
+                    ry, 4 * e0 + 16, 0, 0);
+            } else {
+                u32x4 p;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x2 f = {o[2 * q], o[2 * q + 1]};
+                    p[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(p, ry, 2 * e0, 0, 0);
+            }
+        };
+#pragma unroll
+        for (int k = 0; k < kBTop / 2; ++k) {
+            const int b2 = 2 * k + lb5;
+            if (sb > kBBlk || (sb == kBBlk && b2 > 0))
+                continue;
+            const int ip = sb == kBBlk ? 0 : 1 + kBBlk * b2 + sb;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                float o[8];
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        o[4 * sl + r] = outv(acc[2 * k + t][sl][r], 16 * k + 8 * t + 4 * sl + r);
+                store8(ip * kM2 + 16 * lb4 + 8 * t, o);
+            }
+        }
+        if (sb < kBBlk) {
+            const int ip = 1 + kBBlk * (kBTop - 1) + sb;
+            float o[8];
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    o[4 * sl + r] = outv(acc[kBTop - 1][sl][r], 48 + 4 * sl + r);
+            store8(ip * kM2 + 16 * lb4 + 8 * lb5, o);
+        }
+        lds_barrier();  // the next row is staged; nobody reads this buffer any more
+    }
+}
+
 }  // namespace
 
 bool paley_mfma_available(const Request &r)
 {
+    if (r.op == kDequantInv)  // k = 344 only, one scale per row
+        return r.group == r.n && r.paley.k == kBK && r.paley.p == 7 && r.paley.e == 3 &&
+               r.paley.m2 == kM2 && (r.bits == 4 || r.bits == 8) && (r.y_dtype == kF32 || r.y_dtype == kBF16);
     return r.op == kRotateQuant && !r.dst_rows && r.group == r.n &&
            (r.x_dtype == kBF16 || r.x_dtype == kF16) && r.paley.k > 1 && r.paley.m2 == kM2 &&
            r.paley.k > 320 && r.paley.k <= 352 && r.scale_dtype == kF32;
@@ -755,6 +1039,28 @@ hipError_t launch_paley_mfma(const Request &r, const DeviceInfo &dev)
     pa.mod2 = r.paley.mod[2];
     const int qmax = r.bits == 8 ? 127 : 7;
     pa.kq = (float)(1.0 / (__builtin_sqrt((double)r.n) * qmax));
+    if (r.op == kDequantInv) {
+        pa.codes = const_cast<void *>(r.codes_in);
+        pa.scales = const_cast<void *>(r.scales_in);
+        pa.y = r.y;
+        pa.y_bf16 = r.y_dtype == kBF16;
+        pa.scale_f16 = r.scale_dtype == kF16;
+        pa.rb = (float)(1.0 / __builtin_sqrt((double)r.n));
+        const int64_t gi = kBOcc * (int64_t)dev.cu_count;
+        const int64_t grid = r.rows < gi ? r.rows : gi;
+        if (r.y_dtype == kF32) {
+            if (r.bits == 4)
+                hipLaunchKernelGGL((paley343_inv_kernel<4, kF32>), dim3((unsigned)grid), dim3(kBThreads), 0, r.stream, pa);
+            else
+                hipLaunchKernelGGL((paley343_inv_kernel<8, kF32>), dim3((unsigned)grid), dim3(kBThreads), 0, r.stream, pa);
+        } else {
+            if (r.bits == 4)
+                hipLaunchKernelGGL((paley343_inv_kernel<4, kBF16>), dim3((unsigned)grid), dim3(kBThreads), 0, r.stream, pa);
+            else
+                hipLaunchKernelGGL((paley343_inv_kernel<8, kBF16>), dim3((unsigned)grid), dim3(kBThreads), 0, r.stream, pa);
+        }
+        return hipGetLastError();
+    }
     if (r.paley.k == kBK && r.paley.p == 7 && r.paley.e == 3) {
         const int64_t g3 = kBOcc * (int64_t)dev.cu_count;
         const int64_t grid3 = r.rows < g3 ? r.rows : g3;

@@ -143,3 +143,29 @@ def test_ffn_11008_full_at_full_size_sampled():
     ref = O.rotate_quant(raw[pick], w.x_dtype, w.b, s, w.bits, w.scale_dtype)
     P.check_codes(codes[pick], ref, w.bits, w.n, what="ffn_11008_full sampled codes")
     P.check_scales(scales[pick], ref, w.scale_dtype, what="ffn_11008_full sampled scales")
+
+
+@pytest.mark.parametrize("bits,sd", [(4, W.F32), (8, W.F16)])
+def test_11008_inverse_many_rows_sampled(bits, sd):
+    # the inverse over more rows than workgroups (each walks several rows
+    # through its two staging buffers); seeded codes in [-qmax, qmax] and
+    # positive scales as inputs, the oracle on a sample of rows
+    n, rows = 11008, 600
+    print(f"[paley] inverse 11008 x {rows} bits={bits}", flush=True)
+    rng = np.random.default_rng(77 + bits)
+    qmax = (1 << (bits - 1)) - 1
+    q = rng.integers(-qmax, qmax + 1, size=(rows, n))
+    if bits == 4:
+        codes = ((q[:, 0::2] & 15) | ((q[:, 1::2] & 15) << 4)).astype(np.uint8)
+    else:
+        codes = q.astype(np.int8).view(np.uint8)
+    scales = (rng.random(rows) * 0.5 + 0.01).astype(np.float32)
+    if sd == W.F16:
+        scales = scales.astype(np.float16)
+    s = np.where(rng.integers(0, 2, n) == 1, 1, -1).astype(np.int8)
+    pick = np.array([0, 1, 127, 255, 256, 257, 300, 511, 512, 513, 599])
+    y_ref = O.dequant_rotate_inv(codes[pick], scales[pick], sd, n, s, bits, n)
+    y = G.gpu_dequant_inv(codes, scales, s, n, bits)
+    P.check_inverse(y[pick], y_ref, bf16=False, what=f"11008 inverse bits={bits} f32")
+    yb = G.gpu_dequant_inv(codes, scales, s, n, bits, out_bf16=True)
+    P.check_inverse(P.bf16_bits_to_f64(yb[pick]), y_ref, bf16=True, what=f"11008 inverse bits={bits} bf16")
