@@ -476,7 +476,9 @@ __device__ int block_entry(const unsigned char *sq, int d, int sa, int sb)
     return 0;
 }
 
-template <int IN, int BITS>
+// ROT: rotation only (hq_rotate): the rotated row y / sqrt(n) in fp32 to
+// a.y instead of codes, no maximum and no quantiser
+template <int IN, int BITS, bool ROT = false>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc))) void paley343_kernel(PaleyArgs a)
 {
     constexpr int qmax = (1 << (BITS - 1)) - 1;
@@ -661,6 +663,54 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 acc[kBTop - 1][sl][r] = xbutterfly<32>(acc[kBTop - 1][sl][r], sgn32);
+        if constexpr (ROT) {
+            lds_barrier();  // every wave is done with the staged row
+            if (row + gridDim.x < a.rows) {  // the next row (loaded one row ago) into the staged layout
+                stage();
+                if (row + 2 * gridDim.x < a.rows)
+                    load_row(row + 2 * gridDim.x);
+            }
+            // y / sqrt(n): 16 (block 6: 8) consecutive outputs per lane
+            const auto ry = rsrc((uint8_t *)a.y + row * (int64_t)(n * 4), n * 4);
+            const int lb4r = (lane >> 4) & 1, lb5r = lane >> 5;
+            auto st8 = [&](int e0, const float (&o)[8]) {
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    (u32x4){__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])},
+                    ry, 4 * e0, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    (u32x4){__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])},
+                    ry, 4 * e0 + 16, 0, 0);
+            };
+#pragma unroll
+            for (int k = 0; k < kBTop / 2; ++k) {
+                const int b2 = 2 * k + lb5r;
+                if (sb > kBBlk || (sb == kBBlk && b2 > 0))
+                    continue;
+                const int ip = sb == kBBlk ? 0 : 1 + kBBlk * b2 + sb;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    float o[8];
+#pragma unroll
+                    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            o[4 * sl + r] = acc[2 * k + t][sl][r] * a.rb;
+                    st8(ip * kM2 + 16 * lb4r + 8 * t, o);
+                }
+            }
+            if (sb < kBBlk) {
+                const int ip = 1 + kBBlk * (kBTop - 1) + sb;
+                float o[8];
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        o[4 * sl + r] = acc[kBTop - 1][sl][r] * a.rb;
+                st8(ip * kM2 + 16 * lb4r + 8 * lb5r, o);
+            }
+            lds_barrier();  // the next row is staged
+            continue;
+        }
         // padding columns are 0 and the copies of Z[0] repeat it: neither
         // changes the maximum
 #pragma unroll
@@ -1014,6 +1064,9 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
 
 bool paley_mfma_available(const Request &r)
 {
+    if (r.op == kRotate)  // k = 344 only, 16-bit input
+        return r.paley.k == kBK && r.paley.p == 7 && r.paley.e == 3 && r.paley.m2 == kM2 &&
+               (r.x_dtype == kBF16 || r.x_dtype == kF16);
     if (r.op == kDequantInv)  // k = 344 only, one scale per row
         return r.group == r.n && r.paley.k == kBK && r.paley.p == 7 && r.paley.e == 3 &&
                r.paley.m2 == kM2 && (r.bits == 4 || r.bits == 8) && (r.y_dtype == kF32 || r.y_dtype == kBF16);
@@ -1039,6 +1092,17 @@ hipError_t launch_paley_mfma(const Request &r, const DeviceInfo &dev)
     pa.mod2 = r.paley.mod[2];
     const int qmax = r.bits == 8 ? 127 : 7;
     pa.kq = (float)(1.0 / (__builtin_sqrt((double)r.n) * qmax));
+    if (r.op == kRotate) {
+        pa.y = r.y;
+        pa.rb = (float)(1.0 / __builtin_sqrt((double)r.n));
+        const int64_t gr = kBOcc * (int64_t)dev.cu_count;
+        const int64_t grid = r.rows < gr ? r.rows : gr;
+        if (r.x_dtype == kBF16)
+            hipLaunchKernelGGL((paley343_kernel<kBF16, 4, true>), dim3((unsigned)grid), dim3(kBThreads), 0, r.stream, pa);
+        else
+            hipLaunchKernelGGL((paley343_kernel<kF16, 4, true>), dim3((unsigned)grid), dim3(kBThreads), 0, r.stream, pa);
+        return hipGetLastError();
+    }
     if (r.op == kDequantInv) {
         pa.codes = const_cast<void *>(r.codes_in);
         pa.scales = const_cast<void *>(r.scales_in);

@@ -169,3 +169,14 @@ def test_11008_inverse_many_rows_sampled(bits, sd):
     P.check_inverse(y[pick], y_ref, bf16=False, what=f"11008 inverse bits={bits} f32")
     yb = G.gpu_dequant_inv(codes, scales, s, n, bits, out_bf16=True)
     P.check_inverse(P.bf16_bits_to_f64(yb[pick]), y_ref, bf16=True, what=f"11008 inverse bits={bits} bf16")
+
+
+def test_11008_rotate_many_rows_sampled():
+    # rotation only over more rows than workgroups; the oracle on a sample
+    n, rows = 11008, 600
+    print(f"[paley] rotate 11008 x {rows}", flush=True)
+    raw, s = _input(4321, rows, n, W.BF16, outliers=11)
+    y = G.gpu_rotate(raw, W.BF16, s, n)
+    pick = np.array([0, 1, 255, 256, 257, 511, 512, 599])
+    xr = O.rotate(O.decode(raw[pick], W.BF16), s, n)
+    P.check_rotated(y[pick], xr, what="11008 rotated, sampled rows")
