@@ -60,21 +60,7 @@ struct PaleyArgs {
     float rb;       // 1 / sqrt(n)
 };
 
-// GF(p^e) on element indices c0 + p c1 + p^2 c2 (e <= 3)
-__device__ int gfp_sub(int a, int b, int p, int e)
-{
-    int r = 0, w = 1;
-    for (int i = 0; i < e; ++i) {
-        int d = a % p - b % p;
-        d += d < 0 ? p : 0;
-        r += d * w;
-        w *= p;
-        a /= p;
-        b /= p;
-    }
-    return r;
-}
-
+// GF(p^e) on element indices c0 + p c1 + p^2 c2 (e <= 3): the square of a
 __device__ int gfp_square(int a, const PaleyArgs &g)
 {
     const int p = g.p, e = g.e;
@@ -573,7 +559,6 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
         }
     };
 
-    const float sgn16 = (lane & 16) ? -1.0f : 1.0f;
     const float sgn32 = (lane & 32) ? -1.0f : 1.0f;
     const int sb = 16 * wave + l16;  // this lane's column in every block
     // One row at a time per workgroup, the next one in flight: its loads go
