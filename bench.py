@@ -264,7 +264,7 @@ def main(argv=None):
         return 0
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not "
               "supported (rows are independent, so a multi-GPU run is the one-GPU "
               "throughput per shard)", file=sys.stderr)
         return 2

@@ -394,7 +394,7 @@ const char *hq_status_str(int32_t status)
     switch (status) {
     case HQ_OK: return "HQ_OK: success";
     case HQ_EINVAL: return "HQ_EINVAL: invalid argument";
-    case HQ_EUNSUPPORTED: return "HQ_EUNSUPPORTED: valid request without a kernel in this build";
+    case HQ_EUNSUPPORTED: return "HQ_EUNSUPPORTED: valid request without a kernel in this library";
     case HQ_EHIP: return "HQ_EHIP: HIP runtime error";
     default: return "unknown hq_status";
     }

@@ -61,7 +61,7 @@ typedef enum hq_status {
     HQ_OK = 0,           /* enqueued (or nothing to do)                    */
     HQ_EINVAL = 1,       /* invalid argument: null pointer, bad shape,
                             dtype, bits, or misaligned pointer             */
-    HQ_EUNSUPPORTED = 2, /* valid request this build has no kernel for
+    HQ_EUNSUPPORTED = 2, /* valid request this library has no kernel for
                             (n above hq_max_n(), b above 4096)             */
     HQ_EHIP = 3          /* the HIP runtime reported an error (no device,
                             launch failure); see hq_last_hip_error()       */
@@ -182,7 +182,7 @@ hq_status hq_rotate_quant_append(const void *x, hq_dtype x_dtype, int64_t rows, 
  *             two calls in flight on one workspace race.
  * Errors: HQ_EINVAL for invalid arguments (tokens < 1, q_heads not a
  * multiple of kv_heads, a short workspace, ...); HQ_EUNSUPPORTED for valid
- * requests outside this build's kernel: n != 128, bits != 4, or
+ * requests outside the library's kernel: n != 128, bits != 4, or
  * q_heads / kv_heads not 1, 2, 4 or 8.
  */
 int64_t hq_decode_attention_workspace(int32_t q_heads, int32_t kv_heads, int64_t tokens);
