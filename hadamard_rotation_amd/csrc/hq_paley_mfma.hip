@@ -435,6 +435,16 @@ constexpr int kBK = 344;                 // Paley order
 constexpr int kBRS = kBTop * kBPad + 8;  // LDS row stride of the staged row (elements)
 constexpr int kBCPT = 6;                 // 16-byte chunks per thread (6 x 256 >= 1376)
 constexpr int kBOcc = 2;                 // workgroups per compute unit
+// Staged row of the forward kernel: row j starts at element frow(j).  One
+// staging store of a wave covers 16 consecutive slots of four rows 8 apart;
+// the shift of 16 elements per group of 8 rows puts those four rows in
+// different LDS banks (at the stride kBRS all four share the same 8 banks).
+// The stride 504 (252 dwords, 28 mod 32) keeps the matrix-core operand
+// reads of 8 consecutive rows in distinct banks.
+constexpr int kBRSF = 504;
+constexpr int kDropOffset = 0x7FFFFF00;  // buffer offset past every buffer: the store is dropped
+__device__ __forceinline__ int frow(int j) { return j * kBRSF + 16 * (j >> 3); }
+static_assert(31 * kBRSF + 16 * 3 + kBTop * kBPad <= 32 * kBRSF, "staged row fits");
 
 // entry (sa, sb) of the padded block K_d (see above); sq: the squares of
 // GF(343) by element index.  TR: the blocks of H_k^T instead, for the
@@ -469,7 +479,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
 {
     constexpr int qmax = (1 << (BITS - 1)) - 1;
     constexpr int n = kBK * kM2;
-    __shared__ __align__(16) uint16_t xt[kM2 * kBRS];             // [j][a2][slot]
+    __shared__ __align__(16) uint16_t xt[kM2 * kBRSF];            // [j][a2][slot] from frow(j)
     __shared__ __align__(16) uint32_t cst[n * BITS / 32];         // the row's codes
     __shared__ unsigned char sq[kBK];
     __shared__ float red[kBW];
@@ -480,7 +490,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
     const int l16 = lane & 15, rg = lane >> 4;
 
     // ---- once: zero padding, the squares, this wave's 16 columns of every K_d
-    for (int t = tid; t < kM2 * kBRS / 8; t += kBThreads)
+    for (int t = tid; t < kM2 * kBRSF / 8; t += kBThreads)
         ((u32x4 *)xt)[t] = (u32x4){0u, 0u, 0u, 0u};
     for (int t = tid; t < kBK; t += kBThreads)
         sq[t] = 0;
@@ -523,9 +533,13 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
                 m |= (a.s[8 * q + e] < 0 ? 1u : 0u) << ((e & 1) ? 31 - 2 * (e - 1) : 15 - 2 * e);
         neg[cc] = m;
     }
+    // (no branch around the loads: past the last row the buffer has size 0
+    // and every load reads 0, so the waits before the row is staged count
+    // only these loads, not the stores issued after them)
     u32x4 cur[kBCPT];
     auto load_row = [&](int64_t row) {
-        const auto rs = rsrc((const uint16_t *)a.x + row * n, 2 * n);
+        const bool ok = row < a.rows;
+        const auto rs = rsrc((const uint16_t *)a.x + (ok ? row : 0) * n, ok ? 2 * n : 0);
 #pragma unroll
         for (int cc = 0; cc < kBCPT; ++cc) {
             const int q = kBThreads * cc + tid;
@@ -542,7 +556,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
             if (i >= kBK)
                 continue;
             const int slot = i == 0 ? kBBlk : kBPad * ((i - 1) / kBBlk) + (i - 1) % kBBlk;
-            uint16_t *dst = xt + 8 * (q & 3) * kBRS + slot;
+            uint16_t *dst = xt + frow(8 * (q & 3)) + slot;  // rows 8 (q & 3) + e at dst + e kBRSF
             // (opaque to the compiler: otherwise it keeps all 48 masks of
             // the loop in registers)
             uint32_t ng = neg[cc];
@@ -553,8 +567,8 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
                 // data in the middle operand: the truth table is then the
                 // same whichever outer operand indexes its high bit)
                 const uint32_t wv = __builtin_amdgcn_bitop3_b32(ng << (4 * p), cur[cc][p], 0x80008000u, 0x6C);
-                dst[2 * p * kBRS] = (uint16_t)wv;
-                dst[(2 * p + 1) * kBRS] = (uint16_t)(wv >> 16);
+                dst[2 * p * kBRSF] = (uint16_t)wv;
+                dst[(2 * p + 1) * kBRSF] = (uint16_t)(wv >> 16);
             }
         }
     };
@@ -569,8 +583,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
     if (row < a.rows) {
         load_row(row);
         stage();
-        if (row + gridDim.x < a.rows)
-            load_row(row + gridDim.x);
+        load_row(row + gridDim.x);
     }
     lds_barrier();
     for (; row < a.rows; row += gridDim.x) {
@@ -585,7 +598,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
             for (int c = 0; c < 2; ++c)
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {
-                    const u32x4 av = *(const u32x4 *)&xt[(16 * mt + l16) * kBRS + kBPad * a2 + 32 * c + 8 * rg];
+                    const u32x4 av = *(const u32x4 *)&xt[frow(16 * mt + l16) + kBPad * a2 + 32 * c + 8 * rg];
 #pragma unroll
                     for (int b2 = 0; b2 < kBTop; ++b2)
                         acc[b2][mt] = mma<IN>(av, bd[(a2 - b2 + kBTop) % kBTop][c], acc[b2][mt]);
@@ -650,28 +663,29 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
                 acc[kBTop - 1][sl][r] = xbutterfly<32>(acc[kBTop - 1][sl][r], sgn32);
         if constexpr (ROT) {
             lds_barrier();  // every wave is done with the staged row
-            if (row + gridDim.x < a.rows) {  // the next row (loaded one row ago) into the staged layout
+            if (row + gridDim.x < a.rows)  // the next row (loaded one row ago) into the staged layout
                 stage();
-                if (row + 2 * gridDim.x < a.rows)
-                    load_row(row + 2 * gridDim.x);
-            }
+            load_row(row + 2 * gridDim.x);
             // y / sqrt(n): 16 (block 6: 8) consecutive outputs per lane
             const auto ry = rsrc((uint8_t *)a.y + row * (int64_t)(n * 4), n * 4);
             const int lb4r = (lane >> 4) & 1, lb5r = lane >> 5;
-            auto st8 = [&](int e0, const float (&o)[8]) {
+            // (every lane issues every store, those with nothing to store at
+            // an offset past the buffer, which drops them: no branch, so the
+            // next row's loads wait for loads only)
+            auto st8 = [&](bool ok, int e0, const float (&o)[8]) {
+                const int off = ok ? 4 * e0 : kDropOffset;
                 __builtin_amdgcn_raw_buffer_store_b128(
                     (u32x4){__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])},
-                    ry, 4 * e0, 0, 0);
+                    ry, off, 0, 0);
                 __builtin_amdgcn_raw_buffer_store_b128(
                     (u32x4){__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])},
-                    ry, 4 * e0 + 16, 0, 0);
+                    ry, off + 16, 0, 0);
             };
 #pragma unroll
             for (int k = 0; k < kBTop / 2; ++k) {
                 const int b2 = 2 * k + lb5r;
-                if (sb > kBBlk || (sb == kBBlk && b2 > 0))
-                    continue;
-                const int ip = sb == kBBlk ? 0 : 1 + kBBlk * b2 + sb;
+                const bool ok = sb < kBBlk || (sb == kBBlk && b2 == 0);
+                const int ip = sb >= kBBlk ? 0 : 1 + kBBlk * b2 + sb;
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     float o[8];
@@ -680,18 +694,18 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
                             o[4 * sl + r] = acc[2 * k + t][sl][r] * a.rb;
-                    st8(ip * kM2 + 16 * lb4r + 8 * t, o);
+                    st8(ok, ip * kM2 + 16 * lb4r + 8 * t, o);
                 }
             }
-            if (sb < kBBlk) {
-                const int ip = 1 + kBBlk * (kBTop - 1) + sb;
+            {
+                const int ip = 1 + kBBlk * (kBTop - 1) + (sb < kBBlk ? sb : 0);
                 float o[8];
 #pragma unroll
                 for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         o[4 * sl + r] = acc[kBTop - 1][sl][r] * a.rb;
-                st8(ip * kM2 + 16 * lb4r + 8 * lb5r, o);
+                st8(sb < kBBlk, ip * kM2 + 16 * lb4r + 8 * lb5r, o);
             }
             lds_barrier();  // the next row is staged
             continue;
@@ -762,21 +776,24 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
                 *(u32x2 *)((uint8_t *)cst + e0) =
                     (u32x2){fast::pack_int8(f[0], f[1], f[2], f[3]), fast::pack_int8(f[4], f[5], f[6], f[7])};
         }
-        if (row + gridDim.x < a.rows) {  // the next row (loaded one row ago) into the staged layout
+        if (row + gridDim.x < a.rows)  // the next row (loaded one row ago) into the staged layout
             stage();
-            if (row + 2 * gridDim.x < a.rows)
-                load_row(row + 2 * gridDim.x);
-        }
+        load_row(row + 2 * gridDim.x);
         lds_barrier();  // the codes are in and the next row is staged
         // ---- coalesced stores
+        // (every thread issues every store, the surplus ones at an offset past
+        // the buffer, which drops them: no branch, so the next row's loads
+        // wait for loads only)
         constexpr int kVec = n * BITS / 8 / 16;
-        uint8_t *crow = (uint8_t *)a.codes + row * (int64_t)(n * BITS / 8);
+        const auto rc = rsrc((uint8_t *)a.codes + row * (int64_t)(n * BITS / 8), n * BITS / 8);
 #pragma unroll
-        for (int t0 = 0; t0 < kVec; t0 += kBThreads)
-            if (t0 + tid < kVec)
-                ((u32x4 *)crow)[t0 + tid] = ((const u32x4 *)cst)[t0 + tid];
-        if (tid == 0)
-            ((float *)a.scales)[row] = rq.scale;
+        for (int t0 = 0; t0 < kVec; t0 += kBThreads) {
+            const int t = t0 + tid;
+            __builtin_amdgcn_raw_buffer_store_b128(((const u32x4 *)cst)[t < kVec ? t : kVec - 1], rc,
+                                                   t < kVec ? 16 * t : kDropOffset, 0, 0);
+        }
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rq.scale), rsrc((float *)a.scales + row, 4),
+                                              tid == 0 ? 0 : kDropOffset, 0, 0);
     }
 }
 
@@ -853,15 +870,31 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
     // ---- codes -> f16 in the staged layout [j][block][slot] (no signs: they
     // apply to the outputs).  INT4: chunk c is row i = c (32 codes); INT8:
     // chunk c holds i = c / 2, j = 16 (c % 2) .. +15.
+    // The codes of one row and its scale, loaded together and with no branch
+    // around the loads (past the last row the buffers have size 0 and every
+    // load reads 0), so that the waits before they are used count only these
+    // loads and not the stores of the row before.  The scale comes as two
+    // 16-bit halves: f16 scales are the low half alone (the high one lies
+    // outside their 2-byte buffer and reads 0).
     u32x4 cur[kCPTi];
+    uint32_t sc_lo = 0, sc_hi = 0;
     auto load_row = [&](int64_t row) {
-        const auto rs = rsrc((const uint8_t *)a.codes + row * (int64_t)(n * BITS / 8), n * BITS / 8);
+        const bool ok = row < a.rows;
+        const int64_t rr = ok ? row : 0;
+        const auto rs = rsrc((const uint8_t *)a.codes + rr * (int64_t)(n * BITS / 8), ok ? n * BITS / 8 : 0);
 #pragma unroll
         for (int cc = 0; cc < kCPTi; ++cc) {
             const int c = kBThreads * cc + tid;
             cur[cc] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                     rs, c < kChunks ? 16 * c : 0x7FFFFFF0, 0, kNonTemporal));
         }
+        const int ssz = a.scale_f16 ? 2 : 4;
+        const auto ss = rsrc((const uint8_t *)a.scales + rr * ssz, ok ? ssz : 0);
+        sc_lo = __builtin_amdgcn_raw_buffer_load_b16(ss, 0, 0, 0);
+        sc_hi = __builtin_amdgcn_raw_buffer_load_b16(ss, 2, 0, 0);
+    };
+    auto loaded_scale = [&]() {
+        return a.scale_f16 ? f16_to_f32((uint16_t)sc_lo) : __uint_as_float(sc_lo | (sc_hi << 16));
     };
     auto put2 = [&](uint16_t *dst, int ja, int jb, uint32_t h2) {
         dst[ja * kBRS] = (uint16_t)h2;
@@ -908,16 +941,16 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
     const float sgn32 = (lane & 32) ? -1.0f : 1.0f;
     int64_t row = blockIdx.x;
     const int64_t G = gridDim.x;
+    float sc = 0.0f;  // scale of the staged row
     if (row < a.rows) {
         load_row(row);
         stage(0);
-        if (row + G < a.rows)
-            load_row(row + G);
+        sc = loaded_scale();
+        load_row(row + G);
     }
     lds_barrier();
     int buf = 0;
     for (; row < a.rows; row += G, buf ^= 1) {
-        const float sc = a.scale_f16 ? f16_to_f32(((const uint16_t *)a.scales)[row]) : ((const float *)a.scales)[row];
         // ---- Z on the matrix core
         f32x4 acc[kBTop][2];
 #pragma unroll
@@ -936,13 +969,6 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
                 }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // ---- the next row into the other buffer, the one after it in flight
-        if (row + G < a.rows) {
-            stage(buf ^ 1);
-            if (row + 2 * G < a.rows)
-                load_row(row + 2 * G);
-        }
-
         // ---- 32-point butterflies (as in the forward kernel)
 #pragma unroll
         for (int b2 = 0; b2 < kBTop; ++b2)
@@ -996,14 +1022,19 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
             return __uint_as_float(__builtin_amdgcn_bitop3_b32(sw << (31 - (bit & 31)), __float_as_uint(v * mul),
                                                                0x80000000u, 0x6C));
         };
-        auto store8 = [&](int e0, const float (&o)[8]) {  // 8 consecutive outputs from element e0
+        // 8 consecutive outputs from element e0.  Every lane issues every
+        // store, those with nothing to store (ok false) at an offset past the
+        // buffer, which drops them: no branch, so the next row's loads wait
+        // for loads only.
+        auto store8 = [&](bool ok, int e0, const float (&o)[8]) {
             if constexpr (OUT == kF32) {
+                const int off = ok ? 4 * e0 : kDropOffset;
                 __builtin_amdgcn_raw_buffer_store_b128(
                     (u32x4){__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])},
-                    ry, 4 * e0, 0, 0);
+                    ry, off, 0, 0);
                 __builtin_amdgcn_raw_buffer_store_b128(
                     (u32x4){__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])},
-                    ry, 4 * e0 + 16, 0, 0);
+                    ry, off + 16, 0, 0);
             } else {
                 u32x4 p;
 #pragma unroll
@@ -1011,15 +1042,14 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
                     const f32x2 f = {o[2 * q], o[2 * q + 1]};
                     p[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
                 }
-                __builtin_amdgcn_raw_buffer_store_b128(p, ry, 2 * e0, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(p, ry, ok ? 2 * e0 : kDropOffset, 0, 0);
             }
         };
 #pragma unroll
         for (int k = 0; k < kBTop / 2; ++k) {
             const int b2 = 2 * k + lb5;
-            if (sb > kBBlk || (sb == kBBlk && b2 > 0))
-                continue;
-            const int ip = sb == kBBlk ? 0 : 1 + kBBlk * b2 + sb;
+            const bool ok = sb < kBBlk || (sb == kBBlk && b2 == 0);
+            const int ip = sb >= kBBlk ? 0 : 1 + kBBlk * b2 + sb;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 float o[8];
@@ -1028,19 +1058,29 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         o[4 * sl + r] = outv(acc[2 * k + t][sl][r], 16 * k + 8 * t + 4 * sl + r);
-                store8(ip * kM2 + 16 * lb4 + 8 * t, o);
+                store8(ok, ip * kM2 + 16 * lb4 + 8 * t, o);
             }
         }
-        if (sb < kBBlk) {
-            const int ip = 1 + kBBlk * (kBTop - 1) + sb;
+        {
+            const int ip = 1 + kBBlk * (kBTop - 1) + (sb < kBBlk ? sb : 0);
             float o[8];
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     o[4 * sl + r] = outv(acc[kBTop - 1][sl][r], 48 + 4 * sl + r);
-            store8(ip * kM2 + 16 * lb4 + 8 * lb5, o);
+            store8(sb < kBBlk, ip * kM2 + 16 * lb4 + 8 * lb5, o);
         }
+
+        // ---- the next row into the other buffer, the one after it in flight.
+        // After this row's stores, not before them: the wait for the loads
+        // (issued one row ago) then counts those stores as issued after the
+        // loads and does not wait for them.
+        if (row + G < a.rows) {
+            stage(buf ^ 1);
+            sc = loaded_scale();
+        }
+        load_row(row + 2 * G);
         lds_barrier();  // the next row is staged; nobody reads this buffer any more
     }
 }
