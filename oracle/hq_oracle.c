@@ -376,9 +376,11 @@ static int make_mats(int b, int8_t **Hp, int8_t **Htp)
 }
 
 /* One row: out[kb+i] = sum_j (x[kb+j]*s[kb+j]) * M[i][j] / sqrt(b), with M
- * = Ht for the forward rotation u.H and M = H for the inverse v.H^T. */
+ * = Ht for the forward rotation u.H and M = H for the inverse v.H^T.  When
+ * sums is not NULL it receives the same sums before the division by
+ * sqrt(b). */
 static void rotate_row(const double *x, const int8_t *s, int n, int b,
-                       const int8_t *Ht, double *u, double *out)
+                       const int8_t *Ht, double *u, double *out, double *sums)
 {
     double norm = sqrt((double)b);
     for (int i = 0; i < n; ++i)
@@ -389,6 +391,8 @@ static void rotate_row(const double *x, const int8_t *s, int n, int b,
             double acc = 0.0;
             for (int j = 0; j < b; ++j)
                 acc += u[k + j] * (double)hrow[j];
+            if (sums)
+                sums[k + i] = acc;
             out[k + i] = acc / norm;
         }
     }
@@ -399,11 +403,17 @@ static void rotate_row(const double *x, const int8_t *s, int n, int b,
 static int qmax_of(int bits) { return (1 << (bits - 1)) - 1; }
 
 /* Quantises one rotated row in groups of `group` consecutive elements (one
- * scale each; group == n is one scale per row).  Writes the packed codes,
- * the stored scales [row * (n/group) + k] and optionally the exact (fp64)
- * scales (same index) and the pre-rounding values x'/scale. */
-static void quantize_row(const double *xr, int n, int group, int bits, int scale_dtype,
-                         uint8_t *codes, void *scale_out, int64_t row,
+ * scale each; group == n is one scale per row).  xr is the rotated row x'
+ * and sums the same values before the division by sqrt(b).  Writes the
+ * packed codes, the stored scales [row * (n/group) + k] and optionally the
+ * exact (fp64) scales (same index) and the pre-rounding values x'/scale.
+ *
+ * x'_i / scale = qmax * x'_i / max|x'| = qmax * sums_i / max|sums|: the
+ * 1/sqrt(b) cancels, and the quotient is taken in that last form, so that a
+ * value lying exactly on a .5 boundary (integer inputs, for instance) stays
+ * exactly on it for every block size, irrational sqrt(b) included. */
+static void quantize_row(const double *xr, const double *sums, int n, int group, int bits,
+                         int scale_dtype, uint8_t *codes, void *scale_out, int64_t row,
                          double *scale_exact, double *preround)
 {
     int qmax = qmax_of(bits);
@@ -411,10 +421,13 @@ static void quantize_row(const double *xr, int n, int group, int bits, int scale
     for (int k = 0; k < ngroups; ++k) {
         int i0 = k * group;
         int64_t si = row * ngroups + k;
-        double m = 0.0;
-        for (int i = i0; i < i0 + group; ++i)
+        double m = 0.0, ms = 0.0;
+        for (int i = i0; i < i0 + group; ++i) {
             if (fabs(xr[i]) > m)
                 m = fabs(xr[i]);
+            if (fabs(sums[i]) > ms)
+                ms = fabs(sums[i]);
+        }
         double scale = m / (double)qmax;
         if (scale_exact)
             scale_exact[si] = scale;
@@ -424,7 +437,8 @@ static void quantize_row(const double *xr, int n, int group, int bits, int scale
             ((uint16_t *)scale_out)[si] = hqo_f64_to_f16(scale);
 
         for (int i = i0; i < i0 + group; ++i) {
-            double r = (m > 0.0) ? xr[i] / scale : 0.0; /* all-zero group: codes 0 */
+            /* all-zero group: codes 0 */
+            double r = (ms > 0.0) ? ((double)qmax * sums[i]) / ms : 0.0;
             if (preround)
                 preround[(int64_t)row * n + i] = r;
             double qd = nearbyint(r); /* round half to even */
@@ -490,8 +504,9 @@ static void *worker(void *arg)
     double *xin = (double *)malloc(sizeof(double) * n);
     double *u = (double *)malloc(sizeof(double) * n);
     double *out = (double *)malloc(sizeof(double) * n);
+    double *sums = (double *)malloc(sizeof(double) * n);
     int8_t *ones = (int8_t *)malloc((size_t)n); /* unit signs for the inverse */
-    if (!xin || !u || !out || !ones) {
+    if (!xin || !u || !out || !sums || !ones) {
         j->err = -2;
         goto done;
     }
@@ -499,14 +514,14 @@ static void *worker(void *arg)
     for (int64_t r = j->r0; r < j->r1; ++r) {
         if (j->kind == 0) {
             rotate_row((const double *)j->x + r * n, j->s, n, j->b, j->Ht, u,
-                       j->xr + r * n);
+                       j->xr + r * n, NULL);
         } else if (j->kind == 1) {
             size_t esz = j->x_dtype == HQO_F32 ? 4 : 2;
             hqo_decode((const char *)j->x + (size_t)r * n * esz, j->x_dtype, n, xin);
-            rotate_row(xin, j->s, n, j->b, j->Ht, u, out);
+            rotate_row(xin, j->s, n, j->b, j->Ht, u, out, sums);
             if (j->xr)
                 memcpy(j->xr + r * n, out, sizeof(double) * n);
-            quantize_row(out, n, j->group, j->bits, j->scale_dtype, j->codes, j->scales, r,
+            quantize_row(out, sums, n, j->group, j->bits, j->scale_dtype, j->codes, j->scales, r,
                          j->scale_exact, j->preround);
         } else {
             /* v = q * scale_stored (of the element's group), then v.H/sqrt(b)
@@ -517,7 +532,7 @@ static void *worker(void *arg)
                                          r * ngroups + i / j->group);
                 xin[i] = (double)unpack_code(j->codes_in, r, n, j->bits, i) * sc;
             }
-            rotate_row(xin, ones, n, j->b, j->H, u, out);
+            rotate_row(xin, ones, n, j->b, j->H, u, out, NULL);
             for (int i = 0; i < n; ++i)
                 j->y[r * n + i] = j->s[i] < 0 ? -out[i] : out[i];
         }
@@ -527,6 +542,7 @@ done:
     free(xin);
     free(u);
     free(out);
+    free(sums);
     return NULL;
 }
 
@@ -751,7 +767,7 @@ int hqo_decode_attention(const void *q, int q_dtype, int q_heads, int kv_heads, 
             err = -1;
             goto done;
         }
-        rotate_row(qin, s, n, b, Ht, u, qr);
+        rotate_row(qin, s, n, b, Ht, u, qr, NULL);
         double cmax = -INFINITY;
         for (int64_t t = 0; t < tokens; ++t) {
             int64_t row = t * kv_heads + kh; /* the row of (token t, kv head kh) */
@@ -777,7 +793,7 @@ int hqo_decode_attention(const void *q, int q_dtype, int q_heads, int kv_heads, 
                 o[i] += w * (double)unpack_code(v_codes, row, n, bits, i);
         }
         /* back to the query's space: o . H_b^T / sqrt(b), then * s */
-        rotate_row(o, ones, n, b, H, u, qin);
+        rotate_row(o, ones, n, b, H, u, qin, NULL);
         for (int i = 0; i < n; ++i)
             out[(int64_t)h * n + i] = s[i] < 0 ? -qin[i] : qin[i];
     }

@@ -245,6 +245,36 @@ def test_quantisation_brute_force(bits):
     assert np.sum(np.isclose(frac, 0.5, atol=1e-6)) > 20
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("n,b", [(16, 16), (64, 8), (128, 128), (512, 128), (96, 96),
+                                 (24, 24)])
+def test_exact_ties_round_half_to_even_any_block_size(n, b, bits):
+    # Integer rows built so that x'/scale = y/4 lands exactly on .5 ties
+    # (tests/ties.py).  The expected codes come from exact rational
+    # arithmetic on y = (x*s).H with H from scipy (Sylvester) or the pinned
+    # Paley construction, rounded by the brute-force nearest-even search:
+    # the oracle must agree with no tie window, also where sqrt(b) is
+    # irrational (b = 128, 512, 96, 24).
+    from fractions import Fraction
+    from tests.ties import tie_rows, exact_ties
+    qmax = (1 << (bits - 1)) - 1
+    rng = np.random.default_rng(100 * n + b + bits)
+    s = np.where(rng.integers(0, 2, n) == 1, 1, -1).astype(np.int8)
+    H = scipy_hadamard(b) if (b & (b - 1)) == 0 else O.hadamard(b)
+    x = tie_rows(H, 6, n, s, bits, rng)
+    r = O.rotate_quant(x, O.F32, b, s, bits, O.F32)
+    got = O.unpack_codes(r["codes"], bits, n)
+    u = x.astype(np.int64) * s.astype(np.int64)
+    want = np.empty_like(got)
+    for i in range(x.shape[0]):
+        y = np.concatenate([u[i, k:k + b] @ H.astype(np.int64) for k in range(0, n, b)])
+        m = int(np.abs(y).max())
+        q = np.array([float(Fraction(qmax * int(v), m)) for v in y])
+        want[i] = _brute_force_round(q[None, :], qmax)[0]
+    assert np.array_equal(got, want)
+    assert exact_ties(r["preround"]) > x.size // 8
+
+
 def test_int8_matches_numpy_round_and_clip():
     rng = np.random.default_rng(3)
     x = rng.standard_normal((50, 128)).astype(np.float32)
