@@ -79,29 +79,45 @@ __device__ __forceinline__ int quant_code(float y, float inv, int qmax)
 // Per-row constants of the quantiser.  m = max|y| over the row (unnormalised
 // rotated values); kq = 1 / (sqrt(b) * qmax) rounded to fp32 on the host.
 struct RowQuant {
-    float inv;    // qmax / m, or 0 for a row treated as zero
+    float inv;    // qmax / (m * boost), or 0 for a zero row
     float scale;  // m * kq = max|x'| / qmax
+    float boost;  // 1, or kBoost for a row below kBoostBelow
 };
 
-// Rows whose absmax is below this are treated as all-zero rows (scale 0,
-// codes 0): qmax / m would overflow fp32 for them.
-constexpr float kTinyRow = 0x1p-120f;
+// qmax / m overflows binary32 once m drops below about 2^-121.  The codes
+// depend only on y / m, so a row whose maximum is below kBoostBelow is
+// quantised from its values magnified by kBoost, an exact power of two:
+// y * kBoost and m * kBoost are exact (a subnormal becomes normal), and
+// code = round(y * kBoost * qmax / (m * kBoost)).  Every finite row, down
+// to the smallest subnormal, thus gets the codes of its exact quotients;
+// the scale still comes from m itself.
+constexpr float kBoostBelow = 0x1p-100f;
+constexpr float kBoost = 0x1p+64f;
 
-// inv = qmax / m from the hardware reciprocal refined by one residual step
-// (within about half an ulp of the correctly rounded quotient for normal m;
-// a handful of instructions instead of the full IEEE division sequence,
-// which every lane of a row would otherwise run).
+// inv from the hardware reciprocal refined by one residual step (within
+// about half an ulp of the correctly rounded quotient; a handful of
+// instructions instead of the full IEEE division sequence, which every lane
+// of a row would otherwise run).
 __device__ __forceinline__ RowQuant row_quant(float m, float kq, int qmax)
 {
     const float fq = (float)qmax;
-    const bool live = m >= kTinyRow;
-    const float r = __builtin_amdgcn_rcpf(live ? m : 1.0f);
-    const float q0 = fq * r;
-    const float e = __builtin_fmaf(-m, q0, fq);
+    const bool live = m > 0.0f;
     RowQuant rq;
+    rq.boost = live && m < kBoostBelow ? kBoost : 1.0f;
+    const float mb = m * rq.boost;
+    const float r = __builtin_amdgcn_rcpf(live ? mb : 1.0f);
+    const float q0 = fq * r;
+    const float e = __builtin_fmaf(-mb, q0, fq);
     rq.inv = live ? __builtin_fmaf(e, r, q0) : 0.0f;
-    rq.scale = live ? m * kq : 0.0f;
+    rq.scale = m * kq;
     return rq;
+}
+
+// True on every lane when any lane of the wave holds a magnified row
+// (wave-uniform, so the magnification can sit behind a scalar branch).
+__device__ __forceinline__ bool wave_any_boost(const RowQuant &rq)
+{
+    return __builtin_amdgcn_ballot_w64(rq.boost != 1.0f) != 0;
 }
 
 }  // namespace hq

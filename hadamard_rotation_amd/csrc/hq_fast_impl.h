@@ -535,7 +535,8 @@ void fast_kernel(FastArgs a)
                 else
                     ((float *)a.scales)[sidx] = rq.scale;
             }
-            gm[gi << lg] = rq.inv;
+            // a magnified group is flagged by the sign (inv is otherwise >= 0)
+            gm[gi << lg] = rq.boost != 1.0f ? -rq.inv : rq.inv;
         }
         wave_lds_sync();
         const int64_t e0 = r0 * (int64_t)a.n;  // wave-uniform
@@ -551,6 +552,13 @@ void fast_kernel(FastArgs a)
                     continue;
                 const int idx = LONG ? ou - seg_base : lr * units_row + ou;
                 float inv = gm[idx & ~(gu - 1)];
+                const bool boosted = inv < 0.0f;
+                inv = fabsf(inv);
+                if (__builtin_amdgcn_ballot_w64(boosted) != 0) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        v[k][u][j] *= boosted ? kBoost : 1.0f;
+                }
                 inv = lane_neg ? -inv : inv;
                 if (!row_ok)
                     continue;
@@ -873,6 +881,13 @@ void fast_kernel(FastArgs a)
                 }
                 const int qmax = a.bits == 4 ? 7 : 127;
                 RowQuant rq = row_quant(__uint_as_float(mb), a.kq, qmax);
+                if (wave_any_boost(rq)) {  // rows too small for qmax / max
+#pragma unroll
+                    for (int u = 0; u < UNITS; ++u)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            v[k][u][j] *= rq.boost;
+                }
                 if (row_ok && l == 0 && seg == 0) {
                     if (a.scale_f16)
                         ((uint16_t *)a.scales + r0)[lr] = f32_to_f16(rq.scale);

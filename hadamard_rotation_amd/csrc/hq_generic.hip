@@ -300,11 +300,11 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(GenericArgs a)
                     if constexpr (BITS == 8) {
                         for (int i = lane; i < g; i += 64)
                             ((int8_t *)a.codes)[base + i0 + i] =
-                                (int8_t)quant_code(L[i0 + i], rq.inv, qmax);
+                                (int8_t)quant_code(L[i0 + i] * rq.boost, rq.inv, qmax);
                     } else {
                         for (int j = lane; j < (g >> 1); j += 64) {
-                            int q0 = quant_code(L[i0 + 2 * j], rq.inv, qmax);
-                            int q1 = quant_code(L[i0 + 2 * j + 1], rq.inv, qmax);
+                            int q0 = quant_code(L[i0 + 2 * j] * rq.boost, rq.inv, qmax);
+                            int q1 = quant_code(L[i0 + 2 * j + 1] * rq.boost, rq.inv, qmax);
                             ((uint8_t *)a.codes)[((base + i0) >> 1) + j] =
                                 (uint8_t)((q0 & 15) | ((q1 & 15) << 4));
                         }
@@ -330,11 +330,11 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(GenericArgs a)
                 }
                 if constexpr (BITS == 8) {
                     for (int i = threadIdx.x; live && i < n; i += kThreads)
-                        ((int8_t *)a.codes)[obase + i] = (int8_t)quant_code(L[i], rq.inv, qmax);
+                        ((int8_t *)a.codes)[obase + i] = (int8_t)quant_code(L[i] * rq.boost, rq.inv, qmax);
                 } else {
                     for (int j = threadIdx.x; live && j < (n >> 1); j += kThreads) {
-                        int q0 = quant_code(L[2 * j], rq.inv, qmax);
-                        int q1 = quant_code(L[2 * j + 1], rq.inv, qmax);
+                        int q0 = quant_code(L[2 * j] * rq.boost, rq.inv, qmax);
+                        int q1 = quant_code(L[2 * j + 1] * rq.boost, rq.inv, qmax);
                         ((uint8_t *)a.codes)[(obase >> 1) + j] =
                             (uint8_t)((q0 & 15) | ((q1 & 15) << 4));
                     }

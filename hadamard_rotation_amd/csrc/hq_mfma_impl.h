@@ -509,11 +509,14 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
             // z[q], row rho: tile 4q + rho (T >= 4) or rho & 1 (T == 2)
             const int rho = lane >> 4;
             const bool rep_lane = (pl & ((1 << (logg - 5)) - 1)) == 0 && (T >= 4 || rho < 2);
-            float iz[NZ];
+            float iz[NZ], bz[NZ];
+            bool boosted = false;
 #pragma unroll
             for (int q = 0; q < NZ; ++q) {
                 const uint32_t mb = group_lane_max<D>(z[q], logg);
                 const RowQuant rq = row_quant(__uint_as_float(mb), a.kq, qmax);
+                bz[q] = rq.boost;
+                boosted |= rq.boost != 1.0f;
                 const int t = T >= 4 ? 4 * q + rho : (rho & 1);
                 const int64_t gi = (e0 + t * 512 + 32 * pl) >> logg;
                 if (rep_lane && gi < a.ngroups) {
@@ -524,25 +527,38 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
                 }
                 iz[q] = lane_neg ? -rq.inv : rq.inv;
             }
-            // un-transpose: inv[t] for every tile at every lane of it
-            float inv[T];
-            if constexpr (T >= 4) {
+            // un-transpose: a value per tile at every lane of the tile
+            auto untranspose = [&](const float (&zv)[NZ], float (&out)[T]) {
+                if constexpr (T >= 4) {
 #pragma unroll
-                for (int q = 0; q < NZ; ++q) {
-                    const uint32_t zi = __float_as_uint(iz[q]);
-                    const auto w = __builtin_amdgcn_permlane32_swap(zi, zi, false, false);
+                    for (int q = 0; q < NZ; ++q) {
+                        const uint32_t zi = __float_as_uint(zv[q]);
+                        const auto w = __builtin_amdgcn_permlane32_swap(zi, zi, false, false);
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const auto u = __builtin_amdgcn_permlane16_swap(w[h], w[h], false, false);
-                        inv[4 * q + 2 * h] = __uint_as_float(u[0]);
-                        inv[4 * q + 2 * h + 1] = __uint_as_float(u[1]);
+                        for (int h = 0; h < 2; ++h) {
+                            const auto u = __builtin_amdgcn_permlane16_swap(w[h], w[h], false, false);
+                            out[4 * q + 2 * h] = __uint_as_float(u[0]);
+                            out[4 * q + 2 * h + 1] = __uint_as_float(u[1]);
+                        }
                     }
+                } else {
+                    const uint32_t zi = __float_as_uint(zv[0]);
+                    const auto u = __builtin_amdgcn_permlane16_swap(zi, zi, false, false);
+                    out[0] = __uint_as_float(u[0]);
+                    out[1] = __uint_as_float(u[1]);
                 }
-            } else {
-                const uint32_t zi = __float_as_uint(iz[0]);
-                const auto u = __builtin_amdgcn_permlane16_swap(zi, zi, false, false);
-                inv[0] = __uint_as_float(u[0]);
-                inv[1] = __uint_as_float(u[1]);
+            };
+            float inv[T];
+            untranspose(iz, inv);
+            // groups too small for qmax / max: magnify their values exactly
+            if (__builtin_amdgcn_ballot_w64(boosted) != 0) {
+                float boost[T];
+                untranspose(bz, boost);
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        v[t][j] *= boost[t];
             }
             const int bits = a.bits;
 #pragma unroll
@@ -571,6 +587,13 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
                 constexpr int NDPP = LOGG - 5 < 4 ? LOGG - 5 : 4;
                 const uint32_t mb = row_lane_max<NDPP>(__float_as_uint(m));
                 const RowQuant rq = row_quant(__uint_as_float(mb), a.kq, qmax);
+                if (wave_any_boost(rq)) {  // rows too small for qmax / max
+#pragma unroll
+                    for (int t = t0; t < t0 + TPG; ++t)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            v[t][j] *= rq.boost;
+                }
                 // the lane's group: first element of its outputs >> LOGG
                 const int64_t grp = (e0 + t0 * 512 + out_off) >> LOGG;
                 bool grp_ok = grp < a.ngroups;

@@ -372,6 +372,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int w = 1; w < kWaves; ++w)
             m = fmaxf(m, red[w]);
         const RowQuant rq = row_quant(m, a.kq, qmax);
+        if (rq.boost != 1.0f) {  // workgroup-uniform: a row too small for qmax / max
+#pragma unroll
+            for (int tt = 0; tt < kTPW; ++tt)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    acc[tt][mt] *= rq.boost;
+        }
 
         // ---- codes of y[i'][16 mt + 4 rg .. +3] into LDS
 #pragma unroll
@@ -729,6 +736,13 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
         for (int w = 1; w < kBW; ++w)
             m = fmaxf(m, red[w]);
         const RowQuant rq = row_quant(m, a.kq, qmax);
+        if (rq.boost != 1.0f) {  // workgroup-uniform: a row too small for qmax / max
+#pragma unroll
+            for (int b2 = 0; b2 < kBTop; ++b2)
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl)
+                    acc[b2][sl] *= rq.boost;
+        }
 
         // ---- codes into LDS.  |y| <= m and inv is qmax / m to within an ulp,
         // so |y * inv| < qmax + 1/2 and the codes need no clamp; the fma's

@@ -83,9 +83,8 @@ typedef enum hq_dtype {
  *            bits == 8: [rows, n] int8 in [-127, 127].
  *   scales   [rows], element type scale_dtype (HQ_F32 or HQ_F16), the stored
  *            value of max|x'|/qmax rounded to nearest even.  A row of zeros
- *            gets scale 0 and codes 0, and so does a row whose unnormalised
- *            maximum max|(x*s) H_b| is below 2^-120 (every |x| below about
- *            1e-37): for such a row qmax/max would overflow binary32.
+ *            gets scale 0 and codes 0.  Every other finite row, down to
+ *            subnormal inputs, is quantised as defined above.
  * Codes are computed from the unrounded scale, so they do not depend on
  * scale_dtype.
  */
@@ -118,8 +117,8 @@ hq_status hq_dequant_rotate_inv(const void *codes, const void *scales,
  *            2 <= group < n that divides n; anything else is HQ_EINVAL.
  *            The group size is independent of the block size b.
  *   scales   [rows, n/group] (row-major), element type scale_dtype.
- *   Everything else, including the zero and below-2^-120 rules (applied per
- *   group), is as for hq_rotate_quant.
+ *   Everything else, including the zero rule (applied per group), is as for
+ *   hq_rotate_quant.
  */
 hq_status hq_rotate_quant_grouped(const void *x, hq_dtype x_dtype, int64_t rows, int32_t n,
                                   int32_t b, const int8_t *s, int32_t bits, int32_t group,

@@ -151,24 +151,39 @@ def test_zero_rows_and_spikes():
         assert np.allclose(y[1], raw[1], atol=1e-6)
 
 
-def test_tiny_rows_flush_to_zero():
-    # A row whose unnormalised rotated maximum is below 2^-120 is stored as
-    # a zero row (the library's documented contract: qmax / max would
-    # overflow binary32).  Just above that, rows follow the oracle.
-    # (32768, 4096) takes the generic LDS kernel, the others the fast one.
-    for n, b in ((128, 128), (4096, 4096), (11008, 128), (32768, 4096)):
-        raw = np.zeros((4, n), dtype=np.float32)
-        raw[0, 5] = 1e-38            # flushed
-        raw[1, n - 3] = -2.0 ** -119  # kept: maximum 2^-119
-        raw[2, :] = 2.0 ** -110       # kept
+def test_tiny_rows_follow_the_oracle():
+    # Rows whose maximum lies far below the range where qmax / max fits
+    # binary32, down to subnormal inputs, get the oracle's codes and scales
+    # like any other row.  (32768, 4096) takes the generic LDS kernel, the
+    # fp32 rows the butterfly kernel, the 16-bit rows the matrix core (and
+    # the long-row butterfly kernel for 11008).
+    for n, b in ((128, 128), (4096, 4096), (11008, 128), (32768, 4096), (512, 128)):
+        raw = np.zeros((6, n), dtype=np.float32)
+        raw[0, 5] = 1.5 * 2.0 ** -127                   # subnormal
+        raw[1, n - 3] = -2.0 ** -119
+        raw[2, :] = 2.0 ** -110
         raw[3, 7] = 1.0
+        raw[4, 3] = 2.0 ** -133                          # subnormal
+        raw[4, n // 2] = -3 * 2.0 ** -133
+        raw[5, 1::97] = 2.0 ** -126 * (1 + np.arange(len(raw[5, 1::97])) % 64)
         s = np.where(np.arange(n) % 5 == 0, -1, 1).astype(np.int8)
-        for bits in (4, 8):
-            codes, scales = G.gpu_rotate_quant(raw, W.F32, s, b, bits, W.F32)
-            assert scales[0] == 0 and np.all(codes[0] == 0), (n, bits)
-            ref = O.rotate_quant(raw[1:], W.F32, b, s, bits, W.F32)
-            P.check_codes(codes[1:], ref, bits, n, what=f"tiny n={n} bits={bits}")
-            P.check_scales(scales[1:], ref, W.F32, what=f"tiny n={n} bits={bits}")
+        for dt in (W.F32, W.BF16):
+            # bf16 holds the same exponent range; these values are exact in it
+            x = raw if dt == W.F32 else \
+                (raw.view(np.uint32) >> 16).astype(np.uint16)
+            if dt == W.BF16:
+                assert np.array_equal(O.decode(x, W.BF16), raw.astype(np.float64))
+            for bits in (4, 8):
+                tag = f"tiny n={n} b={b} dt={dt} bits={bits}"
+                print(f"[tiny] {tag}", flush=True)
+                codes, scales = G.gpu_rotate_quant(x, dt, s, b, bits, W.F32)
+                ref = O.rotate_quant(x, dt, b, s, bits, W.F32)
+                P.check_codes(codes, ref, bits, n, what=tag)
+                P.check_scales(scales, ref, W.F32, what=tag)
+                codes16, scales16 = G.gpu_rotate_quant(x, dt, s, b, bits, W.F16)
+                ref16 = O.rotate_quant(x, dt, b, s, bits, W.F16)
+                assert np.array_equal(codes16, codes)
+                P.check_scales(scales16, ref16, W.F16, what=tag + " f16 scales")
 
 
 def test_rows_zero_is_noop():
