@@ -238,18 +238,25 @@ def hq_decode_attention(q: torch.Tensor, s: torch.Tensor, b: int, k_codes: torch
     over a rotated, quantised K/V cache: codes [tokens, kv_heads, n/2] uint8,
     scales [tokens, kv_heads].  Returns out [q_heads, n] float32 in the
     query's space.  The workspace is allocated with torch when not given."""
+    # shapes first (the library reads tokens * kv_heads rows of n/2 code
+    # bytes from each code tensor, so a narrower one would be read past its
+    # end), then placement and types
+    q_heads, n = _rows_n(q, "q")
+    for name, t in (("k_codes", k_codes), ("v_codes", v_codes)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 3:
+            raise ValueError(f"{name} must be a 3-D tensor [tokens, kv_heads, n/2]")
+    tokens, kv_heads, _ = k_codes.shape
+    width = n // 2 if bits == 4 else n
+    for name, t in (("k_codes", k_codes), ("v_codes", v_codes)):
+        if tuple(t.shape) != (tokens, kv_heads, width):
+            raise ValueError(f"{name} must have shape {(tokens, kv_heads, width)} for "
+                             f"n={n}, bits={bits}; got {tuple(t.shape)}")
     _check_dev(q, "q")
     if q.dtype not in _TORCH_TO_HQ:
         raise ValueError(f"q dtype {q.dtype} unsupported")
-    q_heads, n = _rows_n(q, "q")
     _check_dev(s, "s", torch.int8, (n,))
     for name, t in (("k_codes", k_codes), ("v_codes", v_codes)):
         _check_dev(t, name, torch.uint8)
-        if t.dim() != 3:
-            raise ValueError(f"{name} must be [tokens, kv_heads, n/2]")
-    tokens, kv_heads, w = k_codes.shape
-    if tuple(v_codes.shape) != (tokens, kv_heads, w):
-        raise ValueError("k_codes and v_codes must have the same shape")
     if k_scales.dtype not in (torch.float32, torch.float16):
         raise ValueError("scales must be float32 or float16")
     _check_dev(k_scales, "k_scales", None, (tokens, kv_heads))

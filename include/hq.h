@@ -23,10 +23,22 @@
  *       scale = max_i |x'_i| / qmax,   qmax = 2^(bits-1) - 1  (7 or 127)
  *       q_i   = clamp(round_half_even(x'_i / scale), -qmax, qmax)
  *
- *   and the inverse path dequantises and rotates back ([MS] principle: the
- *   normalised H is orthogonal and symmetric, hence its own inverse):
+ *   and the inverse path dequantises and rotates back with the transpose
+ *   ([MS] principle: the normalised H is orthogonal, Q^T = Q^-1):
  *
- *       x_hat[kb+i] = s[kb+i] * sum_j (q[kb+j] * scale) H_b[j][i] / sqrt(b)
+ *       x_hat[kb+i] = s[kb+i] * sum_j (q[kb+j] * scale) H_b[i][j] / sqrt(b)
+ *
+ *   The Sylvester H_b is symmetric, so there H_b^T = H_b; the matrices of
+ *   the full rotations below (H_k (x) H_m) are not, and their inverse
+ *   multiplies by the transpose.
+ *
+ *   Full rotation of a width that is not a power of two (b == n only):
+ *   H_n = H_k (x) H_(n/k), n/k a power of two and H_k Paley's first
+ *   construction over GF(q), q = k - 1 = p^e = 3 (mod 4) a prime power with
+ *   e <= 3; k is the smallest order of the form (odd part of n) * 2^a.
+ *   Element i*(n/k) + j of a row is entry (i, j) of the Kronecker product
+ *   ([RQ] 2.1: larger Hadamard matrices as Kronecker products).  Widths
+ *   without such a factorisation (e.g. 496 = 31 * 16) are HQ_EINVAL.
  *
  * Conventions shared by every entry point
  *   - Every pointer argument except `stream` is a DEVICE pointer owned by the
@@ -38,8 +50,12 @@
  *     Head-dim-innermost layouts ([B,H,S,D], [S,H,D]) are just rows of D.
  *   - s: int8 [n]; an element < 0 means "negate", anything else "keep".
  *     The caller supplies it; the library never draws random numbers.
- *   - Supported shapes: b a power of two with 1 <= b <= 4096, n % b == 0,
- *     n % 16 == 0, 16 <= n <= hq_max_n(); rows >= 0 (rows == 0 is a no-op).
+ *   - Supported shapes: n % 16 == 0, 16 <= n <= hq_max_n(), rows >= 0
+ *     (rows == 0 is a no-op), and either
+ *       b a power of two with n % b == 0 (b > 4096: HQ_EUNSUPPORTED), or
+ *       b == n for a width n = k * 2^m that is not a power of two and has
+ *       a Paley order k as above (e.g. 96 = 12 * 8, 11008 = 344 * 32);
+ *     any other b is HQ_EINVAL.
  *   - Alignment: x, codes, y and s must be 16-byte aligned; scales must be
  *     aligned to their element size.
  *   - Outputs must not overlap inputs.  Inputs are never modified.

@@ -238,3 +238,53 @@ def test_full_width_rotation_that_is_not_a_power_of_two():
     # a block size that is neither a power of two nor the whole width
     assert rq(rows=0, n=11008, b=344) == hq.HQ_EINVAL
     assert rq(rows=0, n=11008, b=5504) == hq.HQ_EINVAL
+
+
+def test_header_documents_every_accepted_block_size():
+    # The header's shape rule, restated here: b a power of two dividing n
+    # (above 4096 unsupported), or b == n for a width with a Paley split
+    # (oracle.hadamard_split finds one); every other b is invalid.  The
+    # library's decisions over a sweep of widths and block sizes must follow
+    # it, and the header must state both accepted classes.
+    from oracle import oracle as O
+    text = open(HEADER).read()
+    assert "b a power of two with n % b == 0" in text
+    assert "b == n for a width n = k * 2^m that is not a power of two" in text
+    assert "inverse" in text and "transpose" in text
+    for n in list(range(16, 2049, 16)) + [11008, 10624, 8192, 16384]:
+        pow2_n = (n & (n - 1)) == 0
+        split = O.hadamard_split(n)
+        for b in sorted({1, 2, 16, 128, 4096, 8192, n, n // 2, 3, 96, 344}):
+            if b < 1:
+                continue
+            got = rq(rows=0, n=n, b=b, x=None, codes=None, scales=None, s=None)
+            if (b & (b - 1)) == 0:
+                want = hq.HQ_EINVAL if n % b else (hq.HQ_EUNSUPPORTED if b > 4096 else hq.HQ_OK)
+            elif b == n and not pow2_n and split is not None:
+                want = hq.HQ_OK
+            else:
+                want = hq.HQ_EINVAL
+            if got == hq.HQ_EUNSUPPORTED and want == hq.HQ_EUNSUPPORTED:
+                continue
+            assert got == want, (n, b, got, want)
+
+
+def test_decode_attention_binding_rejects_code_width():
+    # codes of the wrong width would be read past their end by the kernel:
+    # the binding raises on the host before anything is launched
+    import torch
+    q = torch.zeros((32, 128), dtype=torch.bfloat16)
+    s = torch.ones(128, dtype=torch.int8)
+    sc = torch.zeros((100, 8), dtype=torch.float16)
+    good = torch.zeros((100, 8, 64), dtype=torch.uint8)
+    for bad in (torch.zeros((100, 8, 32), dtype=torch.uint8),
+                torch.zeros((100, 8, 128), dtype=torch.uint8),
+                torch.zeros((100, 4, 64), dtype=torch.uint8),
+                torch.zeros((100, 512), dtype=torch.uint8)):
+        with pytest.raises(ValueError, match="codes must"):
+            hq.hq_decode_attention(q, s, 128, bad, sc, good, sc)
+        with pytest.raises(ValueError, match="codes must"):
+            hq.hq_decode_attention(q, s, 128, good, sc, bad, sc)
+    # the right width gets as far as the device check
+    with pytest.raises(ValueError, match="GPU"):
+        hq.hq_decode_attention(q, s, 128, good, sc, good, sc)
