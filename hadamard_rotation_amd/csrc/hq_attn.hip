@@ -40,9 +40,9 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kHeadDim = 128;
-constexpr int kPartStride = kHeadDim + 4;  // floats per (head, partial): o[128], max, sum, 2 unused
-constexpr int kWaves = 4;                  // waves per workgroup of kernel 1
+constexpr int kHeadDim = kAttnHeadDim;
+constexpr int kPartStride = kAttnPartStride;  // floats per (head, partial): o[128], max, sum, 2 unused
+constexpr int kWaves = kAttnWaves;            // waves per workgroup of kernel 1
 
 struct AttnArgs {
     const void *q;
@@ -661,19 +661,6 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(AttnArgs a
     *(float2 *)&a.out[(int64_t)h * kHeadDim + 2 * lane] = make_float2(s0 < 0 ? -v0 : v0, s1 < 0 ? -v1 : v1);
 }
 
-int parts_for(int kv_heads, int64_t tokens)
-{
-    // about 3072 waves in kernel 1 (12 per CU), whole workgroups, at most one
-    // part per 16-token block
-    const int64_t blocks = (tokens + 15) / 16;
-    int64_t p = (3072 + kv_heads - 1) / kv_heads;
-    p = (p + kWaves - 1) / kWaves * kWaves;
-    const int64_t pmax = (blocks + kWaves - 1) / kWaves * kWaves;
-    if (p > pmax)
-        p = pmax;
-    return (int)(p < kWaves ? kWaves : p);
-}
-
 template <int G>
 hipError_t launch_g(const AttnArgs &aa, hipStream_t st)
 {
@@ -687,11 +674,6 @@ hipError_t launch_g(const AttnArgs &aa, hipStream_t st)
 }
 
 }  // namespace
-
-size_t attention_workspace(int q_heads, int kv_heads, int64_t tokens)
-{
-    return (size_t)q_heads * (parts_for(kv_heads, tokens) / kWaves) * kPartStride * sizeof(float);
-}
 
 hipError_t launch_attention(const AttnRequest &r)
 {
@@ -710,7 +692,7 @@ hipError_t launch_attention(const AttnRequest &r)
     aa.scale_f16 = r.scale_dtype == kF16;
     aa.q_heads = r.q_heads;
     aa.kv_heads = r.kv_heads;
-    aa.nparts = parts_for(r.kv_heads, r.tokens);
+    aa.nparts = attention_parts(r.kv_heads, r.tokens);
     aa.nws = aa.nparts / kWaves;
     int lb = 0;
     while ((1 << lb) < r.b)

@@ -87,7 +87,33 @@ struct AttnRequest {
     hipStream_t stream;
 };
 
-size_t attention_workspace(int q_heads, int kv_heads, int64_t tokens);
+// Work split of the decode attention, shared by the host validation and the
+// kernels: kernel 1 runs workgroups of kAttnWaves waves, each wave one
+// "part" (a token range of one kv head); about 3072 waves in all (12 per
+// CU), whole workgroups, at most one part per 16-token block.  Each
+// workgroup leaves one partial per query head in the workspace:
+// o[128], max, sum and two unused floats.
+constexpr int kAttnHeadDim = 128;
+constexpr int kAttnPartStride = kAttnHeadDim + 4;
+constexpr int kAttnWaves = 4;
+
+inline int attention_parts(int kv_heads, int64_t tokens)
+{
+    const int64_t blocks = (tokens + 15) / 16;
+    int64_t p = (3072 + kv_heads - 1) / kv_heads;
+    p = (p + kAttnWaves - 1) / kAttnWaves * kAttnWaves;
+    const int64_t pmax = (blocks + kAttnWaves - 1) / kAttnWaves * kAttnWaves;
+    if (p > pmax)
+        p = pmax;
+    return (int)(p < kAttnWaves ? kAttnWaves : p);
+}
+
+inline size_t attention_workspace(int q_heads, int kv_heads, int64_t tokens)
+{
+    return (size_t)q_heads * (attention_parts(kv_heads, tokens) / kAttnWaves) * kAttnPartStride *
+           sizeof(float);
+}
+
 hipError_t launch_attention(const AttnRequest &r);
 
 // Generic path: any supported (n, b); one workgroup per row with the row

@@ -83,7 +83,15 @@ typedef enum hq_status {
                             launch failure); see hq_last_hip_error()       */
 } hq_status;
 
-typedef enum hq_dtype {
+/* Under C++ the type is fixed to int32_t, so that any int32 value a caller
+ * passes is a valid value of the type and is rejected as HQ_EINVAL by the
+ * validation (an enum without a fixed type holds only the range of its
+ * enumerators there).  C sees a plain enum of the same size. */
+typedef enum hq_dtype
+#ifdef __cplusplus
+    : int32_t
+#endif
+{
     HQ_F32 = 0,  /* IEEE binary32 */
     HQ_BF16 = 1, /* bfloat16      */
     HQ_F16 = 2   /* IEEE binary16 */
