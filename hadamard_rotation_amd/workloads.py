@@ -204,3 +204,15 @@ def random_rows(seed: int, rows: int, n: int, dtype: int = BF16,
     if dtype == BF16:
         return to_bf16_bits(x), s
     return x.astype(np.float16).view(np.uint16), s
+
+
+def spiked_gaussian_row(seed: int, n: int, index: int, value: float) -> np.ndarray:
+    """One fp32 row [1, n] of standard-normal draws from numpy's default
+    generator seeded with `seed` (drawn in double precision, then rounded to
+    fp32), with entry `index` replaced by `value`: the single-outlier row of
+    the error-reduction example in "旋转量化：大模型低比特量化中的离群值克星"
+    section 2.2 (seed 42, n 4096, a spike of 30)."""
+    rng = np.random.default_rng(seed)
+    row = rng.standard_normal((1, n)).astype(np.float32)
+    row[0, index] = np.float32(value)
+    return row

@@ -16,14 +16,8 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
+from hadamard_rotation_amd import workloads as W  # noqa: E402
 from oracle import oracle as O  # noqa: E402
-
-
-def page_row():
-    rng = np.random.default_rng(42)
-    w = rng.standard_normal((1, 4096)).astype(np.float32)
-    w[0, 123] = 30.0
-    return w
 
 
 def mean_abs_error(w, b):
@@ -35,13 +29,14 @@ def mean_abs_error(w, b):
 
 
 def main():
-    w = page_row()
+    w = W.spiked_gaussian_row(42, 4096, 123, 30.0)
     unrot = mean_abs_error(w, 1)      # b = 1: identity rotation
     rot = mean_abs_error(w, 4096)     # full normalised rotation
     path = os.path.join(HERE, "quant_error_anchor.txt")
     with open(path, "w") as f:
         f.write("# Written by tests/golden/make_quant_error_anchor.py from the CPU oracle.\n")
-        f.write("# Page-4 section 2.2 example (seed 42, spike 30 at index 123, INT4).\n")
+        f.write("# Error-reduction example of \"旋转量化：大模型低比特量化中的离群值克星\"\n")
+        f.write("# section 2.2 (seed 42, spike 30 at index 123, INT4).\n")
         f.write("# The page prints about 0.19 unrotated and below 0.02 rotated; those\n")
         f.write("# figures do not follow from its own recipe and are not pinned.\n")
         f.write(f"unrotated {unrot:.12g}\n")

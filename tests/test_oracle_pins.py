@@ -372,9 +372,8 @@ def test_round_trip_error_bound(n, b, bits, sd):
 def test_error_reduction_page_example():
     # [RQ] 2.2 worked example: rotation cuts the 4-bit error many times over.
     fx = _read_kv("quant_error_anchor.txt")
-    rng = np.random.default_rng(42)
-    w = rng.standard_normal((1, 4096)).astype(np.float32)
-    w[0, 123] = 30.0
+    from hadamard_rotation_amd import workloads as W
+    w = W.spiked_gaussian_row(42, 4096, 123, 30.0)
     ones = np.ones(4096, dtype=np.int8)
     errs = []
     for b in (1, 4096):
