@@ -166,7 +166,11 @@ __device__ __forceinline__ uint32_t group_lane_max(uint32_t v, int logg)
 // WIDE  rows of several 128-blocks with one scale per block, run as rows of
 //       one block (LOGB = LOGN = LOGG = 7): each block row takes the signs of
 //       its place in the real row (MfmaArgs::wide_div blocks per real row)
-template <int OP, int IN, int T, int LOGB, int LOGN, int LOGG, bool APPEND = false, bool WIDE = false>
+// GRID  one group of T tiles per wave and one wave per workgroup (the launch
+//       has a workgroup per group); otherwise persistent workgroups, one per
+//       CU, hand out groups through an LDS counter with a prefetch
+template <int OP, int IN, int T, int LOGB, int LOGN, int LOGG, bool APPEND = false, bool WIDE = false,
+          bool GRID = false>
 __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
 {
     static_assert(!WIDE || (LOGB == 7 && LOGN == 7 && LOGG == 7 && !APPEND), "wide rows run as 128-blocks");
@@ -216,9 +220,10 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
     };
 
     // The two +-1 slices of H_32 as A operands: lane l holds row m = l & 15
-    // at k = 8*(l >> 4) + j; row m of slice h is output Q(m, h).
+    // at k = 8*(l >> 4) + j; row m of slice h is output Q(m, h).  (GRID:
+    // built after the row loads are issued.)
     u32x4 amat[2];
-    {
+    auto make_amat = [&]() {
         const uint32_t one = IN == kF16 ? 0x3C00u : 0x3F80u;
         const int m = l16;
 #pragma unroll
@@ -236,11 +241,13 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
                 amat[h][c] = w;
             }
         }
-    }
+    };
+    if constexpr (!GRID)
+        make_amat();
     // Wide groups keep the operand in LDS and read it back for the products
     // only, so that its 8 registers are free while the butterflies and the
     // quantiser run (what lets 8-tile groups fit four waves per SIMD).
-    constexpr bool kAmatInLds = T == 8;
+    constexpr bool kAmatInLds = T == 8 && !GRID;
     __shared__ u32x4 lds_amat[kAmatInLds ? 2 : 1][64];
     if constexpr (kAmatInLds) {
         if (wave == 0) {
@@ -249,24 +256,40 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
         }
     }
 
-    // ---- work split: one persistent workgroup per CU hands out groups of
-    // T tiles through an LDS counter (groups strided across workgroups)
+    // ---- work split.  GRID: every wave takes one group of T tiles (group
+    // blockIdx.x * waves + wave) and ends; the hardware dispatcher starts
+    // the next workgroups as waves retire.  Otherwise one persistent
+    // workgroup per CU hands out groups through an LDS counter (groups
+    // strided across workgroups), with the next group prefetched.
     __shared__ int pool_next;
-    const int64_t pool_size = (a.groups - blockIdx.x + gridDim.x - 1) / gridDim.x;
     const int nwaves = blockDim.x >> 6;
-    const int64_t first = wave;
+    int64_t pool_size, first;
+    if constexpr (GRID) {
+        first = (int64_t)blockIdx.x * nwaves + wave;
+        pool_size = first < a.groups ? first + 1 : 0;
+    } else {
+        pool_size = (a.groups - blockIdx.x + gridDim.x - 1) / gridDim.x;
+        first = wave;
+        if (threadIdx.x == 0)
+            pool_next = nwaves;
+    }
     const bool has_work = first < pool_size;
-    if (threadIdx.x == 0)
-        pool_next = nwaves;
     auto grab = [&]() -> int64_t {
-        int v = 0;
-        if (lane == 0)
-            v = atomicAdd(&pool_next, 1);
-        return __builtin_amdgcn_readfirstlane(v);
+        if constexpr (GRID) {
+            return pool_size;
+        } else {
+            int v = 0;
+            if (lane == 0)
+                v = atomicAdd(&pool_next, 1);
+            return __builtin_amdgcn_readfirstlane(v);
+        }
     };
     // first element of group g (wave-uniform)
     auto group_elem0 = [&](int64_t g) {
-        return ((int64_t)blockIdx.x + g * gridDim.x) * (int64_t)(T * 512);
+        if constexpr (GRID)
+            return g * (int64_t)(T * 512);
+        else
+            return ((int64_t)blockIdx.x + g * gridDim.x) * (int64_t)(T * 512);
     };
 
     // Addresses: a wave-uniform tile base (scalar registers) plus the lane's
@@ -309,8 +332,10 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
 
     // ---- sign masks (bit 15 of each 16-bit element).  Rows of up to 512
     // elements: the lane's 8 row positions are the same in every tile, so
-    // the masks live in 4 registers.  Wider rows: one 16-byte mask per
-    // (tile of the row, lane) in LDS.
+    // the masks live in 4 registers.  Wider rows: GRID loads the lane's 8
+    // sign bytes of every tile of the row (cache hits: s is n bytes) and
+    // turns them into masks as each tile is used; the persistent kernel
+    // builds one 16-byte mask per (tile of the row, lane) in LDS once.
     u32x4 smask = {0, 0, 0, 0};
     if constexpr (TPR == 1) {
         const int p = lane_off & ((1 << LOGN) - 1);
@@ -322,8 +347,28 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
         }
     }
 
-    u32x4 cur[T];
-    load(has_work ? first : 0, cur);
+    // Wider rows: the sign bytes (the lane's own, or this thread's entries of
+    // the mask table), requested before the rows, so that waiting for them
+    // leaves the rows' loads in flight
+    u32x2 tsb[TPR > 1 ? TPR : 1];
+    constexpr bool kLaneSigns = GRID && TPR > 1;
+    if constexpr (kLaneSigns) {
+        // the lane's own 8 sign bytes of every tile of the row
+#pragma unroll
+        for (int i = 0; i < TPR; ++i)
+            tsb[i] = *(const u32x2 *)(a.s + i * 512 + lane_off);
+    } else if constexpr (TPR > 1) {
+#pragma unroll
+        for (int i = 0; i < TPR; ++i) {
+            const int idx = threadIdx.x + i * (int)blockDim.x;
+            if (idx < TPR * 64) {
+                const int ln = idx & 63;
+                const int p = (idx >> 6) * 512 + 8 * (ln >> 4) + 32 * (ln & 15);
+                tsb[i] = *(const u32x2 *)(a.s + p);
+            }
+        }
+    }
+
     // WIDE: the sign bytes of the lane's 8 inputs of each tile, loaded with
     // the tile (block row v is block v mod wide_div of its real row; the
     // double product is within one of the quotient, one step corrects it)
@@ -343,13 +388,29 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
             }
         }
     };
-    load_signs(has_work ? first : 0);
+    if constexpr (GRID)
+        load_signs(has_work ? first : 0);
 
-    if constexpr (TPR > 1) {
-        for (int idx = threadIdx.x; idx < TPR * 64; idx += blockDim.x) {
-            const int ln = idx & 63;
-            const int p = (idx >> 6) * 512 + 8 * (ln >> 4) + 32 * (ln & 15);
-            const u32x2 sb = *(const u32x2 *)(a.s + p);
+    u32x4 cur[T];
+    load(has_work ? first : 0, cur);
+    if constexpr (GRID) {
+        // every row load is issued before anything waits for the sign loads
+        // (left alone, the scheduler interleaves the mask arithmetic with the
+        // loads and waits for the signs with most of the row not yet
+        // requested)
+        __builtin_amdgcn_sched_barrier(0);
+        make_amat();
+    } else {
+        load_signs(has_work ? first : 0);
+    }
+
+    if constexpr (TPR > 1 && !kLaneSigns) {
+#pragma unroll
+        for (int i = 0; i < TPR; ++i) {
+            const int idx = threadIdx.x + i * (int)blockDim.x;
+            if (idx >= TPR * 64)
+                break;
+            const u32x2 sb = tsb[i];
             u32x4 m;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -360,9 +421,8 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
         }
     }
     // LDS-only release: the barrier must not wait for the row loads
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    if constexpr (!GRID)
+        lds_barrier();
 
     // Loads and stores share one completion counter; this empty asm fixes
     // where the wait for a prefetch happens (see the butterfly kernel).
@@ -378,7 +438,8 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
                 asm volatile("" : "+v"(csg[t][0]), "+v"(csg[t][1]));
         }
     };
-    take_delivery(cur);
+    if constexpr (!GRID)
+        take_delivery(cur);
 
     int64_t g = first;
     while (g < pool_size) {
@@ -399,7 +460,17 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
         for (int t = 0; t < T; ++t) {
             u32x4 m = smask;
             if constexpr (TPR > 1)
-                m = lds_mask[lofs + (t % TPR) * 64];
+            {
+                if constexpr (kLaneSigns) {
+                    const u32x2 sb = tsb[t % TPR];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)  // sign bits of bytes 2c, 2c+1 to bits 15, 31
+                        m[c] = __builtin_amdgcn_perm(0u, sb[c >> 1], (c & 1) ? 0x030c020cu : 0x010c000cu) &
+                               0x80008000u;
+                } else {
+                    m = lds_mask[lofs + (t % TPR) * 64];
+                }
+            }
             if constexpr (WIDE) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
@@ -457,7 +528,8 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
         }
 
         // Take delivery of the prefetched group before this group's stores.
-        take_delivery(cur);
+        if constexpr (!GRID)
+            take_delivery(cur);
 
         // ------------------------------------------------------------ outputs
         const int64_t e0 = group_elem0(g);
@@ -656,10 +728,31 @@ namespace mfma {
 bool plan_ok(const Request &r);
 bool wide_inv_ok(const Request &r);
 bool wide_fwd_ok(const Request &r);
+bool long_fwd_ok(const Request &r);
 void fill_args(MfmaArgs &ma, const Request &r, int tiles_per_group);
 int occupancy_waves(const void *fn, size_t lds);
 
-template <int OP, int IN, int T, int LOGB, int LOGN, int LOGG, bool APPEND = false, bool WIDE = false>
+// Launches with at least this many groups of 8 tiles per CU take the grid
+// form of the kernel (one group per single-wave workgroup); smaller ones the
+// persistent form.  Measured on MI355X (steady state, us per launch):
+//   16384 x 4096 (64 groups per CU)       persistent 31.6, grid 29.5
+//   65536 x 1024 (64 per CU)              persistent 31.4, grid 28.8
+//   1048576 x 128 (128 per CU)            persistent 56.3, grid 55.4
+//   131072 x 128 (16 per CU)              persistent  9.6, grid 10.9
+// In the grid form the dispatcher starts workgroups on whichever CU frees
+// first and a wave holds one group of loads, not two; with a whole launch
+// of one wave per slot (16 groups per CU) nothing overlaps a wave's loads,
+// and the persistent form's prefetch wins.
+constexpr int kGridGroupsPerCu = 32;
+
+inline bool grid_launch(const Request &r, const DeviceInfo &dev)
+{
+    const int64_t groups8 = (r.rows * (int64_t)r.n + 8 * 512 - 1) / (8 * 512);
+    return r.dst_rows == nullptr && groups8 >= (int64_t)dev.cu_count * kGridGroupsPerCu;
+}
+
+template <int OP, int IN, int T, int LOGB, int LOGN, int LOGG, bool APPEND = false, bool WIDE = false,
+          bool GRID = false>
 hipError_t launch_one(const Request &r, const DeviceInfo &dev, int wide_div = 1)
 {
     MfmaArgs ma;
@@ -667,9 +760,15 @@ hipError_t launch_one(const Request &r, const DeviceInfo &dev, int wide_div = 1)
     ma.wide_div = wide_div;
     ma.wide_rdiv = 1.0 / (double)wide_div;
     ma.wide_row_scale = 0;
+    auto fn = mfma_kernel<OP, IN, T, LOGB, LOGN, LOGG, APPEND, WIDE, GRID>;
+    if constexpr (GRID) {
+        // one group per single-wave workgroup; no LDS (the signs of wide
+        // rows are per lane)
+        hipLaunchKernelGGL(fn, dim3((unsigned)ma.groups), dim3(64), 0, r.stream, ma);
+        return hipGetLastError();
+    }
     constexpr int TPR = LOGN > 9 ? 1 << (LOGN - 9) : 1;
     const size_t lds = TPR > 1 ? (size_t)TPR * 64 * 16 : 0;
-    auto fn = mfma_kernel<OP, IN, T, LOGB, LOGN, LOGG, APPEND, WIDE>;
     // One workgroup per CU with every wave the CU can hold, at most 16 for
     // groups of 2 tiles and 12 otherwise (steady-state timings: 131072 x 128
     // rows 9.8 us with 16 waves, 10.4 with 12; 1048576 x 128 rows, groups of
@@ -700,44 +799,56 @@ enum Mode : int { kPerRow = 0, kGrouped = 1, kAppend = 2 };
 // (kGrouped, forward only) a run-time group of 32..256 elements, or whole-tile
 // groups of 512 .. n/2 elements; kAppend: one scale per row, written to the
 // cache rows the caller names.
-template <int OP, int IN, int MODE, int T, int LOGB, int LOGN>
+template <int OP, int IN, int MODE, int T, int LOGB, int LOGN, bool GRID>
 hipError_t launch_g(const Request &r, const DeviceInfo &dev)
 {
     if constexpr (MODE == kAppend && OP == kRotateQuant) {
-        return launch_one<OP, IN, T, LOGB, LOGN, LOGN, true>(r, dev);
+        return launch_one<OP, IN, T, LOGB, LOGN, LOGN, true, false, false>(r, dev);
     } else if constexpr (MODE == kGrouped && OP == kRotateQuant) {
         if (r.logg < 9)
-            return launch_one<OP, IN, T, LOGB, LOGN, 0>(r, dev);
+            return launch_one<OP, IN, T, LOGB, LOGN, 0, false, false, GRID>(r, dev);
         if constexpr (LOGN > 9)
-            if (r.logg == 9) return launch_one<OP, IN, T, LOGB, LOGN, 9>(r, dev);
+            if (r.logg == 9) return launch_one<OP, IN, T, LOGB, LOGN, 9, false, false, GRID>(r, dev);
         if constexpr (LOGN > 10)
-            if (r.logg == 10) return launch_one<OP, IN, T, LOGB, LOGN, 10>(r, dev);
+            if (r.logg == 10) return launch_one<OP, IN, T, LOGB, LOGN, 10, false, false, GRID>(r, dev);
         if constexpr (LOGN > 11)
-            if (r.logg == 11) return launch_one<OP, IN, T, LOGB, LOGN, 11>(r, dev);
+            if (r.logg == 11) return launch_one<OP, IN, T, LOGB, LOGN, 11, false, false, GRID>(r, dev);
         return hipErrorInvalidValue;
     } else {
-        return launch_one<OP, IN, T, LOGB, LOGN, LOGN>(r, dev);
+        return launch_one<OP, IN, T, LOGB, LOGN, LOGN, false, false, GRID>(r, dev);
     }
 }
 
+// Grid or persistent form of a (T, LOGB, LOGN) plan (appends are always
+// persistent: a decode step's few rows).
+template <int OP, int IN, int MODE, int T, int LOGB, int LOGN>
+hipError_t launch_gp(const Request &r, const DeviceInfo &dev, bool grid)
+{
+    if constexpr (MODE != kAppend && T == 8)
+        if (grid)
+            return launch_g<OP, IN, MODE, T, LOGB, LOGN, true>(r, dev);
+    return launch_g<OP, IN, MODE, T, LOGB, LOGN, false>(r, dev);
+}
+
 // Full rotations of n = 32..4096 and 128-blocks of n = 256..4096.
-// Rows of up to 512 elements take groups of 4 tiles, or of 2 tiles when
-// that would leave fewer than 4 groups per wave (the last round of groups
-// then idles less of the machine; measured on 131072 x 128).
-template <int OP, int IN, int MODE, int T>
+// Rows of up to 512 elements take groups of 8 tiles in the grid form; in the
+// persistent form groups of 4 tiles, or of 2 tiles when that would leave
+// fewer than 4 groups per wave (the last round of groups then idles less of
+// the machine; measured on 131072 x 128).
+template <int OP, int IN, int MODE, int T, bool GRID>
 hipError_t dispatch_short(const Request &r, const DeviceInfo &dev)
 {
     const bool full = r.b == r.n;
     switch (r.n) {
-    case 32: return launch_g<OP, IN, MODE, T, 5, 5>(r, dev);
-    case 64: return launch_g<OP, IN, MODE, T, 6, 6>(r, dev);
-    case 128: return launch_g<OP, IN, MODE, T, 7, 7>(r, dev);
+    case 32: return launch_g<OP, IN, MODE, T, 5, 5, GRID>(r, dev);
+    case 64: return launch_g<OP, IN, MODE, T, 6, 6, GRID>(r, dev);
+    case 128: return launch_g<OP, IN, MODE, T, 7, 7, GRID>(r, dev);
     case 256:
-        return full ? launch_g<OP, IN, MODE, T, 8, 8>(r, dev)
-                    : launch_g<OP, IN, MODE, T, 7, 8>(r, dev);
+        return full ? launch_g<OP, IN, MODE, T, 8, 8, GRID>(r, dev)
+                    : launch_g<OP, IN, MODE, T, 7, 8, GRID>(r, dev);
     default:
-        return full ? launch_g<OP, IN, MODE, T, 9, 9>(r, dev)
-                    : launch_g<OP, IN, MODE, T, 7, 9>(r, dev);
+        return full ? launch_g<OP, IN, MODE, T, 9, 9, GRID>(r, dev)
+                    : launch_g<OP, IN, MODE, T, 7, 9, GRID>(r, dev);
     }
 }
 
@@ -745,22 +856,26 @@ template <int OP, int IN, int MODE>
 hipError_t dispatch_op(const Request &r, const DeviceInfo &dev)
 {
     const bool full = r.b == r.n;
+    const bool grid = MODE != kAppend && grid_launch(r, dev);
     if (r.n <= 512) {
+        if constexpr (MODE != kAppend)
+            if (grid)
+                return dispatch_short<OP, IN, MODE, 8, true>(r, dev);
         const int64_t groups4 = (r.rows * (int64_t)r.n + 4 * 512 - 1) / (4 * 512);
         if (groups4 < (int64_t)dev.cu_count * 16 * 4)
-            return dispatch_short<OP, IN, MODE, 2>(r, dev);
-        return dispatch_short<OP, IN, MODE, 4>(r, dev);
+            return dispatch_short<OP, IN, MODE, 2, false>(r, dev);
+        return dispatch_short<OP, IN, MODE, 4, false>(r, dev);
     }
     switch (r.n) {
     case 1024:
-        return full ? launch_g<OP, IN, MODE, 8, 10, 10>(r, dev)
-                    : launch_g<OP, IN, MODE, 8, 7, 10>(r, dev);
+        return full ? launch_gp<OP, IN, MODE, 8, 10, 10>(r, dev, grid)
+                    : launch_gp<OP, IN, MODE, 8, 7, 10>(r, dev, grid);
     case 2048:
-        return full ? launch_g<OP, IN, MODE, 8, 11, 11>(r, dev)
-                    : launch_g<OP, IN, MODE, 8, 7, 11>(r, dev);
+        return full ? launch_gp<OP, IN, MODE, 8, 11, 11>(r, dev, grid)
+                    : launch_gp<OP, IN, MODE, 8, 7, 11>(r, dev, grid);
     default:
-        return full ? launch_g<OP, IN, MODE, 8, 12, 12>(r, dev)
-                    : launch_g<OP, IN, MODE, 8, 7, 12>(r, dev);
+        return full ? launch_gp<OP, IN, MODE, 8, 12, 12>(r, dev, grid)
+                    : launch_gp<OP, IN, MODE, 8, 7, 12>(r, dev, grid);
     }
 }
 

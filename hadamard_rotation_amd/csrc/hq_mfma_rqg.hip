@@ -12,8 +12,19 @@ hipError_t launch_rq_grouped(const Request &r, const DeviceInfo &dev)
 }
 
 // Rows of several 128-blocks with one scale per block (see wide_fwd_ok) as
-// rows of one block with one scale per row; groups of 2 or 4 tiles as for
-// other 128-element rows.
+// rows of one block with one scale per row; the grid form, or groups of 2 or
+// 4 tiles, as for other 128-element rows.
+template <int IN>
+hipError_t launch_wide(const Request &w, const DeviceInfo &dev, int blocks)
+{
+    if (grid_launch(w, dev))
+        return launch_one<kRotateQuant, IN, 8, 7, 7, 7, false, true, true>(w, dev, blocks);
+    const int64_t groups4 = (w.rows * 128 + 4 * 512 - 1) / (4 * 512);
+    if (groups4 < (int64_t)dev.cu_count * 16 * 4)
+        return launch_one<kRotateQuant, IN, 2, 7, 7, 7, false, true>(w, dev, blocks);
+    return launch_one<kRotateQuant, IN, 4, 7, 7, 7, false, true>(w, dev, blocks);
+}
+
 hipError_t launch_rq_wide(const Request &r, const DeviceInfo &dev)
 {
     const int blocks = r.n / 128;
@@ -22,13 +33,9 @@ hipError_t launch_rq_wide(const Request &r, const DeviceInfo &dev)
     w.n = 128;
     w.group = 128;
     w.logg = 7;
-    const int64_t groups4 = (w.rows * 128 + 4 * 512 - 1) / (4 * 512);
-    const bool two = groups4 < (int64_t)dev.cu_count * 16 * 4;
     if (r.x_dtype == kBF16)
-        return two ? launch_one<kRotateQuant, kBF16, 2, 7, 7, 7, false, true>(w, dev, blocks)
-                   : launch_one<kRotateQuant, kBF16, 4, 7, 7, 7, false, true>(w, dev, blocks);
-    return two ? launch_one<kRotateQuant, kF16, 2, 7, 7, 7, false, true>(w, dev, blocks)
-               : launch_one<kRotateQuant, kF16, 4, 7, 7, 7, false, true>(w, dev, blocks);
+        return launch_wide<kBF16>(w, dev, blocks);
+    return launch_wide<kF16>(w, dev, blocks);
 }
 
 }  // namespace mfma
