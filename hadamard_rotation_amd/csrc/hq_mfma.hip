@@ -64,7 +64,7 @@ bool wide_fwd_ok(const Request &r)
 
 bool plan_ok(const Request &r)
 {
-    if (wide_fwd_ok(r))
+    if (wide_fwd_ok(r) || long_fwd_ok(r))
         return true;
     if (r.op == kDequantInv) {
         if (wide_inv_ok(r))
@@ -126,6 +126,7 @@ int occupancy_waves(const void *fn, size_t lds)
 hipError_t launch_rq(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rq_grouped(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rq_wide(const Request &r, const DeviceInfo &dev);
+hipError_t launch_rq_long(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rq_append(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rot(const Request &r, const DeviceInfo &dev);
 hipError_t launch_inv(const Request &r, const DeviceInfo &dev);
@@ -147,6 +148,8 @@ hipError_t launch_mfma(const Request &r, const DeviceInfo &dev)
         return mfma::launch_rq_append(r, dev);
     if (mfma::wide_fwd_ok(r))
         return mfma::launch_rq_wide(r, dev);
+    if (mfma::long_fwd_ok(r))
+        return mfma::launch_rq_long(r, dev);
     return r.group == r.n ? mfma::launch_rq(r, dev) : mfma::launch_rq_grouped(r, dev);
 }
 

@@ -9,11 +9,11 @@ in every step of the GPU's fp32 arithmetic, with a large share of them on a
 (check_codes(exact=True)), which the normal +-1 tie window would not catch
 for a kernel that rounded ties away from zero or truncated them.
 
-One case per kernel family: the matrix-core kernel (16-bit input, full and
+One case per kernel family: the matrix-core kernels (16-bit input, full and
 128-blocks, per-row, whole-tile and sub-tile groups, 128-block rows of wider
-rows, cache append), the butterfly kernel (fp32 input, long rows), the
-generic kernel, and the Paley kernels (generic for 96, block-circulant for
-11008, dense for 10624).
+rows, long rows with one scale per row, cache append), the butterfly kernel
+(fp32 input, long rows), the generic kernel, and the Paley kernels (generic
+for 96, block-circulant for 11008, dense for 10624).
 """
 from __future__ import annotations
 
@@ -56,7 +56,9 @@ CASES = [
     (11008, 128, W.BF16, 3, 128),      # matrix core, 128-block rows of wide rows
     (128, 128, W.F32, 67, None),       # butterfly kernel
     (4096, 4096, W.F32, 5, None),
-    (11008, 128, W.BF16, 3, None),     # butterfly kernel, long rows
+    (11008, 128, W.F32, 3, None),      # butterfly kernel, long rows
+    (11008, 128, W.BF16, 3, None),     # matrix core, one workgroup per long row
+    (640, 128, W.F16, 9, None),        # the same, a partial last tile
     (32768, 4096, W.F32, 2, None),     # generic kernel
     (96, 96, W.F32, 33, None),         # Paley 12 x 8, generic kernel
     (11008, 11008, W.BF16, 3, None),   # Paley 344 x 32, block-circulant kernel
