@@ -28,8 +28,12 @@ _HQ_TO_TORCH = {v: k for k, v in _TORCH_TO_HQ.items()}
 
 EXPORTS = ("hq_rotate_quant", "hq_dequant_rotate_inv", "hq_rotate_quant_grouped",
            "hq_dequant_rotate_inv_grouped", "hq_rotate_quant_append", "hq_decode_attention",
-           "hq_decode_attention_workspace", "hq_rotate", "hq_status_str",
-           "hq_last_hip_error", "hq_max_n", "hq_version")
+           "hq_decode_attention_workspace", "hq_decode_attention_noalloc", "hq_rotate",
+           "hq_status_str", "hq_last_hip_error", "hq_max_n", "hq_version")
+
+# Bytes of the library's own decode-attention workspace on each GPU
+# (HQ_NOALLOC_WORKSPACE_BYTES in include/hq.h).
+NOALLOC_WORKSPACE_BYTES = 4 * 1024 * 1024
 
 _lock = threading.Lock()
 _lib = None
@@ -75,6 +79,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.hq_decode_attention.argtypes = [P, I32, I32, I32, I32, I32, P, I64, I32, P, P, P, P,
                                             I32, P, P, I64, P]
         lib.hq_decode_attention.restype = I32
+        lib.hq_decode_attention_noalloc.argtypes = [P, I32, I32, I32, I32, I32, P, I64, I32, P, P,
+                                                    P, P, I32, P, P]
+        lib.hq_decode_attention_noalloc.restype = I32
         lib.hq_rotate.argtypes = [P, I32, I64, I32, I32, P, P, P]
         lib.hq_rotate.restype = I32
         lib.hq_status_str.argtypes = [I32]
@@ -230,14 +237,9 @@ def hq_decode_attention_workspace(q_heads: int, kv_heads: int, tokens: int) -> i
     return int(load().hq_decode_attention_workspace(int(q_heads), int(kv_heads), int(tokens)))
 
 
-def hq_decode_attention(q: torch.Tensor, s: torch.Tensor, b: int, k_codes: torch.Tensor,
-                        k_scales: torch.Tensor, v_codes: torch.Tensor, v_scales: torch.Tensor,
-                        bits: int = 4, out: torch.Tensor | None = None,
-                        workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Attention of one query token per head (q [q_heads, n], not rotated)
-    over a rotated, quantised K/V cache: codes [tokens, kv_heads, n/2] uint8,
-    scales [tokens, kv_heads].  Returns out [q_heads, n] float32 in the
-    query's space.  The workspace is allocated with torch when not given."""
+def _attention_args(q, s, k_codes, k_scales, v_codes, v_scales, bits, out):
+    """Checks of hq_decode_attention's tensors; returns (q_heads, n, tokens,
+    kv_heads, out)."""
     # shapes first (the library reads tokens * kv_heads rows of n/2 code
     # bytes from each code tensor, so a narrower one would be read past its
     # end), then placement and types
@@ -264,6 +266,19 @@ def hq_decode_attention(q: torch.Tensor, s: torch.Tensor, b: int, k_codes: torch
     if out is None:
         out = torch.empty((q_heads, n), dtype=torch.float32, device=q.device)
     _check_dev(out, "out", torch.float32, (q_heads, n))
+    return q_heads, n, tokens, kv_heads, out
+
+
+def hq_decode_attention(q: torch.Tensor, s: torch.Tensor, b: int, k_codes: torch.Tensor,
+                        k_scales: torch.Tensor, v_codes: torch.Tensor, v_scales: torch.Tensor,
+                        bits: int = 4, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Attention of one query token per head (q [q_heads, n], not rotated)
+    over a rotated, quantised K/V cache: codes [tokens, kv_heads, n/2] uint8,
+    scales [tokens, kv_heads].  Returns out [q_heads, n] float32 in the
+    query's space.  The workspace is allocated with torch when not given."""
+    q_heads, n, tokens, kv_heads, out = _attention_args(q, s, k_codes, k_scales, v_codes,
+                                                        v_scales, bits, out)
     need = hq_decode_attention_workspace(q_heads, kv_heads, tokens)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -275,6 +290,25 @@ def hq_decode_attention(q: torch.Tensor, s: torch.Tensor, b: int, k_codes: torch
                                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                     _stream(stream))
     _raise(st, "hq_decode_attention")
+    return out
+
+
+def hq_decode_attention_noalloc(q: torch.Tensor, s: torch.Tensor, b: int,
+                                k_codes: torch.Tensor, k_scales: torch.Tensor,
+                                v_codes: torch.Tensor, v_scales: torch.Tensor, bits: int = 4,
+                                out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """hq_decode_attention with the library's own per-GPU workspace (no
+    allocation inside the library; pass `out` to allocate nothing here
+    either).  Calls that overlap on one GPU race."""
+    q_heads, n, tokens, kv_heads, out = _attention_args(q, s, k_codes, k_scales, v_codes,
+                                                        v_scales, bits, out)
+    st = load().hq_decode_attention_noalloc(q.data_ptr(), _TORCH_TO_HQ[q.dtype], q_heads,
+                                            kv_heads, n, int(b), s.data_ptr(), tokens, int(bits),
+                                            k_codes.data_ptr(), k_scales.data_ptr(),
+                                            v_codes.data_ptr(), v_scales.data_ptr(),
+                                            _TORCH_TO_HQ[k_scales.dtype], out.data_ptr(),
+                                            _stream(stream))
+    _raise(st, "hq_decode_attention_noalloc")
     return out
 
 

@@ -29,6 +29,8 @@
 // (maximum, sum, 128 accumulators per head) to the workspace.
 // Kernel 2 (attn_merge_kernel): per query head, merges the partials with the
 // usual rescaling and rotates the result back.
+#include <mutex>
+
 #include "hq_device.h"
 #include "hq_internal.h"
 
@@ -673,7 +675,41 @@ hipError_t launch_g(const AttnArgs &aa, hipStream_t st)
     return hipGetLastError();
 }
 
+// The workspace of hq_decode_attention_noalloc (callers that cannot
+// allocate): a file-scope device array, one copy per GPU, alive until the
+// process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: kernels only ever get the address hipGetSymbolAddress
+// returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kAttnStaticWorkspaceBytes];
+
+constexpr int kMaxScratchDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+    void *ptr = nullptr;
+};
+ScratchSlot g_scratch[kMaxScratchDevices];
+
 }  // namespace
+
+hipError_t attention_static_workspace(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return hipErrorInvalidDevice;
+    ScratchSlot &slot = g_scratch[dev];
+    // once per device, with that device current
+    std::call_once(slot.once, [&]() {
+        slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+    });
+    if (slot.err != hipSuccess)
+        return slot.err;
+    *ptr = slot.ptr;
+    return hipSuccess;
+}
 
 hipError_t launch_attention(const AttnRequest &r)
 {

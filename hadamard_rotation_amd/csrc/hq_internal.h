@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "hq.h"
+
 #include <cstdint>
 
 namespace hq {
@@ -115,6 +117,13 @@ inline size_t attention_workspace(int q_heads, int kv_heads, int64_t tokens)
 }
 
 hipError_t launch_attention(const AttnRequest &r);
+
+// The library's own workspace for hq_decode_attention_noalloc: a file-scope
+// device array of this many bytes in the attention kernels' source, one copy
+// per GPU.  attention_static_workspace() returns its address on the current
+// device (looked up once per device).
+constexpr size_t kAttnStaticWorkspaceBytes = HQ_NOALLOC_WORKSPACE_BYTES;
+hipError_t attention_static_workspace(void **ptr);
 
 // Generic path: any supported (n, b); one workgroup per row with the row
 // staged in LDS as fp32.  Requires 4*n <= dev.lds_per_block.

@@ -217,6 +217,31 @@ hq_status hq_decode_attention(const void *q, hq_dtype q_dtype, int32_t q_heads,
                               int64_t workspace_bytes, void *stream);
 
 /*
+ * hq_decode_attention_noalloc -- hq_decode_attention without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine):
+ * the partials live in a device array of HQ_NOALLOC_WORKSPACE_BYTES that the
+ * library holds on each GPU it runs on until the process ends.
+ *   Arguments, results and errors as for hq_decode_attention, plus
+ *   HQ_EUNSUPPORTED when hq_decode_attention_workspace(q_heads, kv_heads,
+ *   tokens) exceeds HQ_NOALLOC_WORKSPACE_BYTES (e.g. 32 query heads over
+ *   8 kv heads need 1.6 MiB at any cache length), and HQ_EHIP if the
+ *   array's address cannot be obtained.
+ * Every call on one GPU shares that GPU's array (it keeps the last call's
+ * partials, which no call reads before writing): calls that overlap on one
+ * GPU, on any streams, race.  Use one stream, or hq_decode_attention with a
+ * workspace of your own per stream.
+ */
+#define HQ_NOALLOC_WORKSPACE_BYTES (4 * 1024 * 1024)
+hq_status hq_decode_attention_noalloc(const void *q, hq_dtype q_dtype, int32_t q_heads,
+                                      int32_t kv_heads, int32_t n, int32_t b, const int8_t *s,
+                                      int64_t tokens, int32_t bits, const void *k_codes,
+                                      const void *k_scales, const void *v_codes,
+                                      const void *v_scales, hq_dtype scale_dtype, float *out,
+                                      void *stream);
+
+/*
  * hq_rotate -- rotation only: y = x' as fp32 [rows, n] (no quantisation).
  * Used to check the rotated values themselves and Q.K^T preservation
  * ([HQA] 1: rotating Q and K with the same matrix keeps Q.K^T).

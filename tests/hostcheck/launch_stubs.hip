@@ -18,5 +18,6 @@ hipError_t launch_paley_mfma(const Request &, const DeviceInfo &) { return hipEr
 hipError_t launch_fast(const Request &, const DeviceInfo &) { return hipErrorNotSupported; }
 hipError_t launch_mfma(const Request &, const DeviceInfo &) { return hipErrorNotSupported; }
 hipError_t launch_attention(const AttnRequest &) { return hipErrorNotSupported; }
+hipError_t attention_static_workspace(void **) { return hipErrorNotSupported; }
 
 }  // namespace hq

@@ -29,7 +29,8 @@ def test_library_loads_and_exports_header_symbols():
     syms = declared_symbols()
     assert set(syms) == {"hq_rotate_quant", "hq_dequant_rotate_inv", "hq_rotate_quant_grouped",
                          "hq_dequant_rotate_inv_grouped", "hq_rotate_quant_append", "hq_rotate",
-                         "hq_decode_attention", "hq_decode_attention_workspace", "hq_status_str",
+                         "hq_decode_attention", "hq_decode_attention_workspace",
+                         "hq_decode_attention_noalloc", "hq_status_str",
                          "hq_last_hip_error", "hq_max_n", "hq_version"}
     for name in syms:
         assert hasattr(lib, name), name
@@ -71,6 +72,12 @@ def att(q=A, qd=1, qh=32, kvh=8, n=128, b=128, s=A, tokens=100, bits=4, kc=A, ks
         sd=2, out=A, ws=A, wsb=1 << 40):
     return hq.load().hq_decode_attention(q, qd, qh, kvh, n, b, s, tokens, bits, kc, ks, vc, vs, sd,
                                          out, ws, wsb, None)
+
+
+def attn0(q=A, qd=1, qh=32, kvh=8, n=128, b=128, s=A, tokens=100, bits=4, kc=A, ks=A, vc=A,
+          vs=A, sd=2, out=A):
+    return hq.load().hq_decode_attention_noalloc(q, qd, qh, kvh, n, b, s, tokens, bits, kc, ks,
+                                                 vc, vs, sd, out, None)
 
 
 def rot(x=A, xd=1, rows=4, n=128, b=128, s=A, y=A):
@@ -168,6 +175,35 @@ def test_decode_attention_einval(kw):
                                 dict(qh=32, kvh=2)])
 def test_decode_attention_unsupported(kw):
     assert att(**kw) == hq.HQ_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(s=None), dict(kc=None), dict(ks=None), dict(vc=None), dict(vs=None),
+    dict(out=None), dict(qh=0), dict(kvh=0), dict(qh=30), dict(tokens=0), dict(n=100),
+    dict(b=96), dict(bits=3), dict(qd=5), dict(sd=1), dict(kc=MIS), dict(out=MIS), dict(ks=MIS),
+])
+def test_decode_attention_noalloc_einval(kw):
+    # the same validation as hq_decode_attention, before anything else
+    assert attn0(**kw) == hq.HQ_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(n=64, b=64), dict(bits=8), dict(qh=24, kvh=8),
+                                dict(qh=32, kvh=2)])
+def test_decode_attention_noalloc_unsupported(kw):
+    assert attn0(**kw) == hq.HQ_EUNSUPPORTED
+
+
+def test_decode_attention_noalloc_limit():
+    # requests whose partials exceed the library's own workspace are
+    # rejected before any device call (HQ_NOALLOC_WORKSPACE_BYTES)
+    from hadamard_rotation_amd import binding as Bd
+    text = open(HEADER).read()
+    m = re.search(r"#define HQ_NOALLOC_WORKSPACE_BYTES \((\d+) \* 1024 \* 1024\)", text)
+    assert m and int(m.group(1)) * 2 ** 20 == Bd.NOALLOC_WORKSPACE_BYTES
+    assert hq.hq_decode_attention_workspace(32, 8, 131072) <= Bd.NOALLOC_WORKSPACE_BYTES
+    big = 1024
+    assert hq.hq_decode_attention_workspace(big * 8, big, 131072) > Bd.NOALLOC_WORKSPACE_BYTES
+    assert attn0(qh=big * 8, kvh=big, tokens=131072) == hq.HQ_EUNSUPPORTED
 
 
 def test_decode_attention_workspace_size():
