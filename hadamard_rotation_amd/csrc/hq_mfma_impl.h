@@ -732,23 +732,27 @@ bool long_fwd_ok(const Request &r);
 void fill_args(MfmaArgs &ma, const Request &r, int tiles_per_group);
 int occupancy_waves(const void *fn, size_t lds);
 
-// Launches with at least this many groups of 8 tiles per CU take the grid
-// form of the kernel (one group per single-wave workgroup); smaller ones the
-// persistent form.  Measured on MI355X (steady state, us per launch):
-//   16384 x 4096 (64 groups per CU)       persistent 31.6, grid 29.5
-//   65536 x 1024 (64 per CU)              persistent 31.4, grid 28.8
-//   1048576 x 128 (128 per CU)            persistent 56.3, grid 55.4
-//   131072 x 128 (16 per CU)              persistent  9.6, grid 10.9
+// Launches with at least this many 4096-element groups per CU take the grid
+// form of the kernel (one group of tiles per single-wave workgroup; rows of
+// up to 512 elements in groups of 4 tiles, wider rows in groups of 8);
+// smaller ones the persistent form.  Measured on MI355X (steady state, us
+// per launch, persistent -> grid):
+//   16384 x 4096 (64 per CU)       31.6 -> 29.5   (8-tile groups)
+//   65536 x 1024 (64 per CU)       31.4 -> 28.8   (8-tile groups)
+//   1048576 x 128 (128 per CU)     55.6 -> 55.0   (4-tile groups)
+//   131072 x 512 (64 per CU)       29.5 -> 28.4   (4-tile groups)
+//   131072 x 128 (16 per CU)       10.0 ->  9.8   (4-tile groups; 10.9 with 8)
 // In the grid form the dispatcher starts workgroups on whichever CU frees
-// first and a wave holds one group of loads, not two; with a whole launch
-// of one wave per slot (16 groups per CU) nothing overlaps a wave's loads,
-// and the persistent form's prefetch wins.
-constexpr int kGridGroupsPerCu = 32;
+// first and a wave holds one group of loads, not two.  Wide rows keep the
+// persistent form below 32 per CU (not measured there).
+constexpr int kGridPerCuShort = 4;
+constexpr int kGridPerCuWide = 32;
 
 inline bool grid_launch(const Request &r, const DeviceInfo &dev)
 {
-    const int64_t groups8 = (r.rows * (int64_t)r.n + 8 * 512 - 1) / (8 * 512);
-    return r.dst_rows == nullptr && groups8 >= (int64_t)dev.cu_count * kGridGroupsPerCu;
+    const int64_t groups = (r.rows * (int64_t)r.n + 8 * 512 - 1) / (8 * 512);
+    const int per_cu = r.n <= 512 ? kGridPerCuShort : kGridPerCuWide;
+    return r.dst_rows == nullptr && groups >= (int64_t)dev.cu_count * per_cu;
 }
 
 template <int OP, int IN, int T, int LOGB, int LOGN, int LOGG, bool APPEND = false, bool WIDE = false,
@@ -831,7 +835,7 @@ hipError_t launch_gp(const Request &r, const DeviceInfo &dev, bool grid)
 }
 
 // Full rotations of n = 32..4096 and 128-blocks of n = 256..4096.
-// Rows of up to 512 elements take groups of 8 tiles in the grid form; in the
+// Rows of up to 512 elements take groups of 4 tiles in the grid form; in the
 // persistent form groups of 4 tiles, or of 2 tiles when that would leave
 // fewer than 4 groups per wave (the last round of groups then idles less of
 // the machine; measured on 131072 x 128).
@@ -860,7 +864,7 @@ hipError_t dispatch_op(const Request &r, const DeviceInfo &dev)
     if (r.n <= 512) {
         if constexpr (MODE != kAppend)
             if (grid)
-                return dispatch_short<OP, IN, MODE, 8, true>(r, dev);
+                return dispatch_short<OP, IN, MODE, 4, true>(r, dev);
         const int64_t groups4 = (r.rows * (int64_t)r.n + 4 * 512 - 1) / (4 * 512);
         if (groups4 < (int64_t)dev.cu_count * 16 * 4)
             return dispatch_short<OP, IN, MODE, 2, false>(r, dev);

@@ -135,6 +135,31 @@ def test_ragged_row_counts(rows):
             P.check_inverse(y, y_ref, bf16=out_bf16, what=f"rows={rows} n={n} inverse")
 
 
+@pytest.mark.parametrize("n,b,rows", [
+    (128, 128, 32768 + 37),   # just past the grid form's threshold, ragged last group
+    (256, 128, 16384 + 3),
+    (512, 512, 8192 + 5),
+    (1024, 1024, 32768 + 5),  # 8-tile groups of wide rows
+    (2048, 128, 16384 + 1),
+])
+def test_grid_form_ragged_tails(n, b, rows):
+    # Launches this large take the grid form of the matrix-core kernel (one
+    # group of tiles per single-wave workgroup); the reduced-size tests above
+    # take its persistent form.  Every row against the oracle, both
+    # directions.
+    raw, s = W.random_rows(rows + n, rows, n, W.BF16, outliers=1)
+    tag = f"grid n={n} b={b} rows={rows}"
+    print(f"[grid] {tag}", flush=True)
+    ref = O.rotate_quant(raw, W.BF16, b, s, 4, W.F16)
+    codes, scales = G.gpu_rotate_quant(raw, W.BF16, s, b, 4, W.F16)
+    P.check_codes(codes, ref, 4, n, what=tag)
+    P.check_scales(scales, ref, W.F16, what=tag)
+    ref.pop("preround")
+    y_ref = O.dequant_rotate_inv(ref["codes"], ref["scales"], W.F16, b, s, 4, n)
+    y = G.gpu_dequant_inv(ref["codes"], ref["scales"], s, b, 4)
+    P.check_inverse(y, y_ref, bf16=False, what=f"{tag} inverse")
+
+
 def test_zero_rows_and_spikes():
     for n, b in ((128, 128), (4096, 4096), (11008, 128)):
         raw = np.zeros((6, n), dtype=np.float32)
