@@ -64,32 +64,44 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _csv_means(path: str, counter: str) -> dict:
+def _counter_means(path: str, counter: str) -> dict:
     """Mean per dispatch of `counter` for every (kernel name, grid size) in a
-    rocprofv3 counter_collection CSV, with the dispatch count and the first
-    dispatch id."""
-    import csv
+    rocprofv3 --pmc result (its SQLite database, *_results.db, or a
+    counter_collection CSV), with the dispatch count and the first dispatch
+    id."""
+    rows = []
+    if path.endswith(".db"):
+        import sqlite3
+        db = sqlite3.connect(path)
+        rows = db.execute("select kernel_name, grid_size, value, dispatch_id from "
+                          "counters_collection where counter_name = ?", (counter,)).fetchall()
+        db.close()
+    else:
+        import csv
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    rows.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"]),
+                                 int(r["Dispatch_Id"])))
     acc: dict = {}
     first: dict = {}
-    with open(path) as f:
-        for r in csv.DictReader(f):
-            if r["Counter_Name"] != counter:
-                continue
-            key = (r["Kernel_Name"], int(r["Grid_Size"]))
-            acc.setdefault(key, []).append(float(r["Counter_Value"]))
-            first[key] = min(first.get(key, 1 << 62), int(r["Dispatch_Id"]))
+    for name, grid, value, disp in rows:
+        key = (name, int(grid))
+        acc.setdefault(key, []).append(float(value))
+        first[key] = min(first.get(key, 1 << 62), int(disp))
     return {k: (sum(v) / len(v), len(v), first[k]) for k, v in acc.items()}
 
 
-def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_bytes: int) -> dict:
+def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_bytes: int,
+                  tcc_db: str | None = None) -> dict:
     """HBM bytes per launch of the dominant hq kernel from two rocprofv3
     --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; both in KiB per
     dispatch), each scaled by what the same counter reads for the plain
     device copy of `copy_bytes` bytes that the script also times (the
     copy launch repeated most often; other copies, e.g. buffer clones,
     have other grid sizes)."""
-    fetch = _csv_means(fetch_csv, "FETCH_SIZE")
-    write = _csv_means(write_csv, "WRITE_SIZE")
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
     copy_key = max((k for k in fetch if "copyBuffer" in k[0]), key=lambda k: fetch[k][1])
     # the timed launch: the first library kernel the script dispatches (the
     # extras, inverse, append and attention, come after it)
@@ -98,12 +110,29 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_bytes: int
     w_scale = copy_bytes / (write[copy_key][0] * 1024.0)
     fb = fetch[kern_key][0] * 1024.0 * f_scale
     wb = write[kern_key][0] * 1024.0 * w_scale
+    if tcc_db:
+        # Reads counted from the L2's memory read requests themselves: on this
+        # GPU a request is 32 or 128 bytes, and TCC_BUBBLE, through which
+        # FETCH_SIZE's formula counts 128-byte requests, reads 0 (so
+        # FETCH_SIZE counts them as 64 bytes: half).  Writes: WRITE_SIZE
+        # as read (its formula matches the 32/64-byte write requests).
+        rd = _counter_means(tcc_db, "TCC_EA0_RDREQ_sum")
+        r32 = _counter_means(tcc_db, "TCC_EA0_RDREQ_32B_sum")
+        bub = _counter_means(tcc_db, "TCC_BUBBLE_sum")
+        kk = min((k for k in rd if "hq::" in k[0]), key=lambda k: rd[k][2])
+        n_rd, n32 = rd[kk][0], r32[kk][0]
+        req_read = (n_rd - n32) * 128.0 + n32 * 32.0
+        req = {"read_requests": n_rd, "read_requests_32B": n32, "bubble": bub[kk][0],
+               "read_bytes": req_read, "write_bytes": write[kern_key][0] * 1024.0,
+               "bytes_per_launch": req_read + write[kern_key][0] * 1024.0}
     out = {"workload": workload, "kernel": kern_key[0], "source_hash": source_hash(),
            "fetch_kib_raw": fetch[kern_key][0], "write_kib_raw": write[kern_key][0],
            "copy_bytes": copy_bytes, "copy_grid": copy_key[1],
            "copy_fetch_kib_raw": fetch[copy_key][0], "copy_write_kib_raw": write[copy_key][0],
            "fetch_scale": f_scale, "write_scale": w_scale, "fetch_bytes": fb,
            "write_bytes": wb, "bytes_per_launch": fb + wb}
+    if tcc_db:
+        out["from_requests"] = req
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -112,15 +141,17 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_bytes: int
 
 def load_traffic(workload: str):
     """HBM bytes per launch measured with rocprofv3 counters for the current
-    kernel sources, or None if no measurement matches them."""
+    kernel sources, scaled by the copy (None if no measurement matches the
+    sources), and the same from the read requests themselves (None if not
+    measured)."""
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
-        return None
+        return None, None
     with open(p) as f:
         t = json.load(f)
     if t.get("source_hash") != source_hash():
-        return None
-    return t.get("bytes_per_launch")
+        return None, None
+    return t.get("bytes_per_launch"), t.get("from_requests", {}).get("bytes_per_launch")
 
 
 def cpu_baseline(workload, target_s: float = 12.0) -> dict:
@@ -149,10 +180,102 @@ def cpu_baseline(workload, target_s: float = 12.0) -> dict:
                    threads=threads, want_preround=False)
     dt = time.perf_counter() - t0
     gbs = w.bytes_per_call(rows) / dt / 1e9
-    return {"value": round(gbs, 6), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": threads, "cpu": cpu_model(),
+            "kind": "oracle",
             "sample": f"{rows} of {w.rows} rows of the same workload (seed 42, same "
                       f"generator), {dt:.2f} s wall on {threads} threads; explicit fp64 "
                       f"H_{w.b} product per block, scalar quantisation"}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def time_workload(name: str, dev, stream, ev0, ev1, calls: int = 200) -> dict:
+    """One workload at its full size: the seeded tensors (every tensor of the
+    workload, e.g. Q and K) resident in HBM, enough copies to exceed the
+    last-level cache, a settle phase, then `calls` timed calls of
+    hq_rotate_quant cycling through them (HIP events on the launch stream).
+    For workloads with an inverse in their definition (the K/V cache round
+    trip), the inverse of the same codes is timed too (fp32 output)."""
+    import numpy as np
+    import torch
+
+    import hadamard_rotation_amd as hq
+    from hadamard_rotation_amd import workloads as W
+
+    w = W.WORKLOADS[name]
+    data = W.generate(name, seed=42)
+    s = torch.from_numpy(data["s"]).to(dev)
+    tdt = {W.F32: torch.float32, W.BF16: torch.bfloat16, W.F16: torch.float16}[w.x_dtype]
+    base = []
+    for t in w.tensors:
+        raw = data[t]
+        if w.x_dtype == W.F32:
+            base.append(torch.from_numpy(raw).to(dev))
+        else:
+            base.append(torch.from_numpy(raw.view(np.int16)).to(dev).view(tdt))
+    del data
+    rows, n = base[0].shape
+    bytes_call = w.bytes_per_call(rows)
+    copies = max(1, int(np.ceil(3 * LLC_BYTES / (bytes_call * len(base)))))
+    xs = [x if c == 0 else x.clone() for c in range(copies) for x in base]
+    sd = torch.float32 if w.scale_dtype == W.F32 else torch.float16
+    cw = n // 2 if w.bits == 4 else n
+    cdt = torch.uint8 if w.bits == 4 else torch.int8
+    codes = [torch.empty((rows, cw), dtype=cdt, device=dev) for _ in xs]
+    scales = [torch.empty((rows,), dtype=sd, device=dev) for _ in xs]
+
+    def call(i):
+        k = i % len(xs)
+        hq.hq_rotate_quant(xs[k], s, w.b, w.bits, sd, codes=codes[k], scales=scales[k],
+                           stream=stream)
+
+    def timed(fn, k):
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < SETTLE_S:
+            for _ in range(10):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
+        ev0.record(stream)
+        for j in range(k):
+            fn(j)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / k
+
+    us = timed(call, calls)
+    rec = {"workload": f"{name}: {w.description}", "tensors": len(w.tensors), "rows": rows,
+           "n": n, "b": w.b, "bits": w.bits, "bytes_per_call": bytes_call,
+           "us_per_call": round(us, 3), "GB/s": round(bytes_call / us / 1e3, 3),
+           "frac_of_8TBs": round(bytes_call / us / 1e3 / HBM_PEAK_GBS, 4)}
+    if name == "kv_cache":
+        ys = [torch.empty((rows, n), dtype=torch.float32, device=dev) for _ in range(2)]
+
+        def inv(i):
+            k = i % len(xs)
+            hq.hq_dequant_rotate_inv(codes[k], scales[k], s, w.b, w.bits, y=ys[i % 2],
+                                     stream=stream)
+
+        for i in range(len(xs)):
+            call(i)
+        ius = timed(inv, max(20, calls // 2))
+        ib = rows * (cw + (4 if w.scale_dtype == W.F32 else 2) + 4 * n)
+        rec["inverse"] = {"us_per_call": round(ius, 3), "GB/s": round(ib / ius / 1e3, 3),
+                          "bytes_per_call": ib, "out_dtype": "f32"}
+    del xs, codes, scales
+    torch.cuda.empty_cache()
+    return rec
 
 
 def time_append(dev, stream, ev0, ev1, seqs: int = 32, heads: int = 8, n: int = 128,
@@ -249,17 +372,27 @@ def main(argv=None):
                     help="group-wise scales: one per GROUP rotated elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the inverse-path and copy timings")
-    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
-                         "WRITE_SIZE) into profiles/traffic_<workload>.json and exit")
+                    help="skip the inverse-path, copy, append, attention and other-workload "
+                         "timings")
+    ap.add_argument("--copy", action="store_true",
+                    help="with --no-extras: still time the same-size device copy (the "
+                         "reference the traffic counters are scaled by)")
+    ap.add_argument("--traffic", nargs="+", metavar="PMC_RESULT",
+                    help="turn rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
+                         "WRITE_SIZE, optionally TCC_EA0_RDREQ_sum TCC_BUBBLE_sum "
+                         "TCC_EA0_RDREQ_32B_sum; their *_results.db or CSV) into "
+                         "profiles/traffic_<workload>.json and exit")
     args = ap.parse_args(argv)
 
     if args.traffic:
         from hadamard_rotation_amd import workloads as W
         w = W.WORKLOADS[args.workload]
+        if len(args.traffic) not in (2, 3):
+            ap.error("--traffic takes the FETCH_SIZE and WRITE_SIZE results and "
+                     "optionally the read-request counters")
         out = write_traffic(args.workload, args.traffic[0], args.traffic[1],
-                            copy_bytes_for(w.bytes_per_call()))
+                            copy_bytes_for(w.bytes_per_call()),
+                            args.traffic[2] if len(args.traffic) == 3 else None)
         print(json.dumps(out))
         return 0
 
@@ -346,7 +479,7 @@ def main(argv=None):
     ms_step = ms / args.steps
     launch_us = ms_step * 1e3  # one kernel launch per step
 
-    traffic = load_traffic(args.workload) if g is None else None
+    traffic, traffic_req = load_traffic(args.workload) if g is None else (None, None)
     if g is not None:
         metric = f"fused rotate+quant GB/s, workload {args.workload}, group {g}"
     elif args.workload == "hidden_4096":
@@ -381,6 +514,7 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(bytes_call / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "traffic_from_requests": traffic_req,
             "kernel_us": round(launch_us, 3),
         },
     }
@@ -404,6 +538,7 @@ def main(argv=None):
                           "GB/s": round(inv_bytes / inv_s / 1e9, 3),
                           "bytes_per_call": inv_bytes, "out_dtype": "f32"}
         del ys
+    if not args.no_extras or args.copy:
         # same-byte-count device copy as the achievable-bandwidth reference
         nb = copy_bytes_for(bytes_call)
         src = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(sets)]
@@ -419,8 +554,15 @@ def main(argv=None):
         cs = ev0.elapsed_time(ev1) / 1e3 / 50
         out["copy_reference"] = {"bytes_moved": 2 * nb, "GB/s": round(2 * nb / cs / 1e9, 3)}
         del src, dst
+    if not args.no_extras:
         out["append"] = time_append(dev, stream, ev0, ev1)
         out["decode_attention"] = time_attention(dev, stream, ev0, ev1)
+        # every workload of the path at its full size (the headline's own
+        # line is the one above), and the full 11008-point Paley rotation
+        del xs, codes, scales
+        torch.cuda.empty_cache()
+        out["workloads"] = [time_workload(name, dev, stream, ev0, ev1)
+                            for name in W.ORDER + ("ffn_11008_full",) if name != args.workload]
 
     if not args.no_cpu_baseline and g is None:
         out["cpu_baseline"] = cpu_baseline(args.workload)
