@@ -38,7 +38,10 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // WIDE  rows wider than one block, run as rows of one 128-block (LOGB =
 //       LOGN = 7): each block row takes the scale of its real row (or its
 //       own, one scale per block) and the signs of its place in the real row
-template <int OUT, int BITS, int T, int LOGB, int LOGN, bool WIDE = false>
+// GRID  one group of T tiles per wave (group blockIdx.x * waves + wave), a
+//       workgroup per few groups; otherwise persistent workgroups, one per
+//       CU, with an LDS work counter and a prefetch
+template <int OUT, int BITS, int T, int LOGB, int LOGN, bool WIDE = false, bool GRID = false>
 __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_kernel(MfmaArgs a)
 {
     static_assert(!WIDE || (LOGB == 7 && LOGN == 7), "wide rows run as 128-blocks");
@@ -103,20 +106,33 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
 
     // ---- work split (as in the forward kernel)
     __shared__ int pool_next;
-    const int64_t pool_size = (a.groups - blockIdx.x + gridDim.x - 1) / gridDim.x;
     const int nwaves = blockDim.x >> 6;
-    const int64_t first = wave;
+    int64_t pool_size, first;
+    if constexpr (GRID) {
+        first = (int64_t)blockIdx.x * nwaves + wave;
+        pool_size = first < a.groups ? first + 1 : 0;
+    } else {
+        pool_size = (a.groups - blockIdx.x + gridDim.x - 1) / gridDim.x;
+        first = wave;
+        if (threadIdx.x == 0)
+            pool_next = nwaves;
+    }
     const bool has_work = first < pool_size;
-    if (threadIdx.x == 0)
-        pool_next = nwaves;
     auto grab = [&]() -> int64_t {
-        int v = 0;
-        if (lane == 0)
-            v = atomicAdd(&pool_next, 1);
-        return __builtin_amdgcn_readfirstlane(v);
+        if constexpr (GRID) {
+            return pool_size;
+        } else {
+            int v = 0;
+            if (lane == 0)
+                v = atomicAdd(&pool_next, 1);
+            return __builtin_amdgcn_readfirstlane(v);
+        }
     };
     auto group_elem0 = [&](int64_t g) {
-        return ((int64_t)blockIdx.x + g * gridDim.x) * (int64_t)(T * 512);
+        if constexpr (GRID)
+            return g * (int64_t)(T * 512);
+        else
+            return ((int64_t)blockIdx.x + g * gridDim.x) * (int64_t)(T * 512);
     };
 
     // ---- raw input of a group: the lane's code bytes per tile and the
@@ -205,6 +221,8 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
 
     Raw cur;
     load(has_work ? first : 0, cur);
+    if constexpr (GRID)
+        __builtin_amdgcn_sched_barrier(0);  // every load issued before the sign table
 
     if constexpr (TPR > 1) {
         for (int idx = threadIdx.x; idx < TPR * 64; idx += blockDim.x) {
@@ -244,7 +262,8 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
                 asm volatile("" : "+v"(raw.sg[i][0]), "+v"(raw.sg[i][1]));
         }
     };
-    take_delivery(cur);
+    if constexpr (!GRID)
+        take_delivery(cur);
 
     int64_t g = first;
     while (g < pool_size) {
@@ -330,7 +349,8 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
                 fast::dpp_stages<D>(v[t], sig0, sig1, sig2, sig3);
         }
 
-        take_delivery(cur);
+        if constexpr (!GRID)
+            take_delivery(cur);
 
         // ------------------------------------------------------------ outputs
         const int64_t e0 = group_elem0(g);
@@ -401,6 +421,22 @@ hipError_t launch_inv_one(const Request &r, const DeviceInfo &dev, int wide_div 
     ma.wide_row_scale = wide_row_scale;
     constexpr int TPR = LOGN > 9 ? 1 << (LOGN - 9) : 1;
     const size_t lds = TPR > 1 ? (size_t)TPR * 64 * 32 : 0;
+    // The grid form for large launches of 128-block rows of wide rows (one
+    // wave per workgroup; 16384 x 11008: fp32 out 198 -> 187 us, bf16 out
+    // 101.5 -> 90) and of 8-tile groups with fp32 out (8 waves per workgroup
+    // sharing the sign table; 16384 x 4096: 64.7 -> 61.0 us, 65536 x 1024:
+    // 67.8 -> 58.6).  Not for bf16 out with 8-tile groups (16384 x 4096:
+    // 33.2 -> 38.2 us) nor for narrow groups with fp32 out, which the
+    // persistent form runs at a capped wave count (see below).
+    constexpr bool kGridForm = WIDE || (T == 8 && OUT == kF32);
+    const int64_t groups8 = (ma.total + 4095) / 4096;
+    if (kGridForm && groups8 >= (int64_t)dev.cu_count * kGridPerCuWide) {
+        const int wpb = WIDE ? 1 : 8;
+        hipLaunchKernelGGL((mfma_inv_kernel<OUT, BITS, T, LOGB, LOGN, WIDE, true>),
+                           dim3((unsigned)((ma.groups + wpb - 1) / wpb)), dim3(64 * wpb), lds,
+                           r.stream, ma);
+        return hipGetLastError();
+    }
     auto fn = mfma_inv_kernel<OUT, BITS, T, LOGB, LOGN, WIDE>;
     // every wave the CU holds, up to a cap per case (steady-state timings):
     // fp32 out, narrow groups 8 (1048576 x 128: 142 us at 8 waves, 210 at

@@ -9,9 +9,10 @@ benchmark times (so the kernel instances a full-size launch selects are the
 ones compared) and checks, for every row:
   codes and scales                         all five workloads
   the fp32 rotation itself (hq_rotate)     the INT8 case, Q/K, hidden 4096
-  the fp32 inverse of the oracle's codes   Q/K, FFN 11008, K/V
-plus the 11008-wide rows with one scale per 128-block (forward and inverse)
-and the 4096-wide rows with 128-element groups.  Tolerances are those of
+  the fp32 inverse of the oracle's codes   Q/K, hidden 4096, FFN 11008, K/V
+  the bf16 inverse as well                 FFN 11008
+plus the 11008-wide rows with one scale per 128-block (forward, fp32 and
+bf16 inverse) and the 4096-wide rows with 128-element groups.  Tolerances are those of
 oracle/parity.py.  The oracle runs on every host core; the largest case
 (16384 x 4096) is 2.7e11 multiply-adds, seconds on the GPU machine's host.
 """
@@ -28,7 +29,8 @@ from tests import gpu_util as G
 pytestmark = pytest.mark.gpu
 
 ROTATE = ("tiny_int8", "qk_heads", "hidden_4096")
-INVERSE = ("qk_heads", "ffn_11008", "kv_cache")
+INVERSE = ("qk_heads", "hidden_4096", "ffn_11008", "kv_cache")
+INVERSE_BF16 = ("ffn_11008",)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -64,7 +66,14 @@ def test_full_size_every_row(name):
                                          w.bits, w.n)
             y = G.gpu_dequant_inv(ref["codes"], ref["scales"], s, w.b, w.bits)
             P.check_inverse(y, y_ref, bf16=False, what=f"{tag} inverse f32")
-            del y, y_ref
+            del y
+            if name in INVERSE_BF16:
+                yb = G.gpu_dequant_inv(ref["codes"], ref["scales"], s, w.b, w.bits,
+                                       out_bf16=True)
+                P.check_inverse(P.bf16_bits_to_f64(yb), y_ref, bf16=True,
+                                what=f"{tag} inverse bf16")
+                del yb
+            del y_ref
         if name == "kv_cache":
             # GPU forward -> GPU inverse stays within the orthogonality bound
             # of the input, row by row
@@ -99,3 +108,7 @@ def test_full_size_grouped_every_row(name, group):
                                  w.n, group=group)
     y = G.gpu_dequant_inv_grouped(ref["codes"], ref["scales"], s, w.b, group, w.bits)
     P.check_inverse(y, y_ref, bf16=False, what=f"{tag} inverse f32")
+    del y
+    yb = G.gpu_dequant_inv_grouped(ref["codes"], ref["scales"], s, w.b, group, w.bits,
+                                   out_bf16=True)
+    P.check_inverse(P.bf16_bits_to_f64(yb), y_ref, bf16=True, what=f"{tag} inverse bf16")
