@@ -535,14 +535,46 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
         const int64_t e0 = group_elem0(g);
         if constexpr (OP == kRotate) {
             const float mul = lane_neg ? -a.rb : a.rb;
+            // Whole tiles: lanes l and l ^ 8 trade the second halves of
+            // their 32 output bytes, so that each of a tile's two 16-byte
+            // stores writes 8 whole 128-byte lines (those of the lanes with
+            // bit 3 clear, then those with it set), not half of each of 16
+            // lines.  The partner's output offset follows from its lane
+            // index as out_off does.
+            // No branch around the stores: past the tensor's end they are
+            // dropped by a descriptor cut there (the whole offset in the
+            // checked vector operand).  At a branch join the compiler once
+            // left out the wait state that a VALU write needs right after a
+            // 16-byte store of the same registers.
+            const int64_t left = a.total - e0;
+            const auto ry = rsrc((float *)a.y + e0, (int)(left < T * 512 ? left : T * 512) * 4);
+            const bool hi8 = (lane >> 3) & 1;
+            int pl8 = l16 ^ 8;
+            if constexpr (D > 0) {
+                const int c = (int)((a.pi >> (4 * (l16 ^ 8))) & 15);
+                constexpr int mask = (1 << D) - 1;
+                pl8 = ((l16 ^ 8) & ~mask) | (c & mask);
+            }
+            const int out_off8 = 8 * (lane >> 4) + 32 * pl8;
+            const int s0 = 4 * (hi8 ? out_off8 + 4 : out_off);  // byte offsets of the two stores
+            const int s1 = 4 * (hi8 ? out_off : out_off8 + 4);
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                const int eo = t * 512 + out_off;
-                if (e0 + eo < a.total) {
-                    float4 *dst = (float4 *)((float *)a.y + e0 + eo);
-                    dst[0] = make_float4(v[t][0] * mul, v[t][1] * mul, v[t][2] * mul, v[t][3] * mul);
-                    dst[1] = make_float4(v[t][4] * mul, v[t][5] * mul, v[t][6] * mul, v[t][7] * mul);
+                u32x4 p0, p1;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    p0[q] = __float_as_uint(v[t][q] * mul);
+                    p1[q] = __float_as_uint(v[t][4 + q] * mul);
                 }
+                u32x4 r, d0, d1;  // r: the partner's second half (row_ror:8 in rows of 16 lanes)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    r[q] = (uint32_t)__builtin_amdgcn_mov_dpp((int)p1[q], 0x128, 0xF, 0xF, false);
+                    d0[q] = hi8 ? r[q] : p0[q];
+                    d1[q] = hi8 ? p0[q] : r[q];
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(d0, ry, t * 2048 + s0, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(d1, ry, t * 2048 + s1, 0, 0);
             }
         } else if constexpr (LOGG == 0) {
             // ---- scale groups of 32..256 elements: each lies in one tile.

@@ -24,6 +24,7 @@
 // output sign bits (a table in LDS for rows wider than one tile).
 #include "hq_mfma_impl.h"
 
+
 namespace hq {
 namespace mfma {
 
@@ -58,6 +59,10 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
     // 16384 x 4096, 70 us plain vs 106-115 us non-temporal; bf16 out 34 vs
     // 37 us, 1048576 x 128 fp32 141 vs 165 us).
     constexpr int kStoreAux = (OUT == kF32 && T == 8) ? 0 : kNonTemporal;
+    // fp32 output of whole tiles as whole 128-byte lines (see below): every
+    // instance but the persistent 8-tile ones, whose 128 registers the
+    // exchange would overflow
+    constexpr bool kFullLine = OUT == kF32 && (GRID || T < 8);
     static_assert(T % TPR == 0, "a group holds whole rows");
     static_assert(LOGB >= 5 && LOGB <= LOGN && LOGN <= 12, "plan");
 
@@ -79,6 +84,21 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
         pl = (l16 & ~mask) | (c & mask);
     }
     const int out_off = 8 * (lane >> 4) + 32 * pl;  // element offset of the 8 outputs
+    // fp32 output of whole tiles: lanes l and l ^ 8 trade the second halves
+    // of their 32 output bytes, so that each of the two 16-byte stores of a
+    // tile writes 8 whole 128-byte lines (those of the lanes with bit 3
+    // clear, then those with it set) instead of half of each of 16 lines.
+    // (MI355X, fp32 out: 1048576 x 128 139.5 -> 127.8 us, 131072 x 128
+    // 22.6 -> 16.6, 131072 x 512 70.8 -> 64.3, 16384 x 4096 60.5 -> 58.6,
+    // 16384 x 11008 in 128-blocks 186.4 -> 179.6.)
+    const bool hi8 = (lane >> 3) & 1;
+    int pl8 = l16 ^ 8;
+    if constexpr (D > 0) {
+        const int c = (int)((a.pi >> (4 * (l16 ^ 8))) & 15);
+        constexpr int mask = (1 << D) - 1;
+        pl8 = ((l16 ^ 8) & ~mask) | (c & mask);
+    }
+    const int out_off8 = 8 * (lane >> 4) + 32 * pl8;  // the partner's
     // lanes 0..15 hold transformed index 0 of their 32-point block in v[t][0]
     const float shift0 = lane < 16 ? kShift : 0.0f;
     const float rbs = lane_neg ? -a.rb : a.rb;
@@ -356,6 +376,9 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
         const int64_t e0 = group_elem0(g);
         const bool full = a.total - e0 >= T * 512;  // wave-uniform
         const auto ry = rsrc((uint8_t *)a.y + e0 * OB, T * 512 * OB);
+        // (the same memory cut at the tensor's end, for stores that are
+        // issued by every lane and dropped past the end)
+        const auto ryc = rsrc((uint8_t *)a.y + e0 * OB, (full ? T * 512 : (int)(a.total - e0)) * OB);
         int lofs = lane;
         asm volatile("" : "+v"(lofs));  // keep the sign-table reads in the loop
 #pragma unroll
@@ -386,16 +409,41 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
             for (int j = 0; j < 8; ++j)
                 o[j] = __uint_as_float(__float_as_uint(v[t][j] * mul) ^ osg[j]);
             const bool ok = full || e0 + t * 512 + out_off < a.total;
-            if (!ok)
-                continue;
             if constexpr (OUT == kF32) {
                 const u32x4 p0 = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
                                   __float_as_uint(o[3])};
                 const u32x4 p1 = {__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]),
                                   __float_as_uint(o[7])};
+                if constexpr (kFullLine) {
+                    // No branch around these stores (a partial tile's stores
+                    // past the end are dropped by the cut descriptor, the
+                    // whole offset being in the checked vector operand): at
+                    // a branch join the compiler once left out the wait
+                    // state that a VALU write needs right after a 16-byte
+                    // store of the same registers.
+                    u32x4 r;  // the partner's second half (row_ror:8 within rows of 16 lanes)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        r[q] = (uint32_t)__builtin_amdgcn_mov_dpp((int)p1[q], 0x128, 0xF, 0xF, false);
+                    u32x4 d0, d1;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        d0[q] = hi8 ? r[q] : p0[q];
+                        d1[q] = hi8 ? p0[q] : r[q];
+                    }
+                    const int a0 = t * 2048 + (hi8 ? out_off8 * 4 + 16 : out_off * 4);
+                    const int a1 = t * 2048 + (hi8 ? out_off * 4 : out_off8 * 4 + 16);
+                    __builtin_amdgcn_raw_buffer_store_b128(d0, ryc, a0, 0, kStoreAux);
+                    __builtin_amdgcn_raw_buffer_store_b128(d1, ryc, a1, 0, kStoreAux);
+                    continue;
+                }
+                if (!ok)
+                    continue;
                 __builtin_amdgcn_raw_buffer_store_b128(p0, ry, out_off * 4, t * 2048, kStoreAux);
                 __builtin_amdgcn_raw_buffer_store_b128(p1, ry, out_off * 4 + 16, t * 2048, kStoreAux);
             } else {
+                if (!ok)
+                    continue;
                 u32x4 p;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {

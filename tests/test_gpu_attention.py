@@ -113,3 +113,31 @@ def test_attention_full_kv_cache():
     rng = np.random.default_rng(43)
     q = W.to_bf16_bits(rng.standard_normal((32, 128), dtype=np.float32))
     _check(q, W.BF16, 8, 128, s, kr, vr, W.F16, "kv_cache 131072 x 8")
+
+
+def test_one_workspace_serves_calls_of_any_shape():
+    # One workspace, sized for the largest call, serves calls of different
+    # shapes one after the other (more kv heads, then fewer, with the
+    # partials of earlier calls left behind, never zeroed): each call must
+    # give what a fresh workspace gives, bit for bit.
+    dev = "cuda"
+    shapes = [(8, 2, 3000), (32, 8, 20000), (8, 1, 500), (64, 8, 7000), (32, 8, 20000)]
+    need = max(hq.hq_decode_attention_workspace(qh, kvh, t) for qh, kvh, t in shapes)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=dev)
+    for i, (q_heads, kv_heads, tokens) in enumerate(shapes):
+        print(f"[attn] shared workspace call {i}: q_heads={q_heads} kv_heads={kv_heads} "
+              f"tokens={tokens}", flush=True)
+        s, kr, vr, _ = _cache(100 + i, tokens, kv_heads, 128, W.F16)
+        q = G.to_dev(W.to_bf16_bits(np.random.default_rng(i).standard_normal(
+            (q_heads, 128), dtype=np.float32)), W.BF16)
+        kc = torch.from_numpy(kr["codes"]).to(dev).view(tokens, kv_heads, 64)
+        vc = torch.from_numpy(vr["codes"]).to(dev).view(tokens, kv_heads, 64)
+        ks = torch.from_numpy(np.ascontiguousarray(kr["scales"])).to(dev)
+        vs = torch.from_numpy(np.ascontiguousarray(vr["scales"])).to(dev)
+        ks = ks.view(torch.float16).view(tokens, kv_heads)
+        vs = vs.view(torch.float16).view(tokens, kv_heads)
+        ref = hq.hq_decode_attention(q, G.s_dev(s), 128, kc, ks, vc, vs, 4)
+        got = hq.hq_decode_attention(q, G.s_dev(s), 128, kc, ks, vc, vs, 4, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.isfinite(ref).all()
+        assert torch.equal(got, ref), (i, (got - ref).abs().max().item())
