@@ -62,9 +62,25 @@ bool wide_fwd_ok(const Request &r)
     return r.rows * (int64_t)(r.n / 128) < ((int64_t)1 << 31);
 }
 
+// The rotation alone of rows of several 128-blocks that the per-row tile
+// plans do not take (wider than 4096, or not a power of two), 16-bit input:
+// with no row scale the blocks are independent, so they run as rows of one
+// block, each with the signs of its place in its real row.
+bool wide_rot_ok(const Request &r)
+{
+    if (r.op != kRotate || r.b != 128 || r.n <= 128 || r.n % 128 != 0)
+        return false;
+    if (r.x_dtype != kBF16 && r.x_dtype != kF16)
+        return false;
+    const bool pow2 = (r.n & (r.n - 1)) == 0;
+    if (pow2 && r.n <= 4096)
+        return false;
+    return r.rows * (int64_t)(r.n / 128) < ((int64_t)1 << 31);
+}
+
 bool plan_ok(const Request &r)
 {
-    if (wide_fwd_ok(r) || long_fwd_ok(r))
+    if (wide_fwd_ok(r) || long_fwd_ok(r) || wide_rot_ok(r))
         return true;
     if (r.op == kDequantInv) {
         if (wide_inv_ok(r))
@@ -129,6 +145,7 @@ hipError_t launch_rq_wide(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rq_long(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rq_append(const Request &r, const DeviceInfo &dev);
 hipError_t launch_rot(const Request &r, const DeviceInfo &dev);
+hipError_t launch_rot_wide(const Request &r, const DeviceInfo &dev);
 hipError_t launch_inv(const Request &r, const DeviceInfo &dev);
 
 }  // namespace mfma
@@ -141,7 +158,7 @@ bool mfma_available(const Request &r)
 hipError_t launch_mfma(const Request &r, const DeviceInfo &dev)
 {
     if (r.op == kRotate)
-        return mfma::launch_rot(r, dev);
+        return mfma::wide_rot_ok(r) ? mfma::launch_rot_wide(r, dev) : mfma::launch_rot(r, dev);
     if (r.op == kDequantInv)
         return mfma::launch_inv(r, dev);
     if (r.dst_rows)

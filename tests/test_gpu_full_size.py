@@ -8,7 +8,7 @@ section 2.2).  Each test runs the whole tensor through the launch the
 benchmark times (so the kernel instances a full-size launch selects are the
 ones compared) and checks, for every row:
   codes and scales                         all five workloads
-  the fp32 rotation itself (hq_rotate)     the INT8 case, Q/K, hidden 4096
+  the fp32 rotation itself (hq_rotate)     the INT8 case, Q/K, hidden 4096, FFN 11008
   the fp32 inverse of the oracle's codes   Q/K, hidden 4096, FFN 11008, K/V
   the bf16 inverse as well                 FFN 11008
 plus the 11008-wide rows with one scale per 128-block (forward, fp32 and
@@ -28,7 +28,7 @@ from tests import gpu_util as G
 
 pytestmark = pytest.mark.gpu
 
-ROTATE = ("tiny_int8", "qk_heads", "hidden_4096")
+ROTATE = ("tiny_int8", "qk_heads", "hidden_4096", "ffn_11008")
 INVERSE = ("qk_heads", "hidden_4096", "ffn_11008", "kv_cache")
 INVERSE_BF16 = ("ffn_11008",)
 

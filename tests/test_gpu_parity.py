@@ -141,16 +141,18 @@ def test_ragged_row_counts(rows):
     (512, 512, 8192 + 5),
     (1024, 1024, 32768 + 5),  # 8-tile groups of wide rows
     (2048, 128, 16384 + 1),
+    (11008, 128, 3101),       # 128-block rows of 11008-wide rows, a partial last group
 ])
 def test_grid_form_ragged_tails(n, b, rows):
     # Launches this large take the grid form of the matrix-core kernel (one
     # group of tiles per single-wave workgroup); the reduced-size tests above
-    # take its persistent form.  Every row against the oracle, both
-    # directions.
+    # take its persistent form.  Every row against the oracle: rotation
+    # alone, rotation + quantisation, and the inverse.
     raw, s = W.random_rows(rows + n, rows, n, W.BF16, outliers=1)
     tag = f"grid n={n} b={b} rows={rows}"
     print(f"[grid] {tag}", flush=True)
-    ref = O.rotate_quant(raw, W.BF16, b, s, 4, W.F16)
+    ref = O.rotate_quant(raw, W.BF16, b, s, 4, W.F16, want_xr=True)
+    P.check_rotated(G.gpu_rotate(raw, W.BF16, s, b), ref.pop("xr"), what=f"{tag} rotate")
     codes, scales = G.gpu_rotate_quant(raw, W.BF16, s, b, 4, W.F16)
     P.check_codes(codes, ref, 4, n, what=tag)
     P.check_scales(scales, ref, W.F16, what=tag)
