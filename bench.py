@@ -47,16 +47,25 @@ def copy_bytes_for(bytes_call: int) -> int:
     return bytes_call // 2
 
 
-# The sources the rotate + quantise launch of 16-bit rows is built from
-# (dispatch, shared primitives, the matrix-core kernel and its host side).
-TRAFFIC_SOURCES = ("hq_api.hip", "hq_internal.h", "hq_device.h", "hq_fast_impl.h",
-                   "hq_mfma_impl.h", "hq_mfma.hip", "hq_mfma_rq.hip")
+# The sources each workload's timed launch is built from: the dispatch and
+# shared primitives, plus the kernel that the workload's shape selects.
+_COMMON_SOURCES = ("hq_api.hip", "hq_internal.h", "hq_device.h", "hq_fast_impl.h",
+                   "hq_mfma_impl.h", "hq_mfma.hip")
+TRAFFIC_SOURCES = {
+    "hidden_4096": _COMMON_SOURCES + ("hq_mfma_rq.hip",),
+    "qk_heads": _COMMON_SOURCES + ("hq_mfma_rq.hip",),
+    "kv_cache": _COMMON_SOURCES + ("hq_mfma_rq.hip",),
+    "ffn_11008": _COMMON_SOURCES + ("hq_mfma_long.hip",),
+    "tiny_int8": _COMMON_SOURCES + ("hq_fast.hip", "hq_fast_rq.hip"),
+    "ffn_11008_full": _COMMON_SOURCES + ("hq_paley.hip", "hq_paley_mfma.hip"),
+}
 
 
-def source_hash() -> str:
-    """Hash of the kernel sources a stored traffic measurement belongs to."""
+def source_hash(workload: str) -> str:
+    """Hash of the kernel sources a stored traffic measurement of `workload`
+    belongs to."""
     h = hashlib.sha256()
-    for name in TRAFFIC_SOURCES:
+    for name in TRAFFIC_SOURCES[workload]:
         p = os.path.join(ROOT, "hadamard_rotation_amd", "csrc", name)
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
@@ -125,7 +134,7 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_bytes: int
         req = {"read_requests": n_rd, "read_requests_32B": n32, "bubble": bub[kk][0],
                "read_bytes": req_read, "write_bytes": write[kern_key][0] * 1024.0,
                "bytes_per_launch": req_read + write[kern_key][0] * 1024.0}
-    out = {"workload": workload, "kernel": kern_key[0], "source_hash": source_hash(),
+    out = {"workload": workload, "kernel": kern_key[0], "source_hash": source_hash(workload),
            "fetch_kib_raw": fetch[kern_key][0], "write_kib_raw": write[kern_key][0],
            "copy_bytes": copy_bytes, "copy_grid": copy_key[1],
            "copy_fetch_kib_raw": fetch[copy_key][0], "copy_write_kib_raw": write[copy_key][0],
@@ -149,7 +158,7 @@ def load_traffic(workload: str):
         return None, None
     with open(p) as f:
         t = json.load(f)
-    if t.get("source_hash") != source_hash():
+    if t.get("source_hash") != source_hash(workload):
         return None, None
     return t.get("bytes_per_launch"), t.get("from_requests", {}).get("bytes_per_launch")
 
@@ -255,10 +264,13 @@ def time_workload(name: str, dev, stream, ev0, ev1, calls: int = 200) -> dict:
         return ev0.elapsed_time(ev1) * 1e3 / k
 
     us = timed(call, calls)
+    print(f"[bench] {name}: {us:.2f} us per call", file=sys.stderr, flush=True)
+    traffic, traffic_req = load_traffic(name)
     rec = {"workload": f"{name}: {w.description}", "tensors": len(w.tensors), "rows": rows,
            "n": n, "b": w.b, "bits": w.bits, "bytes_per_call": bytes_call,
            "us_per_call": round(us, 3), "GB/s": round(bytes_call / us / 1e3, 3),
-           "frac_of_8TBs": round(bytes_call / us / 1e3 / HBM_PEAK_GBS, 4)}
+           "frac_of_8TBs": round(bytes_call / us / 1e3 / HBM_PEAK_GBS, 4),
+           "traffic": traffic, "traffic_from_requests": traffic_req}
     if name == "kv_cache":
         ys = [torch.empty((rows, n), dtype=torch.float32, device=dev) for _ in range(2)]
 
