@@ -163,7 +163,7 @@ def load_traffic(workload: str):
     return t.get("bytes_per_launch"), t.get("from_requests", {}).get("bytes_per_launch")
 
 
-def cpu_baseline(workload, target_s: float = 12.0) -> dict:
+def cpu_baseline(workload, target_s: float = 24.0) -> dict:
     """Time the CPU oracle (as it stands, all host cores) on a bounded sample
     of the same workload: a probe of about 3e9 multiply-adds sizes the
     sample to roughly target_s seconds, capped at the whole workload."""
