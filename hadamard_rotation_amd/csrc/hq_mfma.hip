@@ -85,15 +85,16 @@ bool plan_ok(const Request &r)
     if (r.op == kDequantInv) {
         if (wide_inv_ok(r))
             return true;
-        if (r.group != r.n)
+        // group-wise scales: groups of at least one 32-element chunk
+        if (r.group != r.n && r.logg < 5)
             return false;
     } else if (r.x_dtype != kBF16 && r.x_dtype != kF16) {
         return false;
     }
     if (r.n < 32 || r.n > 4096 || (r.n & (r.n - 1)) != 0)
         return false;
-    // group-wise scales (forward quantisation): groups of 32 .. n/2
-    if (r.group != r.n && (r.op != kRotateQuant || r.logg < 5))
+    // group-wise scales (forward quantisation, inverse): groups of 32 .. n/2
+    if (r.group != r.n && (r.op == kRotate || r.logg < 5))
         return false;
     return r.b == r.n || (r.b == 128 && r.n >= 256);
 }

@@ -42,10 +42,17 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // GRID  one group of T tiles per wave (group blockIdx.x * waves + wave), a
 //       workgroup per few groups; otherwise persistent workgroups, one per
 //       CU, with an LDS work counter and a prefetch
-template <int OUT, int BITS, int T, int LOGB, int LOGN, bool WIDE = false, bool GRID = false>
-__global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_kernel(MfmaArgs a)
+// GRP   one scale per group of 2^logg >= 32 elements: a lane's 8 inputs of a
+//       tile lie in one 32-element chunk, hence in one group, so its scale
+//       is applied to the 8 outputs of the chunk's 32-point product, which
+//       are still exact integers; the later stages mix chunks of different
+//       groups in fp32, as the butterflies of scaled codes would
+template <int OUT, int BITS, int T, int LOGB, int LOGN, bool WIDE = false, bool GRID = false,
+          bool GRP = false>
+__global__ __launch_bounds__(T < 8 || (OUT == kF32 && !GRP) ? 1024 : 768) void mfma_inv_kernel(MfmaArgs a)
 {
     static_assert(!WIDE || (LOGB == 7 && LOGN == 7), "wide rows run as 128-blocks");
+    static_assert(!(WIDE && GRP), "wide rows carry their own scale mode");
     extern __shared__ __align__(16) u32x4 lds_osg[];   // n > 512: [tile of row][lane][2]
     constexpr int D = LOGB - 5 < 4 ? LOGB - 5 : 4;      // DPP stages (lane bits 0..D-1)
     constexpr int R = LOGB > 9 ? LOGB - 9 : 0;          // tile-bit stages
@@ -159,7 +166,7 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
     // scale of each of its rows (RPG rows per group for n >= 512, else the
     // row of each tile)
     constexpr int CW = BITS == 4 ? 1 : 2;     // code words per tile
-    constexpr int NS = LOGN >= 9 ? RPG : T;   // scales per lane and group
+    constexpr int NS = GRP ? T : (LOGN >= 9 ? RPG : T);  // scales per lane and group
     struct Raw {
         uint32_t c[T][CW];
         uint32_t s[NS];
@@ -205,6 +212,20 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
                     raw.c[t][1] = w[1];
                 }
             }
+        }
+        if constexpr (GRP) {
+            // the scale of the group of the lane's chunk in each tile (a
+            // group never straddles rows, so its index is the element
+            // index >> logg), clamped into the tensor for a ragged end
+            const int64_t glast = a.ngroups - 1;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                int64_t gi = (e0 + t * 512 + lane_off) >> a.logg;
+                gi = gi < glast ? gi : glast;
+                raw.s[t] = a.scale_f16 ? (uint32_t)((const uint16_t *)a.scales)[gi]
+                                       : ((const uint32_t *)a.scales)[gi];
+            }
+            return;
         }
         const int64_t row_last = a.rows - 1;
 #pragma unroll
@@ -323,6 +344,14 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
                 v[t][i] = d0[i];
                 v[t][4 + i] = d1[i];
             }
+            if constexpr (GRP) {
+                // the f16 operands' offset (index 0 of the chunk, lanes
+                // 0..15), then the group's scale, while the sums are exact
+                v[t][0] -= shift0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    v[t][j] *= sc[t];
+            }
         }
         u32x2 sgt[WIDE ? T : 1];
         if constexpr (WIDE) {
@@ -348,9 +377,11 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
         // the offset of the f16 operands, on index 0 of every block; placed
         // after the tile stages, which carry it only into index 0 of tile 0
         // of each block (sums of blocks' index 0 entries with signs +1)
+        if constexpr (!GRP) {
 #pragma unroll
-        for (int t = 0; t < T; t += (1 << R))
-            v[t][0] -= (float)(1 << R) * shift0;
+            for (int t = 0; t < T; t += (1 << R))
+                v[t][0] -= (float)(1 << R) * shift0;
+        }
 
         // ------------------------------------- DPP stages (lane bits 0..D-1)
         if constexpr (D > 0) {
@@ -383,7 +414,7 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
         asm volatile("" : "+v"(lofs));  // keep the sign-table reads in the loop
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const float mul = (LOGN >= 9 ? sc[t / TPR] : sc[t]) * rbs;
+            const float mul = GRP ? rbs : (LOGN >= 9 ? sc[t / TPR] : sc[t]) * rbs;
             uint32_t osg[8];
             if constexpr (WIDE) {
                 // (the signs of this tile's block row, loaded with the codes;
@@ -457,7 +488,7 @@ __global__ __launch_bounds__(T < 8 || OUT == kF32 ? 1024 : 768) void mfma_inv_ke
     }
 }
 
-template <int OUT, int BITS, int T, int LOGB, int LOGN, bool WIDE = false>
+template <int OUT, int BITS, int T, int LOGB, int LOGN, bool WIDE = false, bool GRP = false>
 hipError_t launch_inv_one(const Request &r, const DeviceInfo &dev, int wide_div = 1, int wide_row_scale = 0)
 {
     MfmaArgs ma;
@@ -480,19 +511,21 @@ hipError_t launch_inv_one(const Request &r, const DeviceInfo &dev, int wide_div 
     const int64_t groups8 = (ma.total + 4095) / 4096;
     if (kGridForm && groups8 >= (int64_t)dev.cu_count * kGridPerCuWide) {
         const int wpb = WIDE ? 1 : 8;
-        hipLaunchKernelGGL((mfma_inv_kernel<OUT, BITS, T, LOGB, LOGN, WIDE, true>),
+        hipLaunchKernelGGL((mfma_inv_kernel<OUT, BITS, T, LOGB, LOGN, WIDE, true, GRP>),
                            dim3((unsigned)((ma.groups + wpb - 1) / wpb)), dim3(64 * wpb), lds,
                            r.stream, ma);
         return hipGetLastError();
     }
-    auto fn = mfma_inv_kernel<OUT, BITS, T, LOGB, LOGN, WIDE>;
+    auto fn = mfma_inv_kernel<OUT, BITS, T, LOGB, LOGN, WIDE, false, GRP>;
     // every wave the CU holds, up to a cap per case (steady-state timings):
     // fp32 out, narrow groups 8 (1048576 x 128: 142 us at 8 waves, 210 at
     // 12, 215 at 16); fp32 out, 8-tile groups 16 (16384 x 4096: 65.5 us at
     // 16, 68.1 at 12, 74.5 at 8); bf16 out 16 for narrow groups and 12 for
     // 8-tile groups (33.0 us at 12, 33.2 at 16)
     int waves_cu = occupancy_waves((const void *)fn, lds);
-    const int cap = OUT == kF32 ? (T < 8 ? 8 : 16) : (T < 8 ? 16 : 12);
+    // (group scales: at most 12 waves for 8-tile groups, the launch bound
+    // that leaves their extra scale registers room)
+    const int cap = OUT == kF32 ? (T < 8 ? 8 : (GRP ? 12 : 16)) : (T < 8 ? 16 : 12);
     if (waves_cu > cap)
         waves_cu = cap;
     int64_t grid = dev.cu_count;
@@ -506,44 +539,53 @@ hipError_t launch_inv_one(const Request &r, const DeviceInfo &dev, int wide_div 
     return hipGetLastError();
 }
 
-template <int OUT, int BITS, int T>
+template <int OUT, int BITS, int T, bool GRP>
 hipError_t inv_short(const Request &r, const DeviceInfo &dev)
 {
     const bool full = r.b == r.n;
     switch (r.n) {
-    case 32: return launch_inv_one<OUT, BITS, T, 5, 5>(r, dev);
-    case 64: return launch_inv_one<OUT, BITS, T, 6, 6>(r, dev);
-    case 128: return launch_inv_one<OUT, BITS, T, 7, 7>(r, dev);
+    case 32: return launch_inv_one<OUT, BITS, T, 5, 5, false, GRP>(r, dev);
+    case 64: return launch_inv_one<OUT, BITS, T, 6, 6, false, GRP>(r, dev);
+    case 128: return launch_inv_one<OUT, BITS, T, 7, 7, false, GRP>(r, dev);
     case 256:
-        return full ? launch_inv_one<OUT, BITS, T, 8, 8>(r, dev)
-                    : launch_inv_one<OUT, BITS, T, 7, 8>(r, dev);
+        return full ? launch_inv_one<OUT, BITS, T, 8, 8, false, GRP>(r, dev)
+                    : launch_inv_one<OUT, BITS, T, 7, 8, false, GRP>(r, dev);
     default:
-        return full ? launch_inv_one<OUT, BITS, T, 9, 9>(r, dev)
-                    : launch_inv_one<OUT, BITS, T, 7, 9>(r, dev);
+        return full ? launch_inv_one<OUT, BITS, T, 9, 9, false, GRP>(r, dev)
+                    : launch_inv_one<OUT, BITS, T, 7, 9, false, GRP>(r, dev);
     }
 }
 
-template <int OUT, int BITS>
+// GRP: one scale per group of 2^logg >= 32 elements (see the kernel)
+template <int OUT, int BITS, bool GRP>
 hipError_t inv_dispatch(const Request &r, const DeviceInfo &dev)
 {
     const bool full = r.b == r.n;
     if (r.n <= 512) {
         const int64_t groups4 = (r.rows * (int64_t)r.n + 4 * 512 - 1) / (4 * 512);
         if (groups4 < (int64_t)dev.cu_count * 8 * 4)
-            return inv_short<OUT, BITS, 2>(r, dev);
-        return inv_short<OUT, BITS, 4>(r, dev);
+            return inv_short<OUT, BITS, 2, GRP>(r, dev);
+        return inv_short<OUT, BITS, 4, GRP>(r, dev);
     }
     switch (r.n) {
     case 1024:
-        return full ? launch_inv_one<OUT, BITS, 8, 10, 10>(r, dev)
-                    : launch_inv_one<OUT, BITS, 8, 7, 10>(r, dev);
+        return full ? launch_inv_one<OUT, BITS, 8, 10, 10, false, GRP>(r, dev)
+                    : launch_inv_one<OUT, BITS, 8, 7, 10, false, GRP>(r, dev);
     case 2048:
-        return full ? launch_inv_one<OUT, BITS, 8, 11, 11>(r, dev)
-                    : launch_inv_one<OUT, BITS, 8, 7, 11>(r, dev);
+        return full ? launch_inv_one<OUT, BITS, 8, 11, 11, false, GRP>(r, dev)
+                    : launch_inv_one<OUT, BITS, 8, 7, 11, false, GRP>(r, dev);
     default:
-        return full ? launch_inv_one<OUT, BITS, 8, 12, 12>(r, dev)
-                    : launch_inv_one<OUT, BITS, 8, 7, 12>(r, dev);
+        return full ? launch_inv_one<OUT, BITS, 8, 12, 12, false, GRP>(r, dev)
+                    : launch_inv_one<OUT, BITS, 8, 7, 12, false, GRP>(r, dev);
     }
+}
+
+template <bool GRP>
+hipError_t inv_by_type(const Request &r, const DeviceInfo &dev)
+{
+    if (r.y_dtype == kF32)
+        return r.bits == 4 ? inv_dispatch<kF32, 4, GRP>(r, dev) : inv_dispatch<kF32, 8, GRP>(r, dev);
+    return r.bits == 4 ? inv_dispatch<kBF16, 4, GRP>(r, dev) : inv_dispatch<kBF16, 8, GRP>(r, dev);
 }
 
 // Rows of several 128-blocks (see wide_inv_ok) as rows of one block.
@@ -572,9 +614,7 @@ hipError_t launch_inv(const Request &r, const DeviceInfo &dev)
             return r.bits == 4 ? inv_wide<kF32, 4>(r, dev) : inv_wide<kF32, 8>(r, dev);
         return r.bits == 4 ? inv_wide<kBF16, 4>(r, dev) : inv_wide<kBF16, 8>(r, dev);
     }
-    if (r.y_dtype == kF32)
-        return r.bits == 4 ? inv_dispatch<kF32, 4>(r, dev) : inv_dispatch<kF32, 8>(r, dev);
-    return r.bits == 4 ? inv_dispatch<kBF16, 4>(r, dev) : inv_dispatch<kBF16, 8>(r, dev);
+    return r.group == r.n ? inv_by_type<false>(r, dev) : inv_by_type<true>(r, dev);
 }
 
 }  // namespace mfma
