@@ -500,17 +500,25 @@ hipError_t launch_inv_one(const Request &r, const DeviceInfo &dev, int wide_div 
     ma.wide_row_scale = wide_row_scale;
     constexpr int TPR = LOGN > 9 ? 1 << (LOGN - 9) : 1;
     const size_t lds = TPR > 1 ? (size_t)TPR * 64 * 32 : 0;
-    // The grid form for large launches of 128-block rows of wide rows (one
-    // wave per workgroup; 16384 x 11008: fp32 out 198 -> 187 us, bf16 out
-    // 101.5 -> 90) and of 8-tile groups with fp32 out (8 waves per workgroup
-    // sharing the sign table; 16384 x 4096: 64.7 -> 61.0 us, 65536 x 1024:
-    // 67.8 -> 58.6).  Not for bf16 out with 8-tile groups (16384 x 4096:
-    // 33.2 -> 38.2 us) nor for narrow groups with fp32 out, which the
-    // persistent form runs at a capped wave count (see below).
-    constexpr bool kGridForm = WIDE || (T == 8 && OUT == kF32);
+    // The grid form (steady-state timings, whole-line fp32 stores):
+    //  - narrow groups (2 or 4 tiles), 4 waves per workgroup: fp32 out from
+    //    4 groups of 8 tiles per CU (1048576 x 128 131.2 -> 105.5 us,
+    //    131072 x 128 17.2 -> 14.2, 131072 x 512 65.7 -> 52.1; with the
+    //    half-line fp32 stores of before, the grid form had been the slower
+    //    one here), bf16 out from 32 per CU (1048576 x 128 63.4 -> 57.7;
+    //    131072 x 128 9.5 -> 10.3 us in the grid form, so it stays
+    //    persistent);
+    //  - 128-block rows of wide rows, from 32 per CU, one wave per
+    //    workgroup: 16384 x 11008 fp32 out 198 -> 187 us, bf16 101.5 -> 90;
+    //  - 8-tile groups with fp32 out, from 32 per CU, 8 waves per workgroup
+    //    sharing the sign table: 16384 x 4096 64.7 -> 61.0 us, 65536 x 1024
+    //    67.8 -> 58.6.  Not for bf16 out with 8-tile groups (16384 x 4096
+    //    33.2 -> 38.2 us).
+    constexpr bool kGridForm = WIDE || T < 8 || OUT == kF32;
     const int64_t groups8 = (ma.total + 4095) / 4096;
-    if (kGridForm && groups8 >= (int64_t)dev.cu_count * kGridPerCuWide) {
-        const int wpb = WIDE ? 1 : 8;
+    const int per_cu_min = (T < 8 && !WIDE && OUT == kF32) ? kGridPerCuShort : kGridPerCuWide;
+    if (kGridForm && groups8 >= (int64_t)dev.cu_count * per_cu_min) {
+        const int wpb = WIDE ? 1 : (T == 8 ? 8 : 4);
         hipLaunchKernelGGL((mfma_inv_kernel<OUT, BITS, T, LOGB, LOGN, WIDE, true, GRP>),
                            dim3((unsigned)((ma.groups + wpb - 1) / wpb)), dim3(64 * wpb), lds,
                            r.stream, ma);
@@ -518,14 +526,12 @@ hipError_t launch_inv_one(const Request &r, const DeviceInfo &dev, int wide_div 
     }
     auto fn = mfma_inv_kernel<OUT, BITS, T, LOGB, LOGN, WIDE, false, GRP>;
     // every wave the CU holds, up to a cap per case (steady-state timings):
-    // fp32 out, narrow groups 8 (1048576 x 128: 142 us at 8 waves, 210 at
-    // 12, 215 at 16); fp32 out, 8-tile groups 16 (16384 x 4096: 65.5 us at
-    // 16, 68.1 at 12, 74.5 at 8); bf16 out 16 for narrow groups and 12 for
-    // 8-tile groups (33.0 us at 12, 33.2 at 16)
+    // fp32 out 16 (131072 x 128: 15.6 us at 16, 17.2 at 8, with whole-line
+    // stores; 16384 x 4096: 65.5 us at 16, 68.1 at 12, 74.5 at 8), 12 for
+    // 8-tile groups with group scales (their launch bound); bf16 out 16 for
+    // narrow groups and 12 for 8-tile groups (33.0 us at 12, 33.2 at 16)
     int waves_cu = occupancy_waves((const void *)fn, lds);
-    // (group scales: at most 12 waves for 8-tile groups, the launch bound
-    // that leaves their extra scale registers room)
-    const int cap = OUT == kF32 ? (T < 8 ? 8 : (GRP ? 12 : 16)) : (T < 8 ? 16 : 12);
+    const int cap = OUT == kF32 ? (T == 8 && GRP ? 12 : 16) : (T < 8 ? 16 : 12);
     if (waves_cu > cap)
         waves_cu = cap;
     int64_t grid = dev.cu_count;
