@@ -61,11 +61,12 @@ __global__ __launch_bounds__(T < 8 || (OUT == kF32 && !GRP) ? 1024 : 768) void m
     constexpr int CB = BITS == 4 ? 256 : 512;           // code bytes per tile
     constexpr int OB = OUT == kF32 ? 4 : 2;             // output bytes per element
     constexpr float kShift = 32.0f * (BITS == 4 ? 1032.0f : 1152.0f);
-    // Output stores: non-temporal except for fp32 rows of 8-tile groups,
-    // where the hint cost a third of the throughput (measured on MI355X:
-    // 16384 x 4096, 70 us plain vs 106-115 us non-temporal; bf16 out 34 vs
-    // 37 us, 1048576 x 128 fp32 141 vs 165 us).
-    constexpr int kStoreAux = (OUT == kF32 && T == 8) ? 0 : kNonTemporal;
+    // Output stores: non-temporal, except in the persistent form for fp32
+    // rows of 8-tile groups, whose stores are half lines (see kFullLine):
+    // there the hint cost a third of the throughput (16384 x 4096, 70 us
+    // plain vs 106-115 us non-temporal).  With whole-line stores it helps
+    // (grid form, 16384 x 4096 58.0 -> 55.9 us, 65536 x 1024 56.7 -> 54.5).
+    constexpr int kStoreAux = (OUT == kF32 && T == 8 && !GRID) ? 0 : kNonTemporal;
     // fp32 output of whole tiles as whole 128-byte lines (see below): every
     // instance but the persistent 8-tile ones, whose 128 registers the
     // exchange would overflow
