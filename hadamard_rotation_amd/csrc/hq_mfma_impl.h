@@ -200,7 +200,8 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
     }
     const int out_off = 8 * (lane >> 4) + 32 * pl;  // element offset of the 8 outputs
     // store of the 8 codes of tile t of the group at element e0: a uniform
-    // tile base plus the lane's fixed byte offset
+    // tile base plus the lane's fixed byte offset; non-temporal (16384 x
+    // 4096: 29.35 -> 28.85 us; 131072 x 128 10.05 -> 9.75)
     auto store_codes = [&](int64_t e0, int t, int bits, const float (&vt)[8], float inv) {
         uint32_t f[8];
         if (bits == 4) {
@@ -208,14 +209,14 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
             for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 8
                 f[j] = __float_as_uint(__builtin_fmaf(vt[j], inv, 12582920.0f));
             const auto rs = rsrc((uint8_t *)a.codes + (e0 >> 1), T * 256);
-            __builtin_amdgcn_raw_buffer_store_b32(fast::pack_int4(f), rs, out_off >> 1, t * 256, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(fast::pack_int4(f), rs, out_off >> 1, t * 256, kNonTemporal);
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 128
                 f[j] = __float_as_uint(__builtin_fmaf(vt[j], inv, 12583040.0f));
             const auto rs = rsrc((int8_t *)a.codes + e0, T * 512);
             const u32x2 pk = {fast::pack_int8(f[0], f[1], f[2], f[3]), fast::pack_int8(f[4], f[5], f[6], f[7])};
-            __builtin_amdgcn_raw_buffer_store_b64(pk, rs, out_off, t * 512, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(pk, rs, out_off, t * 512, kNonTemporal);
         }
     };
 

@@ -161,7 +161,8 @@ __global__ __launch_bounds__(64 * W) void mfma_long_kernel(LongArgs a)
             ((float *)a.scales)[row] = rq.scale;
     }
 
-    // ---- codes: 8 per lane and tile, stores past the row dropped
+    // ---- codes: 8 per lane and tile, stores past the row dropped;
+    // non-temporal (16384 x 11008: 77.9 -> 72.7 us)
     const float inv = lane_neg ? -rq.inv : rq.inv;
     if (a.bits == 4) {
         const auto rs_c = rsrc((uint8_t *)a.codes + row * (a.n >> 1), a.n >> 1);
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(64 * W) void mfma_long_kernel(LongArgs a)
             for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 8
                 f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv, 12582920.0f));
             __builtin_amdgcn_raw_buffer_store_b32(fast::pack_int4(f), rs_c,
-                                                  (out_off >> 1) + (t0 + t) * 256, 0, 0);
+                                                  (out_off >> 1) + (t0 + t) * 256, 0, kNonTemporal);
         }
     } else {
         const auto rs_c = rsrc((int8_t *)a.codes + row * a.n, a.n);
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(64 * W) void mfma_long_kernel(LongArgs a)
                 f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv, 12583040.0f));
             const u32x2 pk = {fast::pack_int8(f[0], f[1], f[2], f[3]),
                               fast::pack_int8(f[4], f[5], f[6], f[7])};
-            __builtin_amdgcn_raw_buffer_store_b64(pk, rs_c, out_off + (t0 + t) * 512, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(pk, rs_c, out_off + (t0 + t) * 512, 0, kNonTemporal);
         }
     }
 }
