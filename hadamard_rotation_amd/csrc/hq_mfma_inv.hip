@@ -509,8 +509,10 @@ hipError_t launch_inv_one(const Request &r, const DeviceInfo &dev, int wide_div 
     //    one here), bf16 out from 32 per CU (1048576 x 128 63.4 -> 57.7;
     //    131072 x 128 9.5 -> 10.3 us in the grid form, so it stays
     //    persistent);
-    //  - 128-block rows of wide rows, from 32 per CU, one wave per
-    //    workgroup: 16384 x 11008 fp32 out 198 -> 187 us, bf16 101.5 -> 90;
+    //  - 128-block rows of wide rows, from 32 per CU, 4 waves per
+    //    workgroup: 16384 x 11008 fp32 out 198 -> 187 us, bf16 101.5 -> 90
+    //    (one wave per workgroup, half-line stores; with whole-line stores
+    //    4 waves per workgroup: 170.1 -> 166.2 us);
     //  - 8-tile groups with fp32 out, from 32 per CU, 8 waves per workgroup
     //    sharing the sign table: 16384 x 4096 64.7 -> 61.0 us, 65536 x 1024
     //    67.8 -> 58.6.  Not for bf16 out with 8-tile groups (16384 x 4096
@@ -519,7 +521,7 @@ hipError_t launch_inv_one(const Request &r, const DeviceInfo &dev, int wide_div 
     const int64_t groups8 = (ma.total + 4095) / 4096;
     const int per_cu_min = (T < 8 && !WIDE && OUT == kF32) ? kGridPerCuShort : kGridPerCuWide;
     if (kGridForm && groups8 >= (int64_t)dev.cu_count * per_cu_min) {
-        const int wpb = WIDE ? 1 : (T == 8 ? 8 : 4);
+        const int wpb = T == 8 ? 8 : 4;
         hipLaunchKernelGGL((mfma_inv_kernel<OUT, BITS, T, LOGB, LOGN, WIDE, true, GRP>),
                            dim3((unsigned)((ma.groups + wpb - 1) / wpb)), dim3(64 * wpb), lds,
                            r.stream, ma);
