@@ -164,10 +164,10 @@ hipError_t launch_mfma(const Request &r, const DeviceInfo &dev)
         return mfma::launch_inv(r, dev);
     if (r.dst_rows)
         return mfma::launch_rq_append(r, dev);
-    if (mfma::wide_fwd_ok(r))
-        return mfma::launch_rq_wide(r, dev);
     if (mfma::long_fwd_ok(r))
         return mfma::launch_rq_long(r, dev);
+    if (mfma::wide_fwd_ok(r))
+        return mfma::launch_rq_wide(r, dev);
     return r.group == r.n ? mfma::launch_rq(r, dev) : mfma::launch_rq_grouped(r, dev);
 }
 

@@ -1,13 +1,14 @@
 // hq_mfma_long.hip -- matrix-core kernel for rotation + quantisation of
-// long rows in 128-element blocks with ONE scale per row: rows wider than
+// long rows in 128-element blocks with one scale per row or one per block
+// (group = 128): rows wider than
 // the per-row tile plans (e.g. the FFN width 11008 = 86 blocks of 128,
 // which is not a whole number of 512-element tiles), 16-bit input.
 //
 // Pages cited: [RQ] "旋转量化：大模型低比特量化中的离群值克星" section 2.1
 // (a width that is not a power of two is rotated in independent 128-element
 // blocks; H_128 as a Kronecker product, so its first five index bits can be
-// one dense 32-point product) and section 2.2 (per-token absmax scale over
-// the whole row, round and clip); [QT] "手把手教你用QuaRot实现LLM的4位量化：从原理到
+// one dense 32-point product), section 2.2 (per-token absmax scale over
+// the whole row, round and clip) and section 6.2 (group size 128); [QT] "手把手教你用QuaRot实现LLM的4位量化：从原理到
 // 代码实践" section 2.1 (signs, then Hadamard).
 //
 // One workgroup per row.  The row is cut into 512-element tiles (the last
@@ -22,8 +23,9 @@
 // tile read zeros and their stores are dropped: each lane's 8 elements lie
 // in one 128-block, and a 128-block is either inside the row or outside
 // it.  Zeros rotate to
-// zeros, so they never raise the row maximum.  The waves' maxima meet in LDS
-// (one barrier), then every wave quantises and stores its own tiles.
+// zeros, so they never raise the row maximum.  With one scale per row the
+// waves' maxima meet in LDS (one barrier), then every wave quantises and
+// stores its own tiles; with one per block a wave's tiles need no other wave.
 #include "hq_mfma_impl.h"
 
 namespace hq {
@@ -43,8 +45,11 @@ struct LongArgs {
     float kq;       // 1 / (sqrt(128) * qmax)
 };
 
-// W waves per workgroup, T tiles per wave (W * T * 512 >= n).
-template <int IN, int W, int T>
+// W waves per workgroup, T tiles per wave (W * T * 512 >= n).  GRP: one
+// scale per 128-block (group = b = 128) instead of one per row: a block is
+// 16 lanes of a tile (lane bits 2, 3 select it), so its maximum needs no
+// other wave, and scales go to [rows, n / 128].
+template <int IN, int W, int T, bool GRP = false>
 __global__ __launch_bounds__(64 * W) void mfma_long_kernel(LongArgs a)
 {
     constexpr int D = 2;  // DPP stages of a 128-point block: lane bits 0, 1
@@ -131,39 +136,101 @@ __global__ __launch_bounds__(64 * W) void mfma_long_kernel(LongArgs a)
     for (int t = 0; t < T; ++t)
         fast::dpp_stages<D>(v[t], sig0, sig1, 0.0f, 0.0f);
 
-    // ---- row maximum: the lane's values, the wave, then the waves in LDS
-    float m = 0.0f;
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int j = 0; j < 8; j += 2)
-            m = fmaxf(fmaxf(m, fabsf(v[t][j])), fabsf(v[t][j + 1]));
-    uint32_t mb = row_lane_max<4>(__float_as_uint(m));
-    if (lane == 0)
-        red[wave] = mb;
-    lds_barrier();
-#pragma unroll
-    for (int w = 0; w < W; ++w)
-        mb = mb > red[w] ? mb : red[w];
     const int qmax = a.bits == 4 ? 7 : 127;
-    const RowQuant rq = row_quant(__uint_as_float(mb), a.kq, qmax);
-    if (wave_any_boost(rq)) {  // a row too small for qmax / max
+    float inv[T];  // the lane's multiplier of each tile, sign included
+    if constexpr (GRP) {
+        // ---- one scale per 128-block, transposed: permlane16_swap of the
+        // lane maxima of tiles (0, 1) and (2, 3) reduces lane bit 4 and
+        // leaves rows [0, 1, 0, 1] and [2, 3, 2, 3]; permlane32_swap of the
+        // two reduces lane bit 5 and leaves tile rho in 16-lane row rho.  Two
+        // DPP steps over lane bits 0, 1 finish the blocks (lane bits 2, 3),
+        // the reciprocal and the one scale store run once per wave, and the
+        // same swaps in reverse hand every lane its block's multiplier.
+        static_assert(T == 4, "the transposed reduction takes four tiles");
+        uint32_t mt[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            float m = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; j += 2)
+                m = fmaxf(fmaxf(m, fabsf(v[t][j])), fabsf(v[t][j + 1]));
+            mt[t] = __float_as_uint(m);
+        }
+        uint32_t x[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const auto r = __builtin_amdgcn_permlane16_swap(mt[2 * p], mt[2 * p + 1], false, false);
+            x[p] = r[0] > r[1] ? r[0] : r[1];
+        }
+        const auto r32 = __builtin_amdgcn_permlane32_swap(x[0], x[1], false, false);
+        const uint32_t z = group_lane_max<D>(r32[0] > r32[1] ? r32[0] : r32[1], 7);
+        const RowQuant rq = row_quant(__uint_as_float(z), a.kq, qmax);
+        // lanes 4k of row rho store block 4 * (t0 + rho) + k; blocks past
+        // the row end fall outside the row's scales and are dropped
+        const int ss = a.scale_f16 ? 2 : 4;
+        const int nb = a.n >> 7;
+        const auto rs_sc = rsrc((uint8_t *)a.scales + row * nb * ss, nb * ss);
+        const int so = (l16 & 3) == 0 ? (4 * (t0 + (lane >> 4)) + (l16 >> 2)) * ss : 0x7FFFFF00;
+        if (a.scale_f16)
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_f16(rq.scale), rs_sc, so, 0, 0);
+        else
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rq.scale), rs_sc, so, 0, 0);
+        auto untranspose = [](float zv, float (&out)[T]) {
+            const uint32_t zi = __float_as_uint(zv);
+            const auto w = __builtin_amdgcn_permlane32_swap(zi, zi, false, false);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const auto u = __builtin_amdgcn_permlane16_swap(w[h], w[h], false, false);
+                out[2 * h] = __uint_as_float(u[0]);
+                out[2 * h + 1] = __uint_as_float(u[1]);
+            }
+        };
+        untranspose(lane_neg ? -rq.inv : rq.inv, inv);
+        if (wave_any_boost(rq)) {  // blocks too small for qmax / max
+            float boost[T];
+            untranspose(rq.boost, boost);
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    v[t][j] *= boost[t];
+        }
+    } else {
+        // ---- row maximum: the lane's values, the wave, then the waves in LDS
+        float m = 0.0f;
 #pragma unroll
         for (int t = 0; t < T; ++t)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                v[t][j] *= rq.boost;
-    }
-    if (wave == 0 && lane == 0) {
-        if (a.scale_f16)
-            ((uint16_t *)a.scales)[row] = f32_to_f16(rq.scale);
-        else
-            ((float *)a.scales)[row] = rq.scale;
+            for (int j = 0; j < 8; j += 2)
+                m = fmaxf(fmaxf(m, fabsf(v[t][j])), fabsf(v[t][j + 1]));
+        uint32_t mb = row_lane_max<4>(__float_as_uint(m));
+        if (lane == 0)
+            red[wave] = mb;
+        lds_barrier();
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+            mb = mb > red[w] ? mb : red[w];
+        const RowQuant rq = row_quant(__uint_as_float(mb), a.kq, qmax);
+        if (wave_any_boost(rq)) {  // a row too small for qmax / max
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    v[t][j] *= rq.boost;
+        }
+        if (wave == 0 && lane == 0) {
+            if (a.scale_f16)
+                ((uint16_t *)a.scales)[row] = f32_to_f16(rq.scale);
+            else
+                ((float *)a.scales)[row] = rq.scale;
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+            inv[t] = lane_neg ? -rq.inv : rq.inv;
     }
 
     // ---- codes: 8 per lane and tile, stores past the row dropped;
     // non-temporal (16384 x 11008: 77.9 -> 72.7 us)
-    const float inv = lane_neg ? -rq.inv : rq.inv;
     if (a.bits == 4) {
         const auto rs_c = rsrc((uint8_t *)a.codes + row * (a.n >> 1), a.n >> 1);
 #pragma unroll
@@ -171,7 +238,7 @@ __global__ __launch_bounds__(64 * W) void mfma_long_kernel(LongArgs a)
             uint32_t f[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 8
-                f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv, 12582920.0f));
+                f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv[t], 12582920.0f));
             __builtin_amdgcn_raw_buffer_store_b32(fast::pack_int4(f), rs_c,
                                                   (out_off >> 1) + (t0 + t) * 256, 0, kNonTemporal);
         }
@@ -182,7 +249,7 @@ __global__ __launch_bounds__(64 * W) void mfma_long_kernel(LongArgs a)
             uint32_t f[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j)  // 1.5*2^23 + 128
-                f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv, 12583040.0f));
+                f[j] = __float_as_uint(__builtin_fmaf(v[t][j], inv[t], 12583040.0f));
             const u32x2 pk = {fast::pack_int8(f[0], f[1], f[2], f[3]),
                               fast::pack_int8(f[4], f[5], f[6], f[7])};
             __builtin_amdgcn_raw_buffer_store_b64(pk, rs_c, out_off + (t0 + t) * 512, 0, kNonTemporal);
@@ -190,7 +257,7 @@ __global__ __launch_bounds__(64 * W) void mfma_long_kernel(LongArgs a)
     }
 }
 
-template <int IN, int W, int T>
+template <int IN, int W, int T, bool GRP>
 hipError_t launch_long_wt(const Request &r)
 {
     LongArgs la;
@@ -204,35 +271,36 @@ hipError_t launch_long_wt(const Request &r)
     fast::dpp_tables(2, la.pi, la.neg);
     const int qmax = r.bits == 8 ? 127 : 7;
     la.kq = (float)(1.0 / (__builtin_sqrt(128.0) * qmax));
-    hipLaunchKernelGGL((mfma_long_kernel<IN, W, T>), dim3((unsigned)r.rows), dim3(64 * W), 0,
+    hipLaunchKernelGGL((mfma_long_kernel<IN, W, T, GRP>), dim3((unsigned)r.rows), dim3(64 * W), 0,
                        r.stream, la);
     return hipGetLastError();
 }
 
-template <int IN>
+template <int IN, bool GRP>
 hipError_t launch_long_in(const Request &r)
 {
     // four tiles per wave, as many waves as the row needs
     switch ((r.n + 2047) / 2048) {
-    case 1: return launch_long_wt<IN, 1, 4>(r);
-    case 2: return launch_long_wt<IN, 2, 4>(r);
-    case 3: return launch_long_wt<IN, 3, 4>(r);
-    case 4: return launch_long_wt<IN, 4, 4>(r);
-    case 5: return launch_long_wt<IN, 5, 4>(r);
-    case 6: return launch_long_wt<IN, 6, 4>(r);
-    case 7: return launch_long_wt<IN, 7, 4>(r);
-    default: return launch_long_wt<IN, 8, 4>(r);
+    case 1: return launch_long_wt<IN, 1, 4, GRP>(r);
+    case 2: return launch_long_wt<IN, 2, 4, GRP>(r);
+    case 3: return launch_long_wt<IN, 3, 4, GRP>(r);
+    case 4: return launch_long_wt<IN, 4, 4, GRP>(r);
+    case 5: return launch_long_wt<IN, 5, 4, GRP>(r);
+    case 6: return launch_long_wt<IN, 6, 4, GRP>(r);
+    case 7: return launch_long_wt<IN, 7, 4, GRP>(r);
+    default: return launch_long_wt<IN, 8, 4, GRP>(r);
     }
 }
 
 }  // namespace
 
-// Rows of several 128-blocks with one scale per row that the per-row tile
-// plans do not take (wider than 4096, or not a power of two), 16-bit input,
-// at most 32 tiles (16384 elements) per row.
+// Rows of several 128-blocks with one scale per row, or one per block, that
+// the per-row tile plans do not take (wider than 4096, or not a power of
+// two), 16-bit input, at most 32 tiles (16384 elements) per row.
 bool long_fwd_ok(const Request &r)
 {
-    if (r.op != kRotateQuant || r.dst_rows || r.b != 128 || r.group != r.n || r.n % 128 != 0)
+    if (r.op != kRotateQuant || r.dst_rows || r.b != 128 || r.n % 128 != 0 || r.n <= 128 ||
+        (r.group != r.n && r.group != 128))
         return false;
     if (r.x_dtype != kBF16 && r.x_dtype != kF16)
         return false;
@@ -244,9 +312,9 @@ bool long_fwd_ok(const Request &r)
 
 hipError_t launch_rq_long(const Request &r, const DeviceInfo &)
 {
-    if (r.x_dtype == kBF16)
-        return launch_long_in<kBF16>(r);
-    return launch_long_in<kF16>(r);
+    if (r.group == 128)
+        return r.x_dtype == kBF16 ? launch_long_in<kBF16, true>(r) : launch_long_in<kF16, true>(r);
+    return r.x_dtype == kBF16 ? launch_long_in<kBF16, false>(r) : launch_long_in<kF16, false>(r);
 }
 
 }  // namespace mfma

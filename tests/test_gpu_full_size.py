@@ -89,9 +89,9 @@ def test_full_size_every_row(name):
 
 @pytest.mark.parametrize("name,group", [("ffn_11008", 128), ("hidden_4096", 128)])
 def test_full_size_grouped_every_row(name, group):
-    # 16384 x 11008 with one scale per 128-block runs as rows of one block on
-    # the matrix core (forward and inverse); 16384 x 4096 with 128-element
-    # groups takes the sub-tile group reduction
+    # 16384 x 11008 with one scale per 128-block: the forward runs one
+    # workgroup per row on the matrix core, the inverse rows of one block;
+    # 16384 x 4096 with 128-element groups takes the sub-tile group reduction
     w = W.WORKLOADS[name]
     data = W.generate(name, seed=42)
     raw, s = data["x"], data["s"]

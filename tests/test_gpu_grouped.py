@@ -74,7 +74,7 @@ SHAPES = [  # (n, b, group)
     (4096, 128, 1024), (4096, 256, 64), (4096, 64, 128), (4096, 4096, 8), (4096, 4096, 16),
     (128, 128, 16), (128, 128, 8), (128, 128, 2), (256, 256, 4), (11008, 128, 128),
     (11008, 16, 64), (11008, 256, 8), (11008, 128, 2), (8192, 4096, 128), (32768, 4096, 128),
-    (48, 16, 16),
+    (48, 16, 16), (640, 128, 128), (8192, 128, 128), (16384, 128, 128), (16512, 128, 128),
 ]
 
 

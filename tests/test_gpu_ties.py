@@ -53,7 +53,9 @@ CASES = [
     (4096, 4096, W.BF16, 5, None),     # matrix core, the headline shape
     (4096, 128, W.BF16, 5, 128),       # matrix core, sub-tile groups (transposed)
     (4096, 128, W.BF16, 5, 512),       # matrix core, whole-tile groups
-    (11008, 128, W.BF16, 3, 128),      # matrix core, 128-block rows of wide rows
+    (11008, 128, W.BF16, 3, 128),      # matrix core, one workgroup per long row, block scales
+    (640, 128, W.F16, 9, 128),         # the same, a partial last tile
+    (16512, 128, W.BF16, 2, 128),      # matrix core, 128-block rows of wide rows
     (128, 128, W.F32, 67, None),       # butterfly kernel
     (4096, 4096, W.F32, 5, None),
     (11008, 128, W.F32, 3, None),      # butterfly kernel, long rows
