@@ -83,6 +83,45 @@ struct MfmaArgs {
     int wide_row_scale;
 };
 
+// Rows of several 128-blocks run as rows of one block: block row vr is
+// block vr mod div of real row vr div div.  A group's first block row vr0
+// is divided once (the double product is within one of the quotient, one
+// step corrects it); block row vr0 + j, 0 <= j < 32, then needs only the
+// quotient of c0 + j < div + 32 by div, which a float product also gives
+// within one (c0 + j < 2^24 + 32, and the quotient is below 17).
+struct WideSplit {
+    int64_t q0;  // real row of block row vr0
+    int c0;      // its block in that row
+};
+
+// (vr0 is wave-uniform: the results are moved to scalar registers.)
+__device__ __forceinline__ WideSplit wide_split0(int64_t vr0, int div, double rdiv)
+{
+    int64_t q = (int64_t)((double)vr0 * rdiv);
+    const int64_t rem = vr0 - q * div;
+    q += rem < 0 ? -1 : (rem >= div ? 1 : 0);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)q);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)q >> 32));
+    const int c0 = __builtin_amdgcn_readfirstlane((int)(vr0 - q * div));
+    return WideSplit{(int64_t)(((uint64_t)hi << 32) | lo), c0};
+}
+
+// Block row vr0 + j: returns its real row minus q0, and its block in c.
+__device__ __forceinline__ int wide_step(const WideSplit &w, int j, int div, float rdivf, int &c)
+{
+    const int x = w.c0 + j;
+    int dq = (int)((float)x * rdivf);
+    c = x - dq * div;
+    if (c < 0) {
+        dq -= 1;
+        c += div;
+    } else if (c >= div) {
+        dq += 1;
+        c -= div;
+    }
+    return dq;
+}
+
 // 16x16x32 product of the +-1 slice a with the 16-bit tile b (fp32 sums).
 template <int IN>
 __device__ __forceinline__ f32x4 hmma(u32x4 a, u32x4 b)
@@ -371,21 +410,25 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
     }
 
     // WIDE: the sign bytes of the lane's 8 inputs of each tile, loaded with
-    // the tile (block row v is block v mod wide_div of its real row; the
-    // double product is within one of the quotient, one step corrects it)
+    // the tile; the lane's block row in tile t is vr0 + 4t + (l16 >> 2),
+    // clamped to the last one for a ragged end
     u32x2 csg[WIDE ? T : 1];
     auto load_signs = [&](int64_t g) {
         if constexpr (WIDE) {
-            const int64_t e0 = group_elem0(g);
+            static_assert(!WIDE || T <= 8, "block rows vr0 .. vr0 + 31");
+            const int64_t vr0 = group_elem0(g) >> 7;
+            const WideSplit ws = wide_split0(vr0, a.wide_div, a.wide_rdiv);
+            const int64_t jl64 = a.rows - 1 - vr0;
+            const int jl = jl64 < 31 ? (int)jl64 : 31;
+            const float rdivf = (float)a.wide_rdiv;
+            const auto rs_sg = rsrc(a.s, a.wide_div * 128);
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                int64_t vr = (e0 + t * 512 + lane_off) >> 7;
-                vr = vr < a.rows - 1 ? vr : a.rows - 1;
-                int64_t q = (int64_t)((double)vr * a.wide_rdiv);
-                const int64_t rem = vr - q * a.wide_div;
-                q += rem < 0 ? -1 : (rem >= a.wide_div ? 1 : 0);
-                const int64_t p = ((vr - q * a.wide_div) << 7) + (lane_off & 127);
-                csg[t] = *(const u32x2 *)(a.s + p);
+                int j = 4 * t + (l16 >> 2);
+                j = j < jl ? j : jl;
+                int c;
+                wide_step(ws, j, a.wide_div, rdivf, c);
+                csg[t] = __builtin_amdgcn_raw_buffer_load_b64(rs_sg, (c << 7) + (lane_off & 127), 0, 0);
             }
         }
     };

@@ -173,14 +173,6 @@ __global__ __launch_bounds__(T < 8 || (OUT == kF32 && !GRP) ? 1024 : 768) void m
         uint32_t s[NS];
         u32x2 sg[WIDE ? T : 1];  // WIDE: sign bytes of the lane's 8 outputs per tile
     };
-    // WIDE: the real row of block row vr (vr < 2^31; the double product is
-    // within one of the quotient, and one step corrects it)
-    auto wide_row = [&](int64_t vr) -> int64_t {
-        int64_t q = (int64_t)((double)vr * a.wide_rdiv);
-        const int64_t rem = vr - q * a.wide_div;
-        q += rem < 0 ? -1 : (rem >= a.wide_div ? 1 : 0);
-        return q;
-    };
     auto load = [&](int64_t g, Raw &raw) {
         const int64_t e0 = group_elem0(g);
         const int64_t left = a.total - 8 - e0;  // >= 0 for every group
@@ -229,21 +221,41 @@ __global__ __launch_bounds__(T < 8 || (OUT == kF32 && !GRP) ? 1024 : 768) void m
             return;
         }
         const int64_t row_last = a.rows - 1;
+        if constexpr (WIDE) {
+            // the lane's block row in tile i is vr0 + 4i + (l16 >> 2) (input
+            // and output positions of a lane share it), clamped to the last
+            // one for a ragged end
+            static_assert(!WIDE || T <= 8, "block rows vr0 .. vr0 + 31");
+            const int64_t vr0 = e0 >> 7;
+            const WideSplit ws = wide_split0(vr0, a.wide_div, a.wide_rdiv);
+            const int64_t jl64 = row_last - vr0;
+            const int jl = jl64 < 31 ? (int)jl64 : 31;
+            const float rdivf = (float)a.wide_rdiv;
+            // scales from row q0 (one per real row) or block row vr0 on:
+            // at most 17 real rows, or 32 block rows
+            const int ss = a.scale_f16 ? 2 : 4;
+            const auto rs_sc = rsrc((const uint8_t *)a.scales + (a.wide_row_scale ? ws.q0 : vr0) * ss,
+                                    32 * ss);
+            const auto rs_sg = rsrc(a.s, a.wide_div * 128);
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                int j = 4 * i + (l16 >> 2);
+                j = j < jl ? j : jl;
+                int c;
+                const int dq = wide_step(ws, j, a.wide_div, rdivf, c);
+                const int so = (a.wide_row_scale ? dq : j) * ss;
+                raw.sg[i] = __builtin_amdgcn_raw_buffer_load_b64(rs_sg, (c << 7) + (out_off & 127), 0, 0);
+                raw.s[i] = a.scale_f16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs_sc, so, 0, 0)
+                                       : __builtin_amdgcn_raw_buffer_load_b32(rs_sc, so, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             int64_t row = LOGN >= 9 ? (e0 >> LOGN) + i : (e0 + i * 512 + lane_off) >> LOGN;
             row = row < row_last ? row : row_last;
-            int64_t srow = row;
-            if constexpr (WIDE) {
-                // (input and output positions of a lane share the block row)
-                const int64_t rr = wide_row(row);
-                if (a.wide_row_scale)
-                    srow = rr;
-                const int64_t p = ((row - rr * a.wide_div) << 7) + (out_off & 127);
-                raw.sg[i] = *(const u32x2 *)(a.s + p);
-            }
-            raw.s[i] = a.scale_f16 ? (uint32_t)((const uint16_t *)a.scales)[srow]
-                                   : ((const uint32_t *)a.scales)[srow];
+            raw.s[i] = a.scale_f16 ? (uint32_t)((const uint16_t *)a.scales)[row]
+                                   : ((const uint32_t *)a.scales)[row];
         }
     };
 
