@@ -89,8 +89,8 @@ SHAPES = [  # (n, b): generic, butterfly and matrix-core paths, blockwise and fu
     (4096, 1024), (4096, 4096), (8192, 4096), (11008, 16), (11008, 128), (11008, 256),
     (16384, 4096),
     # 128-blocks of rows that are not whole 512-element tiles or wider than
-    # 4096 (one workgroup per row on the matrix core): 5, 24 and 128 blocks
-    (640, 128), (3072, 128), (16384, 128),
+    # 4096 (one workgroup per row on the matrix core): 3, 5, 24 and 128 blocks
+    (384, 128), (640, 128), (3072, 128), (16384, 128),
 ]
 
 
