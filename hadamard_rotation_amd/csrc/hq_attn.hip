@@ -497,21 +497,21 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     };
 
     // two register sets, alternating, so no step copies its data: a set is
-    // refilled with the step after next as soon as its step is done
-    if (b0 < b1) {
-        for (int64_t blk = b0;;) {
-            step(pa, blk);
-            blk += 2;
-            if (blk >= b1)
-                break;
-            load_pair(blk + 2, pa);  // past the range: reads 0
-            step(pb, blk);
-            blk += 2;
-            if (blk >= b1)
-                break;
-            load_pair(blk + 2, pb);
-        }
+    // refilled with the step after next as soon as its step is done (past
+    // the range a load reads 0 without touching memory).  Steps run in
+    // pairs with no exit between them, so the accumulators keep their
+    // registers around the loop; an odd last step runs after it.
+    const int64_t nsteps = (b1 - b0 + 1) / 2;
+    int64_t blk = b0;
+    for (int64_t i = 1; i < nsteps; i += 2) {
+        step(pa, blk);
+        load_pair(blk + 4, pa);
+        step(pb, blk + 2);
+        load_pair(blk + 6, pb);
+        blk += 4;
     }
+    if (nsteps & 1)
+        step(pa, blk);
 
     // ---- partial of this wave: add the lo rows to the hi rows
     float o[4][8];  // [row i][product ng]
