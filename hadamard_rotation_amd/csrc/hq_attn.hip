@@ -570,6 +570,32 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))
     }
 }
 
+// v of lane l ^ m (m = 1, 2, ..., 32): DPP within rows of 16 lanes (lane
+// bits 0-3; bit 2 from two shifts, each writing the banks of 4 lanes that
+// read inside the row), permlane swaps across rows (bits 4, 5).
+__device__ __forceinline__ float xor_lane(float v, int m, int lane)
+{
+    const int x = __float_as_int(v);
+    switch (m) {
+    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xf, 0xf, false));  // quad_perm [1,0,3,2]
+    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xf, 0xf, false));  // quad_perm [2,3,0,1]
+    case 4: {
+        // banks 0, 2 (lane bit 2 clear) read lane + 4 (row_shl:4), banks 1, 3 lane - 4 (row_shr:4)
+        const int t = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xf, 0x5, false);
+        return __int_as_float(__builtin_amdgcn_update_dpp(t, x, 0x114, 0xf, 0xA, false));
+    }
+    case 8: return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x128, 0xf, 0xf, false));  // row_ror:8
+    case 16: {
+        const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+        return __uint_as_float((lane & 16) ? r[0] : r[1]);
+    }
+    default: {
+        const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+        return __uint_as_float((lane & 32) ? r[0] : r[1]);
+    }
+    }
+}
+
 // One workgroup of 4 waves per query head.  Each wave merges every 4th
 // partial online (the largest maximum so far, the rescaled sums and
 // accumulators), lane l holding dimensions 2l and 2l + 1; the partials'
@@ -587,6 +613,9 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(AttnArgs a
     const int wave = threadIdx.x >> 6;
     const int h = blockIdx.x;
     const float *base = a.ws + (int64_t)h * a.nws * kPartStride;
+    // the signs of the lane's two dimensions, requested before the partials
+    // so that their latency is not left for the end
+    const uint32_t sgn = *(const uint16_t *)(a.s + 2 * lane);
     float M = -INFINITY, L = 0.0f;
     float2 O = make_float2(0.0f, 0.0f);
     for (int p0 = wave; p0 < a.nws; p0 += kMergeBatch * kMergeWaves) {
@@ -651,16 +680,21 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(AttnArgs a
         x0 = t0;
         x1 = t1;
     }
-    for (int k = 1; k < a.log_b; ++k) {
+    // (the partner lane l ^ m by DPP moves and permlane swaps, which stay in
+    // the vector unit, instead of permutes through the LDS crossbar)
+#pragma unroll
+    for (int k = 1; k < 7; ++k) {
+        if (k >= a.log_b)  // wave-uniform
+            break;
         const int m = 1 << (k - 1);
-        const float p0 = __shfl_xor(x0, m, 64), p1 = __shfl_xor(x1, m, 64);
-        const bool up = (lane & m) != 0;
-        x0 = up ? p0 - x0 : x0 + p0;
-        x1 = up ? p1 - x1 : x1 + p1;
+        const float p0 = xor_lane(x0, m, lane), p1 = xor_lane(x1, m, lane);
+        const float sg = (lane & m) ? -1.0f : 1.0f;
+        x0 = __builtin_fmaf(x0, sg, p0);  // upper lane: partner - own
+        x1 = __builtin_fmaf(x1, sg, p1);
     }
-    const int8_t s0 = a.s[2 * lane], s1 = a.s[2 * lane + 1];
     const float v0 = x0 * a.rb, v1 = x1 * a.rb;
-    *(float2 *)&a.out[(int64_t)h * kHeadDim + 2 * lane] = make_float2(s0 < 0 ? -v0 : v0, s1 < 0 ? -v1 : v1);
+    *(float2 *)&a.out[(int64_t)h * kHeadDim + 2 * lane] =
+        make_float2((sgn & 0x80u) ? -v0 : v0, (sgn & 0x8000u) ? -v1 : v1);
 }
 
 template <int G>
