@@ -136,3 +136,34 @@ def test_grouped_zero_and_tiny_groups():
             assert np.all(q[zero] == 0)
             P.check_scales(scales, ref, W.F32, what=tag)
             P.check_codes(codes, ref, bits, n, what=tag)
+
+
+def test_grouped_zero_and_tiny_groups_bf16():
+    # the same on the 16-bit paths with one scale per 128-block: the long-row
+    # kernel (640: a partial last tile; 11008), 128-block rows of wider rows
+    # (16512) and sub-tile groups of a per-row plan (4096); bf16 keeps
+    # binary32's exponent range, so the tiny entries stay tiny (3e-45 and
+    # -2^-130 are below bf16's smallest subnormal and become 0)
+    for n in (640, 11008, 16512, 4096):
+        b, group = 128, 128
+        raw = np.zeros((5, n), dtype=np.float32)
+        raw[0, : b] = np.linspace(-3.0, 5.0, b, dtype=np.float32)   # first block only
+        raw[1, :] = 1.0
+        raw[2, 1] = 1e-38
+        raw[2, b + 3] = 2.0 ** -100
+        raw[3, 2] = 3e-45
+        raw[3, b + 5] = -2.0 ** -130
+        raw[4, n - 1] = -7.5                                        # last block only
+        x = W.to_bf16_bits(raw)
+        s = np.where(np.arange(n) % 3 == 0, -1, 1).astype(np.int8)
+        for bits, sd in ((4, W.F32), (8, W.F16)):
+            tag = f"zero/tiny bf16 n={n} g={group} bits={bits}"
+            print(f"[grouped-tiny] {tag}", flush=True)
+            codes, scales = G.gpu_rotate_quant_grouped(x, W.BF16, s, b, group, bits, sd)
+            ref = O.rotate_quant(x, W.BF16, b, s, bits, sd, group=group)
+            zero = ref["scale_exact"] == 0
+            assert np.all(scales[zero] == 0)
+            q = O.unpack_codes(codes, bits, n).reshape(5, n // group, group)
+            assert np.all(q[zero] == 0)
+            P.check_scales(scales, ref, sd, what=tag)
+            P.check_codes(codes, ref, bits, n, what=tag)
