@@ -98,6 +98,18 @@ def test_grouped_ragged_rows(rows):
                inverse=False)
 
 
+def test_grouped_wide_rows_grid_form():
+    # rows wider than 16384 with one scale per 128-block run as rows of one
+    # block; from 32768 block rows on, in the grid form (8 tiles per wave):
+    # 257 rows of 16512 = 129 blocks are 33153 block rows, the last group
+    # ragged.  Every row against the oracle, forward and inverse.
+    n, b, group, rows = 16512, 128, 128, 257
+    raw, s = W.random_rows(n + rows, rows, n, W.BF16, outliers=2)
+    for bits, sd in ((4, W.F32), (8, W.F16)):
+        _check(raw, W.BF16, s, b, group, bits, sd, f"wide grid n={n} rows={rows} bits={bits}",
+               inverse=(bits == 4))
+
+
 def test_grouped_equals_per_row_at_group_n():
     # group == n is the per-row entry point, bit for bit
     import torch
