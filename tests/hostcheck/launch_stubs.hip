@@ -4,7 +4,7 @@
 // host-only with AddressSanitizer and UndefinedBehaviorSanitizer and run
 // without a GPU.  Every request that passes validation and would launch a
 // kernel reaches one of these and is reported as a HIP error instead; the
-// ABI tests run under this build make no such request.
+// ABI tests run against this host-only library make no such request.
 #include "hq_internal.h"
 
 namespace hq {

@@ -14,7 +14,7 @@ ones compared) and checks, for every row:
 plus the 11008-wide rows with one scale per 128-block (forward, fp32 and
 bf16 inverse) and the 4096-wide rows with 128-element groups.  Tolerances are those of
 oracle/parity.py.  The oracle runs on every host core; the largest case
-(16384 x 4096) is 2.7e11 multiply-adds, seconds on the GPU machine's host.
+(16384 x 4096) is 2.7e11 multiply-adds, seconds on a 16-thread host.
 """
 from __future__ import annotations
 
