@@ -110,6 +110,19 @@ def test_grouped_wide_rows_grid_form():
                inverse=(bits == 4))
 
 
+@pytest.mark.parametrize("n", [4224, 6144, 9088, 10240, 12416, 14336])
+def test_long_rows_every_wave_count(n):
+    # rows of 128-blocks up to 16384 wide run one workgroup per row with
+    # ceil(n / 2048) waves; these widths take 3, 5 and 7 waves (a partial
+    # last wave, or a full one), with one scale per row and per block
+    rows = 7
+    raw, s = W.random_rows(n + 5, rows, n, W.BF16, outliers=2)
+    for bits, sd in ((4, W.F32), (8, W.F16)):
+        for group in (n, 128):
+            _check(raw, W.BF16, s, 128, group, bits, sd, f"long n={n} g={group} bits={bits}",
+                   inverse=(bits == 4))
+
+
 def test_grouped_equals_per_row_at_group_n():
     # group == n is the per-row entry point, bit for bit
     import torch
