@@ -443,6 +443,15 @@ __global__ __launch_bounds__(T < 8 ? 1024 : 768) void mfma_kernel(MfmaArgs a)
         // loads and waits for the signs with most of the row not yet
         // requested)
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (OP == kRotate && LOGN == 7) {
+            // The rotation alone of 128-element rows writes fp32, four
+            // bytes out per two in; spacing the waves' requests out helps
+            // it (1048576 x 128 138.4 -> 133.7 us, 131072 x 128 18.7 ->
+            // 18.2 with 512 cycles here; wider rows and the quantising
+            // kernels gained nothing or lost a little)
+            __builtin_amdgcn_s_sleep(8);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         make_amat();
     } else {
         load_signs(has_work ? first : 0);
