@@ -827,6 +827,11 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
     constexpr int OB = OUT == kF32 ? 4 : 2;      // output bytes per element
     __shared__ __align__(16) uint16_t xt[2][kM2 * kBRS];  // [buffer][j][a2][slot]
     __shared__ unsigned char sq[kBK];
+    // fp32 out: each wave's outputs pass through LDS on their way out, 64
+    // bytes per lane at a stride of 80 (the 16-byte accesses of 8
+    // consecutive lanes then fall in distinct banks)
+    constexpr int kOst = OUT == kF32 ? kBW * 64 * 5 : 1;
+    __shared__ __align__(16) u32x4 ost[kOst];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1059,31 +1064,102 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
                 __builtin_amdgcn_raw_buffer_store_b128(p, ry, ok ? 2 * e0 : kDropOffset, 0, 0);
             }
         };
+        if constexpr (OUT == kF32) {
+            // Whole 128-byte lines per store instruction.  Output row ip (32
+            // fp32, one line) sits in two lanes (its halves, lane bit 4), so
+            // a direct store writes a quarter of each of 32 lines; through
+            // LDS, lane c of each group of 8 stores 16-byte chunk c of one
+            // line instead (16384 x 11008: 272.0 -> 206.0 us; without any
+            // stores the kernel took 167.5, so the quarter-line stores had
+            // not overlapped the products at all).  Non-temporal, which
+            // gains about 1 % on whole lines (on quarter lines it had taken
+            // 272 to 831 us).  Stores of the padding columns' rows go past
+            // the end and are dropped, as before.
+            u32x4 *mine = &ost[(wave * 64) * 5];
+            auto line_of = [&](int l16x, int b2) -> int {  // -1: nothing to store
+                const int sbx = 16 * wave + l16x;
+                if (sbx < kBBlk)
+                    return 1 + kBBlk * b2 + sbx;
+                return sbx == kBBlk && b2 == 0 ? 0 : -1;
+            };
 #pragma unroll
-        for (int k = 0; k < kBTop / 2; ++k) {
-            const int b2 = 2 * k + lb5;
-            const bool ok = sb < kBBlk || (sb == kBBlk && b2 == 0);
-            const int ip = sb >= kBBlk ? 0 : 1 + kBBlk * b2 + sb;
+            for (int k = 0; k < kBTop / 2; ++k) {
+                // lane (l16, lb4, lb5): half lb4 of the row of column l16
+                // in block 2k + lb5, 4 chunks of 16 bytes
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int sl = 0; sl < 2; ++sl) {
+                        u32x4 w;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            w[r] = __float_as_uint(outv(acc[2 * k + t][sl][r], 16 * k + 8 * t + 4 * sl + r));
+                        mine[lane * 5 + 2 * t + sl] = w;
+                    }
+                fast::wave_lds_sync();
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    // row (lb5', l16') = 8i + (lane >> 3), chunk c = lane & 7
+                    const int rowx = 8 * i + (lane >> 3), c = lane & 7;
+                    const int l16x = rowx & 15, lb5x = rowx >> 4;
+                    const u32x4 w = mine[(l16x + 16 * (c >> 2) + 32 * lb5x) * 5 + (c & 3)];
+                    const int ipx = line_of(l16x, 2 * k + lb5x);
+                    __builtin_amdgcn_raw_buffer_store_b128(w, ry, ipx < 0 ? kDropOffset : 128 * ipx + 16 * c, 0,
+                                                           kNonTemporal);
+                }
+                fast::wave_lds_sync();
+            }
+            {
+                // block 6: lane (l16, lb4, lb5) holds quarter 2 lb4 + lb5 of
+                // the row of column l16 (2 chunks)
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) {
+                    u32x4 w;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        w[r] = __float_as_uint(outv(acc[kBTop - 1][sl][r], 48 + 4 * sl + r));
+                    mine[lane * 5 + sl] = w;
+                }
+                fast::wave_lds_sync();
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int l16x = 8 * i + (lane >> 3), c = lane & 7;
+                    const int qd = c >> 1;  // quarter: lb4 = qd >> 1, lb5 = qd & 1
+                    const u32x4 w = mine[(l16x + 16 * (qd >> 1) + 32 * (qd & 1)) * 5 + (c & 1)];
+                    const int sbx = 16 * wave + l16x;
+                    const int ipx = 1 + kBBlk * (kBTop - 1) + sbx;
+                    __builtin_amdgcn_raw_buffer_store_b128(w, ry, sbx < kBBlk ? 128 * ipx + 16 * c : kDropOffset,
+                                                           0, kNonTemporal);
+                }
+                fast::wave_lds_sync();
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kBTop / 2; ++k) {
+                const int b2 = 2 * k + lb5;
+                const bool ok = sb < kBBlk || (sb == kBBlk && b2 == 0);
+                const int ip = sb >= kBBlk ? 0 : 1 + kBBlk * b2 + sb;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    float o[8];
+#pragma unroll
+                    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            o[4 * sl + r] = outv(acc[2 * k + t][sl][r], 16 * k + 8 * t + 4 * sl + r);
+                    store8(ok, ip * kM2 + 16 * lb4 + 8 * t, o);
+                }
+            }
+            {
+                const int ip = 1 + kBBlk * (kBTop - 1) + (sb < kBBlk ? sb : 0);
                 float o[8];
 #pragma unroll
                 for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        o[4 * sl + r] = outv(acc[2 * k + t][sl][r], 16 * k + 8 * t + 4 * sl + r);
-                store8(ok, ip * kM2 + 16 * lb4 + 8 * t, o);
+                        o[4 * sl + r] = outv(acc[kBTop - 1][sl][r], 48 + 4 * sl + r);
+                store8(sb < kBBlk, ip * kM2 + 16 * lb4 + 8 * lb5, o);
             }
-        }
-        {
-            const int ip = 1 + kBBlk * (kBTop - 1) + (sb < kBBlk ? sb : 0);
-            float o[8];
-#pragma unroll
-            for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    o[4 * sl + r] = outv(acc[kBTop - 1][sl][r], 48 + 4 * sl + r);
-            store8(sb < kBBlk, ip * kM2 + 16 * lb4 + 8 * lb5, o);
         }
 
         // ---- the next row into the other buffer, the one after it in flight.
