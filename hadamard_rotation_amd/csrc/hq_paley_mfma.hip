@@ -23,6 +23,8 @@
 // of the i' tiles and keeps in registers.  The butterflies then run on the
 // result in registers: j = 16 mt + 4 rg + r is the tile, the lane's row
 // group and the register, so two of the five stages cross lanes.
+#include <mutex>
+
 #include "hq_device.h"
 #include "hq_internal.h"
 #include "hq_fast_impl.h"  // the INT4 / INT8 code packers
@@ -58,6 +60,9 @@ struct PaleyArgs {
     int y_bf16;
     int scale_f16;
     float rb;       // 1 / sqrt(n)
+    // k = 344 forward: the product waves' and the helper's operands (see
+    // paley343h_kernel), [operand][lane], for the input's 16-bit type
+    const void *hop;
 };
 
 // GF(p^e) on element indices c0 + p c1 + p^2 c2 (e <= 3): the square of a
@@ -811,6 +816,450 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
     }
 }
 
+// ---------------------------------------------------------------------------
+// k = 344 forward with a helper wave (paley343h_kernel): the dense count of
+// products and no padded outputs.
+//
+// Input slots.  Slot 48 (the last) of each block and the extra point are
+// taken out of the blocks, so that a block keeps 48 slots: the contraction
+// index ("K-index") of Paley index i is
+//   48 a2 + sa           for i = 1 + 49 a2 + sa, sa < 48     (0 .. 335)
+//   336 + a2             for i = 1 + 49 a2 + 48              (336 .. 342)
+//   343                  for i = 0                            (the extra point)
+// and 344 .. 351 are zero: 11 chunks of 32, the dense count.  Blocks 2p and
+// 2p + 1 fill chunks 3p .. 3p + 2: chunk 3p is block 2p's slots 0..31, chunk
+// 3p + 1 its slots 32..47 and block 2p + 1's slots 0..15, chunk 3p + 2 block
+// 2p + 1's slots 16..47; chunk 9 is block 6's slots 0..31, and chunk 10 holds
+// block 6's slots 32..47, the seven slots 48 and the extra point.  Against
+// the output column (b2, sb), sb < 48, a chunk's 32 x 16 operand therefore
+// depends only on its kind (3p, 3p + 1, 3p + 2) and on (2p - b2) mod 7
+// (H_k's blocks are circulant in the top digit), and chunk 10's on b2: 28
+// operands per 16-column tile of every block, 112 registers.
+//
+// Waves 0..2 each own the 16 columns 16 w .. 16 w + 15 of every block: 154
+// products per row, then the 32-point butterflies of the forward kernel, the
+// maximum of their values and the values themselves (fp32) into an LDS row
+// buffer in natural order.  The fourth wave (the helper) computes the
+// columns that the blocks no longer hold (column 48 of every block and
+// column 0, the extra point's: 8 of a 16-column tile, 22 products), stages
+// the rows (loads, signs, the transposed layout) and quantises the row
+// before from the LDS buffer: the maximum, the codes of 32 consecutive
+// outputs per lane and 1 KB code stores per wave instruction.  Per row the
+// product waves run 154 products and the butterflies, and the work they no
+// longer do (staging, quantiser, stores, the padded columns) goes to the
+// helper, whose products and vector work fit beside theirs.
+constexpr int kHW = 4;                       // waves: three product waves and the helper
+constexpr int kHThreads = 64 * kHW;
+constexpr int kHK = 352;                     // K-indices: 11 chunks of 32
+constexpr int kHRS = 376;                    // staged row stride (188 dwords, 28 mod 32)
+constexpr int kHOS = 36;                     // LDS row buffer: floats per output column
+constexpr int kHChunks = kBK * kM2 / 8;      // 16-byte chunks of a row (1376)
+constexpr int kHCPL = (kHChunks + 63) / 64;  // chunks per helper lane (22)
+// Staged row j starts at element hrow(j).  As in the forward kernel, the
+// stride keeps the operand reads of 8 consecutive rows in distinct banks and
+// the shift of 16 elements per group of 8 rows separates the four rows one
+// staging store covers.
+__device__ __forceinline__ constexpr int hrow(int j) { return j * kHRS + 16 * (j >> 3); }
+static_assert(kHRS >= kHK, "staged rows do not overlap");
+
+// K-index of Paley index i, and back (a K-index past 343 has no index: -1)
+__device__ __forceinline__ int hkappa(int i)
+{
+    if (i == 0)
+        return kBK - 1;
+    const int a2 = (i - 1) / kBBlk, sa = (i - 1) % kBBlk;
+    return sa < kBBlk - 1 ? (kBBlk - 1) * a2 + sa : (kBBlk - 1) * kBTop + a2;
+}
+__device__ __forceinline__ int hindex(int kk)
+{
+    constexpr int kMain = (kBBlk - 1) * kBTop;  // 336
+    if (kk < kMain)
+        return 1 + kBBlk * (kk / (kBBlk - 1)) + kk % (kBBlk - 1);
+    if (kk < kMain + kBTop)
+        return 1 + kBBlk * (kk - kMain) + kBBlk - 1;
+    return kk == kBK - 1 ? 0 : -1;
+}
+// H_k[i][ip] (Paley's first construction, I + [[0, 1^T], [-1, Q]]); 0 for i < 0
+__device__ int hentry(const unsigned char *sq, int i, int ip)
+{
+    if (i < 0 || ip < 0)
+        return 0;
+    if (i == 0)
+        return 1;
+    if (ip == 0)
+        return -1;
+    if (i == ip)
+        return 1;
+    const int x = i - 1, y = ip - 1;
+    const int d0 = (x % 7 - y % 7 + 7) % 7;
+    const int d1 = ((x / 7) % 7 - (y / 7) % 7 + 7) % 7;
+    const int d2 = (x / 49 - y / 49 + 7) % 7;
+    return sq[d0 + 7 * d1 + 49 * d2] ? 1 : -1;
+}
+// the operand slot of chunk c against block b2 (see above), and a chunk and
+// block that use slot ix
+__device__ __forceinline__ constexpr int hslot(int c, int b2)
+{
+    return c == 10 ? 21 + b2
+                   : (c % 3 == 0 ? (2 * (c / 3) - b2 + 7) % 7
+                                 : (c % 3 == 1 ? 7 + (2 * (c / 3) - b2 + 7) % 7 : 14 + (2 * (c / 3) + 1 - b2 + 7) % 7));
+}
+__device__ __forceinline__ constexpr int hrep_c(int ix) { return ix >= 21 ? 10 : ix / 7; }
+__device__ __forceinline__ constexpr int hrep_b2(int ix)
+{
+    return ix >= 21 ? ix - 21 : (ix / 7 == 2 ? (1 - ix % 7 + 7) % 7 : (7 - ix % 7) % 7);
+}
+// output column of lane l16 in the helper's tile: column 48 of block l16
+// (l16 < 7), the extra point's column (l16 = 7), none (l16 > 7)
+__device__ __forceinline__ int hxcol(int l16)
+{
+    return l16 < kBTop ? kBBlk * l16 + kBBlk : (l16 == kBTop ? 0 : -1);
+}
+
+__device__ u32x4 hoperand(const unsigned char *sq, int c, int rg, int ip, uint32_t kOne)
+{
+    u32x4 r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int v = hentry(sq, hindex(32 * c + 8 * rg + 2 * p + h), ip);
+            const uint32_t bits = v == 0 ? 0u : (v > 0 ? kOne : (kOne | 0x8000u));
+            w |= bits << (16 * h);
+        }
+        r[p] = w;
+    }
+    return r;
+}
+
+// The operands every launch of paley343h_kernel uses, built once per GPU:
+// operand 28 w + ix (w < 3) is slot ix of product wave w, operand 84 + c the
+// helper's chunk c; [type][operand][lane], type 0 bf16, 1 f16.
+constexpr int kHOps = 3 * 28 + kHK / 32;
+__global__ __launch_bounds__(64) void paley343h_build(PaleyArgs a, u32x4 *tab)
+{
+    __shared__ unsigned char sq[kBK];
+    const int lane = threadIdx.x, l16 = lane & 15, rg = lane >> 4;
+    for (int t = lane; t < kBK; t += 64)
+        sq[t] = 0;
+    lds_barrier();
+    for (int t = lane + 1; t < kBK - 1; t += 64)
+        sq[gfp_square(t, a)] = 1;  // concurrent writes store the same 1
+    lds_barrier();
+    const int t = blockIdx.x;
+    const uint32_t one = blockIdx.y == 0 ? 0x3F80u : 0x3C00u;
+    u32x4 v;
+    if (t < 84) {
+        const int w = t / 28, ix = t % 28;
+        v = hoperand(sq, hrep_c(ix), rg, 1 + kBBlk * hrep_b2(ix) + 16 * w + l16, one);
+    } else {
+        v = hoperand(sq, t - 84, rg, hxcol(l16), one);
+    }
+    tab[((int)blockIdx.y * kHOps + t) * 64 + lane] = v;
+}
+
+template <int IN, int BITS>
+__global__ __launch_bounds__(kHThreads) __attribute__((amdgpu_waves_per_eu(kBOcc))) void paley343h_kernel(PaleyArgs a)
+{
+    constexpr int qmax = (1 << (BITS - 1)) - 1;
+    constexpr int n = kBK * kM2;
+    constexpr int kRowBytes = n * BITS / 8;
+    __shared__ __align__(16) uint16_t xt[hrow(31) + kHK];  // staged row [j][K-index]
+    __shared__ __align__(16) float ob[kBK * kHOS];        // rotated row [i'][j], fp32
+    __shared__ float red[kHW];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, rg = lane >> 4;
+    const int lb4 = (lane >> 4) & 1, lb5 = lane >> 5;
+    const int64_t G = gridDim.x;
+    int64_t row = blockIdx.x;
+
+    const u32x4 *hop = (const u32x4 *)a.hop;
+    // ---- once: zero the staged row (K-indices 344 .. 351 stay 0)
+    for (int t = tid; t < (hrow(31) + kHK) / 8; t += kHThreads)
+        ((u32x4 *)xt)[t] = (u32x4){0u, 0u, 0u, 0u};
+    lds_barrier();
+
+    if (wave < kHW - 1) {
+        // ================= product waves: columns sb = 16 wave + l16 of every block
+        const int sb = 16 * wave + l16;
+        u32x4 op[28];
+#pragma unroll
+        for (int ix = 0; ix < 28; ++ix)
+            op[ix] = hop[(28 * wave + ix) * 64 + lane];
+        lds_barrier();  // the first row is staged
+        for (; row - G < a.rows; row += G) {
+            const bool valid = row < a.rows;
+            f32x4 acc[kBTop][2];
+            if (valid) {
+#pragma unroll
+                for (int b2 = 0; b2 < kBTop; ++b2)
+                    acc[b2][0] = acc[b2][1] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int c = 0; c < kHK / 32; ++c) {
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) {
+                        const u32x4 av = *(const u32x4 *)&xt[hrow(16 * mt + l16) + 32 * c + 8 * rg];
+#pragma unroll
+                        for (int b2 = 0; b2 < kBTop; ++b2)
+                            acc[b2][mt] = mma<IN>(av, op[hslot(c, b2)], acc[b2][mt]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            lds_barrier();  // (1) the staged row is free; the helper has read the row buffer
+            if (valid) {
+                // 32-point butterflies over j = 16 mt + 4 rg + r, as in the
+                // forward kernel: a lane ends with the 16 outputs j = 16 lb4 +
+                // r + 4 s + 8 t of column 1 + 49 (2k + lb5) + sb (k < 3) and
+                // the 8 outputs j = 16 lb4 + 8 lb5 + r + 4 s of block 6
+#pragma unroll
+                for (int b2 = 0; b2 < kBTop; ++b2)
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) {
+                        const float a0 = acc[b2][mt][0] + acc[b2][mt][1], a1 = acc[b2][mt][0] - acc[b2][mt][1];
+                        const float a2_ = acc[b2][mt][2] + acc[b2][mt][3], a3 = acc[b2][mt][2] - acc[b2][mt][3];
+                        acc[b2][mt][0] = a0 + a2_;
+                        acc[b2][mt][2] = a0 - a2_;
+                        acc[b2][mt][1] = a1 + a3;
+                        acc[b2][mt][3] = a1 - a3;
+                    }
+#pragma unroll
+                for (int b2 = 0; b2 < kBTop; ++b2)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float lo = acc[b2][0][r], hi = acc[b2][1][r];  // bit 4
+                        const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo + hi),
+                                                                        __float_as_uint(lo - hi), false, false);  // bit 2
+                        const float x0 = __uint_as_float(w[0]), x1 = __uint_as_float(w[1]);
+                        acc[b2][0][r] = x0 + x1;
+                        acc[b2][1][r] = x0 - x1;
+                    }
+#pragma unroll
+                for (int k = 0; k < kBTop / 2; ++k)
+#pragma unroll
+                    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[2 * k][sl][r]),
+                                                                            __float_as_uint(acc[2 * k + 1][sl][r]),
+                                                                            false, false);  // bit 3
+                            const float x0 = __uint_as_float(w[0]), x1 = __uint_as_float(w[1]);
+                            acc[2 * k][sl][r] = x0 + x1;
+                            acc[2 * k + 1][sl][r] = x0 - x1;
+                        }
+                const float sgn32 = (lane & 32) ? -1.0f : 1.0f;
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[kBTop - 1][sl][r] = xbutterfly<32>(acc[kBTop - 1][sl][r], sgn32);
+                float mx = 0.0f;
+#pragma unroll
+                for (int b2 = 0; b2 < kBTop; ++b2)
+#pragma unroll
+                    for (int sl = 0; sl < 2; ++sl)
+                        mx = fmaxf(fmaxf(mx, fmaxf(fabsf(acc[b2][sl][0]), fabsf(acc[b2][sl][1]))),
+                                   fmaxf(fabsf(acc[b2][sl][2]), fabsf(acc[b2][sl][3])));
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1)
+                    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+                if (lane == 0)
+                    red[wave] = mx;
+#pragma unroll
+                for (int k = 0; k < kBTop / 2; ++k) {
+                    const int ip = 1 + kBBlk * (2 * k + lb5) + sb;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int sl = 0; sl < 2; ++sl)
+                            *(f32x4 *)&ob[ip * kHOS + 16 * lb4 + 8 * t + 4 * sl] = acc[2 * k + t][sl];
+                }
+                {
+                    const int ip = 1 + kBBlk * (kBTop - 1) + sb;
+#pragma unroll
+                    for (int sl = 0; sl < 2; ++sl)
+                        *(f32x4 *)&ob[ip * kHOS + 16 * lb4 + 8 * lb5 + 4 * sl] = acc[kBTop - 1][sl];
+                }
+            }
+            lds_barrier();  // (2) the row buffer holds this row; the next row is staged
+        }
+        return;
+    }
+
+    // ================= the helper wave
+    const int xcol = hxcol(l16);
+    u32x4 xo[kHK / 32];
+#pragma unroll
+    for (int c = 0; c < kHK / 32; ++c)
+        xo[c] = hop[(84 + c) * 64 + lane];
+    // signs of chunk q = 64 cc + lane (elements 8q .. 8q + 7: i = q / 4, j =
+    // 8 (q % 4) + e) as one word: element 2p's at bit 15 - 4p, 2p + 1's at
+    // bit 31 - 4p, so (w << 4p) & 0x80008000 is the sign mask of dword p
+    uint32_t neg[kHCPL];
+#pragma unroll
+    for (int cc = 0; cc < kHCPL; ++cc) {
+        const int q = 64 * cc + lane;
+        uint32_t m = 0;
+        if (q < kHChunks)
+            for (int e = 0; e < 8; ++e)
+                m |= (a.s[8 * q + e] < 0 ? 1u : 0u) << ((e & 1) ? 31 - 2 * (e - 1) : 15 - 2 * e);
+        neg[cc] = m;
+    }
+    // (no branch around the loads: past the last row the buffer has size 0)
+    u32x4 cur[kHCPL];
+    auto load_row = [&](int64_t r) {
+        const bool ok = r < a.rows;
+        const auto rs = rsrc((const uint16_t *)a.x + (ok ? r : 0) * n, ok ? 2 * n : 0);
+#pragma unroll
+        for (int cc = 0; cc < kHCPL; ++cc) {
+            const int q = 64 * cc + lane;
+            cur[cc] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rs, q < kHChunks ? 16 * q : 0x7FFFFFF0, 0, 0));
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int cc = 0; cc < kHCPL; ++cc) {
+            const int q = 64 * cc + lane;
+            if (q >= kHChunks)
+                continue;
+            uint16_t *dst = xt + hrow(8 * (q & 3)) + hkappa(q >> 2);  // rows 8 (q & 3) + e at dst + e kHRS
+            uint32_t ng = neg[cc];
+            asm volatile("" : "+v"(ng));
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t wv = __builtin_amdgcn_bitop3_b32(ng << (4 * p), cur[cc][p], 0x80008000u, 0x6C);
+                dst[2 * p * kHRS] = (uint16_t)wv;
+                dst[(2 * p + 1) * kHRS] = (uint16_t)(wv >> 16);
+            }
+        }
+    };
+    constexpr float kMagic = BITS == 4 ? 12582920.0f : 12583040.0f;
+    const float sgn16 = (lane & 16) ? -1.0f : 1.0f, sgn32 = (lane & 32) ? -1.0f : 1.0f;
+    if (row < a.rows) {
+        load_row(row);
+        stage();
+        load_row(row + G);
+    }
+    lds_barrier();  // the first row is staged
+    for (; row - G < a.rows; row += G) {
+        const bool valid = row < a.rows;
+        // ---- the helper's columns: two chains per j tile
+        f32x4 xa[2][2];
+        if (valid) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+                xa[mt][0] = xa[mt][1] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int c = 0; c < kHK / 32; ++c)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const u32x4 av = *(const u32x4 *)&xt[hrow(16 * mt + l16) + 32 * c + 8 * rg];
+                    xa[mt][c & 1] = mma<IN>(av, xo[c], xa[mt][c & 1]);
+                }
+        }
+        // ---- codes of the row before (none in the first pass: its buffers have size 0)
+        {
+            const bool have = row != (int64_t)blockIdx.x;
+            const int64_t pr = have ? row - G : 0;
+            const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+            const RowQuant rq = row_quant(m, a.kq, qmax);
+            const auto rc = rsrc((uint8_t *)a.codes + pr * (int64_t)kRowBytes, have ? kRowBytes : 0);
+#pragma unroll
+            for (int it = 0; it < (kBK + 63) / 64; ++it) {
+                const int ip = 64 * it + lane;
+                const int ipc = ip < kBK ? ip : kBK - 1;
+                float v[32];
+#pragma unroll
+                for (int qd = 0; qd < 8; ++qd) {
+                    const f32x4 w = *(const f32x4 *)&ob[ipc * kHOS + 4 * qd];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[4 * qd + r] = w[r];
+                }
+                if (wave_any_boost(rq)) {  // a row too small for qmax / max
+#pragma unroll
+                    for (int e = 0; e < 32; ++e)
+                        v[e] *= rq.boost;
+                }
+                uint32_t f[32];
+#pragma unroll
+                for (int e = 0; e < 32; ++e)
+                    f[e] = __float_as_uint(__builtin_fmaf(v[e], rq.inv, kMagic));
+                if constexpr (BITS == 4) {
+                    u32x4 w;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        uint32_t f8[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            f8[e] = f[8 * g + e];
+                        w[g] = fast::pack_int4(f8);
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b128(w, rc, ip < kBK ? 16 * ip : kDropOffset, 0, kNonTemporal);
+                } else {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        u32x4 w;
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+                            w[g] = fast::pack_int8(f[16 * hh + 4 * g], f[16 * hh + 4 * g + 1], f[16 * hh + 4 * g + 2],
+                                                   f[16 * hh + 4 * g + 3]);
+                        __builtin_amdgcn_raw_buffer_store_b128(w, rc, ip < kBK ? 32 * ip + 16 * hh : kDropOffset, 0,
+                                                               kNonTemporal);
+                    }
+                }
+            }
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rq.scale), rsrc((float *)a.scales + pr, have ? 4 : 0),
+                                                  lane == 0 ? 0 : kDropOffset, 0, 0);
+        }
+        lds_barrier();  // (1)
+        if (valid) {
+            // butterflies of the helper's columns (positions kept: lane (l16,
+            // rg), register (mt, r) holds output j = 16 mt + 4 rg + r)
+            f32x4 v[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+                v[mt] = xa[mt][0] + xa[mt][1];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const float a0 = v[mt][0] + v[mt][1], a1 = v[mt][0] - v[mt][1];
+                const float a2_ = v[mt][2] + v[mt][3], a3 = v[mt][2] - v[mt][3];
+                v[mt][0] = a0 + a2_;
+                v[mt][2] = a0 - a2_;
+                v[mt][1] = a1 + a3;
+                v[mt][3] = a1 - a3;
+            }
+            float mx = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float lo = v[0][r], hi = v[1][r];
+                v[0][r] = xbutterfly<32>(xbutterfly<16>(lo + hi, sgn16), sgn32);
+                v[1][r] = xbutterfly<32>(xbutterfly<16>(lo - hi, sgn16), sgn32);
+                mx = fmaxf(mx, fmaxf(fabsf(v[0][r]), fabsf(v[1][r])));
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1)
+                mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            if (lane == 0)
+                red[kHW - 1] = mx;
+            if (xcol >= 0) {
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    *(f32x4 *)&ob[xcol * kHOS + 16 * mt + 4 * rg] = v[mt];
+            }
+        }
+        if (row + G < a.rows)  // the next row (loaded one row ago) into the staged layout
+            stage();
+        load_row(row + 2 * G);
+        lds_barrier();  // (2)
+    }
+}
+
 // Inverse for k = 344: y = scale * (q . H_n^T) / sqrt(n), then the signs.
 // The codes are integers, exact in f16, and one scale per row commutes with
 // the transform, so the codes go onto the matrix core as they are, with the
@@ -1175,6 +1624,47 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
     }
 }
 
+// The operand table of paley343h_kernel: a file-scope device array, one copy
+// per GPU; kernels get the address hipGetSymbolAddress returns for the
+// current device.  It is built on the first k = 344 forward call on a GPU by
+// one small launch, which that call waits for (the one blocking step of the
+// path); every later call only reads it.
+static __device__ __align__(256) u32x4 hop_table[2 * kHOps * 64];
+constexpr int kMaxHopDevices = 64;
+struct HopSlot {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+    u32x4 *ptr = nullptr;
+};
+HopSlot g_hop[kMaxHopDevices];
+
+hipError_t paley343h_table(const PaleyArgs &pa, const u32x4 **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxHopDevices)
+        return hipErrorInvalidDevice;
+    HopSlot &slot = g_hop[dev];
+    std::call_once(slot.once, [&]() {
+        void *p = nullptr;
+        slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(hop_table));
+        if (slot.err != hipSuccess)
+            return;
+        hipLaunchKernelGGL(paley343h_build, dim3(kHOps, 2), dim3(64), 0, 0, pa, (u32x4 *)p);
+        slot.err = hipGetLastError();
+        if (slot.err == hipSuccess)
+            slot.err = hipDeviceSynchronize();
+        if (slot.err == hipSuccess)
+            slot.ptr = (u32x4 *)p;
+    });
+    if (slot.err != hipSuccess)
+        return slot.err;
+    *out = slot.ptr;
+    return hipSuccess;
+}
+
 }  // namespace
 
 bool paley_mfma_available(const Request &r)
@@ -1241,18 +1731,23 @@ hipError_t launch_paley_mfma(const Request &r, const DeviceInfo &dev)
         return hipGetLastError();
     }
     if (r.paley.k == kBK && r.paley.p == 7 && r.paley.e == 3) {
+        const u32x4 *tab = nullptr;
+        const hipError_t te = paley343h_table(pa, &tab);
+        if (te != hipSuccess)
+            return te;
+        pa.hop = tab + (r.x_dtype == kBF16 ? 0 : kHOps * 64);
         const int64_t g3 = kBOcc * (int64_t)dev.cu_count;
         const int64_t grid3 = r.rows < g3 ? r.rows : g3;
         if (r.x_dtype == kBF16) {
             if (r.bits == 4)
-                hipLaunchKernelGGL((paley343_kernel<kBF16, 4>), dim3((unsigned)grid3), dim3(kBThreads), 0, r.stream, pa);
+                hipLaunchKernelGGL((paley343h_kernel<kBF16, 4>), dim3((unsigned)grid3), dim3(kHThreads), 0, r.stream, pa);
             else
-                hipLaunchKernelGGL((paley343_kernel<kBF16, 8>), dim3((unsigned)grid3), dim3(kBThreads), 0, r.stream, pa);
+                hipLaunchKernelGGL((paley343h_kernel<kBF16, 8>), dim3((unsigned)grid3), dim3(kHThreads), 0, r.stream, pa);
         } else {
             if (r.bits == 4)
-                hipLaunchKernelGGL((paley343_kernel<kF16, 4>), dim3((unsigned)grid3), dim3(kBThreads), 0, r.stream, pa);
+                hipLaunchKernelGGL((paley343h_kernel<kF16, 4>), dim3((unsigned)grid3), dim3(kHThreads), 0, r.stream, pa);
             else
-                hipLaunchKernelGGL((paley343_kernel<kF16, 8>), dim3((unsigned)grid3), dim3(kBThreads), 0, r.stream, pa);
+                hipLaunchKernelGGL((paley343h_kernel<kF16, 8>), dim3((unsigned)grid3), dim3(kHThreads), 0, r.stream, pa);
         }
         return hipGetLastError();
     }
