@@ -853,8 +853,6 @@ constexpr int kHThreads = 64 * kHW;
 constexpr int kHK = 352;                     // K-indices: 11 chunks of 32
 constexpr int kHRS = 376;                    // staged row stride (188 dwords, 28 mod 32)
 constexpr int kHOS = 36;                     // LDS row buffer: floats per output column
-constexpr int kHChunks = kBK * kM2 / 8;      // 16-byte chunks of a row (1376)
-constexpr int kHCPL = (kHChunks + 63) / 64;  // chunks per helper lane (22)
 // Staged row j starts at element hrow(j).  As in the forward kernel, the
 // stride keeps the operand reads of 8 consecutive rows in distinct banks and
 // the shift of 16 elements per group of 8 rows separates the four rows one
@@ -916,6 +914,21 @@ __device__ __forceinline__ int hxcol(int l16)
     return l16 < kBTop ? kBBlk * l16 + kBBlk : (l16 == kBTop ? 0 : -1);
 }
 
+// maximum of a non-negative value over the wave, in every lane (DPP within
+// rows of 16 lanes, then the two permlane swaps)
+__device__ __forceinline__ float wave_max_nonneg(float m)
+{
+    uint32_t v = __float_as_uint(m);
+    v = fast::dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = fast::dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = fast::dpp_max<0x141>(v);  // row_half_mirror
+    v = fast::dpp_max<0x140>(v);  // row_mirror
+    const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = r16[0] > r16[1] ? r16[0] : r16[1];
+    const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(r32[0] > r32[1] ? r32[0] : r32[1]);
+}
+
 __device__ u32x4 hoperand(const unsigned char *sq, int c, int rg, int ip, uint32_t kOne)
 {
     u32x4 r;
@@ -965,6 +978,7 @@ __global__ __launch_bounds__(kHThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
     constexpr int qmax = (1 << (BITS - 1)) - 1;
     constexpr int n = kBK * kM2;
     constexpr int kRowBytes = n * BITS / 8;
+    constexpr float kMagic = BITS == 4 ? 12582920.0f : 12583040.0f;
     __shared__ __align__(16) uint16_t xt[hrow(31) + kHK];  // staged row [j][K-index]
     __shared__ __align__(16) float ob[kBK * kHOS];        // rotated row [i'][j], fp32
     __shared__ float red[kHW];
@@ -994,23 +1008,81 @@ __global__ __launch_bounds__(kHThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
         for (; row - G < a.rows; row += G) {
             const bool valid = row < a.rows;
             f32x4 acc[kBTop][2];
+            // ---- the codes of output columns 64 wave .. 64 wave + 63 of the
+            // row before (none in the first pass: its buffers have size 0),
+            // eight values at a time between the products of this row
+            const bool have = row != (int64_t)blockIdx.x;
+            const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+            const RowQuant rq = row_quant(m, a.kq, qmax);
+            const auto rc = rsrc((uint8_t *)a.codes + (have ? row - G : 0) * (int64_t)kRowBytes, have ? kRowBytes : 0);
+            const int qip = 64 * wave + lane;
+            uint32_t qw[BITS == 4 ? 4 : 8];
+            // (the magnification of tiny rows is a product by 1 for the others:
+            // no branch among the products)
+            auto qgroup = [&](int g) {
+                const f32x4 w0 = *(const f32x4 *)&ob[qip * kHOS + 8 * g];
+                const f32x4 w1 = *(const f32x4 *)&ob[qip * kHOS + 8 * g + 4];
+                float v[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[e] *= rq.boost;
+                uint32_t f[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    f[e] = __float_as_uint(__builtin_fmaf(v[e], rq.inv, kMagic));
+                if constexpr (BITS == 4) {
+                    qw[g] = fast::pack_int4(f);
+                } else {
+                    qw[2 * g] = fast::pack_int8(f[0], f[1], f[2], f[3]);
+                    qw[2 * g + 1] = fast::pack_int8(f[4], f[5], f[6], f[7]);
+                }
+            };
+            auto qstore = [&]() {
+                if constexpr (BITS == 4) {
+                    __builtin_amdgcn_raw_buffer_store_b128((u32x4){qw[0], qw[1], qw[2], qw[3]}, rc, 16 * qip, 0,
+                                                           kNonTemporal);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b128((u32x4){qw[0], qw[1], qw[2], qw[3]}, rc, 32 * qip, 0,
+                                                           kNonTemporal);
+                    __builtin_amdgcn_raw_buffer_store_b128((u32x4){qw[4], qw[5], qw[6], qw[7]}, rc, 32 * qip + 16,
+                                                           0, kNonTemporal);
+                }
+            };
             if (valid) {
 #pragma unroll
                 for (int b2 = 0; b2 < kBTop; ++b2)
                     acc[b2][0] = acc[b2][1] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+                // the operands of chunk c + 1 are read while chunk c multiplies
+                u32x4 av[2][2];
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    av[0][mt] = *(const u32x4 *)&xt[hrow(16 * mt + l16) + 8 * rg];
 #pragma unroll
                 for (int c = 0; c < kHK / 32; ++c) {
+                    if (c + 1 < kHK / 32) {
 #pragma unroll
-                    for (int mt = 0; mt < 2; ++mt) {
-                        const u32x4 av = *(const u32x4 *)&xt[hrow(16 * mt + l16) + 32 * c + 8 * rg];
+                        for (int mt = 0; mt < 2; ++mt)
+                            av[(c + 1) & 1][mt] = *(const u32x4 *)&xt[hrow(16 * mt + l16) + 32 * (c + 1) + 8 * rg];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);  // (the reads go out before the products)
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                         for (int b2 = 0; b2 < kBTop; ++b2)
-                            acc[b2][mt] = mma<IN>(av, op[hslot(c, b2)], acc[b2][mt]);
-                    }
+                            acc[b2][mt] = mma<IN>(av[c & 1][mt], op[hslot(c, b2)], acc[b2][mt]);
+                    if (c < 4)
+                        qgroup(c);
+                    if (c == 3)
+                        qstore();
                     __builtin_amdgcn_sched_barrier(0);
                 }
+            } else {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    qgroup(g);
+                qstore();
             }
-            lds_barrier();  // (1) the staged row is free; the helper has read the row buffer
+            lds_barrier();  // (1) the staged row is free; the row buffer has been read
             if (valid) {
                 // 32-point butterflies over j = 16 mt + 4 rg + r, as in the
                 // forward kernel: a lane ends with the 16 outputs j = 16 lb4 +
@@ -1027,17 +1099,34 @@ __global__ __launch_bounds__(kHThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
                         acc[b2][mt][1] = a1 + a3;
                         acc[b2][mt][3] = a1 - a3;
                     }
+                // (each stage over all blocks before the next: the swaps then
+                // find their inputs computed long before)
+                uint32_t sw[kBTop][4][2];
 #pragma unroll
                 for (int b2 = 0; b2 < kBTop; ++b2)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float lo = acc[b2][0][r], hi = acc[b2][1][r];  // bit 4
-                        const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo + hi),
-                                                                        __float_as_uint(lo - hi), false, false);  // bit 2
-                        const float x0 = __uint_as_float(w[0]), x1 = __uint_as_float(w[1]);
+                        sw[b2][r][0] = __float_as_uint(lo + hi);
+                        sw[b2][r][1] = __float_as_uint(lo - hi);
+                    }
+#pragma unroll
+                for (int b2 = 0; b2 < kBTop; ++b2)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const auto w = __builtin_amdgcn_permlane16_swap(sw[b2][r][0], sw[b2][r][1], false, false);
+                        sw[b2][r][0] = w[0];
+                        sw[b2][r][1] = w[1];
+                    }
+#pragma unroll
+                for (int b2 = 0; b2 < kBTop; ++b2)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {  // bit 2
+                        const float x0 = __uint_as_float(sw[b2][r][0]), x1 = __uint_as_float(sw[b2][r][1]);
                         acc[b2][0][r] = x0 + x1;
                         acc[b2][1][r] = x0 - x1;
                     }
+                uint32_t tw[kBTop / 2][2][4][2];
 #pragma unroll
                 for (int k = 0; k < kBTop / 2; ++k)
 #pragma unroll
@@ -1046,10 +1135,9 @@ __global__ __launch_bounds__(kHThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
                         for (int r = 0; r < 4; ++r) {
                             const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[2 * k][sl][r]),
                                                                             __float_as_uint(acc[2 * k + 1][sl][r]),
-                                                                            false, false);  // bit 3
-                            const float x0 = __uint_as_float(w[0]), x1 = __uint_as_float(w[1]);
-                            acc[2 * k][sl][r] = x0 + x1;
-                            acc[2 * k + 1][sl][r] = x0 - x1;
+                                                                            false, false);
+                            tw[k][sl][r][0] = w[0];
+                            tw[k][sl][r][1] = w[1];
                         }
                 const float sgn32 = (lane & 32) ? -1.0f : 1.0f;
 #pragma unroll
@@ -1057,16 +1145,25 @@ __global__ __launch_bounds__(kHThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         acc[kBTop - 1][sl][r] = xbutterfly<32>(acc[kBTop - 1][sl][r], sgn32);
+#pragma unroll
+                for (int k = 0; k < kBTop / 2; ++k)
+#pragma unroll
+                    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {  // bit 3
+                            const float x0 = __uint_as_float(tw[k][sl][r][0]), x1 = __uint_as_float(tw[k][sl][r][1]);
+                            acc[2 * k][sl][r] = x0 + x1;
+                            acc[2 * k + 1][sl][r] = x0 - x1;
+                        }
                 float mx = 0.0f;
 #pragma unroll
                 for (int b2 = 0; b2 < kBTop; ++b2)
 #pragma unroll
                     for (int sl = 0; sl < 2; ++sl)
-                        mx = fmaxf(fmaxf(mx, fmaxf(fabsf(acc[b2][sl][0]), fabsf(acc[b2][sl][1]))),
-                                   fmaxf(fabsf(acc[b2][sl][2]), fabsf(acc[b2][sl][3])));
 #pragma unroll
-                for (int off = 32; off > 0; off >>= 1)
-                    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+                        for (int r = 0; r < 4; r += 2)
+                            mx = fmaxf(fmaxf(mx, fabsf(acc[b2][sl][r])), fabsf(acc[b2][sl][r + 1]));
+                mx = wave_max_nonneg(mx);
                 if (lane == 0)
                     red[wave] = mx;
 #pragma unroll
@@ -1096,53 +1193,103 @@ __global__ __launch_bounds__(kHThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
 #pragma unroll
     for (int c = 0; c < kHK / 32; ++c)
         xo[c] = hop[(84 + c) * 64 + lane];
-    // signs of chunk q = 64 cc + lane (elements 8q .. 8q + 7: i = q / 4, j =
-    // 8 (q % 4) + e) as one word: element 2p's at bit 15 - 4p, 2p + 1's at
-    // bit 31 - 4p, so (w << 4p) & 0x80008000 is the sign mask of dword p
-    uint32_t neg[kHCPL];
+    // Staging.  Unit U = 64 u + lane is the K-indices 4 G .. 4 G + 3 (G = U /
+    // 4) against j = 8 h .. 8 h + 7 (h = U % 4): four 16-byte loads (the
+    // rows i of the four K-indices), the signs, and a transpose in registers
+    // into eight 8-byte LDS stores (four consecutive K-indices of one row j).
+    // Within a block consecutive K-indices are consecutive rows i, so units
+    // 0 .. 319 read rows i(4G) + t; the last lane group also holds G = 84,
+    // 85 (the slots 48 and the extra point) and the 24 units past 343.
+    constexpr int kHU = kBK;                // units: 86 groups of 4 K-indices x 4 groups of 8 j
+    constexpr int kHUPL = (kHU + 63) / 64;  // 6 per lane
+    int ubase[kHUPL - 1], ulast[4];
+    uint32_t usg[kHUPL];  // signs: bits 15 - k and 31 - k for dword k = 4 t + q
+    {
+        // the unit's 8 signs of each row as one 8-byte load (all issued
+        // before any is used); sign e of a row is bit 7 of its byte
+        const auto rsg = rsrc(a.s, n);
+        u32x2 sw[kHUPL][4];
 #pragma unroll
-    for (int cc = 0; cc < kHCPL; ++cc) {
-        const int q = 64 * cc + lane;
-        uint32_t m = 0;
-        if (q < kHChunks)
-            for (int e = 0; e < 8; ++e)
-                m |= (a.s[8 * q + e] < 0 ? 1u : 0u) << ((e & 1) ? 31 - 2 * (e - 1) : 15 - 2 * e);
-        neg[cc] = m;
+        for (int u = 0; u < kHUPL; ++u) {
+            const int U = 64 * u + lane, Gq = U >> 2, h = U & 3;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int i = U < kHU ? hindex(4 * Gq + t) : -1;
+                const int off = i < 0 ? 0x7FFFFFF0 : 64 * i + 16 * h;
+                if (u < kHUPL - 1) {
+                    if (t == 0)
+                        ubase[u] = off;
+                } else {
+                    ulast[t] = off;
+                }
+                sw[u][t] = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsg, i < 0 ? 0x7FFFFFF0 : i * kM2 + 8 * h, 0, 0));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kHUPL; ++u) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    const int k = 4 * t + (b >> 1);
+                    const uint32_t bit = (sw[u][t][b >> 2] >> (8 * (b & 3) + 7)) & 1u;
+                    m |= bit << ((b & 1) ? 31 - k : 15 - k);
+                }
+            usg[u] = m;
+        }
     }
+    const int uwr = hrow(8 * (lane & 3)) + 4 * (lane >> 2);  // unit 0's first store (elements)
     // (no branch around the loads: past the last row the buffer has size 0)
-    u32x4 cur[kHCPL];
+    u32x4 cur[kHUPL][4];
     auto load_row = [&](int64_t r) {
         const bool ok = r < a.rows;
         const auto rs = rsrc((const uint16_t *)a.x + (ok ? r : 0) * n, ok ? 2 * n : 0);
 #pragma unroll
-        for (int cc = 0; cc < kHCPL; ++cc) {
-            const int q = 64 * cc + lane;
-            cur[cc] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    rs, q < kHChunks ? 16 * q : 0x7FFFFFF0, 0, 0));
-        }
+        for (int u = 0; u < kHUPL; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                cur[u][t] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, u < kHUPL - 1 ? ubase[u] : ulast[t],
+                                                                 u < kHUPL - 1 ? 64 * t : 0, 0));
     };
-    auto stage = [&]() {
+    // signs and transpose, in place: afterwards dwords 2v, 2v + 1 of a unit
+    // (cur[u][v / 2][2 (v % 2)] ..) are row j = 8h + v at K-indices 4G .. 4G + 3
+    auto prep = [&]() {
 #pragma unroll
-        for (int cc = 0; cc < kHCPL; ++cc) {
-            const int q = 64 * cc + lane;
-            if (q >= kHChunks)
-                continue;
-            uint16_t *dst = xt + hrow(8 * (q & 3)) + hkappa(q >> 2);  // rows 8 (q & 3) + e at dst + e kHRS
-            uint32_t ng = neg[cc];
-            asm volatile("" : "+v"(ng));
+        for (int u = 0; u < kHUPL; ++u) {
+            uint32_t d[16], o[16];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const uint32_t wv = __builtin_amdgcn_bitop3_b32(ng << (4 * p), cur[cc][p], 0x80008000u, 0x6C);
-                dst[2 * p * kHRS] = (uint16_t)wv;
-                dst[(2 * p + 1) * kHRS] = (uint16_t)(wv >> 16);
+            for (int k = 0; k < 16; ++k)
+                d[k] = __builtin_amdgcn_bitop3_b32(usg[u] << k, cur[u][k >> 2][k & 3], 0x80008000u, 0x6C);
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const uint32_t sel = (v & 1) ? 0x07060302u : 0x05040100u;
+                o[2 * v] = __builtin_amdgcn_perm(d[4 + (v >> 1)], d[v >> 1], sel);
+                o[2 * v + 1] = __builtin_amdgcn_perm(d[12 + (v >> 1)], d[8 + (v >> 1)], sel);
             }
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                cur[u][k >> 2][k & 3] = o[k];
         }
     };
-    constexpr float kMagic = BITS == 4 ? 12582920.0f : 12583040.0f;
+    auto put = [&]() {
+#pragma unroll
+        for (int u = 0; u < kHUPL; ++u) {
+            if (u == kHUPL - 1 && 64 * u + lane >= kHU)
+                continue;
+#pragma unroll
+            for (int v = 0; v < 8; ++v)
+                *(u32x2 *)&xt[uwr + 64 * u + v * kHRS] =
+                    (u32x2){cur[u][v >> 1][2 * (v & 1)], cur[u][v >> 1][2 * (v & 1) + 1]};
+        }
+    };
     const float sgn16 = (lane & 16) ? -1.0f : 1.0f, sgn32 = (lane & 32) ? -1.0f : 1.0f;
     if (row < a.rows) {
         load_row(row);
-        stage();
+        prep();
+        put();
         load_row(row + G);
     }
     lds_barrier();  // the first row is staged
@@ -1170,7 +1317,7 @@ __global__ __launch_bounds__(kHThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
             const RowQuant rq = row_quant(m, a.kq, qmax);
             const auto rc = rsrc((uint8_t *)a.codes + pr * (int64_t)kRowBytes, have ? kRowBytes : 0);
 #pragma unroll
-            for (int it = 0; it < (kBK + 63) / 64; ++it) {
+            for (int it = kHW - 1; it < (kBK + 63) / 64; ++it) {  // (the product waves take 0 .. 2)
                 const int ip = 64 * it + lane;
                 const int ipc = ip < kBK ? ip : kBK - 1;
                 float v[32];
@@ -1217,6 +1364,8 @@ __global__ __launch_bounds__(kHThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rq.scale), rsrc((float *)a.scales + pr, have ? 4 : 0),
                                                   lane == 0 ? 0 : kDropOffset, 0, 0);
         }
+        if (row + G < a.rows)  // the next row (loaded one row ago): signs and transpose
+            prep();
         lds_barrier();  // (1)
         if (valid) {
             // butterflies of the helper's columns (positions kept: lane (l16,
@@ -1242,9 +1391,7 @@ __global__ __launch_bounds__(kHThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
                 v[1][r] = xbutterfly<32>(xbutterfly<16>(lo - hi, sgn16), sgn32);
                 mx = fmaxf(mx, fmaxf(fabsf(v[0][r]), fabsf(v[1][r])));
             }
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1)
-                mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            mx = wave_max_nonneg(mx);
             if (lane == 0)
                 red[kHW - 1] = mx;
             if (xcol >= 0) {
@@ -1253,8 +1400,8 @@ __global__ __launch_bounds__(kHThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
                     *(f32x4 *)&ob[xcol * kHOS + 16 * mt + 4 * rg] = v[mt];
             }
         }
-        if (row + G < a.rows)  // the next row (loaded one row ago) into the staged layout
-            stage();
+        if (row + G < a.rows)  // the next row into the staged layout
+            put();
         load_row(row + 2 * G);
         lds_barrier();  // (2)
     }
