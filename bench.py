@@ -112,9 +112,10 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_bytes: int
     fetch = _counter_means(fetch_csv, "FETCH_SIZE")
     write = _counter_means(write_csv, "WRITE_SIZE")
     copy_key = max((k for k in fetch if "copyBuffer" in k[0]), key=lambda k: fetch[k][1])
-    # the timed launch: the first library kernel the script dispatches (the
-    # extras, inverse, append and attention, come after it)
-    kern_key = min((k for k in fetch if "hq::" in k[0]), key=lambda k: fetch[k][2])
+    # the timed launch: the first library kernel the script dispatches more
+    # than once (the extras, inverse, append and attention, come after it;
+    # a once-per-GPU set-up launch, such as the Paley operand table, before)
+    kern_key = min((k for k in fetch if "hq::" in k[0] and fetch[k][1] > 1), key=lambda k: fetch[k][2])
     f_scale = copy_bytes / (fetch[copy_key][0] * 1024.0)
     w_scale = copy_bytes / (write[copy_key][0] * 1024.0)
     fb = fetch[kern_key][0] * 1024.0 * f_scale
@@ -128,7 +129,7 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_bytes: int
         rd = _counter_means(tcc_db, "TCC_EA0_RDREQ_sum")
         r32 = _counter_means(tcc_db, "TCC_EA0_RDREQ_32B_sum")
         bub = _counter_means(tcc_db, "TCC_BUBBLE_sum")
-        kk = min((k for k in rd if "hq::" in k[0]), key=lambda k: rd[k][2])
+        kk = min((k for k in rd if "hq::" in k[0] and rd[k][1] > 1), key=lambda k: rd[k][2])
         n_rd, n32 = rd[kk][0], r32[kk][0]
         req_read = (n_rd - n32) * 128.0 + n32 * 32.0
         req = {"read_requests": n_rd, "read_requests_32B": n32, "bubble": bub[kk][0],

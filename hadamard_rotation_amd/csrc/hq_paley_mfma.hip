@@ -1,9 +1,11 @@
 // hq_paley_mfma.hip -- matrix-core kernels for the full-width rotation of
 // rows whose width is not a power of two: n = k * 32, H_n = H_k (x) H_32 with
 // H_k from Paley's first construction, fused with the per-row quantiser.
-// paley343_kernel takes k = 344 (the FFN width 11008, GF(7^3)) from the
-// block structure of H_344 (see its own comment); paley_mfma_kernel takes
-// the other orders in (320, 352] as one dense product.
+// For k = 344 (the FFN width 11008, GF(7^3)) paley343h_kernel quantises
+// (three product waves and a helper wave, see its own comment),
+// paley343_kernel rotates only and paley343_inv_kernel inverts, both from the
+// block structure of H_344; paley_mfma_kernel takes the other orders in
+// (320, 352] as one dense product.
 //
 // Pages cited: [RQ] "旋转量化：大模型低比特量化中的离群值克星" section 2.1 (larger
 // Hadamard matrices as Kronecker products; the transform is additions and
@@ -484,17 +486,13 @@ __device__ int block_entry(const unsigned char *sq, int d, int sa, int sb)
     return 0;
 }
 
-// ROT: rotation only (hq_rotate): the rotated row y / sqrt(n) in fp32 to
-// a.y instead of codes, no maximum and no quantiser
-template <int IN, int BITS, bool ROT = false>
+// Rotation only (hq_rotate): the rotated row y / sqrt(n) in fp32 to a.y
+template <int IN>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc))) void paley343_kernel(PaleyArgs a)
 {
-    constexpr int qmax = (1 << (BITS - 1)) - 1;
     constexpr int n = kBK * kM2;
     __shared__ __align__(16) uint16_t xt[kM2 * kBRSF];            // [j][a2][slot] from frow(j)
-    __shared__ __align__(16) uint32_t cst[n * BITS / 32];         // the row's codes
     __shared__ unsigned char sq[kBK];
-    __shared__ float red[kBW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -632,7 +630,6 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
         // So for k < 3 a lane ends with the 16 outputs j = 16 (lane bit 4) +
         // r + 4 s + 8 t of row 1 + 49 (2k + lane bit 5) + sb, and with the 8
         // outputs j = 16 (lane bit 4) + 8 (lane bit 5) + r + 4 s of block 6.
-        float mx = 0.0f;
 #pragma unroll
         for (int b2 = 0; b2 < kBTop; ++b2)
 #pragma unroll
@@ -673,146 +670,52 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBOcc
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 acc[kBTop - 1][sl][r] = xbutterfly<32>(acc[kBTop - 1][sl][r], sgn32);
-        if constexpr (ROT) {
-            lds_barrier();  // every wave is done with the staged row
-            if (row + gridDim.x < a.rows)  // the next row (loaded one row ago) into the staged layout
-                stage();
-            load_row(row + 2 * gridDim.x);
-            // y / sqrt(n): 16 (block 6: 8) consecutive outputs per lane
-            const auto ry = rsrc((uint8_t *)a.y + row * (int64_t)(n * 4), n * 4);
-            const int lb4r = (lane >> 4) & 1, lb5r = lane >> 5;
-            // (every lane issues every store, those with nothing to store at
-            // an offset past the buffer, which drops them: no branch, so the
-            // next row's loads wait for loads only)
-            auto st8 = [&](bool ok, int e0, const float (&o)[8]) {
-                const int off = ok ? 4 * e0 : kDropOffset;
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    (u32x4){__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])},
-                    ry, off, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    (u32x4){__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])},
-                    ry, off + 16, 0, 0);
-            };
+        lds_barrier();  // every wave is done with the staged row
+        if (row + gridDim.x < a.rows)  // the next row (loaded one row ago) into the staged layout
+            stage();
+        load_row(row + 2 * gridDim.x);
+        // y / sqrt(n): 16 (block 6: 8) consecutive outputs per lane
+        const auto ry = rsrc((uint8_t *)a.y + row * (int64_t)(n * 4), n * 4);
+        const int lb4r = (lane >> 4) & 1, lb5r = lane >> 5;
+        // (every lane issues every store, those with nothing to store at
+        // an offset past the buffer, which drops them: no branch, so the
+        // next row's loads wait for loads only)
+        auto st8 = [&](bool ok, int e0, const float (&o)[8]) {
+            const int off = ok ? 4 * e0 : kDropOffset;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                (u32x4){__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])},
+                ry, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                (u32x4){__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])},
+                ry, off + 16, 0, 0);
+        };
 #pragma unroll
-            for (int k = 0; k < kBTop / 2; ++k) {
-                const int b2 = 2 * k + lb5r;
-                const bool ok = sb < kBBlk || (sb == kBBlk && b2 == 0);
-                const int ip = sb >= kBBlk ? 0 : 1 + kBBlk * b2 + sb;
+        for (int k = 0; k < kBTop / 2; ++k) {
+            const int b2 = 2 * k + lb5r;
+            const bool ok = sb < kBBlk || (sb == kBBlk && b2 == 0);
+            const int ip = sb >= kBBlk ? 0 : 1 + kBBlk * b2 + sb;
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    float o[8];
-#pragma unroll
-                    for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            o[4 * sl + r] = acc[2 * k + t][sl][r] * a.rb;
-                    st8(ok, ip * kM2 + 16 * lb4r + 8 * t, o);
-                }
-            }
-            {
-                const int ip = 1 + kBBlk * (kBTop - 1) + (sb < kBBlk ? sb : 0);
+            for (int t = 0; t < 2; ++t) {
                 float o[8];
 #pragma unroll
                 for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        o[4 * sl + r] = acc[kBTop - 1][sl][r] * a.rb;
-                st8(sb < kBBlk, ip * kM2 + 16 * lb4r + 8 * lb5r, o);
-            }
-            lds_barrier();  // the next row is staged
-            continue;
-        }
-        // padding columns are 0 and the copies of Z[0] repeat it: neither
-        // changes the maximum
-#pragma unroll
-        for (int b2 = 0; b2 < kBTop; ++b2)
-#pragma unroll
-            for (int sl = 0; sl < 2; ++sl)
-                mx = fmaxf(fmaxf(mx, fmaxf(fabsf(acc[b2][sl][0]), fabsf(acc[b2][sl][1]))),
-                           fmaxf(fabsf(acc[b2][sl][2]), fabsf(acc[b2][sl][3])));
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-            mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-        if (lane == 0)
-            red[wave] = mx;
-        lds_barrier();  // every wave is done with the staged row and its maximum is in
-        float m = red[0];
-#pragma unroll
-        for (int w = 1; w < kBW; ++w)
-            m = fmaxf(m, red[w]);
-        const RowQuant rq = row_quant(m, a.kq, qmax);
-        if (rq.boost != 1.0f) {  // workgroup-uniform: a row too small for qmax / max
-#pragma unroll
-            for (int b2 = 0; b2 < kBTop; ++b2)
-#pragma unroll
-                for (int sl = 0; sl < 2; ++sl)
-                    acc[b2][sl] *= rq.boost;
-        }
-
-        // ---- codes into LDS.  |y| <= m and inv is qmax / m to within an ulp,
-        // so |y * inv| < qmax + 1/2 and the codes need no clamp; the fma's
-        // constant is 1.5 * 2^23 plus the offset the packers expect.
-        constexpr float kMagic = BITS == 4 ? 12582920.0f : 12583040.0f;
-        auto fcode = [&](float v) { return __float_as_uint(__builtin_fmaf(v, rq.inv, kMagic)); };
-        const int lb4 = (lane >> 4) & 1, lb5 = lane >> 5;
-#pragma unroll
-        for (int k = 0; k < kBTop / 2; ++k) {
-            const int b2 = 2 * k + lb5;
-            if (sb > kBBlk || (sb == kBBlk && b2 > 0))
-                continue;
-            const int ip = sb == kBBlk ? 0 : 1 + kBBlk * b2 + sb;
-            const int e0 = ip * kM2 + 16 * lb4;  // the first of 16 consecutive outputs
-            uint32_t f[2][8];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        f[t][4 * sl + r] = fcode(acc[2 * k + t][sl][r]);
-            if constexpr (BITS == 4) {
-                *(u32x2 *)((uint8_t *)cst + (e0 >> 1)) = (u32x2){fast::pack_int4(f[0]), fast::pack_int4(f[1])};
-            } else {
-                *(u32x4 *)((uint8_t *)cst + e0) =
-                    (u32x4){fast::pack_int8(f[0][0], f[0][1], f[0][2], f[0][3]),
-                            fast::pack_int8(f[0][4], f[0][5], f[0][6], f[0][7]),
-                            fast::pack_int8(f[1][0], f[1][1], f[1][2], f[1][3]),
-                            fast::pack_int8(f[1][4], f[1][5], f[1][6], f[1][7])};
+                        o[4 * sl + r] = acc[2 * k + t][sl][r] * a.rb;
+                st8(ok, ip * kM2 + 16 * lb4r + 8 * t, o);
             }
         }
-        if (sb < kBBlk) {  // block 6
-            const int ip = 1 + kBBlk * (kBTop - 1) + sb;
-            const int e0 = ip * kM2 + 16 * lb4 + 8 * lb5;  // the first of 8 consecutive outputs
-            uint32_t f[8];
+        {
+            const int ip = 1 + kBBlk * (kBTop - 1) + (sb < kBBlk ? sb : 0);
+            float o[8];
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    f[4 * sl + r] = fcode(acc[kBTop - 1][sl][r]);
-            if constexpr (BITS == 4)
-                *(uint32_t *)((uint8_t *)cst + (e0 >> 1)) = fast::pack_int4(f);
-            else
-                *(u32x2 *)((uint8_t *)cst + e0) =
-                    (u32x2){fast::pack_int8(f[0], f[1], f[2], f[3]), fast::pack_int8(f[4], f[5], f[6], f[7])};
+                    o[4 * sl + r] = acc[kBTop - 1][sl][r] * a.rb;
+            st8(sb < kBBlk, ip * kM2 + 16 * lb4r + 8 * lb5r, o);
         }
-        if (row + gridDim.x < a.rows)  // the next row (loaded one row ago) into the staged layout
-            stage();
-        load_row(row + 2 * gridDim.x);
-        lds_barrier();  // the codes are in and the next row is staged
-        // ---- coalesced stores
-        // (every thread issues every store, the surplus ones at an offset past
-        // the buffer, which drops them: no branch, so the next row's loads
-        // wait for loads only)
-        constexpr int kVec = n * BITS / 8 / 16;
-        const auto rc = rsrc((uint8_t *)a.codes + row * (int64_t)(n * BITS / 8), n * BITS / 8);
-#pragma unroll
-        for (int t0 = 0; t0 < kVec; t0 += kBThreads) {
-            const int t = t0 + tid;
-            __builtin_amdgcn_raw_buffer_store_b128(((const u32x4 *)cst)[t < kVec ? t : kVec - 1], rc,
-                                                   t < kVec ? 16 * t : kDropOffset, 0, 0);
-        }
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rq.scale), rsrc((float *)a.scales + row, 4),
-                                              tid == 0 ? 0 : kDropOffset, 0, 0);
+        lds_barrier();  // the next row is staged
     }
 }
 
@@ -1850,9 +1753,9 @@ hipError_t launch_paley_mfma(const Request &r, const DeviceInfo &dev)
         const int64_t gr = kBOcc * (int64_t)dev.cu_count;
         const int64_t grid = r.rows < gr ? r.rows : gr;
         if (r.x_dtype == kBF16)
-            hipLaunchKernelGGL((paley343_kernel<kBF16, 4, true>), dim3((unsigned)grid), dim3(kBThreads), 0, r.stream, pa);
+            hipLaunchKernelGGL((paley343_kernel<kBF16>), dim3((unsigned)grid), dim3(kBThreads), 0, r.stream, pa);
         else
-            hipLaunchKernelGGL((paley343_kernel<kF16, 4, true>), dim3((unsigned)grid), dim3(kBThreads), 0, r.stream, pa);
+            hipLaunchKernelGGL((paley343_kernel<kF16>), dim3((unsigned)grid), dim3(kBThreads), 0, r.stream, pa);
         return hipGetLastError();
     }
     if (r.op == kDequantInv) {
