@@ -4,8 +4,9 @@ route of [RQ] "旋转量化：大模型低比特量化中的离群值克星" sec
 block size of the [MS] "QuaRot：基于旋转的离群值抑制算法说明" YAML table).
 
 Widths: 48 = 12 x 4, 96 = 12 x 8, 160 = 20 x 8, 688 = 344 x 2, the FFN
-width 11008 = 344 x 32 (Paley over GF(7^3): the block-circulant matrix-core
-kernel) and 10624 = 332 x 32, 11136 = 348 x 32 (prime fields: the dense
+width 11008 = 344 x 32 (Paley over GF(7^3): the matrix-core kernels, the
+forward on a dense chunk layout with a helper wave, rotation only and the
+inverse in block-circulant form) and 10624 = 332 x 32, 11136 = 348 x 32 (prime fields: the dense
 matrix-core kernel).  Inputs are seeded Gaussians
 with outlier channels; expected values come from the oracle only, with the
 tolerances of oracle/parity.py.
@@ -180,3 +181,33 @@ def test_11008_rotate_many_rows_sampled():
     pick = np.array([0, 1, 255, 256, 257, 511, 512, 599])
     xr = O.rotate(O.decode(raw[pick], W.BF16), s, n)
     P.check_rotated(y[pick], xr, what="11008 rotated, sampled rows")
+
+
+def test_11008_tiny_and_zero_rows_across_the_pipeline():
+    # Rows far below binary32's range for qmax / max (down to subnormal
+    # inputs) and zero rows, mixed with ordinary rows over enough rows that
+    # every workgroup of the 11008-wide forward codes several of them: the
+    # codes of a row are written one row later, a third by the product waves
+    # and the rest by the helper wave, each with its own magnification path.
+    n, rows = 11008, 1100
+    rng = np.random.default_rng(11008)
+    raw = rng.standard_normal((rows, n), dtype=np.float32)
+    raw[::7] = 0.0
+    tiny = raw[3::7]
+    tiny[:] = 0.0
+    tiny[0::3, 5] = 1.5 * 2.0 ** -127                    # subnormal
+    tiny[1::3, :] = 2.0 ** -110
+    tiny[2::3, 3] = 2.0 ** -133                          # subnormal
+    tiny[2::3, n // 2] = -3 * 2.0 ** -133
+    raw[3::7] = tiny
+    raw[5::7] = 0.0
+    raw[5::7, 1::97] = 2.0 ** -126 * (1 + np.arange(len(range(1, n, 97))) % 64)
+    x = (raw.view(np.uint32) >> 16).astype(np.uint16)  # exact in bf16
+    s = np.where(np.arange(n) % 5 == 0, -1, 1).astype(np.int8)
+    for bits in (4, 8):
+        tag = f"11008 tiny/zero rows bits={bits}"
+        print(f"[paley] {tag}", flush=True)
+        codes, scales = G.gpu_rotate_quant(x, W.BF16, s, n, bits, W.F32)
+        ref = O.rotate_quant(x, W.BF16, n, s, bits, W.F32)
+        P.check_codes(codes, ref, bits, n, what=tag)
+        P.check_scales(scales, ref, W.F32, what=tag)
