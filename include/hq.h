@@ -43,9 +43,16 @@
  * Conventions shared by every entry point
  *   - Every pointer argument except `stream` is a DEVICE pointer owned by the
  *     caller.  The library allocates no memory and keeps no per-call state;
- *     it caches a few device properties per device.  It is thread-safe.
+ *     it caches a few device properties per device, and, for the full-width
+ *     rotation of order k = 344 (n = 11008) with one scale per row, a
+ *     constant operand table in its own static device memory.  It is
+ *     thread-safe.
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*;
  *     NULL is the null stream).  On return with HQ_OK the work is enqueued.
+ *     One exception: the first such k = 344 rotate + quantise call on a
+ *     device builds that table and waits for the device to be idle before
+ *     it enqueues its work (so that first call cannot be captured into a
+ *     graph); every later call is asynchronous.
  *   - A row is n contiguous elements; rows are contiguous (row stride n).
  *     Head-dim-innermost layouts ([B,H,S,D], [S,H,D]) are just rows of D.
  *   - s: int8 [n]; an element < 0 means "negate", anything else "keep".
