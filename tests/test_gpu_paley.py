@@ -131,19 +131,35 @@ def test_11008_many_rows_sampled(x_dtype, bits):
     P.check_scales(scales[pick], ref, W.F32, what=f"11008 sampled scales")
 
 
-def test_ffn_11008_full_at_full_size_sampled():
+def test_ffn_11008_full_at_full_size_first_and_last_rows():
     # the benchmarked call: 16384 x 11008 from the workload's own generator,
-    # in the launch configuration bench.py times; the oracle checks a sample
-    # of rows spread over every workgroup's range
+    # in the launch configuration bench.py times (512 workgroups, workgroup
+    # b taking rows b, b + 512, ...).  The oracle checks rows 0 .. 1023 and
+    # 15360 .. 16383: the first two and the last two rows of every
+    # workgroup, i.e. each one's pipeline start and end, 2048 rows in all
+    # (every row would cost the oracle minutes).  Then the inverse of the
+    # oracle's codes for the same rows at the benchmarked size (fp32 out).
     w = W.WORKLOADS["ffn_11008_full"]
     data = W.generate("ffn_11008_full", seed=42)
     raw, s = data["x"], data["s"]
-    print(f"[paley] ffn_11008_full {raw.shape}", flush=True)
+    pick = np.r_[0:1024, raw.shape[0] - 1024:raw.shape[0]]
+    print(f"[paley] ffn_11008_full {raw.shape} forward", flush=True)
     codes, scales = G.gpu_rotate_quant(raw, w.x_dtype, s, w.b, w.bits, w.scale_dtype)
-    pick = np.array([0, 1, 255, 256, 4095, 8191, 12000, 16128, 16383])
     ref = O.rotate_quant(raw[pick], w.x_dtype, w.b, s, w.bits, w.scale_dtype)
-    P.check_codes(codes[pick], ref, w.bits, w.n, what="ffn_11008_full sampled codes")
-    P.check_scales(scales[pick], ref, w.scale_dtype, what="ffn_11008_full sampled scales")
+    st = P.check_codes(codes[pick], ref, w.bits, w.n, what="ffn_11008_full codes")
+    P.check_scales(scales[pick], ref, w.scale_dtype, what="ffn_11008_full scales")
+    print(f"[paley] ffn_11008_full codes ok ({st['tie_flips']} tie flips of {st['elements']})", flush=True)
+    # the inverse at the benchmarked size: the oracle's codes for the picked
+    # rows, the GPU's own codes elsewhere (the launch shape is the same)
+    all_codes = codes.copy()
+    all_codes[pick] = ref["codes"]
+    all_scales = scales.copy()
+    all_scales[pick] = ref["scales"]
+    del codes, scales, raw
+    print("[paley] ffn_11008_full inverse", flush=True)
+    y = G.gpu_dequant_inv(all_codes, all_scales, s, w.n, w.bits)
+    y_ref = O.dequant_rotate_inv(ref["codes"], ref["scales"], w.scale_dtype, w.n, s, w.bits, w.n)
+    P.check_inverse(y[pick], y_ref, bf16=False, what="ffn_11008_full inverse f32")
 
 
 @pytest.mark.parametrize("bits,sd", [(4, W.F32), (8, W.F16)])
